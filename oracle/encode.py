@@ -1,0 +1,218 @@
+"""Oracle: a plain round-to-nearest encoder for the four codecs (CPU, NumPy).
+
+Test infrastructure only (see ``oracle/__init__``).  It makes the configs'
+weights; it is not part of the decode contract.
+
+What the pages fix: only the interface (mlx-kquant ``bindings.cpp`` page,
+``quantize`` docstring: float weights whose last dim is a multiple of the
+block size go to uint8 wire bytes; an optional importance vector steers the
+encoder; it is not used here).  The algorithm is not on the pages.
+
+Reading taken (listed in the design doc as reading R5): plain deterministic
+round-to-nearest against the STORED (fp16-rounded) block parameters.  Every
+arithmetic step is IEEE fp32 with round-to-nearest-even, in the order written,
+so that any other implementation that performs the same fp32 operations gets
+the same bytes.  ``rint`` rounds half to even; ``f16()`` is RNE to binary16.
+
+  q8_0 : d = f16(amax/127); q = rint(w/D)                      (D = float(d))
+  q4_0 : d = f16(amax/7);   q = rint(w/D) + 8
+  q4_K : per 32-value sub-block j: lo = min(0, min w), hi = max(w),
+         scale_j = (hi - lo)/15, min_j = -lo;
+         d = f16(max_j scale_j / 63), dmin = f16(max_j min_j / 63);
+         sc_j = rint(scale_j/D), m_j = rint(min_j/DM)  (clamped to 0..63);
+         q = rint((w + DM*m_j) / (D*sc_j))
+  q6_K : per 16-value sub-block j: scale_j = amax_j/31;
+         d = f16(max_j scale_j / 127); sc_j = rint(scale_j/D) (clamped -128..127);
+         q = rint(w/(D*sc_j)) + 32
+Codes are clamped to the codec's range.  Then each code is moved to the
+NEAREST point of the block's decoded grid among {q-1, q, q+1} (distance
+|w - decode(q)| taken in float64; ties go to the lower code), so that every
+code is the nearest grid point.  Where the grid step is zero the code is the
+zero-point code (q8_0: 0, q4_0: 8, q4_K: 0, q6_K: 32).
+
+Pins (tests/test_oracle_encode.py): brute force over every code of the block
+on tiny tensors (the chosen code is a nearest grid point, ties to the lower
+code); q8_0 error <= D/2 per value; the stored d/dmin are the fp16 of the
+stated fp32 quotients; decode of the bytes reproduces the byte totals.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import block_bytes, block_values, row_bytes
+
+F32 = np.float32
+
+
+def _f16_bits(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> binary16 by RNE, returned as the uint16 bit pattern."""
+    return np.asarray(x32, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _f16_value(bits: np.ndarray) -> np.ndarray:
+    return bits.view(np.float16).astype(np.float32)
+
+
+def _div(a, b):
+    """fp32 a/b where b may be zero (callers mask those lanes out)."""
+    with np.errstate(divide="ignore", invalid="ignore"):
+        return (np.asarray(a, F32) / np.asarray(b, F32)).astype(F32)
+
+
+def _nearest(w32, q0, lo, hi, decode):
+    """Move code q0 to the nearest decoded grid point among q0-1, q0, q0+1.
+
+    ``decode(q)`` returns the fp32 decoded value for code array q.  Distance is
+    |w - decode(q)| in float64; on a tie the lower code wins.
+    """
+    w64 = w32.astype(np.float64)
+    best_q = np.clip(q0 - 1, lo, hi)
+    best_e = np.abs(w64 - decode(best_q).astype(np.float64))
+    for delta in (0, 1):
+        cand = np.clip(q0 + delta, lo, hi)
+        e = np.abs(w64 - decode(cand).astype(np.float64))
+        take = e < best_e  # strict: ties keep the lower code
+        best_q = np.where(take, cand, best_q)
+        best_e = np.where(take, e, best_e)
+    return best_q
+
+
+def _rows(w, codec):
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    k = w.shape[-1]
+    bv = block_values(codec)
+    if k % bv:
+        raise ValueError(f"K={k} is not a multiple of {bv} for {codec}")
+    return w.reshape(-1, k), k
+
+
+def encode_q8_0(w: np.ndarray) -> np.ndarray:
+    w2, k = _rows(w, "q8_0")
+    x = w2.reshape(w2.shape[0], k // 32, 32)
+    amax = np.max(np.abs(x), axis=-1)
+    dbits = _f16_bits(_div(amax, F32(127)))
+    D = _f16_value(dbits)[..., None]
+    q0 = np.clip(np.rint(_div(x, D)), -128, 127)
+    q0 = np.where(D == 0, 0, q0).astype(np.int64)
+
+    def dec(q):
+        return (D * q.astype(F32)).astype(F32)
+
+    q = np.where(D == 0, 0, _nearest(x, q0, -128, 127, dec))
+    out = np.empty(x.shape[:-1] + (34,), dtype=np.uint8)
+    out[..., 0] = dbits & 255
+    out[..., 1] = dbits >> 8
+    out[..., 2:] = (q & 255).astype(np.uint8)
+    return out.reshape(w.shape[:-1] + (row_bytes("q8_0", k),))
+
+
+def encode_q4_0(w: np.ndarray) -> np.ndarray:
+    w2, k = _rows(w, "q4_0")
+    x = w2.reshape(w2.shape[0], k // 32, 32)
+    amax = np.max(np.abs(x), axis=-1)
+    dbits = _f16_bits(_div(amax, F32(7)))
+    D = _f16_value(dbits)[..., None]
+    q0 = np.clip(np.rint(_div(x, D)) + 8, 0, 15)
+    q0 = np.where(D == 0, 8, q0).astype(np.int64)
+
+    def dec(q):
+        return (D * (q - 8).astype(F32)).astype(F32)
+
+    q = np.where(D == 0, 8, _nearest(x, q0, 0, 15, dec))
+    out = np.empty(x.shape[:-1] + (18,), dtype=np.uint8)
+    out[..., 0] = dbits & 255
+    out[..., 1] = dbits >> 8
+    out[..., 2:] = (q[..., :16] | (q[..., 16:] << 4)).astype(np.uint8)
+    return out.reshape(w.shape[:-1] + (row_bytes("q4_0", k),))
+
+
+def encode_q4_k(w: np.ndarray) -> np.ndarray:
+    w2, k = _rows(w, "q4_k")
+    x = w2.reshape(w2.shape[0], k // 256, 8, 32)
+    lo = np.minimum(F32(0), np.min(x, axis=-1))  # [n, nb, 8]
+    hi = np.max(x, axis=-1)
+    scale = _div((hi - lo).astype(F32), F32(15))
+    mins = (-lo).astype(F32)
+    dbits = _f16_bits(_div(np.max(scale, axis=-1), F32(63)))
+    mbits = _f16_bits(_div(np.max(mins, axis=-1), F32(63)))
+    D = _f16_value(dbits)[..., None]  # [n, nb, 1]
+    DM = _f16_value(mbits)[..., None]
+    sc = np.where(D > 0, np.clip(np.rint(_div(scale, D)), 0, 63), 0).astype(np.int64)
+    m = np.where(DM > 0, np.clip(np.rint(_div(mins, DM)), 0, 63), 0).astype(np.int64)
+    S = (D * sc.astype(F32)).astype(F32)[..., None]  # exact: 11 x 6 bits
+    MN = (DM * m.astype(F32)).astype(F32)[..., None]
+    q0 = np.clip(np.rint(_div((x + MN).astype(F32), S)), 0, 15)
+    q0 = np.where(S == 0, 0, q0).astype(np.int64)
+
+    def dec(q):
+        return ((S * q.astype(F32)).astype(F32) - MN).astype(F32)
+
+    q = np.where(S == 0, 0, _nearest(x, q0, 0, 15, dec))  # [n, nb, 8, 32]
+
+    out = np.zeros(x.shape[:2] + (144,), dtype=np.uint8)
+    out[..., 0] = dbits & 255
+    out[..., 1] = dbits >> 8
+    out[..., 2] = mbits & 255
+    out[..., 3] = mbits >> 8
+    s = np.zeros(x.shape[:2] + (12,), dtype=np.int64)
+    for j in range(4):
+        s[..., j] = (sc[..., j] & 63) | ((sc[..., j + 4] >> 4) << 6)
+        s[..., j + 4] = (m[..., j] & 63) | ((m[..., j + 4] >> 4) << 6)
+        s[..., j + 8] = (sc[..., j + 4] & 15) | ((m[..., j + 4] & 15) << 4)
+    out[..., 4:16] = s.astype(np.uint8)
+    for p in range(4):
+        out[..., 16 + 32 * p: 16 + 32 * p + 32] = (q[..., 2 * p, :] | (q[..., 2 * p + 1, :] << 4)).astype(np.uint8)
+    return out.reshape(w.shape[:-1] + (row_bytes("q4_k", k),))
+
+
+def encode_q6_k(w: np.ndarray) -> np.ndarray:
+    w2, k = _rows(w, "q6_k")
+    x = w2.reshape(w2.shape[0], k // 256, 16, 16)
+    amax = np.max(np.abs(x), axis=-1)  # [n, nb, 16]
+    scale = _div(amax, F32(31))
+    dbits = _f16_bits(_div(np.max(scale, axis=-1), F32(127)))
+    D = _f16_value(dbits)[..., None]
+    sc = np.where(D > 0, np.clip(np.rint(_div(scale, D)), -128, 127), 0).astype(np.int64)
+    S = (D * sc.astype(F32)).astype(F32)[..., None]  # exact: 11 x 8 bits
+    q0 = np.clip(np.rint(_div(x, S)) + 32, 0, 63)
+    q0 = np.where(S == 0, 32, q0).astype(np.int64)
+
+    def dec(q):
+        return (S * (q - 32).astype(F32)).astype(F32)
+
+    q = np.where(S == 0, 32, _nearest(x, q0, 0, 63, dec)).reshape(x.shape[:2] + (256,))
+
+    out = np.zeros(x.shape[:2] + (210,), dtype=np.uint8)
+    ql = np.zeros(x.shape[:2] + (128,), dtype=np.int64)
+    qh = np.zeros(x.shape[:2] + (64,), dtype=np.int64)
+    for v in range(256):
+        h, r = divmod(v, 128)
+        c, l = divmod(r, 32)
+        low4 = q[..., v] & 15
+        high2 = q[..., v] >> 4
+        idx = 64 * h + l + 32 * (c & 1)
+        ql[..., idx] |= low4 if c < 2 else (low4 << 4)
+        qh[..., 32 * h + l] |= high2 << (2 * c)
+    out[..., 0:128] = ql.astype(np.uint8)
+    out[..., 128:192] = qh.astype(np.uint8)
+    out[..., 192:208] = (sc & 255).astype(np.uint8)
+    out[..., 208] = dbits & 255
+    out[..., 209] = dbits >> 8
+    return out.reshape(w.shape[:-1] + (row_bytes("q6_k", k),))
+
+
+ENCODERS = {
+    "q8_0": encode_q8_0,
+    "q4_0": encode_q4_0,
+    "q4_k": encode_q4_k,
+    "q6_k": encode_q6_k,
+}
+
+
+def quantize(codec: str, w: np.ndarray) -> np.ndarray:
+    """float weights [..., K] -> uint8 wire bytes [..., row_bytes] (reading R5)."""
+    return ENCODERS[codec](w)
+
+
+assert all(block_bytes(c) == b for c, b in (("q4_k", 144), ("q6_k", 210), ("q8_0", 34), ("q4_0", 18)))

@@ -1,0 +1,90 @@
+"""Oracle: quantized matmul, expert tile map and expert-sorted gather (CPU, NumPy).
+
+Test infrastructure only (see ``oracle/__init__``).
+
+Definitions followed
+  * mlx-kquant ``bindings.cpp`` page, ``quantized_matmul`` docstring: the
+    result is ``x @ dequant(w)`` with ``w`` laid out [N, K] (transpose=True);
+    nuvec-core ``quantized.rs`` page, ``quantized_matmul``: ``x`` times the
+    transposed dequantized weight.  Here: ``y[m, n] = sum_k x[m, k] * W[n, k]``
+    with W the exact dequantized values, accumulated in float64.  Both
+    operands are exact in float64 (x is fp16, W is an fp32 number), so the
+    only error is float64 accumulation.
+  * mlx-kquant ``bindings.cpp`` page, ``expert_tile_map`` docstring: from
+    expert ids sorted ascending, tile each expert's segment into 64-row tiles
+    (expert, row_start, num_rows); only the last tile of a segment may be
+    partial; a count of valid tiles.  Tile order is unspecified there; this
+    oracle emits expert-major, ascending row_start.
+  * mlx-kquant ``bindings.cpp`` page, ``gather_qmm_seg`` docstring: for each
+    valid tile, rows [row_start, row_start+num_rows) of the expert-sorted x
+    times expert ``e``'s dequantized weight, transposed; rows no tile covers
+    are left unwritten.  hanzo-ml ``quantized/mod.rs`` page,
+    ``moe_grouped_per_expert``: group routed rows by expert, one product per
+    expert, scatter the rows back.  nuvec-core ``quantized.rs`` page,
+    ``gather_qmm``: output batch i is x[lhs[i]] times dequantize(w)[rhs[i]]
+    transposed.
+
+Pins (tests/test_oracle_matmul.py): exact rational dot products (Python
+``fractions``) on tiny shapes; one-hot x rows return weight columns exactly;
+tile-map invariants by brute force plus a hand example; the gather equals a
+per-row loop of the nuvec gather definition and reduces to qmm with one expert.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from .codecs import dequantize
+
+TILE_ROWS = 64
+
+
+def matmul_f64(x: np.ndarray, wdeq: np.ndarray) -> np.ndarray:
+    """y = x @ wdeq.T in float64 (x [M, K], wdeq [N, K])."""
+    return np.asarray(x, dtype=np.float64) @ np.asarray(wdeq, dtype=np.float64).T
+
+
+def qmatmul(codec: str, w: np.ndarray, k: int, x: np.ndarray) -> np.ndarray:
+    """Reference for kq_qmv and kq_qmm: x [M, K] (fp16 values) times dequant(w) [N, K], transposed."""
+    return matmul_f64(x, dequantize(codec, w, k, np.float32))
+
+
+def expert_tile_map(sorted_ids: np.ndarray, n_experts: int):
+    """Tiles (expert, row_start, num_rows) of <= 64 rows per expert segment.
+
+    For each expert e with c_e > 0 rows starting at s_e, tiles
+    (e, s_e + 64 t, min(64, c_e - 64 t)) for t < ceil(c_e / 64).  Ids outside
+    [0, n_experts) get no tile.  Returns (tiles [T, 3] uint32, T).
+    """
+    ids = np.asarray(sorted_ids, dtype=np.int64)
+    tiles = []
+    for e in range(n_experts):
+        rows = np.nonzero(ids == e)[0]
+        if rows.size == 0:
+            continue
+        s, c = int(rows[0]), int(rows.size)
+        for t in range(0, c, TILE_ROWS):
+            tiles.append((e, s + t, min(TILE_ROWS, c - t)))
+    arr = np.array(tiles, dtype=np.uint32).reshape(-1, 3)
+    return arr, arr.shape[0]
+
+
+def tile_map_capacity(rows: int, n_experts: int) -> int:
+    """An upper bound on the tile count: ceil(rows/64) + min(n_experts, rows).
+
+    sum_e ceil(c_e/64) <= sum_e (c_e/64 + 1) over the non-empty experts.
+    """
+    return -(-rows // TILE_ROWS) + min(n_experts, rows)
+
+
+def gather_qmm_seg(codec: str, w: np.ndarray, k: int, x: np.ndarray, tiles: np.ndarray, fill=np.nan) -> np.ndarray:
+    """Reference for kq_gather_qmm_seg: per tile, x rows times its expert's weight, transposed.
+
+    w: [E, N, row_bytes]; x: [rows, K] expert-sorted; tiles: [T, 3].
+    Rows no tile covers hold ``fill`` (they are unwritten by the contract).
+    """
+    n = w.shape[1]
+    y = np.full((x.shape[0], n), fill, dtype=np.float64)
+    for e, s, c in np.asarray(tiles, dtype=np.int64):
+        y[s:s + c] = qmatmul(codec, w[e], k, x[s:s + c])
+    return y

@@ -1,0 +1,112 @@
+"""Pins for the oracle's encoder (reading R5: round to nearest against the stored parameters).
+
+  * Brute force: for every value, decode the block with EVERY code of the
+    codec and check the chosen code is a nearest grid point, ties to the
+    lower code.
+  * q8_0 closed form: |w - y| <= D/2 for every value (D the stored fp16 d).
+  * Zero blocks encode to the zero-point code and decode to exact zeros.
+  * Decoding then re-encoding a q8_0 / q4_0 tensor gives the same bytes.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import codecs, encode
+
+
+def _all_codes_block(codec, blk, c):
+    """A copy of the blocks with every code replaced by code c (packed per the layout reading)."""
+    b = blk.copy()
+    if codec == "q8_0":
+        b[..., 2:34] = np.uint8(c & 255)
+    elif codec == "q4_0":
+        b[..., 2:18] = np.uint8(c | (c << 4))
+    elif codec == "q4_k":
+        b[..., 16:144] = np.uint8(c | (c << 4))
+    elif codec == "q6_k":
+        lo, h2 = c & 15, c >> 4
+        b[..., 0:128] = np.uint8(lo | (lo << 4))
+        b[..., 128:192] = np.uint8(h2 | (h2 << 2) | (h2 << 4) | (h2 << 6))
+    return b
+
+
+CODE_RANGE = {"q8_0": range(-128, 128), "q4_0": range(16), "q4_k": range(16), "q6_k": range(64)}
+
+
+def _codes(codec, blk):
+    if codec == "q8_0":
+        return codecs.fields_q8_0(blk)[1].reshape(blk.shape[0], -1)
+    if codec == "q4_0":
+        return codecs.fields_q4_0(blk)[1].reshape(blk.shape[0], -1)
+    if codec == "q4_k":
+        return codecs.fields_q4_k(blk)[4].reshape(blk.shape[0], -1)
+    return codecs.fields_q6_k(blk)[2].reshape(blk.shape[0], -1)
+
+
+@pytest.mark.parametrize("codec", codecs.CODECS)
+@pytest.mark.parametrize("dist", ["normal", "t5", "positive", "negative"])
+def test_chosen_code_is_nearest_grid_point(codec, dist):
+    rng = np.random.default_rng(hash((codec, dist)) % 2**32)
+    k = codecs.block_values(codec)
+    n = 6
+    if dist == "normal":
+        w = rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02)
+    elif dist == "t5":
+        w = (rng.standard_t(5, (n, k)) * 0.02).astype(np.float32)
+    elif dist == "positive":
+        w = rng.uniform(0.01, 1.0, (n, k)).astype(np.float32)
+    else:
+        w = -rng.uniform(0.01, 1.0, (n, k)).astype(np.float32)
+    wq = encode.quantize(codec, w)
+    blk = wq.reshape(n, 1, -1)
+    chosen = _codes(codec, blk)
+    grid = []
+    codes = list(CODE_RANGE[codec])
+    for c in codes:
+        grid.append(codecs.dequantize(codec, _all_codes_block(codec, blk, c).reshape(n, -1), k).astype(np.float64))
+    grid = np.stack(grid, axis=-1)  # [n, k, ncodes]
+    err = np.abs(w.astype(np.float64)[..., None] - grid)
+    best = np.array(codes)[np.argmin(err, axis=-1)]  # argmin takes the first = lowest code on ties
+    assert np.array_equal(chosen, best)
+    # and the decoded tensor is the grid point of the chosen code
+    y = codecs.dequantize(codec, wq, k).astype(np.float64)
+    assert np.array_equal(y, np.take_along_axis(grid, (chosen - codes[0])[..., None], -1)[..., 0])
+
+
+def test_q8_0_error_bound_half_step():
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((32, 512)).astype(np.float32) * np.float32(0.02)
+    wq = encode.quantize("q8_0", w)
+    y = codecs.dequantize("q8_0", wq, 512).astype(np.float64)
+    d = codecs.fields_q8_0(wq.reshape(32, 16, 34))[0]  # [32, 16]
+    D = np.repeat(d, 32, axis=1)
+    assert np.all(np.abs(w - y) <= D / 2)
+
+
+@pytest.mark.parametrize("codec", codecs.CODECS)
+def test_zero_block(codec):
+    k = codecs.block_values(codec)
+    wq = encode.quantize(codec, np.zeros((2, k), np.float32))
+    y = codecs.dequantize(codec, wq, k)
+    assert np.all(y == 0) and not np.any(np.signbit(y))
+
+
+@pytest.mark.parametrize("codec", ["q8_0", "q4_0"])
+def test_decode_encode_fixed_point(codec):
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((8, 256)).astype(np.float32)
+    wq = encode.quantize(codec, w)
+    y = codecs.dequantize(codec, wq, 256)
+    assert np.array_equal(encode.quantize(codec, y), wq)
+
+
+@pytest.mark.parametrize("codec", codecs.CODECS)
+def test_round_trip_error_small_relative_to_block(codec):
+    rng = np.random.default_rng(9)
+    k = 4 * codecs.block_values(codec)
+    w = rng.standard_normal((16, k)).astype(np.float32) * np.float32(0.02)
+    y = codecs.dequantize(codec, encode.quantize(codec, w), k)
+    bits = codecs.GEOMETRY[codec][1]
+    rel = np.sqrt(np.mean((w - y) ** 2)) / np.sqrt(np.mean(w ** 2))
+    # uniform-noise rms of a b-bit grid spanning roughly +-3 sigma: ~ 6 / 2^b / sqrt(12)
+    assert rel < 2.5 * 6 / 2 ** bits / np.sqrt(12)

@@ -1,0 +1,141 @@
+"""Pins for the oracle's fp64 quantized matmul, tile map and expert-sorted gather."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from gguf_quant_matmul_amd import workloads
+from oracle import codecs, encode, matmul
+
+
+@pytest.mark.parametrize("codec", codecs.CODECS)
+def test_qmatmul_matches_exact_rational(codec):
+    rng = np.random.default_rng(21)
+    m, n, k = 3, 4, 256
+    w = rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02)
+    wq = encode.quantize(codec, w)
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    y = matmul.qmatmul(codec, wq, k, x)
+    wd = codecs.dequantize(codec, wq, k)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(float(x[i, t])) * Fraction(float(wd[j, t])) for t in range(k))
+            assert abs(y[i, j] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+@pytest.mark.parametrize("codec", codecs.CODECS)
+def test_one_hot_rows_return_weight_columns(codec):
+    rng = np.random.default_rng(22)
+    n, k = 5, 512
+    wq = encode.quantize(codec, rng.standard_normal((n, k)).astype(np.float32))
+    cols = [0, 31, 32, 255, 256, 511]
+    x = np.zeros((len(cols), k), np.float16)
+    for i, c in enumerate(cols):
+        x[i, c] = 1
+    y = matmul.qmatmul(codec, wq, k, x)
+    wd = codecs.dequantize(codec, wq, k)
+    for i, c in enumerate(cols):
+        assert np.array_equal(y[i], wd[:, c].astype(np.float64))
+
+
+def test_tile_map_hand_example():
+    ids = np.array([0] * 70 + [2] * 5 + [3] * 128, dtype=np.uint32)
+    tiles, count = matmul.expert_tile_map(ids, 4)
+    assert count == 5
+    assert tiles.tolist() == [[0, 0, 64], [0, 64, 6], [2, 70, 5], [3, 75, 64], [3, 139, 64]]
+    assert count <= matmul.tile_map_capacity(ids.size, 4)
+
+
+def _check_invariants(ids, n_experts, tiles, count):
+    ids = np.asarray(ids, dtype=np.int64)
+    covered = np.zeros(ids.size, np.int64)
+    last_of_expert = {}
+    for e, s, c in tiles[:count].astype(np.int64):
+        assert 1 <= c <= 64
+        assert np.all(ids[s:s + c] == e), "tile spans experts or rows"
+        covered[s:s + c] += 1
+        last_of_expert.setdefault(e, []).append((s, c))
+    valid = (ids >= 0) & (ids < n_experts)
+    assert np.all(covered[valid] == 1) and np.all(covered[~valid] == 0)
+    for e, lst in last_of_expert.items():
+        lst.sort()
+        assert all(c == 64 for s, c in lst[:-1]), "only the last tile of a segment may be partial"
+    counts = np.bincount(ids[valid], minlength=n_experts)
+    assert count == int(np.sum((counts + 63) // 64))
+    assert count <= matmul.tile_map_capacity(ids.size, n_experts)
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_tile_map_invariants_random(seed):
+    rng = np.random.default_rng(seed)
+    e = int(rng.integers(1, 200))
+    rows = int(rng.integers(0, 3000))
+    ids = np.sort(rng.integers(0, e, rows)) if seed % 2 else np.sort(rng.zipf(1.5, rows) % e)
+    tiles, count = matmul.expert_tile_map(ids, e)
+    _check_invariants(ids, e, tiles, count)
+
+
+def test_tile_map_ids_out_of_range_get_no_tile():
+    ids = np.array([0, 0, 1, 5, 5, 9], dtype=np.uint32)
+    tiles, count = matmul.expert_tile_map(ids, 4)
+    assert tiles.tolist() == [[0, 0, 2], [1, 2, 1]]
+    _check_invariants(ids, 4, tiles, count)
+
+
+def test_tile_map_capacity_is_tight_bound():
+    # Capacity is reached: every expert holds 64t+1 rows.
+    e = 8
+    ids = np.repeat(np.arange(e), 65)
+    tiles, count = matmul.expert_tile_map(ids, e)
+    assert count == 2 * e
+    assert matmul.tile_map_capacity(ids.size, e) >= count
+
+
+def test_moe_workload_routing_and_tiles():
+    cfg = workloads.CFG5_MOE_SEG
+    r = workloads.routing(cfg.seed, cfg.tokens, cfg.top_k, cfg.n_experts)
+    assert r.sorted_ids.size == 4096
+    assert np.all(np.diff(r.sorted_ids.astype(np.int64)) >= 0)
+    # every token routes to 8 distinct experts
+    assert all(len(set(row)) == 8 for row in r.ids.tolist())
+    tiles, count = matmul.expert_tile_map(r.sorted_ids, cfg.n_experts)
+    _check_invariants(r.sorted_ids, cfg.n_experts, tiles, count)
+    per_expert = np.bincount(r.sorted_ids, minlength=64)
+    assert count == int(np.sum((per_expert + 63) // 64))
+    # The recipe reproduces the count derived for this workload when it was specified:
+    # 92 tiles, 48..80 rows per expert.
+    assert count == 92 and per_expert.min() == 48 and per_expert.max() == 80
+
+
+def _gather_rowwise(codec, w, k, x, ids, n_experts):
+    """nuvec-core quantized.rs, gather_qmm: output row i = x[i] . dequantize(w)[ids[i]]^T, one row at a time."""
+    y = np.full((x.shape[0], w.shape[1]), np.nan)
+    for i in range(x.shape[0]):
+        if ids[i] < n_experts:
+            wd = codecs.dequantize(codec, w[ids[i]], k).astype(np.float64)
+            y[i] = wd @ x[i].astype(np.float64)
+    return y
+
+
+def test_gather_seg_equals_rowwise_gather():
+    rng = np.random.default_rng(31)
+    e, n, k = 5, 24, 256
+    w = encode.quantize("q4_k", rng.standard_normal((e, n, k)).astype(np.float32) * np.float32(0.02))
+    ids = np.sort(rng.integers(0, e, 150)).astype(np.uint32)
+    x = rng.standard_normal((150, k)).astype(np.float16)
+    tiles, count = matmul.expert_tile_map(ids, e)
+    y = matmul.gather_qmm_seg("q4_k", w, k, x, tiles[:count])
+    ref = _gather_rowwise("q4_k", w, k, x, ids, e)
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_gather_seg_one_expert_is_qmm():
+    rng = np.random.default_rng(32)
+    n, k = 16, 512
+    w = encode.quantize("q6_k", rng.standard_normal((1, n, k)).astype(np.float32))
+    x = rng.standard_normal((130, k)).astype(np.float16)
+    tiles, count = matmul.expert_tile_map(np.zeros(130, np.uint32), 1)
+    assert count == 3
+    y = matmul.gather_qmm_seg("q6_k", w, k, x, tiles[:count])
+    assert np.array_equal(y, matmul.qmatmul("q6_k", w[0], k, x))
