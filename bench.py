@@ -1,0 +1,314 @@
+#!/usr/bin/env python3
+"""Benchmark of the kq hot path on one MI355X: q4_K decode GEMV (kq_qmv) and
+q4_K prefill GEMM (kq_qmm), plus every other row of the path measured once.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-rows] [--no-cpu]
+
+One step = one cold q4_K GEMV (4096 x 4096, one activation row, float32 out;
+its weight copy is one of 64 rotating copies, 604 MB in all, so it is not in
+the 256 MB Infinity Cache) followed by one q4_K GEMM (M=2048, N=14336,
+K=4096, float16 out).  Kernel durations come from HIP events recorded on the
+stream the kernels run on (torch's current stream) around each launch.
+
+Prints ONE JSON line.  ``value`` is the GEMV's algorithmic HBM rate (wire
+bytes + activations + outputs per launch / mean launch duration).
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "q4_K qmv GB/s (% of HBM peak); q4_K qmm TFLOP/s (% of f16 MFMA peak)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA, published
+COLD_BYTES = 512 << 20         # rotate weight copies until this much is touched (> 256 MB MALL)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=64)
+    p.add_argument("--warmup", type=int, default=8)
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
+    p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    return p.parse_args()
+
+
+class Timer:
+    """Per-launch HIP events on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def run(self, fn):
+        s, e = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+
+
+def gpu_weights(torch, kq, codec, seed, n, k, dist):
+    from gguf_quant_matmul_amd import workloads as W
+
+    wf = torch.from_numpy(W.weight_rows(seed, n, k, dist)).cuda()
+    wq = torch.empty((n, kq.kq_row_bytes(codec, k)), dtype=torch.uint8, device="cuda")
+    kq.kq_quantize(codec, wf, wq)
+    del wf
+    return wq
+
+
+def copies_for(nbytes):
+    return max(1, min(64, math.ceil(COLD_BYTES / nbytes)))
+
+
+def measure_rows(torch, kq):
+    """Each remaining row of the path once, cold where the data would fit the MALL."""
+    from gguf_quant_matmul_amd import workloads as W
+
+    rows = []
+
+    def gemv_row(cfg, reps=None):
+        wq = gpu_weights(torch, kq, cfg.codec, cfg.seed, cfg.n, cfg.k, cfg.dist)
+        nb = wq.numel()
+        nc = copies_for(nb)
+        ws = [wq] + [wq.clone() for _ in range(nc - 1)]
+        x = torch.from_numpy(W.gemv_activations(cfg)).cuda()
+        y = torch.empty((cfg.m, cfg.n), dtype=torch.float32, device="cuda")
+        for i in range(min(nc, 4)):
+            kq.kq_qmv(cfg.codec, ws[i], cfg.n, cfg.k, x, y)
+        t = Timer(torch)
+        for i in range(reps or max(nc, 8)):
+            t.run(lambda i=i: kq.kq_qmv(cfg.codec, ws[i % nc], cfg.n, cfg.k, x, y))
+        ms = t.mean_ms()
+        alg = nb + x.numel() * 2 + y.numel() * 4
+        gbs = alg / ms / 1e6
+        rows.append({"row": "kq_qmv", "workload": cfg.name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 3), "alg_bytes": alg, "copies": nc})
+        del ws, wq
+        torch.cuda.empty_cache()
+
+    for cfg in W.CFG2_GEMV:
+        gemv_row(cfg)
+    gemv_row(W.CFG3_Q6K_LMHEAD, reps=8)
+
+    # MoE: tile map + expert-segment GEMM
+    cfg = W.CFG5_MOE_SEG
+    wq = gpu_weights(torch, kq, cfg.codec, cfg.seed, cfg.n_experts * cfg.n, cfg.k, "normal")
+    nc = copies_for(wq.numel())
+    ws = [wq] + [wq.clone() for _ in range(nc - 1)]
+    r = W.routing(cfg.seed, cfg.tokens, cfg.top_k, cfg.n_experts)
+    x = torch.from_numpy(W.activations(cfg.seed, cfg.tokens, cfg.k)[r.token_of_row]).cuda()
+    ids = torch.from_numpy(r.sorted_ids.view(np.int32)).cuda()
+    cap = kq.kq_expert_tile_map_capacity(ids.numel(), cfg.n_experts)
+    map_ = torch.empty((cap, 3), dtype=torch.int32, device="cuda")
+    counts = torch.empty((1,), dtype=torch.int32, device="cuda")
+    y = torch.empty((x.shape[0], cfg.n), dtype=torch.float16, device="cuda")
+    tm, sg = Timer(torch), Timer(torch)
+    for i in range(2 + 8):
+        fm = lambda: kq.kq_expert_tile_map(ids, cfg.n_experts, map_, counts)  # noqa: E731
+        fs = lambda i=i: kq.kq_gather_qmm_seg(cfg.codec, ws[i % nc], cfg.n_experts, cfg.n, cfg.k, x, map_, counts, y)  # noqa: E731
+        if i < 2:
+            fm(), fs()
+        else:
+            tm.run(fm)
+            sg.run(fs)
+    ms_map, ms_seg = tm.mean_ms(), sg.mean_ms()
+    alg = wq.numel() + x.numel() * 2 + y.numel() * 2
+    flop = 2 * x.shape[0] * cfg.n * cfg.k
+    rows.append({"row": "kq_expert_tile_map", "workload": cfg.name, "us": round(ms_map * 1e3, 2)})
+    rows.append({"row": "kq_gather_qmm_seg", "workload": cfg.name, "us": round(ms_seg * 1e3, 2),
+                 "GB/s": round(alg / ms_seg / 1e6, 1), "hbm_frac": round(alg / ms_seg / 1e6 / HBM_PEAK_GBS, 3),
+                 "TFLOP/s": round(flop / ms_seg / 1e9, 1),
+                 "mfma_frac": round(flop / ms_seg / 1e9 / MFMA_F16_PEAK_TFLOPS, 3), "alg_bytes": alg, "copies": nc})
+    del ws, wq
+    torch.cuda.empty_cache()
+
+    # dequantize (q4_K 4096 x 4096 -> float16)
+    c1 = W.CFG1_Q4K_GEMV
+    wq = gpu_weights(torch, kq, c1.codec, c1.seed, c1.n, c1.k, c1.dist)
+    out = torch.empty((c1.n, c1.k), dtype=torch.float16, device="cuda")
+    nc = copies_for(wq.numel() + out.numel() * 2)
+    ws = [wq] + [wq.clone() for _ in range(nc - 1)]
+    kq.kq_dequantize(c1.codec, wq, c1.k, out)
+    t = Timer(torch)
+    for i in range(nc):
+        t.run(lambda i=i: kq.kq_dequantize(c1.codec, ws[i], c1.k, out))
+    ms = t.mean_ms()
+    alg = wq.numel() + out.numel() * 2
+    rows.append({"row": "kq_dequantize", "workload": "q4_K 4096x4096 -> f16", "us": round(ms * 1e3, 2),
+                 "GB/s": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3),
+                 "alg_bytes": alg})
+    del ws, wq, out
+    torch.cuda.empty_cache()
+    return rows
+
+
+def cpu_baseline():
+    """The oracle as it stands, on a bounded sample of the two workloads, on this host."""
+    from gguf_quant_matmul_amd import workloads as W
+    from oracle import codecs, encode, matmul
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
+    except Exception:  # pragma: no cover
+        blas = 1
+    c1, c4 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM
+    # GEMV: 1024 of the 4096 weight rows, repeated for ~10 s
+    rows = 1024
+    wq = encode.quantize(c1.codec, W.weight_rows(c1.seed, c1.n, c1.k, c1.dist, rows=np.arange(rows)))
+    x = W.gemv_activations(c1)
+    reps, t0 = 0, time.perf_counter()
+    while reps < 2 or time.perf_counter() - t0 < 10.0:
+        matmul.qmatmul(c1.codec, wq, c1.k, x)
+        reps += 1
+    dt = (time.perf_counter() - t0) / reps
+    gbs = (wq.nbytes + x.nbytes + rows * 4) / dt / 1e9
+    # GEMM: 128 of the 14336 weight rows x all 2048 activation rows
+    nr = 128
+    wq4 = encode.quantize(c4.codec, W.weight_rows(c4.seed, c4.n, c4.k, c4.dist, rows=np.arange(nr)))
+    x4 = W.gemv_activations(c4)
+    t0 = time.perf_counter()
+    matmul.qmatmul(c4.codec, wq4, c4.k, x4)
+    dt4 = time.perf_counter() - t0
+    tflops = 2 * c4.m * nr * c4.k / dt4 / 1e12
+    return {
+        "value": round(gbs, 3), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+        "sample": f"q4_K GEMV on {rows} of 4096 weight rows (K=4096, M=1), NumPy decode + float64 matmul, "
+                  f"{reps} reps, {dt * 1e3:.0f} ms each; threads = BLAS threads (decode is single-threaded NumPy)",
+        "qmm": {"value": round(tflops, 5), "unit": "TFLOP/s",
+                "sample": f"q4_K GEMM on {nr} of 14336 weight rows x 2048 activation rows, {dt4:.1f} s"},
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: the kq path is a single-GPU kernel library "
+              "(its multi-GPU sharding is a design note, not built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from gguf_quant_matmul_amd import kq
+    from gguf_quant_matmul_amd import workloads as W
+
+    assert torch.cuda.is_available(), "needs a GPU"
+    dev_name = torch.cuda.get_device_properties(0).name
+    log(f"device: {dev_name}")
+
+    c1, c4 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM
+    log("preparing inputs (weights drawn on the host, encoded on the GPU by kq_quantize)")
+    w1 = gpu_weights(torch, kq, c1.codec, c1.seed, c1.n, c1.k, c1.dist)
+    n_cold = 64
+    w1s = [w1] + [w1.clone() for _ in range(n_cold - 1)]
+    x1 = torch.from_numpy(W.gemv_activations(c1)).cuda()
+    y1 = torch.empty((1, c1.n), dtype=torch.float32, device="cuda")
+    w4 = gpu_weights(torch, kq, c4.codec, c4.seed, c4.n, c4.k, c4.dist)
+    x4 = torch.from_numpy(W.gemv_activations(c4)).cuda()
+    y4 = torch.empty((c4.m, c4.n), dtype=torch.float16, device="cuda")
+
+    alg1 = w1.numel() + x1.numel() * 2 + y1.numel() * 4           # 9,461,760 B
+    flop4 = 2 * c4.m * c4.n * c4.k                                 # 240,518,168,576
+    alg4 = w4.numel() + x4.numel() * 2 + y4.numel() * 2
+
+    def step(i, t1=None, t4=None):
+        f1 = lambda: kq.kq_qmv(c1.codec, w1s[i % n_cold], c1.n, c1.k, x1, y1)  # noqa: E731
+        f4 = lambda: kq.kq_qmm(c4.codec, w4, c4.n, c4.k, x4, y4)  # noqa: E731
+        (t1.run(f1) if t1 else f1())
+        (t4.run(f4) if t4 else f4())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t1, t4 = Timer(torch), Timer(torch)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i, t1, t4)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms1, ms4 = t1.mean_ms(), t4.mean_ms()
+
+    # back-to-back stream rate over the 64 cold copies (what a decode loop sees)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(n_cold):
+        kq.kq_qmv(c1.codec, w1s[i], c1.n, c1.k, x1, y1)
+    e.record()
+    torch.cuda.synchronize()
+    stream_ms = s.elapsed_time(e) / n_cold
+
+    gbs = alg1 / ms1 / 1e6
+    tflops = flop4 / ms4 / 1e9
+    out = {
+        "metric": METRIC,
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded; weights drawn on the host, q4_K-encoded on the GPU)",
+        "config": {
+            "workload": "q4_K decode GEMV N=4096 K=4096 M=1 f32-out, cold (64 rotating weight copies); "
+                        "q4_K prefill GEMM M=2048 N=14336 K=4096 f16-out",
+            "global_batch": 1,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "kq_qmv q4_K (qmv_kernel<12,1,false>)", "alg_bytes_per_launch": alg1,
+            "mean_launch_us": round(ms1 * 1e3, 3),
+        },
+        "qmm": {
+            "value": round(tflops, 1), "unit": "TFLOP/s", "mean_launch_us": round(ms4 * 1e3, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                         "kernel": "kq_qmm q4_K (qmm_kernel)", "alg_flop_per_launch": flop4,
+                         "alg_bytes_per_launch": alg4},
+        },
+        "qmv_stream_GBps": round(alg1 / stream_ms / 1e6, 1),
+        "qmv_stream_us": round(stream_ms * 1e3, 3),
+        "device": dev_name,
+    }
+    del w1s, w1, w4, x4, y4
+    torch.cuda.empty_cache()
+    if not args.no_rows:
+        log("measuring the other rows")
+        out["rows"] = measure_rows(torch, kq)
+    if not args.no_cpu:
+        log("timing the oracle on the host")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,235 @@
+// C ABI of libkq: argument validation and kernel dispatch.
+//
+// Every entry point validates on the host and returns before any HIP call
+// when an argument is wrong (outputs untouched); otherwise it enqueues the
+// kernels on the caller's stream and returns without synchronizing.  The
+// error style mirrors the "[module.op] message" invalid-argument text of the
+// mlx-kquant bindings.cpp page and the "op: msg" errors of nuvec-core's
+// quantized.rs page.
+#include <ctype.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "kq_internal.h"
+#include "../../include/kq.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* op, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = std::string("[") + op + "] " + buf;
+  return status;
+}
+
+const char* codec_name(int c) {
+  switch (c) {
+    case KQ_Q4_0: return "q4_0";
+    case KQ_Q8_0: return "q8_0";
+    case KQ_Q4_K: return "q4_k";
+    case KQ_Q6_K: return "q6_k";
+    default: return "?";
+  }
+}
+
+bool geometry(int c, int* bv, int* bb) {
+  switch (c) {
+    case KQ_Q4_0: *bv = 32; *bb = 18; return true;
+    case KQ_Q8_0: *bv = 32; *bb = 34; return true;
+    case KQ_Q4_K: *bv = 256; *bb = 144; return true;
+    case KQ_Q6_K: *bv = 256; *bb = 210; return true;
+    default: return false;
+  }
+}
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+constexpr int64_t kMaxElems = (int64_t)1 << 40;
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// Shared checks: codec, K, row bytes.  Returns KQ_OK and fills row_bytes.
+int check_codec_k(const char* op, int codec, int64_t k, int64_t* row_bytes) {
+  int bv, bb;
+  if (!geometry(codec, &bv, &bb)) return fail(KQ_ERR_CODEC, op, "unknown codec id %d", codec);
+  if (k <= 0 || k >= kMaxDim) return fail(KQ_ERR_SHAPE, op, "K=%lld out of range", (long long)k);
+  if (k % bv)
+    return fail(KQ_ERR_SHAPE, op, "K=%lld is not a multiple of %d for %s", (long long)k, bv, codec_name(codec));
+  *row_bytes = k / bv * bb;
+  return KQ_OK;
+}
+
+int check_dtype(const char* op, int dt) {
+  if (dt != KQ_F32 && dt != KQ_F16) return fail(KQ_ERR_ARG, op, "output dtype %d is not KQ_F32 or KQ_F16", dt);
+  return KQ_OK;
+}
+
+int hip_status(const char* op, hipError_t e) {
+  if (e != hipSuccess) return fail(KQ_ERR_HIP, op, "HIP launch failed: %s", hipGetErrorString(e));
+  g_err.clear();
+  return KQ_OK;
+}
+
+int check_matmul(const char* op, int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m,
+                 const void* y, int y_dtype, int64_t* rb) {
+  int st = check_codec_k(op, codec, k, rb);
+  if (st) return st;
+  if ((st = check_dtype(op, y_dtype))) return st;
+  if (n < 0 || n >= kMaxDim) return fail(KQ_ERR_ARG, op, "N=%lld out of range", (long long)n);
+  if (m < 0 || m >= kMaxDim) return fail(KQ_ERR_ARG, op, "M=%lld out of range", (long long)m);
+  if (n * k >= kMaxElems || m * k >= kMaxElems || m * n >= kMaxElems)
+    return fail(KQ_ERR_ARG, op, "tensor too large (M=%lld N=%lld K=%lld)", (long long)m, (long long)n, (long long)k);
+  if (n == 0 || m == 0) return KQ_OK;
+  if (!w || !x || !y) return fail(KQ_ERR_ARG, op, "null pointer (w=%p x=%p y=%p)", w, x, y);
+  if (!aligned(w, 16)) return fail(KQ_ERR_ALIGN, op, "w=%p is not 16-byte aligned", w);
+  if (!aligned(x, 16)) return fail(KQ_ERR_ALIGN, op, "x=%p is not 16-byte aligned", x);
+  if (!aligned(y, y_dtype == KQ_F32 ? 4 : 2)) return fail(KQ_ERR_ALIGN, op, "y=%p is not element aligned", y);
+  return KQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kq_last_error(void) { return g_err.c_str(); }
+
+const char* kq_version(void) { return "kq 0.1 (gfx950)"; }
+
+int kq_codec_from_name(const char* name, int* codec) {
+  if (!name || !codec) return fail(KQ_ERR_ARG, "kq_codec_from_name", "null argument");
+  char low[16];
+  size_t i = 0;
+  for (; name[i] && i + 1 < sizeof low; ++i) low[i] = (char)tolower((unsigned char)name[i]);
+  low[i] = 0;
+  static const struct { const char* n; int c; } table[] = {
+      {"q4_0", KQ_Q4_0}, {"q8_0", KQ_Q8_0}, {"q4_k", KQ_Q4_K}, {"q6_k", KQ_Q6_K}};
+  for (const auto& t : table)
+    if (!name[i] && strcmp(low, t.n) == 0) {
+      *codec = t.c;
+      return KQ_OK;
+    }
+  return fail(KQ_ERR_CODEC, "kq_codec_from_name", "unknown codec '%s' (known: q4_0, q8_0, q4_k, q6_k)", name);
+}
+
+int kq_codec_info(int codec, int* block_values, int* block_bytes) {
+  int bv, bb;
+  if (!geometry(codec, &bv, &bb)) return fail(KQ_ERR_CODEC, "kq_codec_info", "unknown codec id %d", codec);
+  if (block_values) *block_values = bv;
+  if (block_bytes) *block_bytes = bb;
+  return KQ_OK;
+}
+
+int kq_row_bytes(int codec, int64_t k, int64_t* row_bytes) {
+  int64_t rb;
+  int st = check_codec_k("kq_row_bytes", codec, k, &rb);
+  if (st) return st;
+  if (!row_bytes) return fail(KQ_ERR_ARG, "kq_row_bytes", "null output");
+  *row_bytes = rb;
+  return KQ_OK;
+}
+
+int kq_dequantize(int codec, const void* w, int64_t rows, int64_t k, void* out, int out_dtype, void* stream) {
+  const char* op = "kq_dequantize";
+  int64_t rb;
+  int st = check_codec_k(op, codec, k, &rb);
+  if (st) return st;
+  if ((st = check_dtype(op, out_dtype))) return st;
+  if (rows < 0 || rows >= kMaxDim || rows * k >= kMaxElems)
+    return fail(KQ_ERR_ARG, op, "rows=%lld out of range", (long long)rows);
+  if (rows == 0) return KQ_OK;
+  if (!w || !out) return fail(KQ_ERR_ARG, op, "null pointer (w=%p out=%p)", w, out);
+  if (!aligned(w, 16)) return fail(KQ_ERR_ALIGN, op, "w=%p is not 16-byte aligned", w);
+  if (!aligned(out, 16)) return fail(KQ_ERR_ALIGN, op, "out=%p is not 16-byte aligned", out);
+  return hip_status(op, kq::launch_dequantize(codec, (const uint8_t*)w, rows, k, rb, out, out_dtype == KQ_F16,
+                                              (hipStream_t)stream));
+}
+
+int kq_qmv(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y, int y_dtype,
+           void* stream) {
+  const char* op = "kq_qmv";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb);
+  if (st) return st;
+  if (m > 8) return fail(KQ_ERR_SHAPE, op, "M=%lld rows; the GEMV takes 1..8 (use kq_qmm)", (long long)m);
+  if (n == 0 || m == 0) return KQ_OK;
+  return hip_status(op, kq::launch_qmv(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, (int)m, y,
+                                       y_dtype == KQ_F16, (hipStream_t)stream));
+}
+
+int kq_qmm(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y, int y_dtype,
+           void* stream) {
+  const char* op = "kq_qmm";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb);
+  if (st) return st;
+  if (n == 0 || m == 0) return KQ_OK;
+  return hip_status(op, kq::launch_qmm(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, m, y,
+                                       y_dtype == KQ_F16, (hipStream_t)stream));
+}
+
+int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
+                        int y_dtype, void* stream) {
+  if (m >= 0 && m <= 8) return kq_qmv(codec, w, n, k, x, m, y, y_dtype, stream);
+  return kq_qmm(codec, w, n, k, x, m, y, y_dtype, stream);
+}
+
+int64_t kq_expert_tile_map_capacity(int64_t rows, int64_t n_experts) {
+  if (rows < 0 || n_experts < 0) return -1;
+  return (rows + 63) / 64 + (n_experts < rows ? n_experts : rows);
+}
+
+int kq_expert_tile_map(const uint32_t* ids, int64_t rows, int64_t n_experts, uint32_t* map, uint32_t* counts,
+                       int64_t cap, uint32_t* status, void* stream) {
+  const char* op = "kq_expert_tile_map";
+  if (rows < 0 || rows >= kMaxDim) return fail(KQ_ERR_ARG, op, "rows=%lld out of range", (long long)rows);
+  if (n_experts <= 0 || n_experts >= kMaxDim)
+    return fail(KQ_ERR_ARG, op, "n_experts=%lld out of range", (long long)n_experts);
+  const int64_t need = kq_expert_tile_map_capacity(rows, n_experts);
+  if (cap < need || cap >= kMaxDim)
+    return fail(KQ_ERR_CAPACITY, op, "cap=%lld is below the bound %lld for rows=%lld, n_experts=%lld",
+                (long long)cap, (long long)need, (long long)rows, (long long)n_experts);
+  if (!counts || (rows > 0 && (!ids || !map))) return fail(KQ_ERR_ARG, op, "null pointer");
+  if (!aligned(counts, 4) || (ids && !aligned(ids, 4)) || (map && !aligned(map, 4)) || (status && !aligned(status, 4)))
+    return fail(KQ_ERR_ALIGN, op, "ids/map/counts/status must be 4-byte aligned");
+  return hip_status(op, kq::launch_tile_map(ids, rows, n_experts, map, counts, cap, status, (hipStream_t)stream));
+}
+
+int kq_gather_qmm_seg(int codec, const void* w, int64_t n_experts, int64_t n, int64_t k, const void* x,
+                      int64_t rows, const uint32_t* map, const uint32_t* counts, int64_t cap, void* y, int y_dtype,
+                      void* stream) {
+  const char* op = "kq_gather_qmm_seg";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, rows, y, y_dtype, &rb);
+  if (st) return st;
+  if (n_experts <= 0 || n_experts >= kMaxDim || n_experts * n >= kMaxDim * 64)
+    return fail(KQ_ERR_ARG, op, "n_experts=%lld out of range", (long long)n_experts);
+  if (cap < 0 || cap >= kMaxDim) return fail(KQ_ERR_ARG, op, "cap=%lld out of range", (long long)cap);
+  if (n == 0 || rows == 0 || cap == 0) return KQ_OK;
+  if (!map || !counts) return fail(KQ_ERR_ARG, op, "null map or counts");
+  if (!aligned(map, 4) || !aligned(counts, 4)) return fail(KQ_ERR_ALIGN, op, "map/counts must be 4-byte aligned");
+  return hip_status(op, kq::launch_gather_qmm_seg(codec, (const uint8_t*)w, n_experts, n, k, rb,
+                                                  (const kq::half_t*)x, rows, map, counts, cap, y,
+                                                  y_dtype == KQ_F16, (hipStream_t)stream));
+}
+
+int kq_quantize(int codec, const float* w, int64_t rows, int64_t k, void* out, void* stream) {
+  const char* op = "kq_quantize";
+  int64_t rb;
+  int st = check_codec_k(op, codec, k, &rb);
+  if (st) return st;
+  if (rows < 0 || rows >= kMaxDim || rows * k >= kMaxElems)
+    return fail(KQ_ERR_ARG, op, "rows=%lld out of range", (long long)rows);
+  if (rows == 0) return KQ_OK;
+  if (!w || !out) return fail(KQ_ERR_ARG, op, "null pointer (w=%p out=%p)", (const void*)w, out);
+  if (!aligned(w, 16) || !aligned(out, 16)) return fail(KQ_ERR_ALIGN, op, "w and out must be 16-byte aligned");
+  return hip_status(op, kq::launch_quantize(codec, w, rows, k, rb, (uint8_t*)out, (hipStream_t)stream));
+}
+
+}  // extern "C"

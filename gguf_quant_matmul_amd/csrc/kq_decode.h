@@ -1,0 +1,84 @@
+// Scalar reference-style decode of 8 consecutive values of a weight row,
+// shared by kq_dequantize and the generic (odd-shape) GEMV.  Every value is
+// the codec formula rounded once to float32 (see kq_dequant.hip).
+#pragma once
+
+#include "kq_internal.h"
+
+namespace kq {
+
+// 8 bytes at a 2-byte-aligned address as two dwords.
+__device__ __forceinline__ u32x2 ld8_a2(const uint8_t* p) {
+  const uint32_t a = ld_u16(p), b = ld_u16(p + 2), c = ld_u16(p + 4), d = ld_u16(p + 6);
+  return u32x2{a | (b << 16), c | (d << 16)};
+}
+
+template <int C>
+__device__ __forceinline__ void decode8(const uint8_t* __restrict__ row, int64_t v0, float out[8]);
+
+template <>
+__device__ __forceinline__ void decode8<Q8_0>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  const uint8_t* blk = row + (v0 / 32) * 34;
+  const float d = f16_to_f32(ld_u16(blk));
+  const u32x2 c = ld8_a2(blk + 2 + (v0 % 32));
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = (int)(int8_t)(((i < 4 ? c.x : c.y) >> (8 * (i & 3))) & 0xFFu);
+    out[i] = d * (float)q;
+  }
+}
+
+template <>
+__device__ __forceinline__ void decode8<Q4_0>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  const uint8_t* blk = row + (v0 / 32) * 18;
+  const float d = f16_to_f32(ld_u16(blk));
+  const int vb = (int)(v0 % 32);
+  const u32x2 c = ld8_a2(blk + 2 + (vb & 15));
+  const int sh = vb >= 16 ? 4 : 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = (int)((((i < 4 ? c.x : c.y) >> (8 * (i & 3) + sh))) & 15u);
+    out[i] = d * (float)(q - 8);
+  }
+}
+
+template <>
+__device__ __forceinline__ void decode8<Q4_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  const uint8_t* blk = row + (v0 / 256) * 144;  // 16-byte aligned: rows are multiples of 144 bytes
+  const int vi = (int)(v0 % 256);
+  const int j = vi / 32, l0 = vi % 32;
+  const u32x4 h = ld_16B(blk);
+  const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
+  uint32_t sc, m;
+  q4k_scale_min(h.y, h.z, h.w, j, sc, m);
+  const float dsc = d * (float)sc;   // exact
+  const float dm = dmin * (float)m;  // exact
+  const u32x2 c = *(const u32x2*)(blk + 16 + 32 * (j / 2) + l0);
+  const int sh = (j & 1) ? 4 : 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t q = (((i < 4 ? c.x : c.y) >> (8 * (i & 3) + sh))) & 15u;
+    out[i] = dsc * (float)q - dm;  // one rounding
+  }
+}
+
+template <>
+__device__ __forceinline__ void decode8<Q6_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  const uint8_t* blk = row + (v0 / 256) * 210;
+  const int vi = (int)(v0 % 256);
+  const int h = vi / 128, r = vi % 128, c = r / 32, l0 = r % 32;
+  const u32x2 ql = ld8_a2(blk + 64 * h + l0 + 32 * (c & 1));
+  const u32x2 qh = ld8_a2(blk + 128 + 32 * h + l0);
+  const float d = f16_to_f32(ld_u16(blk + 208));
+  const float dsc = d * (float)(int8_t)blk[192 + vi / 16];  // exact
+  const int lsh = c < 2 ? 0 : 4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lw = i < 4 ? ql.x : ql.y, hw = i < 4 ? qh.x : qh.y;
+    const uint32_t lo4 = (lw >> (8 * (i & 3) + lsh)) & 15u;
+    const uint32_t hi2 = (hw >> (8 * (i & 3) + 2 * c)) & 3u;
+    out[i] = dsc * (float)((int)(lo4 | (hi2 << 4)) - 32);
+  }
+}
+
+}  // namespace kq

@@ -19,6 +19,8 @@ never matters):
 
 from __future__ import annotations
 
+import concurrent.futures as cf
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -31,20 +33,34 @@ def weight_rows(seed: int, n: int, k: int, dist: str = "normal", rows=None) -> n
     if rows is None:
         rows = np.arange(n)
     rows = np.asarray(rows, dtype=np.int64)
+    if dist not in ("normal", "t5"):
+        raise ValueError(dist)
     out = np.empty((rows.size, k), dtype=np.float32)
     chunks = np.unique(rows // ROW_CHUNK)
-    for c in chunks:
+    contiguous = rows.size == n and np.array_equal(rows, np.arange(n))
+
+    def one(c):
         lo = int(c) * ROW_CHUNK
         cnt = min(ROW_CHUNK, n - lo)
         rng = np.random.default_rng([seed, 0, int(c)])
         if dist == "normal":
             blk = rng.standard_normal((cnt, k), dtype=np.float32) * np.float32(0.02)
-        elif dist == "t5":
-            blk = (rng.standard_t(5, (cnt, k)) * 0.02).astype(np.float32)
         else:
-            raise ValueError(dist)
-        sel = np.nonzero(rows // ROW_CHUNK == c)[0]
-        out[sel] = blk[rows[sel] - lo]
+            blk = (rng.standard_t(5, (cnt, k)) * 0.02).astype(np.float32)
+        if contiguous:
+            out[lo:lo + cnt] = blk
+        else:
+            sel = np.nonzero(rows // ROW_CHUNK == c)[0]
+            out[sel] = blk[rows[sel] - lo]
+
+    # chunks are independent streams: draw them on a few threads
+    workers = min(16, os.cpu_count() or 1, len(chunks))
+    if workers > 1:
+        with cf.ThreadPoolExecutor(workers) as ex:
+            list(ex.map(one, chunks))
+    else:
+        for c in chunks:
+            one(c)
     return out
 
 

@@ -1,0 +1,144 @@
+/*
+ * kq.h -- C ABI of libkq: GGUF K-quant dequantize and quantized matmul on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Operations follow the mlx-kquant ops as documented on the mlx-kquant
+ * bindings.cpp page (docstrings of dequantize, quantized_matmul,
+ * expert_tile_map, gather_qmm_seg, quantize) and the codec geometry of the
+ * mlx-kquant README ("Codec reference" table).  Byte layouts inside a block
+ * are GGUF's.
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named w, x, y, out, map, counts, ids, status are DEVICE
+ *    pointers; the caller owns every buffer.  The library allocates no device
+ *    memory and keeps no state except a thread-local error message.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call only enqueues work on that stream; none synchronizes the
+ *    device or the host.
+ *  - Weights are the codec's wire bytes, row-major [rows][row_bytes] with
+ *    row_bytes = K / block_values * block_bytes (the quantized_matmul
+ *    docstring's transpose=True layout: one weight row per output column).
+ *    The "scales" argument of the pages' ops is vestigial (their docstrings
+ *    say the kernel ignores it) and is absent here.
+ *  - Activations x are float16, row-major [M][K].
+ *  - w and x must be 16-byte aligned, y/out 16-byte aligned, map/counts/ids
+ *    4-byte aligned: otherwise KQ_ERR_ALIGN.
+ *  - K must be a positive multiple of the codec's block (256 for q4_K and
+ *    q6_K, 32 for q8_0 and q4_0): otherwise KQ_ERR_SHAPE.  Sizes must be
+ *    below 2^31 (element counts below 2^40).
+ *  - On any error nothing is launched and outputs are untouched; the return
+ *    value is a kq_status and kq_last_error() describes it.
+ *  - Calls on one stream are ordered; calls on different streams that write
+ *    the same output race.
+ */
+#ifndef KQ_H
+#define KQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Codec ids: GGML's type numbers for these four codecs (the names are the
+ * authority: "q4_0", "q8_0", "q4_k", "q6_k").  Geometry per the mlx-kquant
+ * README "Codec reference" table:
+ *   q4_0  32 values,  4 bits,  18 bytes per block
+ *   q8_0  32 values,  8 bits,  34 bytes per block
+ *   q4_K 256 values,  4 bits, 144 bytes per superblock
+ *   q6_K 256 values,  6 bits, 210 bytes per superblock */
+typedef enum { KQ_Q4_0 = 2, KQ_Q8_0 = 8, KQ_Q4_K = 12, KQ_Q6_K = 14 } kq_codec;
+
+/* Output element types. */
+typedef enum { KQ_F32 = 0, KQ_F16 = 1 } kq_dtype;
+
+typedef enum {
+  KQ_OK = 0,
+  KQ_ERR_ARG = -1,      /* null pointer, bad dtype, size out of range       */
+  KQ_ERR_CODEC = -2,    /* unknown codec id or name                          */
+  KQ_ERR_SHAPE = -3,    /* K not a multiple of the block, M out of range     */
+  KQ_ERR_ALIGN = -4,    /* pointer not aligned as required                   */
+  KQ_ERR_CAPACITY = -5, /* tile-map capacity below kq_expert_tile_map_capacity */
+  KQ_ERR_HIP = -6       /* a HIP launch failed; message has the HIP error    */
+} kq_status;
+
+/* ---- codec registry (mlx-kquant bindings.cpp page: codecs(); README codec table) ---- */
+
+/* Name ("q4_k", "q6_k", "q8_0", "q4_0"; case-insensitive) -> codec id. */
+int kq_codec_from_name(const char* name, int* codec);
+/* Values and bytes per block of a codec. */
+int kq_codec_info(int codec, int* block_values, int* block_bytes);
+/* Bytes of one weight row of K values. */
+int kq_row_bytes(int codec, int64_t k, int64_t* row_bytes);
+/* Message of the last failed call on this thread ("" if none). */
+const char* kq_last_error(void);
+/* Library version string. */
+const char* kq_version(void);
+
+/* ---- dequantize (mlx-kquant bindings.cpp page, dequantize docstring) ----
+ * w [rows][row_bytes] -> out [rows][K] as float32 or float16.
+ * Bit-exact: each value is the codec formula evaluated exactly and rounded
+ * once to float32 (q4_K: (d*sc)*q - dmin*m; q6_K: (d*sc)*(q-32);
+ * q8_0: d*q; q4_0: d*(q-8)); float16 output is RNE of that float32 value. */
+int kq_dequantize(int codec, const void* w, int64_t rows, int64_t k,
+                  void* out, int out_dtype, void* stream);
+
+/* ---- quantized matmul (mlx-kquant bindings.cpp page, quantized_matmul docstring) ----
+ * y[m][n] = sum_k x[m][k] * dequant(w)[n][k], float32 accumulation.
+ * w [N][row_bytes], x float16 [M][K], y [M][N] float32 or float16.
+ *
+ * kq_qmv: decode-shaped GEMV, 1 <= M <= 8 (one weight read serves all M rows).
+ * kq_qmm: prefill GEMM on f16 matrix cores, any M >= 1.
+ * kq_quantized_matmul: kq_qmv for M <= 8, else kq_qmm.
+ * The K-reduction order is fixed per (codec, N, K, M): results are
+ * deterministic run to run, and a row's result does not depend on the other
+ * rows of x. */
+int kq_qmv(int codec, const void* w, int64_t n, int64_t k,
+           const void* x, int64_t m, void* y, int y_dtype, void* stream);
+int kq_qmm(int codec, const void* w, int64_t n, int64_t k,
+           const void* x, int64_t m, void* y, int y_dtype, void* stream);
+int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k,
+                        const void* x, int64_t m, void* y, int y_dtype, void* stream);
+
+/* ---- expert tile map (mlx-kquant bindings.cpp page, expert_tile_map docstring) ----
+ * From expert ids sorted ascending (uint32 [rows]), write tiles
+ * map[t] = (expert, row_start, num_rows) that cut each expert's segment into
+ * 64-row tiles, only the last tile of a segment partial, and counts[0] = the
+ * number of valid tiles.  Built on the GPU: no host sync.  Tiles are written
+ * in expert-major order; slots past counts[0] are left as they were.
+ * Ids >= n_experts get no tile (their rows stay uncovered).
+ * cap (rows of map) must be >= kq_expert_tile_map_capacity(rows, n_experts).
+ * status (nullable device word) is overwritten with: bit0 = ids not sorted,
+ * bit1 = an id >= n_experts, bit2 = tiles exceeded cap (only possible with
+ * unsorted ids; counts[0] is then clamped to cap). */
+int64_t kq_expert_tile_map_capacity(int64_t rows, int64_t n_experts);
+int kq_expert_tile_map(const uint32_t* sorted_ids, int64_t rows, int64_t n_experts,
+                       uint32_t* map, uint32_t* counts, int64_t cap,
+                       uint32_t* status, void* stream);
+
+/* ---- expert-sorted gather GEMM (mlx-kquant bindings.cpp page, gather_qmm_seg docstring) ----
+ * w [n_experts][N][row_bytes]; x float16 [rows][K], rows sorted by expert;
+ * map/counts as written by kq_expert_tile_map (device memory, read on the
+ * device: no host sync).  For each valid tile (e, s, c):
+ *   y[r][n] = sum_k x[r][k] * dequant(w[e])[n][k]   for s <= r < s+c.
+ * Rows no valid tile covers are left unwritten.  Tiles with e >= n_experts,
+ * num_rows outside 1..64 or rows past `rows` are skipped.  Valid tiles must
+ * not overlap (the pages' contract); overlapping tiles race. */
+int kq_gather_qmm_seg(int codec, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                      const void* x, int64_t rows,
+                      const uint32_t* map, const uint32_t* counts, int64_t cap,
+                      void* y, int y_dtype, void* stream);
+
+/* ---- encoder (mlx-kquant bindings.cpp page, quantize docstring; no imatrix) ----
+ * float32 w [rows][K] -> wire bytes out [rows][row_bytes], round to nearest
+ * against the stored fp16 block parameters, every step in IEEE float32 in a
+ * fixed order, each code then moved to the nearest point of its block's
+ * decoded grid (distance in float64, ties to the lower code). */
+int kq_quantize(int codec, const float* w, int64_t rows, int64_t k,
+                void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KQ_H */

@@ -1,0 +1,360 @@
+"""GPU parity: every libkq entry point against the oracle on seeded inputs.
+
+Sizes span several tiles and a ragged tail; edge cases: odd K (generic
+kernels), rows that are not 4-byte aligned (q6_K with an odd superblock count),
+K longer than one LDS chunk, subnormal / negative / zero block scales, empty
+tiles, ids outside the expert range.
+"""
+
+import zlib
+
+import numpy as np
+import pytest
+
+from _gpu import TOL, assert_close_rows, dev, host, say, u32
+from oracle import codecs, encode, matmul
+
+pytestmark = pytest.mark.gpu
+
+CODECS = ("q4_k", "q6_k", "q8_0", "q4_0")
+
+
+@pytest.fixture(scope="module")
+def kq():
+    from gguf_quant_matmul_amd import kq as mod
+
+    return mod
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _weights(codec, n, k, seed, scale=0.02):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * scale).astype(np.float32)
+    return encode.quantize(codec, w)
+
+
+def _x(m, k, seed):
+    return np.random.default_rng(seed + 1000).standard_normal((m, k)).astype(np.float16)
+
+
+# ---------------------------------------------------------------------------
+# dequantize: bit-exact
+# ---------------------------------------------------------------------------
+
+def _random_wire(codec, n, k, rng):
+    """Random wire bytes with finite fp16 fields (exponent 31 replaced)."""
+    rb = codecs.row_bytes(codec, k)
+    w = rng.integers(0, 256, size=(n, rb), dtype=np.uint8)
+    bb = codecs.block_bytes(codec)
+    blk = w.reshape(n, -1, bb)
+    offs = {"q8_0": [0], "q4_0": [0], "q4_k": [0, 2], "q6_k": [208]}[codec]
+    for o in offs:
+        hi = blk[..., o + 1]
+        bad = (hi & 0x7C) == 0x7C
+        blk[..., o + 1] = np.where(bad, hi & 0xBF, hi)
+    return blk.reshape(n, rb)
+
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("out_dtype", ["f32", "f16"])
+@pytest.mark.parametrize("kind", ["encoded", "random_bytes"])
+def test_dequantize_bit_exact(kq, codec, out_dtype, kind):
+    torch = _torch()
+    rng = np.random.default_rng(zlib.crc32(repr((codec, kind)).encode()))
+    k = 256 * 5 if codec in ("q4_k", "q6_k") else 32 * 7
+    n = 67
+    w = _weights(codec, n, k, 1) if kind == "encoded" else _random_wire(codec, n, k, rng)
+    dt = np.float32 if out_dtype == "f32" else np.float16
+    say(f"dequantize {codec} {out_dtype} {kind} n={n} k={k}")
+    out = torch.empty((n, k), dtype=torch.float32 if dt == np.float32 else torch.float16, device="cuda")
+    kq.kq_dequantize(codec, dev(w), k, out)
+    got = host(out)
+    ref = codecs.dequantize(codec, w, k, dt)
+    ui = np.uint32 if dt == np.float32 else np.uint16
+    assert np.array_equal(got.view(ui), ref.view(ui)), f"{codec}: {np.sum(got.view(ui) != ref.view(ui))} values differ"
+
+
+def _q4k_double_rounding_blocks(count=12):
+    """q4_K blocks whose value d*sc*q - dmin*m rounds differently to float16
+    directly and via float32: the float16 output must be RNE of the float32."""
+    rng = np.random.default_rng(2024)
+    blocks = []
+    while len(blocks) < count:
+        d, dm = int(rng.integers(0x0400, 0x7800)), int(rng.integers(0x0400, 0x7800))
+        sc, m, q = int(rng.integers(1, 64)), int(rng.integers(1, 64)), int(rng.integers(0, 16))
+        D, DM = float(np.uint16(d).view(np.float16)), float(np.uint16(dm).view(np.float16))
+        exact = D * sc * q - DM * m
+        with np.errstate(over="ignore"):
+            via32, direct = np.float16(np.float32(exact)), np.float16(exact)
+        if via32 == direct or not np.isfinite(via32):
+            continue
+        b = np.zeros(144, np.uint8)
+        b[0], b[1], b[2], b[3] = d & 255, d >> 8, dm & 255, dm >> 8
+        b[4], b[8] = sc, m            # sub-block 0: sc_0 = s[0] & 63, m_0 = s[4] & 63
+        b[16:48] = q                  # low nibbles of qs[0..31]: values 0..31 of sub-block 0
+        blocks.append((b, via32))
+    return blocks
+
+
+def test_dequantize_f16_rounds_via_f32(kq):
+    torch = _torch()
+    cases = _q4k_double_rounding_blocks()
+    w = np.stack([b for b, _ in cases])
+    out = torch.empty((len(cases), 256), dtype=torch.float16, device="cuda")
+    kq.kq_dequantize("q4_k", dev(w), 256, out)
+    got = host(out)
+    ref = codecs.dequantize("q4_k", w, 256, np.float16)
+    for i, (_, via32) in enumerate(cases):
+        assert ref[i, 0] == via32
+        assert got[i, 0] == via32, (i, got[i, 0], via32)
+    assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
+
+
+@pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt"])
+def test_dequantize_golden_blocks(kq, name):
+    from test_oracle_codecs import _load_golden
+
+    torch = _torch()
+    codec, blk, values = _load_golden(name)
+    k = codecs.block_values(codec)
+    w = np.tile(blk, (3, 1))  # 3 rows (row starts 2-byte aligned for q6_K)
+    for tdt, ndt in ((torch.float32, np.float32), (torch.float16, np.float16)):
+        out = torch.empty((3, k), dtype=tdt, device="cuda")
+        kq.kq_dequantize(codec, dev(w), k, out)
+        got = host(out)
+        for v, expect in values:
+            for r in range(3):
+                assert float(got[r, v]) == expect and np.signbit(got[r, v]) == np.signbit(expect), (name, r, v)
+        ref = codecs.dequantize(codec, w, k, ndt)
+        ui = np.uint32 if ndt == np.float32 else np.uint16
+        assert np.array_equal(got.view(ui), ref.view(ui))
+
+
+# ---------------------------------------------------------------------------
+# qmv / qmm: tolerance vs fp64 oracle
+# ---------------------------------------------------------------------------
+
+def _shapes_qmv(codec):
+    if codec in ("q4_k", "q6_k"):
+        return [(37, 512), (300, 256 * 17)]   # 17 superblocks: q6_K rows only 2-byte aligned
+    return [(37, 96), (300, 4160), (45, 2048 + 32)]  # 96 and 2080: odd block counts -> generic kernel
+
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+def test_qmv_parity(kq, codec, m):
+    torch = _torch()
+    for n, k in _shapes_qmv(codec):
+        w = _weights(codec, n, k, 7 + n)
+        x = _x(m, k, n)
+        say(f"qmv {codec} m={m} n={n} k={k}")
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        kq.kq_qmv(codec, dev(w), n, k, dev(x), y)
+        ref = matmul.qmatmul(codec, w, k, x)
+        assert_close_rows(host(y), ref, what=f"qmv {codec} m={m} n={n} k={k}")
+        # float16 output
+        y16 = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        kq.kq_qmv(codec, dev(w), n, k, dev(x), y16)
+        assert_close_rows(host(y16), ref, what=f"qmv f16 {codec} m={m}")
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_qmm_parity(kq, codec):
+    torch = _torch()
+    shapes = [(1, 37, 512), (130, 200, 512), (257, 131, 256 * 9 if codec in ("q4_k", "q6_k") else 64 * 9)]
+    if codec in ("q8_0", "q4_0"):
+        shapes.append((70, 40, 96))  # odd block count -> generic kernel
+    for m, n, k in shapes:
+        w = _weights(codec, n, k, 11 + m)
+        x = _x(m, k, m + n)
+        ref = matmul.qmatmul(codec, w, k, x)
+        for tdt in (torch.float16, torch.float32):
+            say(f"qmm {codec} m={m} n={n} k={k} {tdt}")
+            y = torch.empty((m, n), dtype=tdt, device="cuda")
+            kq.kq_qmm(codec, dev(w), n, k, dev(x), y)
+            assert_close_rows(host(y).astype(np.float64), ref, what=f"qmm {codec} m={m} n={n} k={k}")
+
+
+def test_quantized_matmul_routes_by_m(kq):
+    torch = _torch()
+    n, k = 64, 512
+    w = _weights("q4_k", n, k, 3)
+    for m in (1, 8, 9, 40):
+        x = _x(m, k, m)
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        kq.kq_quantized_matmul("q4_k", dev(w), n, k, dev(x), y)
+        assert_close_rows(host(y), matmul.qmatmul("q4_k", w, k, x), what=f"quantized_matmul m={m}")
+
+
+def test_qmm_row_independence_and_determinism(kq):
+    torch = _torch()
+    m, n, k = 200, 96, 1024
+    w = dev(_weights("q4_k", n, k, 5))
+    x = _x(m, k, 1)
+    y1 = torch.empty((m, n), dtype=torch.float16, device="cuda")
+    y2 = torch.empty_like(y1)
+    kq.kq_qmm("q4_k", w, n, k, dev(x), y1)
+    kq.kq_qmm("q4_k", w, n, k, dev(x), y2)
+    assert torch.equal(y1, y2), "run-to-run determinism"
+    sub = np.array([0, 5, 77, 128, 199])
+    ys = torch.empty((sub.size, n), dtype=torch.float16, device="cuda")
+    kq.kq_qmm("q4_k", w, n, k, dev(x[sub]), ys)
+    assert np.array_equal(host(ys).view(np.uint16), host(y1)[sub].view(np.uint16)), "row independence"
+
+
+def test_qmv_row_bits_do_not_depend_on_other_rows(kq):
+    torch = _torch()
+    n, k, m = 200, 1024, 4
+    w = dev(_weights("q6_k", n, k, 9))
+    x = _x(m, k, 2)
+    x2 = x.copy()
+    x2[1:] = _x(m - 1, k, 3)
+    ya = torch.empty((m, n), dtype=torch.float32, device="cuda")
+    yb = torch.empty_like(ya)
+    kq.kq_qmv("q6_k", w, n, k, dev(x), ya)
+    kq.kq_qmv("q6_k", w, n, k, dev(x2), yb)
+    assert torch.equal(ya[0], yb[0])
+
+
+# ---------------------------------------------------------------------------
+# expert tile map and expert-sorted gather GEMM
+# ---------------------------------------------------------------------------
+
+def _tile_map_gpu(kq, ids, e):
+    torch = _torch()
+    cap = kq.kq_expert_tile_map_capacity(ids.size, e)
+    map_ = torch.full((max(cap, 1), 3), -1, dtype=torch.int32, device="cuda")
+    counts = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    kq.kq_expert_tile_map(u32(ids) if ids.size else torch.empty(0, dtype=torch.int32, device="cuda"), e,
+                          map_[:cap] if cap else map_, counts, status)
+    return map_, counts, int(host(counts)[0]), int(host(status)[0]), cap
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tile_map_matches_oracle(kq, seed):
+    rng = np.random.default_rng(seed)
+    e = int(rng.integers(1, 300))
+    rows = int(rng.integers(0, 5000))
+    ids = np.sort(rng.integers(0, e, rows)).astype(np.uint32) if seed % 2 else \
+        np.sort(rng.zipf(1.3, rows) % e).astype(np.uint32)
+    say(f"tile map e={e} rows={rows}")
+    map_, _, count, status, cap = _tile_map_gpu(kq, ids, e)
+    tiles, ref_count = matmul.expert_tile_map(ids, e)
+    assert count == ref_count and status == 0
+    got = host(map_)[:count].view(np.uint32)
+    assert np.array_equal(got, tiles)  # both expert-major
+    # slots past the count are untouched
+    assert np.all(host(map_)[count:cap] == -1)
+
+
+def test_tile_map_workload_and_status_flags(kq):
+    from gguf_quant_matmul_amd import workloads
+
+    r = workloads.routing(4, 512, 8, 64)
+    map_, _, count, status, _ = _tile_map_gpu(kq, r.sorted_ids, 64)
+    assert count == 92 and status == 0
+    # ids past the expert range: no tile, status bit 1
+    ids = np.array([0, 0, 1, 7, 7], np.uint32)
+    _, _, count, status, _ = _tile_map_gpu(kq, ids, 4)
+    assert count == 2 and status == 2
+    # unsorted ids: status bit 0
+    ids = np.array([3, 1, 2, 2, 0], np.uint32)
+    _, _, _, status, _ = _tile_map_gpu(kq, ids, 4)
+    assert status & 1
+    # no rows
+    _, _, count, status, _ = _tile_map_gpu(kq, np.zeros(0, np.uint32), 4)
+    assert count == 0 and status == 0
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_gather_qmm_seg_parity(kq, codec):
+    torch = _torch()
+    rng = np.random.default_rng(17)
+    e, n = 6, 96
+    k = 512 if codec in ("q4_k", "q6_k") else 320
+    ids = np.sort(np.concatenate([rng.integers(0, e - 1, 190), [e - 1] * 3, [e + 2] * 4])).astype(np.uint32)
+    rows = ids.size
+    wf = (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32)
+    w = encode.quantize(codec, wf)
+    x = _x(rows, k, 5)
+    map_, counts, count, status, cap = _tile_map_gpu(kq, ids, e)
+    assert status == 2
+    tiles = host(map_)[:count].view(np.uint32)
+    for tdt in (torch.float16, torch.float32):
+        say(f"seg {codec} e={e} n={n} k={k} rows={rows} {tdt}")
+        y = torch.full((rows, n), float("nan"), dtype=tdt, device="cuda")
+        kq.kq_gather_qmm_seg(codec, dev(w), e, n, k, dev(x), map_[:cap], counts, y)
+        got = host(y).astype(np.float64)
+        ref = matmul.gather_qmm_seg(codec, w, k, x, tiles)
+        covered = ids < e
+        assert np.all(np.isnan(got[~covered])), "uncovered rows must stay unwritten"
+        assert_close_rows(got[covered], ref[covered], what=f"seg {codec}")
+
+
+def test_gather_seg_one_expert_equals_qmm_bits(kq):
+    torch = _torch()
+    n, k, rows = 100, 1024, 150
+    w = _weights("q4_k", n, k, 21)
+    x = dev(_x(rows, k, 8))
+    ids = np.zeros(rows, np.uint32)
+    map_, counts, count, _, cap = _tile_map_gpu(kq, ids, 1)
+    assert count == 3
+    ys = torch.empty((rows, n), dtype=torch.float16, device="cuda")
+    kq.kq_gather_qmm_seg("q4_k", dev(w[None]), 1, n, k, x, map_[:cap], counts, ys)
+    ref = matmul.qmatmul("q4_k", w, k, host(x))
+    assert_close_rows(host(ys).astype(np.float64), ref, what="seg one expert")
+
+
+def test_gather_seg_row_independence(kq):
+    torch = _torch()
+    rng = np.random.default_rng(3)
+    e, n, k = 4, 64, 512
+    w = dev(encode.quantize("q4_k", (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32)))
+    ids = np.sort(rng.integers(0, e, 200)).astype(np.uint32)
+    x = _x(200, k, 4)
+    map_, counts, _, _, cap = _tile_map_gpu(kq, ids, e)
+    y = torch.empty((200, n), dtype=torch.float16, device="cuda")
+    kq.kq_gather_qmm_seg("q4_k", w, e, n, k, dev(x), map_[:cap], counts, y)
+    keep = np.sort(rng.choice(200, 60, replace=False))
+    map2, counts2, _, _, cap2 = _tile_map_gpu(kq, ids[keep], e)
+    y2 = torch.empty((60, n), dtype=torch.float16, device="cuda")
+    kq.kq_gather_qmm_seg("q4_k", w, e, n, k, dev(x[keep]), map2[:cap2], counts2, y2)
+    # rows land in different tiles (and tile positions) but each row's bits are the same
+    assert np.array_equal(host(y2).view(np.uint16), host(y)[keep].view(np.uint16))
+
+
+# ---------------------------------------------------------------------------
+# encoder: bit-exact bytes
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("codec", CODECS)
+@pytest.mark.parametrize("dist", ["normal", "t5", "positive", "negative", "mixed"])
+def test_quantize_bytes_match_oracle(kq, codec, dist):
+    torch = _torch()
+    rng = np.random.default_rng(zlib.crc32(repr((codec, dist)).encode()))
+    n, k = 48, 1024
+    if dist == "normal":
+        w = rng.standard_normal((n, k)).astype(np.float32) * np.float32(0.02)
+    elif dist == "t5":
+        w = (rng.standard_t(5, (n, k)) * 0.02).astype(np.float32)
+    elif dist == "positive":
+        w = rng.uniform(0.001, 1, (n, k)).astype(np.float32)
+    elif dist == "negative":
+        w = -rng.uniform(0.001, 1, (n, k)).astype(np.float32)
+    else:
+        w = rng.standard_normal((n, k)).astype(np.float32)
+        w[::3] *= np.float32(1e-6)
+        w[1::5] = 0
+        w[2, :300] = 0
+    say(f"quantize {codec} {dist}")
+    out = torch.empty((n, codecs.row_bytes(codec, k)), dtype=torch.uint8, device="cuda")
+    kq.kq_quantize(codec, dev(w), out)
+    got = host(out)
+    ref = encode.quantize(codec, w)
+    assert np.array_equal(got, ref), f"{np.sum(got != ref)} bytes differ"

@@ -1,0 +1,114 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration the
+benchmark times, checked on sampled outputs the oracle computes one by one.
+
+For each workload: the float32 weights are drawn (seeded, see
+gguf_quant_matmul_amd/workloads.py), encoded on the GPU by kq_quantize, and the
+GPU bytes of sampled rows must equal the oracle encoder's bytes for those rows.
+The kernel runs over the whole tensor; sampled output columns (all activation
+rows) are compared with the fp64 oracle; dequantize is compared bit for bit on
+the sampled rows.
+"""
+
+import numpy as np
+import pytest
+
+from _gpu import assert_close_rows, dev, host, say, u32
+from gguf_quant_matmul_amd import workloads as W
+from oracle import codecs, encode, matmul
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def kq():
+    from gguf_quant_matmul_amd import kq as mod
+
+    return mod
+
+
+def _sample(n, count, seed):
+    rng = np.random.default_rng(seed)
+    s = set(rng.choice(n, count - 2, replace=False).tolist()) | {0, n - 1}
+    return np.array(sorted(s))
+
+
+GEMV_CFGS = [W.CFG1_Q4K_GEMV, *W.CFG2_GEMV, W.CFG3_Q6K_LMHEAD, W.CFG4_Q4K_GEMM]
+
+
+@pytest.mark.parametrize("cfg", GEMV_CFGS, ids=[c.name for c in GEMV_CFGS])
+def test_gemv_gemm_workload(kq, cfg):
+    import torch
+
+    say(f"workload {cfg.name}: drawing weights")
+    wf = W.weight_rows(cfg.seed, cfg.n, cfg.k, cfg.dist)
+    wdev = dev(wf)
+    del wf
+    rb = codecs.row_bytes(cfg.codec, cfg.k)
+    wq = torch.empty((cfg.n, rb), dtype=torch.uint8, device="cuda")
+    kq.kq_quantize(cfg.codec, wdev, wq)
+    del wdev
+    ns = _sample(cfg.n, 48, cfg.seed)
+    wf_s = W.weight_rows(cfg.seed, cfg.n, cfg.k, cfg.dist, rows=ns)
+    ref_bytes = encode.quantize(cfg.codec, wf_s)
+    got_bytes = host(wq[torch.from_numpy(ns).cuda()])
+    assert np.array_equal(got_bytes, ref_bytes), "kq_quantize bytes differ from the oracle encoder"
+
+    x = W.gemv_activations(cfg)
+    out_t = torch.float32 if cfg.out_dtype == "f32" else torch.float16
+    y = torch.empty((cfg.m, cfg.n), dtype=out_t, device="cuda")
+    say(f"workload {cfg.name}: kernel")
+    if cfg.m <= 8:
+        kq.kq_qmv(cfg.codec, wq, cfg.n, cfg.k, dev(x), y)
+    else:
+        kq.kq_qmm(cfg.codec, wq, cfg.n, cfg.k, dev(x), y)
+    got = host(y)[:, ns].astype(np.float64)
+    ref = matmul.qmatmul(cfg.codec, ref_bytes, cfg.k, x)
+    err = assert_close_rows(got, ref, what=cfg.name)
+    say(f"workload {cfg.name}: max row-normalized error {err:.2e}")
+
+    if cfg.m == 1:
+        say(f"workload {cfg.name}: dequantize")
+        out = torch.empty((ns.size, cfg.k), dtype=torch.float32, device="cuda")
+        kq.kq_dequantize(cfg.codec, wq[torch.from_numpy(ns).cuda()].contiguous(), cfg.k, out)
+        assert np.array_equal(host(out).view(np.uint32), codecs.dequantize(cfg.codec, ref_bytes, cfg.k).view(np.uint32))
+    del wq, y
+    torch.cuda.empty_cache()
+
+
+def test_moe_seg_workload(kq):
+    import torch
+
+    cfg = W.CFG5_MOE_SEG
+    say(f"workload {cfg.name}: drawing weights")
+    rows_w = cfg.n_experts * cfg.n
+    wdev = dev(W.weight_rows(cfg.seed, rows_w, cfg.k))
+    rb = codecs.row_bytes(cfg.codec, cfg.k)
+    wq = torch.empty((rows_w, rb), dtype=torch.uint8, device="cuda")
+    kq.kq_quantize(cfg.codec, wdev, wq)
+    del wdev
+    r = W.routing(cfg.seed, cfg.tokens, cfg.top_k, cfg.n_experts)
+    x = W.activations(cfg.seed, cfg.tokens, cfg.k)[r.token_of_row]
+    rows = x.shape[0]
+    cap = kq.kq_expert_tile_map_capacity(rows, cfg.n_experts)
+    map_ = torch.empty((cap, 3), dtype=torch.int32, device="cuda")
+    counts = torch.empty((1,), dtype=torch.int32, device="cuda")
+    say(f"workload {cfg.name}: tile map + seg")
+    kq.kq_expert_tile_map(u32(r.sorted_ids), cfg.n_experts, map_, counts)
+    y = torch.empty((rows, cfg.n), dtype=torch.float16, device="cuda")
+    kq.kq_gather_qmm_seg(cfg.codec, wq, cfg.n_experts, cfg.n, cfg.k, dev(x), map_, counts, y)
+    count = int(host(counts)[0])
+    tiles, ref_count = matmul.expert_tile_map(r.sorted_ids, cfg.n_experts)
+    assert count == ref_count == 92
+    assert np.array_equal(host(map_)[:count].view(np.uint32), tiles)
+
+    ns = _sample(cfg.n, 24, cfg.seed)
+    widx = (np.arange(cfg.n_experts)[:, None] * cfg.n + ns[None, :]).reshape(-1)
+    wf_s = W.weight_rows(cfg.seed, rows_w, cfg.k, rows=widx)
+    ref_bytes = encode.quantize(cfg.codec, wf_s)
+    assert np.array_equal(host(wq[torch.from_numpy(widx).cuda()]), ref_bytes)
+    ref = matmul.gather_qmm_seg(cfg.codec, ref_bytes.reshape(cfg.n_experts, ns.size, rb), cfg.k, x, tiles)
+    got = host(y)[:, ns].astype(np.float64)
+    err = assert_close_rows(got, ref, what=cfg.name)
+    say(f"workload {cfg.name}: max row-normalized error {err:.2e}")
+    del wq, y
+    torch.cuda.empty_cache()
