@@ -4,11 +4,11 @@ q4_K prefill GEMM (kq_qmm), plus every other row of the path measured once.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-rows] [--no-cpu]
 
-One step = one cold q4_K GEMV (4096 x 4096, one activation row, float32 out;
-its weight copy is one of 64 rotating copies, 604 MB in all, so it is not in
-the 256 MB Infinity Cache) followed by one q4_K GEMM (M=2048, N=14336,
-K=4096, float16 out).  Kernel durations come from HIP events recorded on the
-stream the kernels run on (torch's current stream) around each launch.
+One step = 64 back-to-back q4_K GEMVs (4096 x 4096, one activation row,
+float32 out), each over its own weight copy (604 MB in all, so no copy is in
+the 256 MB Infinity Cache when it is read), then one q4_K GEMM (M=2048,
+N=14336, K=4096, float16 out).  Each is a HIP graph replayed on torch's
+current stream; HIP events on that stream bracket each replay.
 
 Prints ONE JSON line.  ``value`` is the GEMV's algorithmic HBM rate (wire
 bytes + activations + outputs per launch / mean launch duration).
@@ -48,23 +48,31 @@ def parse():
     return p.parse_args()
 
 
-class Timer:
-    """Per-launch HIP events on the current stream."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
-
-    def run(self, fn):
-        s, e = self.torch.cuda.Event(enable_timing=True), self.torch.cuda.Event(enable_timing=True)
-        s.record()
+def capture(torch, fn):
+    """A HIP graph of the launches fn() makes on the capture stream (no memsets inside)."""
+    fn()  # eager run first (also warms the code objects)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
         fn()
-        e.record()
-        self.pairs.append((s, e))
+    torch.cuda.synchronize()
+    return g
 
-    def mean_ms(self):
-        self.torch.cuda.synchronize()
-        return float(np.mean([s.elapsed_time(e) for s, e in self.pairs]))
+
+def time_graph(torch, g, launches, reps, warmup=2):
+    """Mean milliseconds per launch over `reps` replays, HIP events around each replay."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    evs = []
+    for _ in range(reps):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        evs.append((s, e))
+    torch.cuda.synchronize()
+    return float(np.mean([s.elapsed_time(e) for s, e in evs])) / launches
 
 
 def gpu_weights(torch, kq, codec, seed, n, k, dist):
@@ -94,12 +102,9 @@ def measure_rows(torch, kq):
         ws = [wq] + [wq.clone() for _ in range(nc - 1)]
         x = torch.from_numpy(W.gemv_activations(cfg)).cuda()
         y = torch.empty((cfg.m, cfg.n), dtype=torch.float32, device="cuda")
-        for i in range(min(nc, 4)):
-            kq.kq_qmv(cfg.codec, ws[i], cfg.n, cfg.k, x, y)
-        t = Timer(torch)
-        for i in range(reps or max(nc, 8)):
-            t.run(lambda i=i: kq.kq_qmv(cfg.codec, ws[i % nc], cfg.n, cfg.k, x, y))
-        ms = t.mean_ms()
+        nl = reps or max(nc, 8)
+        g = capture(torch, lambda: [kq.kq_qmv(cfg.codec, ws[i % nc], cfg.n, cfg.k, x, y) for i in range(nl)])
+        ms = time_graph(torch, g, nl, 5)
         alg = nb + x.numel() * 2 + y.numel() * 4
         gbs = alg / ms / 1e6
         rows.append({"row": "kq_qmv", "workload": cfg.name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
@@ -123,16 +128,11 @@ def measure_rows(torch, kq):
     map_ = torch.empty((cap, 3), dtype=torch.int32, device="cuda")
     counts = torch.empty((1,), dtype=torch.int32, device="cuda")
     y = torch.empty((x.shape[0], cfg.n), dtype=torch.float16, device="cuda")
-    tm, sg = Timer(torch), Timer(torch)
-    for i in range(2 + 8):
-        fm = lambda: kq.kq_expert_tile_map(ids, cfg.n_experts, map_, counts)  # noqa: E731
-        fs = lambda i=i: kq.kq_gather_qmm_seg(cfg.codec, ws[i % nc], cfg.n_experts, cfg.n, cfg.k, x, map_, counts, y)  # noqa: E731
-        if i < 2:
-            fm(), fs()
-        else:
-            tm.run(fm)
-            sg.run(fs)
-    ms_map, ms_seg = tm.mean_ms(), sg.mean_ms()
+    nl = max(nc, 6)
+    gm = capture(torch, lambda: [kq.kq_expert_tile_map(ids, cfg.n_experts, map_, counts) for _ in range(nl)])
+    gs = capture(torch, lambda: [kq.kq_gather_qmm_seg(cfg.codec, ws[i % nc], cfg.n_experts, cfg.n, cfg.k, x, map_,
+                                                      counts, y) for i in range(nl)])
+    ms_map, ms_seg = time_graph(torch, gm, nl, 5), time_graph(torch, gs, nl, 5)
     alg = wq.numel() + x.numel() * 2 + y.numel() * 2
     flop = 2 * x.shape[0] * cfg.n * cfg.k
     rows.append({"row": "kq_expert_tile_map", "workload": cfg.name, "us": round(ms_map * 1e3, 2)})
@@ -149,11 +149,8 @@ def measure_rows(torch, kq):
     out = torch.empty((c1.n, c1.k), dtype=torch.float16, device="cuda")
     nc = copies_for(wq.numel() + out.numel() * 2)
     ws = [wq] + [wq.clone() for _ in range(nc - 1)]
-    kq.kq_dequantize(c1.codec, wq, c1.k, out)
-    t = Timer(torch)
-    for i in range(nc):
-        t.run(lambda i=i: kq.kq_dequantize(c1.codec, ws[i], c1.k, out))
-    ms = t.mean_ms()
+    g = capture(torch, lambda: [kq.kq_dequantize(c1.codec, ws[i], c1.k, out) for i in range(nc)])
+    ms = time_graph(torch, g, nc, 5)
     alg = wq.numel() + out.numel() * 2
     rows.append({"row": "kq_dequantize", "workload": "q4_K 4096x4096 -> f16", "us": round(ms * 1e3, 2),
                  "GB/s": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3),
@@ -234,32 +231,26 @@ def main():
     flop4 = 2 * c4.m * c4.n * c4.k                                 # 240,518,168,576
     alg4 = w4.numel() + x4.numel() * 2 + y4.numel() * 2
 
-    def step(i, t1=None, t4=None):
-        f1 = lambda: kq.kq_qmv(c1.codec, w1s[i % n_cold], c1.n, c1.k, x1, y1)  # noqa: E731
-        f4 = lambda: kq.kq_qmm(c4.codec, w4, c4.n, c4.k, x4, y4)  # noqa: E731
-        (t1.run(f1) if t1 else f1())
-        (t4.run(f4) if t4 else f4())
-
-    for i in range(args.warmup):
-        step(i)
+    # One step: the 64 cold GEMVs (one HIP graph) and one GEMM (one HIP graph).
+    g1 = capture(torch, lambda: [kq.kq_qmv(c1.codec, w1s[i], c1.n, c1.k, x1, y1) for i in range(n_cold)])
+    g4 = capture(torch, lambda: kq.kq_qmm(c4.codec, w4, c4.n, c4.k, x4, y4))
+    for _ in range(args.warmup):
+        g1.replay()
+        g4.replay()
     torch.cuda.synchronize()
-    t1, t4 = Timer(torch), Timer(torch)
-    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(args.warmup + i, t1, t4)
+        ev[i][0].record()
+        g1.replay()
+        ev[i][1].record()
+        g4.replay()
+        ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms1, ms4 = t1.mean_ms(), t4.mean_ms()
-
-    # back-to-back stream rate over the 64 cold copies (what a decode loop sees)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(n_cold):
-        kq.kq_qmv(c1.codec, w1s[i], c1.n, c1.k, x1, y1)
-    e.record()
-    torch.cuda.synchronize()
-    stream_ms = s.elapsed_time(e) / n_cold
+    ms1 = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) / n_cold
+    ms4 = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    stream_ms = ms1
 
     gbs = alg1 / ms1 / 1e6
     tflops = flop4 / ms4 / 1e9
@@ -295,8 +286,9 @@ def main():
                          "kernel": "kq_qmm q4_K (qmm_kernel)", "alg_flop_per_launch": flop4,
                          "alg_bytes_per_launch": alg4},
         },
-        "qmv_stream_GBps": round(alg1 / stream_ms / 1e6, 1),
-        "qmv_stream_us": round(stream_ms * 1e3, 3),
+        "timing": "HIP graphs: one replay = 64 GEMVs over distinct cold weight copies (back to back on one "
+                  "stream), one replay = one GEMM; HIP events around each replay; per-launch time = replay "
+                  "time / launches (includes the GPU-side gap between consecutive kernels)",
         "device": dev_name,
     }
     del w1s, w1, w4, x4, y4

@@ -6,28 +6,40 @@
 // tile, dead rows of a partial tile skipped, uncovered rows unwritten).
 //
 // Design.
-//  * Workgroup tile BM x BN of the output, K walked 64 values (one "unit") at
-//    a time.  Per step the workgroup stages the x tile (BM x 64 float16) and
-//    DECODES the weight tile (BN rows x 64 values) straight from wire bytes
-//    into LDS as float16 -- each thread decodes half a unit (32 values) with
-//    packed float16 math -- then 4 waves run v_mfma_f32_32x32x16_f16 on it
-//    with float32 accumulators.
-//  * Within a 64-value step the order of k does not matter to the
-//    contraction, only that x and W agree: a q6_K unit's four 16-value
-//    segments are not contiguous in K, so x is gathered with the same
-//    segment map the decode writes with.
-//  * Weights are decoded once per BM rows of x; activations once per BN
-//    weight rows.
-//  * The segment variant takes one tile per workgroup row of the grid: it
-//    reads (expert, row_start, num_rows) and the valid-tile count on the
-//    device, so no host sync sits between the tile map and this kernel.
+//  * A workgroup of 8 waves (2 per SIMD, so one wave's decode overlaps the
+//    other's matrix work) computes a BM x BN output tile, walking K 64 values
+//    (one "unit") per step.  Each step stages the x tile (BM x 64 float16) and
+//    DECODES the weight tile (BN rows x 64 values) from wire bytes into LDS as
+//    float16; the waves then run v_mfma_f32_16x16x32_f16 with float32
+//    accumulators.  LDS is double-buffered and the next step's wire bytes and
+//    activations are loaded into registers before the current step's MFMAs,
+//    so global latency hides behind matrix work; one barrier per step.
+//  * Every decoded weight is rounded to float16 once, from its exact value
+//    (q4_K: one float32 FMA, then RNE; q6_K: exact integer code*scale times
+//    d; q8_0 / q4_0: d times the code), never through a rounded per-block
+//    scale, which would put one correlated error on a whole sub-block.
+//  * Within a 64-value step only the agreement of x and W on k matters to
+//    the contraction: a q6_K unit's four 16-value segments are not
+//    contiguous in K, so x is gathered with the same segment map.
+//  * Tiles are ordered so that the workgroups on one XCD (blocks are dealt to
+//    the 8 XCDs round-robin) share activation panels in that XCD's L2.
+//  * The segment variant reads (expert, row_start, num_rows) and the valid
+//    tile count on the device (no host sync after the tile map); MFMAs of
+//    16-row fragments past num_rows are skipped.
+#include <type_traits>
+
 #include "kq_decode.h"
 
 namespace kq {
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK + 8;  // halves; 144-byte rows spread 16-byte reads over the banks
+constexpr int LDS_STRIDE = BK;  // halves: 128-byte rows of eight 16-byte chunks
+// Chunk c of row r lives at chunk c ^ (r & 7): the MFMA operand reads (16 rows
+// x 16 bytes at one column) then touch every bank once (a plain or 16-byte
+// padded row stride makes them conflict, measured with SQ_LDS_BANK_CONFLICT).
+__device__ __forceinline__ void st_chunk(half_t* row, int sw, int c, u32x4 v) { *(u32x4*)(row + 8 * (c ^ sw)) = v; }
+constexpr int NXCD = 8;
 
 // Row offset of segment t (16 values) of unit u.
 template <int C>
@@ -38,74 +50,97 @@ __device__ __forceinline__ int seg_off(int u, int t) {
 
 __device__ __forceinline__ half2_t h2(half_t a) { return half2_t{a, a}; }
 
-// Decode half of unit u of one weight row into 32 float16 values.  Writes
-// values to dst[16 * t + i] for its two segments t.
+// 16 bytes at a 2-byte-aligned address: dwords from the dword-aligned address
+// below it (never past the 16 bytes), shifted by sh = addr & 3 bytes.
+struct Raw16 {
+  u32x4 a;
+  uint32_t b;
+  __device__ __forceinline__ void load(const uint8_t* p, uint32_t sh) {
+    const uint8_t* q = p - sh;
+    a = ld_16B_a4(q);
+    b = ld_u32(q + 16 - (sh ? 0 : 4));
+  }
+  __device__ __forceinline__ void get(uint32_t sh, uint32_t o[4]) const {
+    o[0] = alignbyte(a.y, a.x, sh);
+    o[1] = alignbyte(a.z, a.y, sh);
+    o[2] = alignbyte(a.w, a.z, sh);
+    o[3] = alignbyte(b, a.w, sh);
+  }
+};
+
+// Half of unit u of one weight row: load() issues its global loads into
+// registers, store() decodes them into 32 float16 values: segment t (16
+// values) is LDS chunks 2t and 2t+1 of the row at dst (swizzle sw = row & 7).
 template <int C> struct HalfUnit;
 
 template <> struct HalfUnit<Q4_K> {
-  // half hh: qs bytes 16*hh..16*hh+15 of the pair = positions l in [16hh, 16hh+16)
-  // of sub-blocks j0 = 2P (low nibbles, segment hh) and j1 = 2P+1 (high, segment 2+hh).
-  // Each weight is the exact float32 value (d*sc)*q - dmin*m (one FMA, inputs
-  // exact) rounded once to float16: rounding d*sc or dmin*m to float16 first
-  // would put one correlated error on all 32 weights of a sub-block.
-  __device__ __forceinline__ static void run(const uint8_t* row, int u, int hh, half_t* dst) {
+  // half hh: qs bytes 16hh..16hh+15 of sub-block pair P = u%4: positions
+  // l in [16hh, 16hh+16) of sub-blocks 2P (low nibbles, segment hh) and 2P+1
+  // (high nibbles, segment 2+hh).
+  u32x4 h, q;
+  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
     const uint8_t* blk = row + (u >> 2) * 144;
-    const u32x4 h = ld_16B(blk);
-    const u32x4 q = ld_16B(blk + 16 + 32 * (u & 3) + 16 * hh);
+    h = ld_16B(blk);
+    q = ld_16B(blk + 16 + 32 * (u & 3) + 16 * hh);
+  }
+  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
     const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
     uint32_t sc0, m0, sc1, m1;
     q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3), sc0, m0);
     q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3) + 1, sc1, m1);
-    const float s0 = d * (float)sc0, n0 = -(dmin * (float)m0);
-    const float s1 = d * (float)sc1, n1 = -(dmin * (float)m1);
+    // Codes come as float16 (1024 + q) from one byte permute per pair; the
+    // weight is fma((1024 + q), s, -(1024 s + dmin m)) in float32 (s and
+    // dmin m exact, the constant rounded once in float32, about 2^-24 of
+    // 1024 s) and rounded once to float16 (v_fma_mix).
+    const float s0 = d * (float)sc0, c0 = -(1024.f * s0 + dmin * (float)m0);
+    const float s1 = d * (float)sc1, c1 = -(1024.f * s1 + dmin * (float)m1);
     const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
     uint32_t lo[8], hi[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t l = qw[i] & 0x0F0F0F0Fu, t = (qw[i] >> 4) & 0x0F0F0F0Fu;
-      lo[2 * i] = pack_h2(fmaf(s0, byte_f32<0>(l), n0), fmaf(s0, byte_f32<1>(l), n0));
-      lo[2 * i + 1] = pack_h2(fmaf(s0, byte_f32<2>(l), n0), fmaf(s0, byte_f32<3>(l), n0));
-      hi[2 * i] = pack_h2(fmaf(s1, byte_f32<0>(t), n1), fmaf(s1, byte_f32<1>(t), n1));
-      hi[2 * i + 1] = pack_h2(fmaf(s1, byte_f32<2>(t), n1), fmaf(s1, byte_f32<3>(t), n1));
+      const half2_t l01 = as_h2(pair01(l)), l23 = as_h2(pair23(l));
+      const half2_t t01 = as_h2(pair01(t)), t23 = as_h2(pair23(t));
+      lo[2 * i] = pack_h2(fmaf((float)l01.x, s0, c0), fmaf((float)l01.y, s0, c0));
+      lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, s0, c0), fmaf((float)l23.y, s0, c0));
+      hi[2 * i] = pack_h2(fmaf((float)t01.x, s1, c1), fmaf((float)t01.y, s1, c1));
+      hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, s1, c1), fmaf((float)t23.y, s1, c1));
     }
-    *(u32x4*)(dst + 16 * hh) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    *(u32x4*)(dst + 16 * hh + 8) = u32x4{lo[4], lo[5], lo[6], lo[7]};
-    *(u32x4*)(dst + 16 * (2 + hh)) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-    *(u32x4*)(dst + 16 * (2 + hh) + 8) = u32x4{hi[4], hi[5], hi[6], hi[7]};
+    st_chunk(dst, sw, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    st_chunk(dst, sw, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
+    st_chunk(dst, sw, 4 + 2 * hh, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    st_chunk(dst, sw, 5 + 2 * hh, u32x4{hi[4], hi[5], hi[6], hi[7]});
   }
 };
-
-// 16 bytes at a 2-byte-aligned address (see kq_qmv.hip: never reads past them).
-__device__ __forceinline__ void ld16_a2(const uint8_t* p, uint32_t sh, uint32_t o[4]) {
-  const uint8_t* q = p - sh;
-  const u32x4 a = ld_16B_a4(q);
-  const uint32_t b = ld_u32(q + 16 - (sh ? 0 : 4));
-  o[0] = alignbyte(a.y, a.x, sh);
-  o[1] = alignbyte(a.z, a.y, sh);
-  o[2] = alignbyte(a.w, a.z, sh);
-  o[3] = alignbyte(b, a.w, sh);
-}
 
 template <> struct HalfUnit<Q6_K> {
   // unit u = (superblock s, h, half); half hh takes c = hh (low nibbles) and
   // c = hh + 2 (high nibbles) of ql[64h + 32hh + 16half + i].
-  __device__ __forceinline__ static void run(const uint8_t* row, int u, int hh, half_t* dst) {
+  Raw16 rq, rh, rs;
+  uint32_t dbits, sh;
+  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
     const uint8_t* blk = row + (u >> 2) * 210;
     const int h = (u >> 1) & 1, half = u & 1;
-    const uint32_t sh = (uint32_t)((uintptr_t)blk & 3);
+    sh = (uint32_t)((uintptr_t)blk & 3);
+    rq.load(blk + 64 * h + 32 * hh + 16 * half, sh);
+    rh.load(blk + 128 + 32 * h + 16 * half, sh);
+    rs.load(blk + 192, sh);
+    dbits = ld_u16(blk + 208);
+  }
+  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+    const int h = (u >> 1) & 1, half = u & 1;
     uint32_t Q[4], H[4], S[4];
-    ld16_a2(blk + 64 * h + 32 * hh + 16 * half, sh, Q);
-    ld16_a2(blk + 128 + 32 * h + 16 * half, sh, H);
-    ld16_a2(blk + 192, sh, S);
-    const float d = f16_to_f32(ld_u16(blk + 208));  // exact in float16 again below
+    rq.get(sh, Q);
+    rh.get(sh, H);
+    rs.get(sh, S);
     // scales[8h + 2c + half]: c = hh in dword 2h (byte half + 2hh), c = hh+2 in dword 2h+1
     const uint32_t slo = h ? S[2] : S[0], shi = h ? S[3] : S[1];
     const int bsh = 8 * (half + 2 * hh);
-    // value = ((q - 32) * sc) * d: (q - 32) * sc is an integer of magnitude <= 4096
-    // (exact in float16 up to 2048), so each weight is rounded once, by itself.
+    // value = ((q - 32) * sc) * d: (q - 32) * sc is an integer of magnitude
+    // <= 4096 (exact in float16 up to 2048), so each weight rounds by itself.
     const half2_t sa = h2((half_t)(float)(int)(int8_t)(slo >> bsh));
     const half2_t sb = h2((half_t)(float)(int)(int8_t)(shi >> bsh));
-    const half2_t dd = h2((half_t)d);
+    const half2_t dd = h2(__builtin_bit_cast(half_t, (uint16_t)dbits));
     const half2_t k1056 = h2((half_t)1056.f);
     const int hs = 2 * hh;
     uint32_t a[8], b[8];
@@ -118,21 +153,27 @@ template <> struct HalfUnit<Q6_K> {
       b[2 * i] = as_u32(((as_h2(pair01(cb)) - k1056) * sb) * dd);
       b[2 * i + 1] = as_u32(((as_h2(pair23(cb)) - k1056) * sb) * dd);
     }
-    *(u32x4*)(dst + 16 * hh) = u32x4{a[0], a[1], a[2], a[3]};
-    *(u32x4*)(dst + 16 * hh + 8) = u32x4{a[4], a[5], a[6], a[7]};
-    *(u32x4*)(dst + 16 * (hh + 2)) = u32x4{b[0], b[1], b[2], b[3]};
-    *(u32x4*)(dst + 16 * (hh + 2) + 8) = u32x4{b[4], b[5], b[6], b[7]};
+    st_chunk(dst, sw, 2 * hh, u32x4{a[0], a[1], a[2], a[3]});
+    st_chunk(dst, sw, 2 * hh + 1, u32x4{a[4], a[5], a[6], a[7]});
+    st_chunk(dst, sw, 2 * hh + 4, u32x4{b[0], b[1], b[2], b[3]});
+    st_chunk(dst, sw, 2 * hh + 5, u32x4{b[4], b[5], b[6], b[7]});
   }
 };
 
 template <> struct HalfUnit<Q8_0> {
   // unit u = two blocks at 68u; half hh = block hh (34 bytes) -> segments 2hh, 2hh+1.
-  __device__ __forceinline__ static void run(const uint8_t* row, int u, int hh, half_t* dst) {
+  // Nine dwords from the dword below the block cover it (sh = 0 or 2).
+  u32x4 r0, r1;
+  uint32_t r8, sh;
+  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
     const uint8_t* p = row + 68 * u + 34 * hh;
-    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+    sh = (uint32_t)((uintptr_t)p & 3);
     const uint8_t* a = p - sh;
-    const u32x4 r0 = ld_16B_a4(a), r1 = ld_16B_a4(a + 16);
-    const uint32_t r8 = ld_u32(a + 32);
+    r0 = ld_16B_a4(a);
+    r1 = ld_16B_a4(a + 16);
+    r8 = ld_u32(a + 32);
+  }
+  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
     const uint32_t R[9] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w, r8};
     const half2_t d = h2(__builtin_bit_cast(half_t, (uint16_t)(sh ? (R[0] >> 16) : (R[0] & 0xFFFFu))));
     const half2_t k1152 = h2((half_t)1152.f);
@@ -140,23 +181,27 @@ template <> struct HalfUnit<Q8_0> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t c = (sh ? R[i + 1] : alignbyte(R[i + 1], R[i], 2)) ^ 0x80808080u;
-      o[2 * i] = as_u32((as_h2(pair01(c)) - k1152) * d);
+      o[2 * i] = as_u32((as_h2(pair01(c)) - k1152) * d);  // exact code, one rounding
       o[2 * i + 1] = as_u32((as_h2(pair23(c)) - k1152) * d);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) *(u32x4*)(dst + 32 * hh + 8 * i) = u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
+    for (int i = 0; i < 4; ++i) st_chunk(dst, sw, 4 * hh + i, u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]});
   }
 };
 
 template <> struct HalfUnit<Q4_0> {
   // unit u = two blocks at 36u; half hh = block hh (18 bytes): low nibbles are
   // values 0..15 (segment 2hh), high nibbles 16..31 (segment 2hh+1).
-  __device__ __forceinline__ static void run(const uint8_t* row, int u, int hh, half_t* dst) {
+  u32x4 r0;
+  uint32_t r4, sh;
+  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
     const uint8_t* p = row + 36 * u + 18 * hh;
-    const uint32_t sh = (uint32_t)((uintptr_t)p & 3);
+    sh = (uint32_t)((uintptr_t)p & 3);
     const uint8_t* a = p - sh;
-    const u32x4 r0 = ld_16B_a4(a);
-    const uint32_t r4 = ld_u32(a + 16);
+    r0 = ld_16B_a4(a);
+    r4 = ld_u32(a + 16);
+  }
+  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
     const uint32_t R[5] = {r0.x, r0.y, r0.z, r0.w, r4};
     const half2_t d = h2(__builtin_bit_cast(half_t, (uint16_t)(sh ? (R[0] >> 16) : (R[0] & 0xFFFFu))));
     const half2_t k1032 = h2((half_t)1032.f);
@@ -170,35 +215,58 @@ template <> struct HalfUnit<Q4_0> {
       hi[2 * i] = as_u32((as_h2(pair01(t)) - k1032) * d);
       hi[2 * i + 1] = as_u32((as_h2(pair23(t)) - k1032) * d);
     }
-    *(u32x4*)(dst + 32 * hh) = u32x4{lo[0], lo[1], lo[2], lo[3]};
-    *(u32x4*)(dst + 32 * hh + 8) = u32x4{lo[4], lo[5], lo[6], lo[7]};
-    *(u32x4*)(dst + 32 * hh + 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
-    *(u32x4*)(dst + 32 * hh + 24) = u32x4{hi[4], hi[5], hi[6], hi[7]};
+    st_chunk(dst, sw, 4 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    st_chunk(dst, sw, 4 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
+    st_chunk(dst, sw, 4 * hh + 2, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    st_chunk(dst, sw, 4 * hh + 3, u32x4{hi[4], hi[5], hi[6], hi[7]});
   }
 };
 
-template <int C, int BM, int BN, int WM, int WN, bool SEG, bool F16>
-__global__ __launch_bounds__(256) void qmm_kernel(const uint8_t* __restrict__ w, int n, int k, int64_t row_bytes,
-                                                  int64_t expert_stride, int n_experts,
-                                                  const half_t* __restrict__ x, int m_total,
-                                                  const uint32_t* __restrict__ map, const uint32_t* __restrict__ counts,
-                                                  void* __restrict__ y) {
-  static_assert(WM * WN == 4, "4 waves");
-  constexpr int TM = BM / WM / 32, TN = BN / WN / 32;
-  static_assert(TM >= 1 && TN >= 1, "wave tile");
-  __shared__ __attribute__((aligned(16))) half_t As[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) half_t Bs[BN * LDS_STRIDE];
+constexpr int QMM_THREADS = 512;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Tile of the (tiles_m x nb, n fastest) grid run by this block: block b runs
+// on XCD b % 8, and XCD x takes the contiguous tile range
+// [x * per_xcd, (x+1) * per_xcd), so its workgroups share x panels in its L2.
+__device__ __forceinline__ int xcd_tile(int per_xcd) {
+  return (int)(blockIdx.x % NXCD) * per_xcd + (int)(blockIdx.x / NXCD);
+}
+
+constexpr int gcd_c(int a, int b) { return b ? gcd_c(b, a % b) : a; }
+constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
+
+// PDA / PDB: prefetch distances in K-steps for activations and weights.  The
+// loads for step s are issued at the start of step s - PD into register slot
+// s % PD, stored (weights: decoded) to LDS buffer s % 2 during step s - 1, and
+// consumed by the MFMAs of step s.  Activations come from L2 (their panel is
+// shared by the tiles of one XCD) and need a shorter distance than weights.
+template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB, bool SEG, bool F16>
+__global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restrict__ w, int n, int k,
+                                                          int64_t row_bytes, int64_t expert_stride, int n_experts,
+                                                          const half_t* __restrict__ x, int m_total,
+                                                          const uint32_t* __restrict__ map,
+                                                          const uint32_t* __restrict__ counts, int tiles_total,
+                                                          int per_xcd, void* __restrict__ y) {
+  static_assert(WM * WN == QMM_THREADS / 64, "8 waves");
+  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
+  constexpr int TM = WTM / 16, TN = WTN / 16;  // 16x16 MFMA tiles per wave
+  static_assert(TM >= 1 && TN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
+  static_assert(PDA >= 1 && PDB >= 1, "prefetch distance");
+  constexpr int A_CHUNKS = BM * 8, A_PER_T = (A_CHUNKS + QMM_THREADS - 1) / QMM_THREADS;
+  constexpr int B_HALVES = BN * 2, B_PER_T = (B_HALVES + QMM_THREADS - 1) / QMM_THREADS;
+  constexpr int UNR = lcm_c(lcm_c(PDA, PDB), 2);
+  __shared__ __attribute__((aligned(16))) half_t As[2][BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) half_t Bs[2][BN * LDS_STRIDE];
+
+  const int t = xcd_tile(per_xcd);
+  if (t >= tiles_total) return;
   const int nb = (n + BN - 1) / BN;
-  const int by = (int)(blockIdx.x / nb);
-  const int n0 = (int)(blockIdx.x % nb) * BN;
+  const int by = t / nb;
+  const int n0 = (t - by * nb) * BN;
   int m0, mrows;
   const uint8_t* wbase = w;
   if (SEG) {
-    const int tile = by;
-    if (tile >= (int)counts[0]) return;
-    const uint32_t* mt = map + 3 * (size_t)tile;
+    if (by >= (int)counts[0]) return;
+    const uint32_t* mt = map + 3 * (size_t)by;
     const uint32_t e = mt[0], rs = mt[1], nr = mt[2];
     if (e >= (uint32_t)n_experts || nr == 0 || nr > 64 || rs >= (uint32_t)m_total || nr > (uint32_t)m_total - rs)
       return;
@@ -210,70 +278,152 @@ __global__ __launch_bounds__(256) void qmm_kernel(const uint8_t* __restrict__ w,
     mrows = min(BM, m_total - m0);
   }
 
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
-  const int wr0 = wm * (BM / WM), wc0 = wn * (BN / WN);
-  const bool wave_live = wr0 < mrows;  // dead row fragments of a partial tile skip the MFMAs
+  const int wr0 = wm * WTM, wc0 = wn * WTN;
+  // 16-row fragments of this wave that hold live rows (the rest skip their MFMAs)
+  const int live_tm = min(TM, max(0, (mrows - wr0 + 15) / 16));
 
-  float16_t acc[TM][TN];
+  float4_t acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+    for (int j = 0; j < TN; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int units = k / BK;
-  for (int u = 0; u < units; ++u) {
-    // x tile: BM rows x 4 segments x 2 halves of 8 values
-    for (int c = tid; c < BM * 8; c += 256) {
-      const int r = c >> 3, part = c & 7, t = part >> 1, hf = part & 1;
-      u32x4 v = {0, 0, 0, 0};
-      if (r < mrows) v = *(const u32x4*)(x + (int64_t)(m0 + r) * k + seg_off<C>(u, t) + 8 * hf);
-      *(u32x4*)(As + r * LDS_STRIDE + 16 * t + 8 * hf) = v;
-    }
-    // weight tile: BN rows x 2 half-units
-    for (int c = tid; c < BN * 2; c += 256) {
-      const int r = c >> 1, hh = c & 1;
-      half_t* dst = Bs + r * LDS_STRIDE;
-      if (n0 + r < n) {
-        HalfUnit<C>::run(wbase + (int64_t)(n0 + r) * row_bytes, u, hh, dst);
-      } else {
-        const u32x4 z = {0, 0, 0, 0};
+  u32x4 areg[PDA][A_PER_T];
+  HalfUnit<C> braw[PDB][B_PER_T];
+
+  // Activation chunks: 8 per tile row (4 segments x 2 halves of 8 values).
+  // Rows past the tile read a clamped valid row; their outputs are never
+  // stored, so no predicate sits in the K loop.
+  const half_t* xrow[A_PER_T];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(u32x4*)(dst + 32 * hh + 8 * i) = z;
-      }
-    }
-    __syncthreads();
-    if (wave_live) {
-#pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        half8_t a[TM], b[TN];
-        const int kk = 16 * ks + 8 * (lane >> 5);
-#pragma unroll
-        for (int i = 0; i < TM; ++i) a[i] = *(const half8_t*)(As + (wr0 + 32 * i + (lane & 31)) * LDS_STRIDE + kk);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) b[j] = *(const half8_t*)(Bs + (wc0 + 32 * j + (lane & 31)) * LDS_STRIDE + kk);
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+  for (int i = 0; i < A_PER_T; ++i) {
+    const int c = min(tid + i * QMM_THREADS, A_CHUNKS - 1), r = c >> 3;
+    xrow[i] = x + (int64_t)min(m0 + r, m_total - 1) * k + 8 * (c & 1);
   }
+  // Weight half-units: wave w decodes rows [w * RPW, (w+1) * RPW), two lanes
+  // (halves) per row, so every wave has the same decode work.  Spare lanes
+  // redo the wave's last row (same values to the same LDS bytes), so no lane
+  // is masked off.  Rows past N read a clamped valid row (finite values,
+  // outputs never stored).
+  constexpr int RPW = BN / 8;  // rows per wave
+  static_assert(BN % 8 == 0 && 2 * RPW <= 64 && B_PER_T == 1, "one half-unit per lane");
+  const int brow0 = wave * RPW + min(lane >> 1, RPW - 1);
+  const uint8_t* const wrow0 = wbase + (int64_t)min(n0 + brow0, n - 1) * row_bytes;
 
-  if (!wave_live) return;
-  // 32x32 accumulator layout: lane holds column (lane & 31); register r holds
-  // row 8*(r/4) + 4*(lane/32) + (r%4).
+  auto issue_a = [&](int slot, int u) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int part = (tid + i * QMM_THREADS) & 7;
+      areg[slot][i] = *(const u32x4*)(xrow[i] + seg_off<C>(u, part >> 1));
+    }
+  };
+  auto issue_b = [&](int slot, int u) { braw[slot][0].load(wrow0, u, lane & 1); };
+  auto stage = [&](int sa, int sb, int buf, int u) {
+#pragma unroll
+    for (int i = 0; i < A_PER_T; ++i) {
+      const int c = tid + i * QMM_THREADS;
+      if (A_CHUNKS % QMM_THREADS == 0 || c < A_CHUNKS) {
+        const int r = c >> 3, part = c & 7;
+        st_chunk(&As[buf][r * LDS_STRIDE], r & 7, part, areg[sa][i]);
+      }
+    }
+    braw[sb][0].store(u, lane & 1, &Bs[buf][brow0 * LDS_STRIDE], brow0 & 7);
+  };
+  // All fragment reads of a 32-wide K slice are issued before its MFMAs, in
+  // the order the MFMAs consume them, so one LDS round trip per slice is
+  // exposed instead of one per A fragment.  Full tiles take a copy without
+  // the dead-fragment test.
+  auto mfma_slice = [&](int buf, int ks, auto full) {
+    constexpr bool FULL = decltype(full)::value;
+    const int kk = 8 * ((4 * ks + (lane >> 4)) ^ (lane & 7));
+    half8_t a[TM], b[TN];
+    a[0] = *(const half8_t*)(&As[buf][(wr0 + (lane & 15)) * LDS_STRIDE + kk]);
+#pragma unroll
+    for (int j = 0; j < TN; ++j) b[j] = *(const half8_t*)(&Bs[buf][(wc0 + 16 * j + (lane & 15)) * LDS_STRIDE + kk]);
+#pragma unroll
+    for (int i = 1; i < TM; ++i) a[i] = *(const half8_t*)(&As[buf][(wr0 + 16 * i + (lane & 15)) * LDS_STRIDE + kk]);
+    asm volatile("" ::: "memory");  // keep every read above the MFMAs (the scheduler would sink them)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (FULL || i < live_tm) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+  const bool full_rows = live_tm == TM;
+  auto mfma_step = [&](int buf) {
+    if (full_rows) {
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) mfma_slice(buf, ks, std::true_type{});
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < BK / 32; ++ks) mfma_slice(buf, ks, std::false_type{});
+    }
+  };
+
+  // Waves w and w+4 share a SIMD: the first four stage the next step before
+  // their MFMAs, the other four after, so one wave's decode runs while its
+  // partner's MFMAs occupy the matrix unit.  The steady-state loop body has no
+  // branches (step indices are clamped instead: a clamped extra load or stage
+  // is harmless), so the compiler keeps PD steps of loads in flight.
+  const int units = k / BK;
+  const int last = units - 1;
+#pragma unroll
+  for (int s = 0; s < PDA; ++s) issue_a(s, min(s, last));
+#pragma unroll
+  for (int s = 0; s < PDB; ++s) issue_b(s, min(s, last));
+  stage(0, 0, 0, 0);
+  __syncthreads();
+  const int units_main = units - units % UNR;
+  auto kloop = [&](auto sf) {
+    constexpr bool SF = decltype(sf)::value;
+    for (int u0 = 0; u0 < units_main; u0 += UNR) {
+#pragma unroll
+      for (int du = 0; du < UNR; ++du) {
+        const int u = u0 + du;
+        issue_a(du % PDA, min(u + PDA, last));
+        issue_b(du % PDB, min(u + PDB, last));
+        if (SF) stage((du + 1) % PDA, (du + 1) % PDB, (du + 1) & 1, min(u + 1, last));
+        mfma_step(du & 1);
+        if (!SF) stage((du + 1) % PDA, (du + 1) % PDB, (du + 1) & 1, min(u + 1, last));
+        __syncthreads();
+      }
+    }
+    // leftover steps (units not a multiple of UNR): slot = du % PD still holds
+    // because units_main is a multiple of both distances
+#pragma unroll
+    for (int du = 0; du < UNR; ++du) {
+      const int u = units_main + du;
+      if (u < units) {
+        issue_a(du % PDA, min(u + PDA, last));
+        issue_b(du % PDB, min(u + PDB, last));
+        if (SF) stage((du + 1) % PDA, (du + 1) % PDB, (du + 1) & 1, min(u + 1, last));
+        mfma_step(du & 1);
+        if (!SF) stage((du + 1) % PDA, (du + 1) % PDB, (du + 1) & 1, min(u + 1, last));
+        __syncthreads();
+      }
+    }
+  };
+  if (wave < 4)
+    kloop(std::true_type{});
+  else
+    kloop(std::false_type{});
+
+  // 16x16 accumulator layout: lane holds column (lane & 15); register r holds
+  // row 4*(lane/16) + r.
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    if (i >= live_tm) continue;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wc0 + 32 * j + (lane & 31);
+      const int col = n0 + wc0 + 16 * j + (lane & 15);
       if (col >= n) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wr0 + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = wr0 + 16 * i + 4 * (lane >> 4) + r;
         if (row < mrows) {
           const int64_t o = (int64_t)(m0 + row) * n + col;
           if (F16)
@@ -283,35 +433,41 @@ __global__ __launch_bounds__(256) void qmm_kernel(const uint8_t* __restrict__ w,
         }
       }
     }
+  }
 }
 
-template <int C, bool SEG, int BM, int BN, int WM, int WN>
+template <int C, bool SEG, int BM, int BN, int WM, int WN, int PDA, int PDB>
 hipError_t launch_t(const uint8_t* w, int64_t n, int64_t k, int64_t rb, int64_t estride, int64_t ne, const half_t* x,
-                    int64_t m, const uint32_t* map, const uint32_t* counts, int64_t gy, void* y, int f16, hipStream_t s) {
-  const dim3 grid((unsigned)(((n + BN - 1) / BN) * gy));
+                    int64_t m, const uint32_t* map, const uint32_t* counts, int64_t tiles_m, void* y, int f16,
+                    hipStream_t s) {
+  const int64_t tiles = tiles_m * ((n + BN - 1) / BN);
+  const int64_t per_xcd = (tiles + NXCD - 1) / NXCD;
+  const dim3 grid((unsigned)(per_xcd * NXCD));
   if (f16)
-    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, SEG, true>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb,
-                       estride, (int)ne, x, (int)m, map, counts, y);
+    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, SEG, true>), grid, dim3(QMM_THREADS), 0, s, w, (int)n, (int)k,
+                       rb, estride, (int)ne, x, (int)m, map, counts, (int)tiles, (int)per_xcd, y);
   else
-    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, SEG, false>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb,
-                       estride, (int)ne, x, (int)m, map, counts, y);
+    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, SEG, false>), grid, dim3(QMM_THREADS), 0, s, w, (int)n, (int)k,
+                       rb, estride, (int)ne, x, (int)m, map, counts, (int)tiles, (int)per_xcd, y);
   return hipGetLastError();
 }
 
 template <int C>
 hipError_t launch_dense(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m, void* y,
                         int f16, hipStream_t s) {
-  return launch_t<C, false, 128, 128, 2, 2>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, (m + 127) / 128, y, f16, s);
+  if (m > 128)  // prefill: 256 x 224 tiles (N = 14336 gives 64 tile columns)
+    return launch_t<C, false, 256, 224, 4, 2, 1, 2>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, (m + 255) / 256, y, f16, s);
+  if (m > 64)
+    return launch_t<C, false, 128, 256, 2, 4, 2, 3>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, (m + 127) / 128, y, f16, s);
+  return launch_t<C, false, 64, 256, 2, 4, 2, 4>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, (m + 63) / 64, y, f16, s);
 }
 
 template <int C>
 hipError_t launch_seg(const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t rows,
                       const uint32_t* map, const uint32_t* counts, int64_t cap, void* y, int f16, hipStream_t s) {
-  return launch_t<C, true, 64, 128, 2, 2>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+  return launch_t<C, true, 64, 256, 2, 4, 2, 4>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
 }
 
-// Generic fallback for K with an odd number of 32-value blocks (q8_0 / q4_0):
-// one float32 dot per output, 64 lanes over K.  Correct, not fast.
 template <int C, bool SEG, bool F16>
 __global__ __launch_bounds__(256) void qmm_generic_kernel(const uint8_t* __restrict__ w, int n, int k, int64_t rb,
                                                           int64_t estride, int n_experts, const half_t* __restrict__ x,
