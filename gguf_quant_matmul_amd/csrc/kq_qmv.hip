@@ -33,10 +33,11 @@ constexpr int ROWS_PER_WAVE = 64 / LANES_PER_ROW;
 constexpr int ROWS_PER_BLOCK = ROWS_PER_WAVE * (QMV_THREADS / 64);
 constexpr int UNROLL = 4;
 
-// K values per LDS chunk for M activation rows (x: 2.25 bytes/value/row with
-// padding, sums: 0.25 bytes/value/row) -- about 40 KB.
+// K values per LDS chunk for M activation rows: at most 8192 activation
+// values per chunk, so each thread stages at most four 16-byte pieces of x
+// (held in registers while the weight loads go out).
 __host__ __device__ constexpr int kchunk_max(int m) {
-  return m <= 1 ? 16384 : m <= 2 ? 8192 : m <= 4 ? 4096 : 2048;
+  return m <= 2 ? 4096 : m <= 4 ? 2048 : 1024;
 }
 __host__ __device__ constexpr int xpad(int v) { return v + (v >> 6) * 8; }  // padded LDS offset (halves)
 
@@ -295,17 +296,38 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
   for (int c0 = 0; c0 < k; c0 += KC) {
     const int kc = (k - c0) < KC ? (k - c0) : KC;
     const int ub = c0 / 64, ue = (c0 + kc) / 64;
+    // Unit u of this lane in group g is ub + uslot + LANES_PER_ROW * (g * UNROLL + j).
+    // Loads are never predicated: an index past the chunk is clamped to its
+    // last unit (and its product skipped), so all loads of a group go out
+    // back to back with no wait between them.
+    const int ngroups = (ue - ub + LANES_PER_ROW * UNROLL - 1) / (LANES_PER_ROW * UNROLL);
+    // Activation loads first, then the first group's weight loads: loads
+    // retire in order, so the LDS staging below waits for x only, and the
+    // weights keep streaming in while x is staged and summed.
+    constexpr int XPT = (M * KC / 8 + QMV_THREADS - 1) / QMV_THREADS;
+    const int xpieces = M * (kc / 8);
+    u32x4 xr[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      int c = tid + i * QMV_THREADS;
+      c = c < xpieces ? c : xpieces - 1;
+      const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
+      xr[i] = *(const u32x4*)(x + (int64_t)m * k + c0 + v);
+    }
     Unit cur[UNROLL];
-    // issue the first group's weight loads before staging x
 #pragma unroll
     for (int j = 0; j < UNROLL; ++j) {
       const int u = ub + uslot + LANES_PER_ROW * j;
-      if (row_ok && u < ue) cur[j].load(wrow, u);
+      cur[j].load(wrow, u < ue ? u : ue - 1);
     }
     if (c0) __syncthreads();  // previous chunk done with LDS
-    for (int i = tid; i < M * (kc / 8); i += QMV_THREADS) {
-      const int m = i / (kc / 8), v = (i % (kc / 8)) * 8;
-      *(u32x4*)(xs + m * xstride + xpad(v)) = *(const u32x4*)(x + (int64_t)m * k + c0 + v);
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * QMV_THREADS;
+      if (c < xpieces) {
+        const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
+        *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
+      }
     }
     __syncthreads();
     for (int i = tid; i < M * (kc / 16); i += QMV_THREADS) {
@@ -320,14 +342,14 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
     }
     __syncthreads();
     const Xv xv{xs, xsum, xstride, sstride, c0};
-    for (int u0 = ub + uslot; u0 < ue; u0 += LANES_PER_ROW * UNROLL) {
+    for (int g = 0; g < ngroups; ++g) {
+      const int u0 = ub + uslot + LANES_PER_ROW * UNROLL * g;
       Unit nxt[UNROLL];
-      const int un = u0 + LANES_PER_ROW * UNROLL;
-      if (un < ue) {
+      if (g + 1 < ngroups) {  // uniform across the block
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
-          const int u = un + LANES_PER_ROW * j;
-          if (row_ok && u < ue) nxt[j].load(wrow, u);
+          const int u = u0 + LANES_PER_ROW * (UNROLL + j);
+          nxt[j].load(wrow, u < ue ? u : ue - 1);
         }
       }
 #pragma unroll
