@@ -3,6 +3,7 @@
 q4_K prefill GEMM (kq_qmm), plus every other row of the path measured once.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-rows] [--no-cpu]
+    python bench.py --counters      # eager launches for rocprofv3 --pmc passes
 
 One step = 64 back-to-back q4_K GEMVs (4096 x 4096, one activation row,
 float32 out), each over its own weight copy (604 MB in all, so no copy is in
@@ -17,6 +18,7 @@ bytes + activations + outputs per launch / mean launch duration).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -32,6 +34,32 @@ METRIC = "q4_K qmv GB/s (% of HBM peak); q4_K qmm TFLOP/s (% of f16 MFMA peak)"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16 MFMA, published
 COLD_BYTES = 512 << 20         # rotate weight copies until this much is touched (> 256 MB MALL)
+COPY_REF_BYTES = 256 << 20     # the elementwise copy that scales the HBM byte counters
+
+# HBM bytes per launch from rocprofv3 counter passes over ``bench.py --counters``
+# (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's reading for a
+# copy of COPY_REF_BYTES).  A figure is reported only while the digest of the
+# kernel's sources still matches the one the counters were taken on.
+TRAFFIC = {
+    "qmv": {"sources": ("kq_qmv.hip", "kq_decode.h", "kq_internal.h"), "digest": "9d3e8788fcc51e57",
+            "bytes": 9646699},
+    "qmm": {"sources": ("kq_qmm.hip", "kq_internal.h"), "digest": "91a9fc386d78b403", "bytes": 357126232},
+}
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "gguf_quant_matmul_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(kernel):
+    t = TRAFFIC[kernel]
+    if t["bytes"] is None or t["digest"] != source_digest(t["sources"]):
+        return None
+    return t["bytes"]
 
 
 def log(*a):
@@ -45,6 +73,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=8)
     p.add_argument("--no-rows", action="store_true", help="skip the per-row measurements")
     p.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    p.add_argument("--counters", action="store_true",
+                   help="no timing: eager launches of the copy reference, the 64 cold GEMVs and 2 GEMMs, "
+                        "for rocprofv3 --pmc passes")
+    p.add_argument("--digests", action="store_true", help="print the kernels' source digests and exit")
     return p.parse_args()
 
 
@@ -160,6 +192,29 @@ def measure_rows(torch, kq):
     return rows
 
 
+def counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4):
+    """Eager launches for hardware-counter passes.  First a plain elementwise
+    copy (torch.neg) of COPY_REF_BYTES four times: it reads and writes exactly
+    that many bytes, which calibrates FETCH_SIZE and WRITE_SIZE.  Then the
+    timed workloads as the timed region runs them: one GEMV per cold weight
+    copy and two GEMMs."""
+    from gguf_quant_matmul_amd import workloads as W
+
+    c1, c4 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM
+    src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    for w in w1s:
+        kq.kq_qmv(c1.codec, w, c1.n, c1.k, x1, y1)
+    for _ in range(2):
+        kq.kq_qmm(c4.codec, w4, c4.n, c4.k, x4, y4)
+    torch.cuda.synchronize()
+    return {"mode": "counters", "copy_ref_bytes": COPY_REF_BYTES, "copy_launches": 4,
+            "qmv_launches": len(w1s), "qmm_launches": 2}
+
+
 def cpu_baseline():
     """The oracle as it stands, on a bounded sample of the two workloads, on this host."""
     from gguf_quant_matmul_amd import workloads as W
@@ -202,6 +257,9 @@ def cpu_baseline():
 
 def main():
     args = parse()
+    if args.digests:
+        print(json.dumps({k: source_digest(v["sources"]) for k, v in TRAFFIC.items()}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the kq path is a single-GPU kernel library "
               "(its multi-GPU sharding is a design note, not built).", file=sys.stderr)
@@ -230,6 +288,9 @@ def main():
     alg1 = w1.numel() + x1.numel() * 2 + y1.numel() * 4           # 9,461,760 B
     flop4 = 2 * c4.m * c4.n * c4.k                                 # 240,518,168,576
     alg4 = w4.numel() + x4.numel() * 2 + y4.numel() * 2
+    if args.counters:
+        print(json.dumps(counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4)), flush=True)
+        return
 
     # One step: the 64 cold GEMVs (one HIP graph) and one GEMM (one HIP graph).
     g1 = capture(torch, lambda: [kq.kq_qmv(c1.codec, w1s[i], c1.n, c1.k, x1, y1) for i in range(n_cold)])
@@ -275,14 +336,14 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic("qmv"),
             "kernel": "kq_qmv q4_K (qmv_kernel<12,1,false>)", "alg_bytes_per_launch": alg1,
             "mean_launch_us": round(ms1 * 1e3, 3),
         },
         "qmm": {
             "value": round(tflops, 1), "unit": "TFLOP/s", "mean_launch_us": round(ms4 * 1e3, 2),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                         "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic("qmm"),
                          "kernel": "kq_qmm q4_K (qmm_kernel)", "alg_flop_per_launch": flop4,
                          "alg_bytes_per_launch": alg4},
         },
