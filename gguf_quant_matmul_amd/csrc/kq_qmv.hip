@@ -10,10 +10,11 @@
 //  * A "unit" is 64 weights of one row: q4_K one sub-block pair (its 16-byte
 //    header + 32 bytes of qs), q6_K one (h, half) slice of a superblock (16 B
 //    of each ql half, 16 B of qh, 4 scales), q8_0 / q4_0 two blocks.
-//  * A wave owns 4 rows; each row is split over 16 lanes that walk the row's
-//    units with a stride of 16.  Every load is a 16-byte (or 4-byte aligned
-//    multi-dword) load of raw wire bytes; all loads of a lane's units are
-//    issued before any is used.
+//  * A row is split over 16 lanes (a wave owns 4 rows) or, for one
+//    activation row and a matrix with few rows, over a whole wave; the lanes
+//    walk the row's units with a stride of the lane count.  Every load is a 16-byte (or 4-byte
+//    aligned multi-dword) load of raw wire bytes; all loads of a lane's units
+//    are issued before any is used.
 //  * Codes become float16 pairs by byte permutes onto a 0x64 exponent byte
 //    (value 1024 + code); v_dot2 with float16 activations accumulates in
 //    float32, and the 1024 offset (plus each codec's zero point) is removed
@@ -21,17 +22,18 @@
 //  * x is staged once per workgroup in LDS as float16 (with 16 bytes of
 //    padding per 64 values against bank conflicts) together with its 16-value
 //    sums.  Long K is processed in chunks that fit LDS.
-//  * Partial sums of a row's 16 lanes are reduced with DPP row rotations.
+//  * Partial sums of a row's lanes are reduced with DPP row rotations (and
+//    lane swaps across 16-lane rows).
 #include "kq_decode.h"
 
 namespace kq {
 namespace {
 
 constexpr int QMV_THREADS = 256;
-constexpr int LANES_PER_ROW = 16;
-constexpr int ROWS_PER_WAVE = 64 / LANES_PER_ROW;
-constexpr int ROWS_PER_BLOCK = ROWS_PER_WAVE * (QMV_THREADS / 64);
-constexpr int UNROLL = 4;
+// A row is split over LPR lanes (16, 32 or 64); a lane takes UNITS_PER_GROUP /
+// LPR units per load group, so a group is always 64 units of a row.
+constexpr int UNITS_PER_GROUP = 64;
+__host__ __device__ constexpr int rows_per_block(int lpr) { return (64 / lpr) * (QMV_THREADS / 64); }
 
 // K values per LDS chunk for M activation rows: at most 8192 activation
 // values per chunk, so each thread stages at most four 16-byte pieces of x
@@ -270,7 +272,17 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
-template <int C, int M, bool F16>
+// Sum over the LPR lanes of a row: DPP within 16-lane rows, then swaps
+// across them.
+template <int LPR>
+__device__ __forceinline__ float lanes_sum(float v) {
+  v = row16_sum(v);
+  if (LPR >= 32) v += __shfl_xor(v, 16);
+  if (LPR >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+template <int C, int M, int LPR, bool F16>
 __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                           int64_t row_bytes, const half_t* __restrict__ x,
                                                           void* __restrict__ y) {
@@ -284,6 +296,7 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
   const int sstride = kc_alloc / 16;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int LANES_PER_ROW = LPR, ROWS_PER_WAVE = 64 / LPR, UNROLL = UNITS_PER_GROUP / LPR;
   const int rslot = lane / LANES_PER_ROW, uslot = lane % LANES_PER_ROW;
   const int row = (blockIdx.x * (QMV_THREADS / 64) + wave) * ROWS_PER_WAVE + rslot;
   const bool row_ok = row < n;
@@ -321,24 +334,21 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
       cur[j].load(wrow, u < ue ? u : ue - 1);
     }
     if (c0) __syncthreads();  // previous chunk done with LDS
+    // Stage x and its 16-value sums in one pass: pieces 2g and 2g + 1 (8
+    // values each) sit in adjacent lanes, so each lane sums its own 8 values
+    // and adds its neighbour's with a DPP quad permutation [1, 0, 3, 2].
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int c = tid + i * QMV_THREADS;
+      const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0)
+      float s = 0.f;
+      s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
+      s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
       if (c < xpieces) {
         const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
         *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
+        if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
       }
-    }
-    __syncthreads();
-    for (int i = tid; i < M * (kc / 16); i += QMV_THREADS) {
-      const int m = i / (kc / 16), g = i % (kc / 16);
-      const u32x4 a = *(const u32x4*)(xs + m * xstride + xpad(16 * g));
-      const u32x4 b = *(const u32x4*)(xs + m * xstride + xpad(16 * g) + 8);
-      float s = 0.f;
-      const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0)
-      s = dot2(a.x, one2, s); s = dot2(a.y, one2, s); s = dot2(a.z, one2, s); s = dot2(a.w, one2, s);
-      s = dot2(b.x, one2, s); s = dot2(b.y, one2, s); s = dot2(b.z, one2, s); s = dot2(b.w, one2, s);
-      xsum[m * sstride + g] = s;
     }
     __syncthreads();
     const Xv xv{xs, xsum, xstride, sstride, c0};
@@ -363,7 +373,7 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
   }
 
 #pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = row16_sum(acc[m]);
+  for (int m = 0; m < M; ++m) acc[m] = lanes_sum<LPR>(acc[m]);
   if (row_ok && uslot < M) {
     float v = acc[0];
 #pragma unroll
@@ -413,17 +423,28 @@ __global__ __launch_bounds__(256) void qmv_generic_kernel(const uint8_t* __restr
   }
 }
 
+template <int C, int M, int LPR>
+hipError_t launch_ml(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
+                     hipStream_t s) {
+  const int kc = (int)(k < kchunk_max(M) ? k : kchunk_max(M));
+  const size_t lds = (size_t)M * xpad(kc) * 2 + (size_t)M * (kc / 16) * 4;
+  const dim3 grid((unsigned)((n + rows_per_block(LPR) - 1) / rows_per_block(LPR)));
+  if (f16)
+    hipLaunchKernelGGL((qmv_kernel<C, M, LPR, true>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y);
+  else
+    hipLaunchKernelGGL((qmv_kernel<C, M, LPR, false>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y);
+  return hipGetLastError();
+}
+
+// One wave per row (64 lanes, one 64-value unit each at K = 4096) for one
+// activation row and a matrix with few rows: four times the workgroups and a
+// quarter of the serial work per lane.  Otherwise 16 lanes per row, so the
+// activation staging is shared by 16 rows per workgroup.
 template <int C, int M>
 hipError_t launch_m(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
                     hipStream_t s) {
-  const int kc = (int)(k < kchunk_max(M) ? k : kchunk_max(M));
-  const size_t lds = (size_t)M * xpad(kc) * 2 + (size_t)M * (kc / 16) * 4;
-  const dim3 grid((unsigned)((n + ROWS_PER_BLOCK - 1) / ROWS_PER_BLOCK));
-  if (f16)
-    hipLaunchKernelGGL((qmv_kernel<C, M, true>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y);
-  else
-    hipLaunchKernelGGL((qmv_kernel<C, M, false>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y);
-  return hipGetLastError();
+  if (M == 1 && n <= 32768) return launch_ml<C, M, 64>(w, n, k, rb, x, y, f16, s);
+  return launch_ml<C, M, 16>(w, n, k, rb, x, y, f16, s);
 }
 
 template <int C>
