@@ -24,6 +24,8 @@
 //    sums.  Long K is processed in chunks that fit LDS.
 //  * Partial sums of a row's lanes are reduced with DPP row rotations (and
 //    lane swaps across 16-lane rows).
+#include <type_traits>
+
 #include "kq_decode.h"
 
 namespace kq {
@@ -423,6 +425,298 @@ __global__ __launch_bounds__(256) void qmv_generic_kernel(const uint8_t* __restr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core GEMV for 3 <= M <= 8 activation rows.  With more than two rows
+// the dot2 path spends M v_dot2 per pair of weights; here each weight is
+// decoded once to float16 (its exact value rounded once) and the products go
+// to v_mfma_f32_16x16x32_f16.  B operand: 16 weight rows x 32 K values, lane
+// l holding row (l & 15) and 8 consecutive values of unit 4g + (l >> 4) of
+// that row, so each lane still decodes whole units from their wire bytes.
+// The contraction only needs A and B to agree on K, so the 32 K values of an
+// MFMA come from four different units.  A operand: the same K positions of
+// activation row (l & 15); rows past M repeat row M - 1 and their outputs are
+// dropped.  A wave owns 16 weight rows and a part of K (MMA_KSPLIT waves of a
+// workgroup share a row group); the parts meet in LDS at the end.
+// ---------------------------------------------------------------------------
+
+// Two float16 pairs (1024 + code) -> weights fma(1024 + code, s, c), each
+// rounded once to float16.
+__device__ __forceinline__ uint32_t fma_pair(uint32_t p, float s, float c) {
+  const half2_t h = as_h2(p);
+  return pack_h2(fmaf((float)h.x, s, c), fmaf((float)h.y, s, c));
+}
+__device__ __forceinline__ void slice8(uint32_t c0, uint32_t c1, float s, float c, uint32_t f[4]) {
+  f[0] = fma_pair(pair01(c0), s, c);
+  f[1] = fma_pair(pair23(c0), s, c);
+  f[2] = fma_pair(pair01(c1), s, c);
+  f[3] = fma_pair(pair23(c1), s, c);
+}
+
+// Slice S (8 consecutive K values) of a unit: get<S> gives its float16
+// weights f[4] (all zero for a lane that keeps nothing); koff(u) is the row
+// offset of the unit's first value and xstep<S> the slice's offset from it in
+// padded LDS units.
+template <int C> struct MmaSlices;
+
+template <> struct MmaSlices<Q4_K> {
+  // values 0..31: low nibbles of the 32 qs bytes (sub-block 2P), 32..63: high
+  // nibbles (sub-block 2P + 1); weight = d sc q - dmin m
+  float s0, c0, s1, c1;
+  uint32_t qw[8];
+  __device__ __forceinline__ MmaSlices(const UnitQ4K& un, int u, bool keep) {
+    const float d = keep ? f16_to_f32(un.h.x) : 0.f, dmin = keep ? f16_to_f32(un.h.x >> 16) : 0.f;
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(un.h.y, un.h.z, un.h.w, 2 * (u & 3), sc0, m0);
+    q4k_scale_min(un.h.y, un.h.z, un.h.w, 2 * (u & 3) + 1, sc1, m1);
+    s0 = d * (float)sc0; c0 = -(1024.f * s0 + dmin * (float)m0);
+    s1 = d * (float)sc1; c1 = -(1024.f * s1 + dmin * (float)m1);
+    qw[0] = un.q0.x; qw[1] = un.q0.y; qw[2] = un.q0.z; qw[3] = un.q0.w;
+    qw[4] = un.q1.x; qw[5] = un.q1.y; qw[6] = un.q1.z; qw[7] = un.q1.w;
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int t = S & 3;
+    if (S < 4)
+      slice8(qw[2 * t] & 0x0F0F0F0Fu, qw[2 * t + 1] & 0x0F0F0F0Fu, s0, c0, f);
+    else
+      slice8((qw[2 * t] >> 4) & 0x0F0F0F0Fu, (qw[2 * t + 1] >> 4) & 0x0F0F0F0Fu, s1, c1, f);
+  }
+};
+
+template <> struct MmaSlices<Q6_K> {
+  // four 16-value segments cc at base + 32 cc; weight = d sc (q - 32)
+  uint32_t c[4][4];
+  float sc[4];
+  int base;
+  __device__ __forceinline__ MmaSlices(const UnitQ6K& un, int u, bool keep) {
+    const int h = (u >> 1) & 1, half = u & 1;
+    uint32_t A[4], B[4], H[4], S[4];
+    un.qa.get(un.sh, A); un.qb.get(un.sh, B); un.qhh.get(un.sh, H); un.scl.get(un.sh, S);
+    const float d = keep ? f16_to_f32(un.dbits) : 0.f;
+    const uint32_t slo = h ? S[2] : S[0], shi = h ? S[3] : S[1];
+    sc[0] = d * (float)(int)(int8_t)(slo >> (8 * half));
+    sc[1] = d * (float)(int)(int8_t)(slo >> (8 * (half + 2)));
+    sc[2] = d * (float)(int)(int8_t)(shi >> (8 * half));
+    sc[3] = d * (float)(int)(int8_t)(shi >> (8 * (half + 2)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[0][i] = (A[i] & 0x0F0F0F0Fu) | ((H[i] << 4) & 0x30303030u);
+      c[1][i] = (B[i] & 0x0F0F0F0Fu) | ((H[i] << 2) & 0x30303030u);
+      c[2][i] = ((A[i] >> 4) & 0x0F0F0F0Fu) | (H[i] & 0x30303030u);
+      c[3][i] = ((B[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u);
+    }
+    base = 256 * (u >> 2) + 128 * h + 16 * half;
+  }
+  // the unit starts 0 or 16 values into a 64-value block and spans 128
+  // values, so segments 2 and 3 sit one padding step further in LDS
+  static __device__ __forceinline__ int koff(int u) { return 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1); }
+  template <int S>
+  static constexpr int xstep() { return 32 * (S >> 1) + 8 * (S & 1) + 8 * (S >> 2); }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int cc = S >> 1, sub = S & 1;
+    slice8(c[cc][2 * sub], c[cc][2 * sub + 1], sc[cc], -1056.f * sc[cc], f);
+  }
+};
+
+template <> struct MmaSlices<Q8_0> {
+  // block b = S >> 2 (values 32 b ..); code + 128 from a sign-bit flip; weight = d q
+  uint32_t c[2][8];
+  float d[2];
+  __device__ __forceinline__ MmaSlices(const UnitQ8_0& un, int, bool keep) {
+    const uint32_t R[17] = {un.r0.x, un.r0.y, un.r0.z, un.r0.w, un.r1.x, un.r1.y, un.r1.z, un.r1.w,
+                            un.r2.x, un.r2.y, un.r2.z, un.r2.w, un.r3.x, un.r3.y, un.r3.z, un.r3.w, un.r4};
+    d[0] = keep ? f16_to_f32(R[0]) : 0.f;
+    d[1] = keep ? f16_to_f32(R[8] >> 16) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c[0][i] = alignbyte(R[i + 1], R[i], 2) ^ 0x80808080u;
+      c[1][i] = R[9 + i] ^ 0x80808080u;
+    }
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int b = S >> 2, t = S & 3;
+    slice8(c[b][2 * t], c[b][2 * t + 1], d[b], -1152.f * d[b], f);
+  }
+};
+
+template <> struct MmaSlices<Q4_0> {
+  // block b = S >> 2: values 0..15 low nibbles of its 16 bytes, 16..31 high; weight = d (q - 8)
+  uint32_t q[2][4];
+  float d[2];
+  __device__ __forceinline__ MmaSlices(const UnitQ4_0& un, int, bool keep) {
+    const uint32_t R[9] = {un.r0.x, un.r0.y, un.r0.z, un.r0.w, un.r1.x, un.r1.y, un.r1.z, un.r1.w, un.r2};
+    d[0] = keep ? f16_to_f32(R[0]) : 0.f;
+    d[1] = keep ? f16_to_f32(R[4] >> 16) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[0][i] = alignbyte(R[i + 1], R[i], 2);
+      q[1][i] = R[5 + i];
+    }
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int b = S >> 2, t = S & 3, dw = 2 * (t & 1), sh = 4 * (t >> 1);
+    slice8((q[b][dw] >> sh) & 0x0F0F0F0Fu, (q[b][dw + 1] >> sh) & 0x0F0F0F0Fu, d[b], -1032.f * d[b], f);
+  }
+};
+
+constexpr int MMA_THREADS = 256;
+constexpr int MMA_KSPLIT = 2;  // waves of a workgroup sharing one 16-row group, each a part of K
+constexpr int MMA_PD = 4;      // units of a lane in flight ahead of the one decoded
+// K values per LDS chunk: at most 64 KiB of activations.
+__host__ __device__ constexpr int mma_kchunk(int m) { return (32768 / m) & ~255; }
+__host__ __device__ constexpr int mma_xstride(int kc) { return xpad(kc) + 8; }  // +16 B: rows start on different banks
+
+template <int C, int M, bool F16>
+__global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __restrict__ w, int n, int k,
+                                                              int64_t row_bytes, const half_t* __restrict__ x,
+                                                              void* __restrict__ y) {
+  typedef typename UnitOf<C>::T Unit;
+  static_assert(M >= 1 && M <= 16, "activation rows");
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  constexpr int KC = mma_kchunk(M);
+  const int kc_alloc = k < KC ? k : KC;
+  half_t* xs = (half_t*)smem;
+  const int xstride = mma_xstride(kc_alloc);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rgroup = blockIdx.x * (4 / MMA_KSPLIT) + wave / MMA_KSPLIT, kpart = wave % MMA_KSPLIT;
+  const int r = lane & 15, cu = lane >> 4;
+  const int row = rgroup * 16 + r;
+  const uint8_t* wrow = w + (int64_t)min(row, n - 1) * row_bytes;
+  const int xm = min(r, M - 1);
+
+  float4_t acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};  // even / odd slices
+  for (int c0 = 0; c0 < k; c0 += KC) {
+    const int kc = (k - c0) < KC ? (k - c0) : KC;
+    const int ub = c0 / 64, ue = (c0 + kc) / 64;
+    // this wave's groups (4 units each): [g0, g1) of the chunk's groups
+    const int ngroups = (ue - ub + 3) / 4, gper = (ngroups + MMA_KSPLIT - 1) / MMA_KSPLIT;
+    const int g0 = min(kpart * gper, ngroups), g1 = min(g0 + gper, ngroups);
+    const int last = ue - 1;
+    // Activation loads first (all of this thread's pieces at once, so their
+    // latencies overlap), then the first units' weight loads.
+    constexpr int XPT = (M * KC / 8 + MMA_THREADS - 1) / MMA_THREADS;
+    const int xpieces = M * (kc / 8);
+    u32x4 xr[XPT];
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      int c = tid + i * MMA_THREADS;
+      c = c < xpieces ? c : xpieces - 1;
+      const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
+      xr[i] = *(const u32x4*)(x + (int64_t)m * k + c0 + v);
+    }
+    Unit ring[MMA_PD];
+#pragma unroll
+    for (int p = 0; p < MMA_PD; ++p) ring[p].load(wrow, min(ub + 4 * (g0 + p) + cu, last));
+    if (c0) __syncthreads();  // previous chunk done with LDS
+#pragma unroll
+    for (int i = 0; i < XPT; ++i) {
+      const int c = tid + i * MMA_THREADS;
+      if (c < xpieces) {
+        const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
+        *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
+      }
+    }
+    __syncthreads();
+    const half_t* xrow = xs + xm * xstride;
+    // Slot j of the ring always holds group g + j: the loop is unrolled by
+    // the ring depth so no register is copied while its load is in flight.
+    // Groups past g1 (the last pass) are masked, not branched around.
+    for (int g = g0; g < g1; g += MMA_PD) {
+#pragma unroll
+      for (int j = 0; j < MMA_PD; ++j) {
+        const int u = ub + 4 * (g + j) + cu;
+        const bool valid = g + j < g1 && u < ue;  // else this lane adds zeros
+        const int uc = valid ? u : last;           // (and reads in-range x)
+        // Activation fragments and the unit's eight weight fragments first,
+        // so the slot's bytes are dead before its next load is issued (the
+        // load then reuses the slot's registers: nothing is copied, nothing
+        // waits at the loop edge).
+        half8_t a[8];
+        u32x4 fw[8];
+        const MmaSlices<C> sl(ring[j], uc, valid);
+        const half_t* xb = xrow + xpad(MmaSlices<C>::koff(uc) - c0);
+        auto prep = [&](auto sc) __attribute__((always_inline)) {
+          constexpr int S = decltype(sc)::value;
+          a[S] = *(const half8_t*)(xb + MmaSlices<C>::template xstep<S>());
+          uint32_t f[4];
+          sl.template get<S>(f);
+          fw[S] = u32x4{f[0], f[1], f[2], f[3]};
+        };
+        prep(std::integral_constant<int, 0>{});
+        prep(std::integral_constant<int, 1>{});
+        prep(std::integral_constant<int, 2>{});
+        prep(std::integral_constant<int, 3>{});
+        prep(std::integral_constant<int, 4>{});
+        prep(std::integral_constant<int, 5>{});
+        prep(std::integral_constant<int, 6>{});
+        prep(std::integral_constant<int, 7>{});
+        __builtin_amdgcn_sched_barrier(0);
+        ring[j].load(wrow, min(u + 4 * MMA_PD, last));
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], __builtin_bit_cast(half8_t, fw[t]), acc, 0, 0, 0);
+          acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t + 1], __builtin_bit_cast(half8_t, fw[t + 1]), acc2, 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // Combine the K parts: lane l holds activation rows 4 (l >> 4) + i of
+  // weight row 16 rgroup + (l & 15).
+  acc += acc2;
+  __syncthreads();
+  float4_t* part = (float4_t*)smem;
+  const int pbase = (wave / MMA_KSPLIT) * (MMA_KSPLIT - 1) * 64;
+  if (kpart) part[pbase + (kpart - 1) * 64 + lane] = acc;
+  __syncthreads();
+  if (kpart == 0) {
+#pragma unroll
+    for (int p = 0; p + 1 < MMA_KSPLIT; ++p) acc += part[pbase + p * 64 + lane];
+    const int col = rgroup * 16 + (lane & 15);
+    if (col < n) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 4 * (lane >> 4) + i;
+        if (m < M) {
+          if (F16)
+            ((half_t*)y)[(int64_t)m * n + col] = (half_t)acc[i];
+          else
+            ((float*)y)[(int64_t)m * n + col] = acc[i];
+        }
+      }
+    }
+  }
+}
+
+template <int C, int M>
+hipError_t launch_mma(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
+                      hipStream_t s) {
+  const int kc = (int)(k < mma_kchunk(M) ? k : mma_kchunk(M));
+  size_t lds = (size_t)M * mma_xstride(kc) * 2;
+  const size_t part_bytes = (size_t)(4 / MMA_KSPLIT) * (MMA_KSPLIT - 1) * 64 * sizeof(float4_t);
+  if (lds < part_bytes) lds = part_bytes;
+  constexpr int rows_per_block = 16 * (4 / MMA_KSPLIT);
+  const dim3 grid((unsigned)((n + rows_per_block - 1) / rows_per_block));
+  if (f16)
+    hipLaunchKernelGGL((qmv_mma_kernel<C, M, true>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x, y);
+  else
+    hipLaunchKernelGGL((qmv_mma_kernel<C, M, false>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x, y);
+  return hipGetLastError();
+}
+
 template <int C, int M, int LPR>
 hipError_t launch_ml(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
                      hipStream_t s) {
@@ -436,15 +730,24 @@ hipError_t launch_ml(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const h
   return hipGetLastError();
 }
 
-// One wave per row (64 lanes, one 64-value unit each at K = 4096) for one
-// activation row and a matrix with few rows: four times the workgroups and a
-// quarter of the serial work per lane.  Otherwise 16 lanes per row, so the
-// activation staging is shared by 16 rows per workgroup.
+// Three or more activation rows (five or more for q8_0) go to the matrix
+// cores.  Fewer take the dot2 kernel: one wave per row (64 lanes, one 64-value unit each at
+// K = 4096) for one activation row and a matrix with few rows (four times
+// the workgroups and a quarter of the serial work per lane), otherwise 16
+// lanes per row, so the activation staging is shared by 16 rows per
+// workgroup.
 template <int C, int M>
 hipError_t launch_m(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
                     hipStream_t s) {
-  if (M == 1 && n <= 32768) return launch_ml<C, M, 64>(w, n, k, rb, x, y, f16, s);
-  return launch_ml<C, M, 16>(w, n, k, rb, x, y, f16, s);
+  // q8_0's decode costs the matrix path more per byte: its dot2 kernel is
+  // still the faster one at four rows.
+  constexpr int mma_from = C == Q8_0 ? 5 : 3;
+  if constexpr (M >= mma_from) {
+    return launch_mma<C, M>(w, n, k, rb, x, y, f16, s);
+  } else {
+    if (M == 1 && n <= 32768) return launch_ml<C, M, 64>(w, n, k, rb, x, y, f16, s);
+    return launch_ml<C, M, 16>(w, n, k, rb, x, y, f16, s);
+  }
 }
 
 template <int C>
