@@ -172,7 +172,22 @@ def measure_rows(torch, kq):
                  "GB/s": round(alg / ms_seg / 1e6, 1), "hbm_frac": round(alg / ms_seg / 1e6 / HBM_PEAK_GBS, 3),
                  "TFLOP/s": round(flop / ms_seg / 1e9, 1),
                  "mfma_frac": round(flop / ms_seg / 1e9 / MFMA_F16_PEAK_TFLOPS, 3), "alg_bytes": alg, "copies": nc})
-    del ws, wq
+    # MoE decode: one token's top-8 routed rows through kq_gather_qmv on the same
+    # expert weights; launch i takes token i's experts and weight copy i % nc
+    nl = max(nc, 16)
+    dec_ids = torch.from_numpy(np.ascontiguousarray(r.ids[:nl].astype(np.uint32)).view(np.int32)).cuda()
+    xtok = W.activations(cfg.seed, nl, cfg.k)
+    xd = [torch.from_numpy(np.repeat(xtok[i:i + 1], cfg.top_k, axis=0)).cuda() for i in range(nl)]
+    yd = torch.empty((cfg.top_k, cfg.n), dtype=torch.float16, device="cuda")
+    gd = capture(torch, lambda: [kq.kq_gather_qmv(cfg.codec, ws[i % nc], cfg.n_experts, cfg.n, cfg.k, xd[i],
+                                                  dec_ids[i], yd) for i in range(nl)])
+    ms_dec = time_graph(torch, gd, nl, 5)
+    alg_dec = cfg.top_k * cfg.n * wq.shape[1] + cfg.top_k * cfg.k * 2 + cfg.top_k * cfg.n * 2
+    rows.append({"row": "kq_gather_qmv", "workload": f"MoE decode gather_qmv 1 tok top-{cfg.top_k} of "
+                 f"{cfg.n_experts} experts, {cfg.n}x{cfg.k} {cfg.codec}", "us": round(ms_dec * 1e3, 2),
+                 "GB/s": round(alg_dec / ms_dec / 1e6, 1), "hbm_frac": round(alg_dec / ms_dec / 1e6 / HBM_PEAK_GBS, 3),
+                 "alg_bytes": alg_dec, "copies": nc})
+    del ws, wq, xd
     torch.cuda.empty_cache()
 
     # dequantize (q4_K 4096 x 4096 -> float16)

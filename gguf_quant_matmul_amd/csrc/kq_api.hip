@@ -219,6 +219,23 @@ int kq_gather_qmm_seg(int codec, const void* w, int64_t n_experts, int64_t n, in
                                                   y_dtype == KQ_F16, (hipStream_t)stream));
 }
 
+int kq_gather_qmv(int codec, const void* w, int64_t n_experts, int64_t n, int64_t k, const void* x,
+                  const uint32_t* ids, int64_t rows, void* y, int y_dtype, void* stream) {
+  const char* op = "kq_gather_qmv";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, rows, y, y_dtype, &rb);
+  if (st) return st;
+  if (k % 256)
+    return fail(KQ_ERR_SHAPE, op, "K=%lld is not a multiple of 256 (one activation row per slot)", (long long)k);
+  if (n_experts <= 0 || n_experts >= kMaxDim || n_experts * n >= kMaxDim * 64)
+    return fail(KQ_ERR_ARG, op, "n_experts=%lld out of range", (long long)n_experts);
+  if (n == 0 || rows == 0) return KQ_OK;
+  if (!ids) return fail(KQ_ERR_ARG, op, "null ids");
+  if (!aligned(ids, 4)) return fail(KQ_ERR_ALIGN, op, "ids=%p is not 4-byte aligned", (const void*)ids);
+  return hip_status(op, kq::launch_gather_qmv(codec, (const uint8_t*)w, n_experts, n, k, rb, (const kq::half_t*)x,
+                                              ids, rows, y, y_dtype == KQ_F16, (hipStream_t)stream));
+}
+
 int kq_quantize(int codec, const float* w, int64_t rows, int64_t k, void* out, void* stream) {
   const char* op = "kq_quantize";
   int64_t rb;

@@ -284,10 +284,10 @@ __device__ __forceinline__ float lanes_sum(float v) {
   return v;
 }
 
+// The GEMV of one workgroup: rows [blk * rows_per_block, ...) of w.
 template <int C, int M, int LPR, bool F16>
-__global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restrict__ w, int n, int k,
-                                                          int64_t row_bytes, const half_t* __restrict__ x,
-                                                          void* __restrict__ y) {
+__device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, int k, int64_t row_bytes,
+                                         const half_t* __restrict__ x, void* __restrict__ y, int blk) {
   typedef typename UnitOf<C>::T Unit;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int KC = kchunk_max(M);
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   constexpr int LANES_PER_ROW = LPR, ROWS_PER_WAVE = 64 / LPR, UNROLL = UNITS_PER_GROUP / LPR;
   const int rslot = lane / LANES_PER_ROW, uslot = lane % LANES_PER_ROW;
-  const int row = (blockIdx.x * (QMV_THREADS / 64) + wave) * ROWS_PER_WAVE + rslot;
+  const int row = (blk * (QMV_THREADS / 64) + wave) * ROWS_PER_WAVE + rslot;
   const bool row_ok = row < n;
   const uint8_t* wrow = w + (int64_t)(row_ok ? row : 0) * row_bytes;
 
@@ -386,6 +386,30 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
     else
       ((float*)y)[(int64_t)uslot * n + row] = v;
   }
+}
+
+template <int C, int M, int LPR, bool F16>
+__global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restrict__ w, int n, int k,
+                                                          int64_t row_bytes, const half_t* __restrict__ x,
+                                                          void* __restrict__ y) {
+  qmv_rows<C, M, LPR, F16>(w, n, k, row_bytes, x, y, blockIdx.x);
+}
+
+// Gathered GEMV (mlx-kquant bindings.cpp page, gather_qmv_kq docstring: one
+// activation row per expert slot, output row r = x[r] times expert ids[r]'s
+// dequantized weight, transposed).  blockIdx.y is the routed row; a row
+// whose id is not below n_experts is left unwritten.
+template <int C, int LPR, bool F16>
+__global__ __launch_bounds__(QMV_THREADS) void gather_qmv_kernel(const uint8_t* __restrict__ w, int n_experts,
+                                                                 int64_t expert_stride, int n, int k,
+                                                                 int64_t row_bytes, const half_t* __restrict__ x,
+                                                                 const uint32_t* __restrict__ ids, int row0,
+                                                                 void* __restrict__ y) {
+  const int r = row0 + (int)blockIdx.y;
+  const uint32_t e = ids[r];
+  if (e >= (uint32_t)n_experts) return;  // the whole workgroup leaves before any barrier
+  void* yr = F16 ? (void*)((half_t*)y + (int64_t)r * n) : (void*)((float*)y + (int64_t)r * n);
+  qmv_rows<C, 1, LPR, F16>(w + (int64_t)e * expert_stride, n, k, row_bytes, x + (int64_t)r * k, yr, blockIdx.x);
 }
 
 // Generic GEMV for shapes the unit kernels do not take (q8_0 / q4_0 with an
@@ -775,7 +799,46 @@ hipError_t launch_c(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
   return hipErrorInvalidValue;
 }
 
+template <int C, int LPR>
+hipError_t launch_gather_l(const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb, const half_t* x,
+                           const uint32_t* ids, int64_t rows, void* y, int f16, hipStream_t s) {
+  const int kc = (int)(k < kchunk_max(1) ? k : kchunk_max(1));
+  const size_t lds = (size_t)xpad(kc) * 2 + (size_t)(kc / 16) * 4;
+  const unsigned gx = (unsigned)((n + rows_per_block(LPR) - 1) / rows_per_block(LPR));
+  for (int64_t r0 = 0; r0 < rows; r0 += 65535) {  // grid y holds at most 65535 rows per launch
+    const dim3 grid(gx, (unsigned)(rows - r0 < 65535 ? rows - r0 : 65535));
+    if (f16)
+      hipLaunchKernelGGL((gather_qmv_kernel<C, LPR, true>), grid, dim3(QMV_THREADS), lds, s, w, (int)ne, n * rb,
+                         (int)n, (int)k, rb, x, ids, (int)r0, y);
+    else
+      hipLaunchKernelGGL((gather_qmv_kernel<C, LPR, false>), grid, dim3(QMV_THREADS), lds, s, w, (int)ne, n * rb,
+                         (int)n, (int)k, rb, x, ids, (int)r0, y);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int C>
+hipError_t launch_gather_c(const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb, const half_t* x,
+                           const uint32_t* ids, int64_t rows, void* y, int f16, hipStream_t s) {
+  if (n <= 32768) return launch_gather_l<C, 64>(w, ne, n, k, rb, x, ids, rows, y, f16, s);
+  return launch_gather_l<C, 16>(w, ne, n, k, rb, x, ids, rows, y, f16, s);
+}
+
 }  // namespace
+
+hipError_t launch_gather_qmv(int codec, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,
+                             int64_t row_bytes, const half_t* x, const uint32_t* ids, int64_t rows, void* y,
+                             int f16out, hipStream_t s) {
+  switch (codec) {
+    case Q4_0: return launch_gather_c<Q4_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+    case Q8_0: return launch_gather_c<Q8_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+    case Q4_K: return launch_gather_c<Q4_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+    case Q6_K: return launch_gather_c<Q6_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_qmv(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m, void* y,
                       int f16, hipStream_t s) {

@@ -35,6 +35,7 @@ _SIGS = {
     "kq_expert_tile_map_capacity": (c_i64, [c_i64, c_i64]),
     "kq_expert_tile_map": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp]),
     "kq_gather_qmm_seg": (c_int, [c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_int, c_vp]),
+    "kq_gather_qmv": (c_int, [c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_int, c_vp]),
     "kq_quantize": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_vp]),
 }
 
@@ -164,6 +165,12 @@ def kq_gather_qmm_seg(codec, w, n_experts: int, n: int, k: int, x, map_, counts,
     """w uint8 [E, n, row_bytes]; x float16 [rows, k] expert-sorted; y [rows, n]."""
     _check(_lib.kq_gather_qmm_seg(_codec(codec), _ptr(w), n_experts, n, k, _ptr(x), x.shape[0], _ptr(map_),
                                   _ptr(counts), map_.shape[0], _ptr(y), _dtype_id(y), _stream(stream)))
+
+
+def kq_gather_qmv(codec, w, n_experts: int, n: int, k: int, x, ids, y, stream=None) -> None:
+    """w uint8 [E, n, row_bytes]; x float16 [rows, k]; ids int32/uint32 [rows]; y [rows, n]."""
+    _check(_lib.kq_gather_qmv(_codec(codec), _ptr(w), n_experts, n, k, _ptr(x), _ptr(ids), x.shape[0], _ptr(y),
+                              _dtype_id(y), _stream(stream)))
 
 
 def kq_quantize(codec, w, out, stream=None) -> None:

@@ -4,9 +4,9 @@
  *
  * Operations follow the mlx-kquant ops as documented on the mlx-kquant
  * bindings.cpp page (docstrings of dequantize, quantized_matmul,
- * expert_tile_map, gather_qmm_seg, quantize) and the codec geometry of the
- * mlx-kquant README ("Codec reference" table).  Byte layouts inside a block
- * are GGUF's.
+ * expert_tile_map, gather_qmm_seg, gather_qmv_kq, quantize) and the codec
+ * geometry of the mlx-kquant README ("Codec reference" table).  Byte layouts
+ * inside a block are GGUF's.
  *
  * Conventions shared by every entry point
  *  - Pointers named w, x, y, out, map, counts, ids, status are DEVICE
@@ -128,6 +128,21 @@ int kq_gather_qmm_seg(int codec, const void* w, int64_t n_experts, int64_t n, in
                       const void* x, int64_t rows,
                       const uint32_t* map, const uint32_t* counts, int64_t cap,
                       void* y, int y_dtype, void* stream);
+
+/* ---- gathered GEMV (mlx-kquant bindings.cpp page, gather_qmv_kq docstring) ----
+ * The decode-shaped MoE product: one activation row per (token, slot).
+ * w [n_experts][N][row_bytes]; x float16 [rows][K] (the pages' [T, R, K]
+ * flattened); ids uint32 [rows] (device memory, any order).  For each row r
+ * with ids[r] < n_experts:
+ *   y[r][n] = sum_k x[r][k] * dequant(w[ids[r]])[n][k]
+ * float32 accumulation.  Rows with ids[r] >= n_experts are left unwritten
+ * (ids are read on the device, not checked on the host).  K must be a
+ * multiple of 256 (the pages' constraint), else KQ_ERR_SHAPE; ids 4-byte
+ * aligned.  The pages' bias (for other codecs) and LoRA arguments are not
+ * supported. */
+int kq_gather_qmv(int codec, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                  const void* x, const uint32_t* ids, int64_t rows,
+                  void* y, int y_dtype, void* stream);
 
 /* ---- encoder (mlx-kquant bindings.cpp page, quantize docstring; no imatrix) ----
  * float32 w [rows][K] -> wire bytes out [rows][row_bytes], round to nearest

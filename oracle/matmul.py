@@ -15,6 +15,8 @@ Definitions followed
     (expert, row_start, num_rows); only the last tile of a segment may be
     partial; a count of valid tiles.  Tile order is unspecified there; this
     oracle emits expert-major, ascending row_start.
+  * mlx-kquant ``bindings.cpp`` page, ``gather_qmv_kq`` docstring: one
+    activation row per expert slot; row r times expert ``indices[r]``.
   * mlx-kquant ``bindings.cpp`` page, ``gather_qmm_seg`` docstring: for each
     valid tile, rows [row_start, row_start+num_rows) of the expert-sorted x
     times expert ``e``'s dequantized weight, transposed; rows no tile covers
@@ -27,7 +29,9 @@ Definitions followed
 Pins (tests/test_oracle_matmul.py): exact rational dot products (Python
 ``fractions``) on tiny shapes; one-hot x rows return weight columns exactly;
 tile-map invariants by brute force plus a hand example; the gather equals a
-per-row loop of the nuvec gather definition and reduces to qmm with one expert.
+per-row loop of the nuvec gather definition and reduces to qmm with one expert;
+the gathered GEMV equals exact rational dot products per row and reduces to
+qmm when every row names the same expert.
 """
 
 from __future__ import annotations
@@ -87,4 +91,22 @@ def gather_qmm_seg(codec: str, w: np.ndarray, k: int, x: np.ndarray, tiles: np.n
     y = np.full((x.shape[0], n), fill, dtype=np.float64)
     for e, s, c in np.asarray(tiles, dtype=np.int64):
         y[s:s + c] = qmatmul(codec, w[e], k, x[s:s + c])
+    return y
+
+
+def gather_qmv(codec: str, w: np.ndarray, k: int, x: np.ndarray, ids: np.ndarray, fill=np.nan) -> np.ndarray:
+    """Reference for kq_gather_qmv: row r is x[r] times expert ids[r]'s weight, transposed.
+
+    mlx-kquant ``bindings.cpp`` page, ``gather_qmv_kq`` docstring: one
+    activation row per expert slot, w laid out (n_experts, N, bytes_per_row),
+    output row r uses expert indices[r].  w: [E, N, row_bytes]; x: [rows, K];
+    ids: [rows].  Rows whose id is not below E hold ``fill`` (unwritten by the
+    contract).
+    """
+    n_experts, n = w.shape[0], w.shape[1]
+    ids = np.asarray(ids, dtype=np.int64)
+    y = np.full((x.shape[0], n), fill, dtype=np.float64)
+    for r, e in enumerate(ids):
+        if 0 <= e < n_experts:
+            y[r] = qmatmul(codec, w[e], k, x[r:r + 1])[0]
     return y

@@ -297,6 +297,50 @@ def test_gather_qmm_seg_parity(kq, codec):
         assert_close_rows(got[covered], ref[covered], what=f"seg {codec}")
 
 
+@pytest.mark.parametrize("codec", CODECS)
+def test_gather_qmv_parity(kq, codec):
+    # one activation row per routed slot, ids in any order; an id past the
+    # expert count leaves its row unwritten.  A 40000-row case takes the
+    # 16-lanes-per-row layout, the small ones a whole wave per row.
+    torch = _torch()
+    rng = np.random.default_rng(19)
+    cases = [(5, 100, 512, 9), (3, 33, 256, 4)]
+    if codec == "q4_0":
+        cases.append((2, 40000, 256, 3))
+    for e, n, k, rows in cases:
+        wf = (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32)
+        w = encode.quantize(codec, wf)
+        x = _x(rows, k, 7 + n)
+        ids = rng.integers(0, e, rows).astype(np.uint32)
+        ids[1] = e + 3
+        ref = matmul.gather_qmv(codec, w, k, x, ids)
+        live = ids < e
+        for tdt in (torch.float32, torch.float16):
+            say(f"gather_qmv {codec} e={e} n={n} k={k} rows={rows} {tdt}")
+            y = torch.full((rows, n), float("nan"), dtype=tdt, device="cuda")
+            kq.kq_gather_qmv(codec, dev(w), e, n, k, dev(x), u32(ids), y)
+            got = host(y).astype(np.float64)
+            assert np.all(np.isnan(got[~live])), "rows with an out-of-range id must stay unwritten"
+            assert_close_rows(got[live], ref[live], what=f"gather_qmv {codec} n={n} {tdt}")
+
+
+def test_gather_qmv_row_equals_qmv_bits(kq):
+    # a routed row runs the same kernel as a one-row GEMV on its expert
+    torch = _torch()
+    rng = np.random.default_rng(20)
+    e, n, k = 4, 64, 1024
+    w = encode.quantize("q4_k", (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32))
+    x = _x(3, k, 9)
+    ids = np.array([3, 0, 3], dtype=np.uint32)
+    y = torch.empty((3, n), dtype=torch.float32, device="cuda")
+    wd = dev(w)
+    kq.kq_gather_qmv("q4_k", wd, e, n, k, dev(x), u32(ids), y)
+    for r, ex in enumerate(ids):
+        y1 = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        kq.kq_qmv("q4_k", wd[int(ex)], n, k, dev(x[r:r + 1]), y1)
+        assert torch.equal(y[r:r + 1], y1)
+
+
 def test_gather_seg_one_expert_equals_qmm_bits(kq):
     torch = _torch()
     n, k, rows = 100, 1024, 150

@@ -110,5 +110,15 @@ def test_moe_seg_workload(kq):
     got = host(y)[:, ns].astype(np.float64)
     err = assert_close_rows(got, ref, what=cfg.name)
     say(f"workload {cfg.name}: max row-normalized error {err:.2e}")
-    del wq, y
+
+    # decode shape on the same experts: token 0's eight routed rows through
+    # kq_gather_qmv, checked on the sampled columns
+    ids0 = r.ids[0].astype(np.uint32)
+    xd = np.repeat(W.activations(cfg.seed, cfg.tokens, cfg.k)[:1], cfg.top_k, axis=0)
+    yd = torch.empty((cfg.top_k, cfg.n), dtype=torch.float16, device="cuda")
+    kq.kq_gather_qmv(cfg.codec, wq, cfg.n_experts, cfg.n, cfg.k, dev(xd), u32(ids0), yd)
+    refd = matmul.gather_qmv(cfg.codec, ref_bytes.reshape(cfg.n_experts, ns.size, rb), cfg.k, xd, ids0)
+    errd = assert_close_rows(host(yd)[:, ns].astype(np.float64), refd, what="MoE decode gather_qmv")
+    say(f"workload MoE decode gather_qmv (token 0, top-{cfg.top_k}): max row-normalized error {errd:.2e}")
+    del wq, y, yd
     torch.cuda.empty_cache()

@@ -139,3 +139,32 @@ def test_gather_seg_one_expert_is_qmm():
     assert count == 3
     y = matmul.gather_qmm_seg("q6_k", w, k, x, tiles[:count])
     assert np.array_equal(y, matmul.qmatmul("q6_k", w[0], k, x))
+
+
+def test_gather_qmv_rows_are_exact_rational_dots():
+    # each output row is x[r] . dequant(w[ids[r]])[n] exactly (fp64 accumulation
+    # of exact products), checked with rational arithmetic on a tiny case;
+    # an id out of range leaves the row at the fill value
+    rng = np.random.default_rng(33)
+    e, n, k = 3, 4, 256
+    w = encode.quantize("q4_0", rng.standard_normal((e, n, k)).astype(np.float32) * np.float32(0.02))
+    x = rng.standard_normal((4, k)).astype(np.float16)
+    ids = np.array([2, 0, 7, 2], dtype=np.uint32)
+    y = matmul.gather_qmv("q4_0", w, k, x, ids)
+    for r, ex in enumerate(ids):
+        if ex >= e:
+            assert np.all(np.isnan(y[r]))
+            continue
+        wd = codecs.dequantize("q4_0", w[ex], k)
+        for j in range(n):
+            exact = sum(Fraction(float(x[r, t])) * Fraction(float(wd[j, t])) for t in range(k))
+            assert abs(y[r, j] - float(exact)) <= 1e-12 * max(1.0, abs(float(exact)))
+
+
+def test_gather_qmv_one_expert_is_qmm():
+    rng = np.random.default_rng(34)
+    n, k = 12, 512
+    w = encode.quantize("q6_k", rng.standard_normal((2, n, k)).astype(np.float32))
+    x = rng.standard_normal((5, k)).astype(np.float16)
+    y = matmul.gather_qmv("q6_k", w, k, x, np.ones(5, np.uint32))
+    assert np.array_equal(y, matmul.qmatmul("q6_k", w[1], k, x))
