@@ -1,0 +1,373 @@
+// kq_units.h -- 64-value weight units shared by the GEMV kernels and the
+// expert-segment matrix-core kernel: the loads of one unit's wire bytes, its
+// v_dot2 product with float16 activations (GEMV, M <= 8), and its eight
+// 8-value float16 MFMA operand slices.
+//
+// Byte layouts per the codec table of the mlx-kquant README (block geometry)
+// read as GGUF's layouts (a unit is whole blocks or whole sub-blocks).
+#pragma once
+
+#include "kq_decode.h"
+
+namespace kq {
+namespace {
+
+__host__ __device__ constexpr int xpad(int v) { return v + (v >> 6) * 8; }  // padded LDS offset (halves)
+
+// ---------------------------------------------------------------------------
+// Units.  load(row, u): issue the loads of unit u of a row.
+// dot<M>(...): accumulate the unit's v_dot2 product into acc[0..M).
+// ---------------------------------------------------------------------------
+
+struct Xv {  // activation views for one chunk
+  const half_t* xs;  // LDS [M][xpad(kc)]
+  const float* xsum; // LDS [M][kc/16]
+  int xstride, sstride, c0;
+  __device__ __forceinline__ const uint32_t* pairs(int m, int off) const {  // off: row offset, multiple of 16
+    return (const uint32_t*)(xs + m * xstride + xpad(off - c0));
+  }
+  __device__ __forceinline__ float sum16(int m, int off) const { return xsum[m * sstride + ((off - c0) >> 4)]; }
+};
+
+// sum over 16 values: (float16 pairs of codes) . (x pairs), 4 code dwords (p01, p23 per dword)
+__device__ __forceinline__ float dot16(const uint32_t* cp /*8 pairs*/, const uint32_t* xp, float s) {
+  const u32x4 a = *(const u32x4*)xp, b = *(const u32x4*)(xp + 4);
+  s = dot2(cp[0], a.x, s); s = dot2(cp[1], a.y, s); s = dot2(cp[2], a.z, s); s = dot2(cp[3], a.w, s);
+  s = dot2(cp[4], b.x, s); s = dot2(cp[5], b.y, s); s = dot2(cp[6], b.z, s); s = dot2(cp[7], b.w, s);
+  return s;
+}
+
+// 4 code-byte dwords (16 codes) -> 8 float16 pairs (1024 + code)
+__device__ __forceinline__ void pairs16(const uint32_t c[4], uint32_t p[8]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { p[2 * i] = pair01(c[i]); p[2 * i + 1] = pair23(c[i]); }
+}
+
+struct UnitQ4K {
+  u32x4 h, q0, q1;
+  __device__ __forceinline__ void load(const uint8_t* row, int u) {
+    const uint8_t* blk = row + (u >> 2) * 144;
+    h = ld_16B(blk);
+    const uint8_t* qs = blk + 16 + 32 * (u & 3);
+    q0 = ld_16B(qs);
+    q1 = ld_16B(qs + 16);
+  }
+  template <int M>
+  __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
+    const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
+    const int j0 = 2 * (u & 3);
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(h.y, h.z, h.w, j0, sc0, m0);
+    q4k_scale_min(h.y, h.z, h.w, j0 + 1, sc1, m1);
+    const float dsc0 = d * (float)sc0, dm0 = dmin * (float)m0;
+    const float dsc1 = d * (float)sc1, dm1 = dmin * (float)m1;
+    const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t lo[16], hi[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t l = qw[i] & 0x0F0F0F0Fu, hh = (qw[i] >> 4) & 0x0F0F0F0Fu;
+      lo[2 * i] = pair01(l); lo[2 * i + 1] = pair23(l);
+      hi[2 * i] = pair01(hh); hi[2 * i + 1] = pair23(hh);
+    }
+    const int base = 64 * u;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s0 = 0.f, s1 = 0.f;
+      s0 = dot16(lo, xv.pairs(m, base), s0);
+      s0 = dot16(lo + 8, xv.pairs(m, base + 16), s0);
+      s1 = dot16(hi, xv.pairs(m, base + 32), s1);
+      s1 = dot16(hi + 8, xv.pairs(m, base + 48), s1);
+      const float4_t xs = *(const float4_t*)&xv.xsum[m * xv.sstride + ((base - xv.c0) >> 4)];
+      const float x0 = xs.x + xs.y, x1 = xs.z + xs.w;
+      acc[m] += dsc0 * (s0 - 1024.f * x0) - dm0 * x0 + dsc1 * (s1 - 1024.f * x1) - dm1 * x1;
+    }
+  }
+};
+
+// 16 bytes at a 2-byte aligned address: dwords loaded from the dword-aligned
+// address below it, then shifted by (addr & 3) bytes.
+struct Shift16 {
+  u32x4 a;
+  uint32_t b;
+  __device__ __forceinline__ void load(const uint8_t* p, uint32_t sh) {
+    const uint8_t* q = p - sh;
+    a = ld_16B_a4(q);
+    b = ld_u32(q + 16 - (sh ? 0 : 4));  // sh == 0: re-read the 4th dword, never past the 16 bytes
+  }
+  __device__ __forceinline__ void get(uint32_t sh, uint32_t o[4]) const {
+    o[0] = alignbyte(a.y, a.x, sh);
+    o[1] = alignbyte(a.z, a.y, sh);
+    o[2] = alignbyte(a.w, a.z, sh);
+    o[3] = alignbyte(b, a.w, sh);
+  }
+};
+
+struct UnitQ6K {
+  Shift16 qa, qb, qhh, scl;
+  uint32_t dbits, sh;
+  __device__ __forceinline__ void load(const uint8_t* row, int u) {
+    const uint8_t* blk = row + (u >> 2) * 210;
+    const int h = (u >> 1) & 1, half = u & 1;
+    sh = (uint32_t)((uintptr_t)blk & 3);
+    qa.load(blk + 64 * h + 16 * half, sh);
+    qb.load(blk + 64 * h + 32 + 16 * half, sh);
+    qhh.load(blk + 128 + 32 * h + 16 * half, sh);
+    scl.load(blk + 192, sh);
+    dbits = ld_u16(blk + 208);
+  }
+  template <int M>
+  __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
+    const int h = (u >> 1) & 1, half = u & 1;
+    uint32_t A[4], B[4], H[4], S[4];
+    qa.get(sh, A); qb.get(sh, B); qhh.get(sh, H); scl.get(sh, S);
+    const float d = f16_to_f32(dbits);
+    const uint32_t slo = h ? S[2] : S[0], shi = h ? S[3] : S[1];
+    float dsc[4];
+    dsc[0] = d * (float)(int)(int8_t)(slo >> (8 * half));
+    dsc[1] = d * (float)(int)(int8_t)(slo >> (8 * (half + 2)));
+    dsc[2] = d * (float)(int)(int8_t)(shi >> (8 * half));
+    dsc[3] = d * (float)(int)(int8_t)(shi >> (8 * (half + 2)));
+    uint32_t c[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[0][i] = (A[i] & 0x0F0F0F0Fu) | ((H[i] << 4) & 0x30303030u);
+      c[1][i] = (B[i] & 0x0F0F0F0Fu) | ((H[i] << 2) & 0x30303030u);
+      c[2][i] = ((A[i] >> 4) & 0x0F0F0F0Fu) | (H[i] & 0x30303030u);
+      c[3][i] = ((B[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u);
+    }
+    uint32_t p[4][8];
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) pairs16(c[cc], p[cc]);
+    const int base = 256 * (u >> 2) + 128 * h + 16 * half;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float t = 0.f;
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int off = base + 32 * cc;
+        const float s = dot16(p[cc], xv.pairs(m, off), 0.f);
+        const float xs = xv.sum16(m, off);
+        t += dsc[cc] * (s - 1056.f * xs);
+      }
+      acc[m] += t;
+    }
+  }
+};
+
+struct UnitQ8_0 {  // two 34-byte blocks, 68 bytes, dword aligned
+  u32x4 r0, r1, r2, r3;
+  uint32_t r4;
+  __device__ __forceinline__ void load(const uint8_t* row, int u) {
+    const uint8_t* p = row + 68 * u;
+    r0 = ld_16B_a4(p); r1 = ld_16B_a4(p + 16); r2 = ld_16B_a4(p + 32); r3 = ld_16B_a4(p + 48);
+    r4 = ld_u32(p + 64);
+  }
+  template <int M>
+  __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
+    const uint32_t R[17] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w,
+                            r2.x, r2.y, r2.z, r2.w, r3.x, r3.y, r3.z, r3.w, r4};
+    const float d0 = f16_to_f32(R[0]), d1 = f16_to_f32(R[8] >> 16);
+    uint32_t c0[8], c1[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c0[i] = alignbyte(R[i + 1], R[i], 2) ^ 0x80808080u;  // code + 128
+      c1[i] = R[9 + i] ^ 0x80808080u;
+    }
+    uint32_t p0[16], p1[16];
+    pairs16(c0, p0); pairs16(c0 + 4, p0 + 8);
+    pairs16(c1, p1); pairs16(c1 + 4, p1 + 8);
+    const int base = 64 * u;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s0 = dot16(p0, xv.pairs(m, base), 0.f);
+      s0 = dot16(p0 + 8, xv.pairs(m, base + 16), s0);
+      float s1 = dot16(p1, xv.pairs(m, base + 32), 0.f);
+      s1 = dot16(p1 + 8, xv.pairs(m, base + 48), s1);
+      const float4_t xs = *(const float4_t*)&xv.xsum[m * xv.sstride + ((base - xv.c0) >> 4)];
+      const float x0 = xs.x + xs.y, x1 = xs.z + xs.w;
+      acc[m] += d0 * (s0 - 1152.f * x0) + d1 * (s1 - 1152.f * x1);
+    }
+  }
+};
+
+struct UnitQ4_0 {  // two 18-byte blocks, 36 bytes, dword aligned
+  u32x4 r0, r1;
+  uint32_t r2;
+  __device__ __forceinline__ void load(const uint8_t* row, int u) {
+    const uint8_t* p = row + 36 * u;
+    r0 = ld_16B_a4(p); r1 = ld_16B_a4(p + 16);
+    r2 = ld_u32(p + 32);
+  }
+  template <int M>
+  __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
+    const uint32_t R[9] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w, r2};
+    const float d0 = f16_to_f32(R[0]), d1 = f16_to_f32(R[4] >> 16);
+    uint32_t q0[4], q1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { q0[i] = alignbyte(R[i + 1], R[i], 2); q1[i] = R[5 + i]; }
+    uint32_t l0[4], h0[4], l1[4], h1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      l0[i] = q0[i] & 0x0F0F0F0Fu; h0[i] = (q0[i] >> 4) & 0x0F0F0F0Fu;
+      l1[i] = q1[i] & 0x0F0F0F0Fu; h1[i] = (q1[i] >> 4) & 0x0F0F0F0Fu;
+    }
+    uint32_t pl0[8], ph0[8], pl1[8], ph1[8];
+    pairs16(l0, pl0); pairs16(h0, ph0); pairs16(l1, pl1); pairs16(h1, ph1);
+    const int base = 64 * u;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s0 = dot16(pl0, xv.pairs(m, base), 0.f);
+      s0 = dot16(ph0, xv.pairs(m, base + 16), s0);
+      float s1 = dot16(pl1, xv.pairs(m, base + 32), 0.f);
+      s1 = dot16(ph1, xv.pairs(m, base + 48), s1);
+      const float4_t xs = *(const float4_t*)&xv.xsum[m * xv.sstride + ((base - xv.c0) >> 4)];
+      const float x0 = xs.x + xs.y, x1 = xs.z + xs.w;
+      acc[m] += d0 * (s0 - 1032.f * x0) + d1 * (s1 - 1032.f * x1);
+    }
+  }
+};
+
+template <int C> struct UnitOf;
+template <> struct UnitOf<Q4_K> { typedef UnitQ4K T; };
+template <> struct UnitOf<Q6_K> { typedef UnitQ6K T; };
+template <> struct UnitOf<Q8_0> { typedef UnitQ8_0 T; };
+template <> struct UnitOf<Q4_0> { typedef UnitQ4_0 T; };
+
+// ---------------------------------------------------------------------------
+// Matrix-core operand slices of a unit.
+// ---------------------------------------------------------------------------
+
+// Two float16 pairs (1024 + code) -> weights fma(1024 + code, s, c), each
+// rounded once to float16.
+__device__ __forceinline__ uint32_t fma_pair(uint32_t p, float s, float c) {
+  const half2_t h = as_h2(p);
+  return pack_h2(fmaf((float)h.x, s, c), fmaf((float)h.y, s, c));
+}
+__device__ __forceinline__ void slice8(uint32_t c0, uint32_t c1, float s, float c, uint32_t f[4]) {
+  f[0] = fma_pair(pair01(c0), s, c);
+  f[1] = fma_pair(pair23(c0), s, c);
+  f[2] = fma_pair(pair01(c1), s, c);
+  f[3] = fma_pair(pair23(c1), s, c);
+}
+
+// Slice S (8 consecutive K values) of a unit: get<S> gives its float16
+// weights f[4] (all zero for a lane that keeps nothing); koff(u) is the row
+// offset of the unit's first value and xstep<S> the slice's offset from it in
+// padded LDS units.
+template <int C> struct MmaSlices;
+
+template <> struct MmaSlices<Q4_K> {
+  // values 0..31: low nibbles of the 32 qs bytes (sub-block 2P), 32..63: high
+  // nibbles (sub-block 2P + 1); weight = d sc q - dmin m
+  float s0, c0, s1, c1;
+  uint32_t qw[8];
+  __device__ __forceinline__ MmaSlices(const UnitQ4K& un, int u, bool keep) {
+    const float d = keep ? f16_to_f32(un.h.x) : 0.f, dmin = keep ? f16_to_f32(un.h.x >> 16) : 0.f;
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(un.h.y, un.h.z, un.h.w, 2 * (u & 3), sc0, m0);
+    q4k_scale_min(un.h.y, un.h.z, un.h.w, 2 * (u & 3) + 1, sc1, m1);
+    s0 = d * (float)sc0; c0 = -(1024.f * s0 + dmin * (float)m0);
+    s1 = d * (float)sc1; c1 = -(1024.f * s1 + dmin * (float)m1);
+    qw[0] = un.q0.x; qw[1] = un.q0.y; qw[2] = un.q0.z; qw[3] = un.q0.w;
+    qw[4] = un.q1.x; qw[5] = un.q1.y; qw[6] = un.q1.z; qw[7] = un.q1.w;
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int t = S & 3;
+    if (S < 4)
+      slice8(qw[2 * t] & 0x0F0F0F0Fu, qw[2 * t + 1] & 0x0F0F0F0Fu, s0, c0, f);
+    else
+      slice8((qw[2 * t] >> 4) & 0x0F0F0F0Fu, (qw[2 * t + 1] >> 4) & 0x0F0F0F0Fu, s1, c1, f);
+  }
+};
+
+template <> struct MmaSlices<Q6_K> {
+  // four 16-value segments cc at base + 32 cc; weight = d sc (q - 32)
+  uint32_t c[4][4];
+  float sc[4];
+  int base;
+  __device__ __forceinline__ MmaSlices(const UnitQ6K& un, int u, bool keep) {
+    const int h = (u >> 1) & 1, half = u & 1;
+    uint32_t A[4], B[4], H[4], S[4];
+    un.qa.get(un.sh, A); un.qb.get(un.sh, B); un.qhh.get(un.sh, H); un.scl.get(un.sh, S);
+    const float d = keep ? f16_to_f32(un.dbits) : 0.f;
+    const uint32_t slo = h ? S[2] : S[0], shi = h ? S[3] : S[1];
+    sc[0] = d * (float)(int)(int8_t)(slo >> (8 * half));
+    sc[1] = d * (float)(int)(int8_t)(slo >> (8 * (half + 2)));
+    sc[2] = d * (float)(int)(int8_t)(shi >> (8 * half));
+    sc[3] = d * (float)(int)(int8_t)(shi >> (8 * (half + 2)));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c[0][i] = (A[i] & 0x0F0F0F0Fu) | ((H[i] << 4) & 0x30303030u);
+      c[1][i] = (B[i] & 0x0F0F0F0Fu) | ((H[i] << 2) & 0x30303030u);
+      c[2][i] = ((A[i] >> 4) & 0x0F0F0F0Fu) | (H[i] & 0x30303030u);
+      c[3][i] = ((B[i] >> 4) & 0x0F0F0F0Fu) | ((H[i] >> 2) & 0x30303030u);
+    }
+    base = 256 * (u >> 2) + 128 * h + 16 * half;
+  }
+  // the unit starts 0 or 16 values into a 64-value block and spans 128
+  // values, so segments 2 and 3 sit one padding step further in LDS
+  static __device__ __forceinline__ int koff(int u) { return 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 16 * (u & 1); }
+  template <int S>
+  static constexpr int xstep() { return 32 * (S >> 1) + 8 * (S & 1) + 8 * (S >> 2); }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int cc = S >> 1, sub = S & 1;
+    slice8(c[cc][2 * sub], c[cc][2 * sub + 1], sc[cc], -1056.f * sc[cc], f);
+  }
+};
+
+template <> struct MmaSlices<Q8_0> {
+  // block b = S >> 2 (values 32 b ..); code + 128 from a sign-bit flip; weight = d q
+  uint32_t c[2][8];
+  float d[2];
+  __device__ __forceinline__ MmaSlices(const UnitQ8_0& un, int, bool keep) {
+    const uint32_t R[17] = {un.r0.x, un.r0.y, un.r0.z, un.r0.w, un.r1.x, un.r1.y, un.r1.z, un.r1.w,
+                            un.r2.x, un.r2.y, un.r2.z, un.r2.w, un.r3.x, un.r3.y, un.r3.z, un.r3.w, un.r4};
+    d[0] = keep ? f16_to_f32(R[0]) : 0.f;
+    d[1] = keep ? f16_to_f32(R[8] >> 16) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      c[0][i] = alignbyte(R[i + 1], R[i], 2) ^ 0x80808080u;
+      c[1][i] = R[9 + i] ^ 0x80808080u;
+    }
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int b = S >> 2, t = S & 3;
+    slice8(c[b][2 * t], c[b][2 * t + 1], d[b], -1152.f * d[b], f);
+  }
+};
+
+template <> struct MmaSlices<Q4_0> {
+  // block b = S >> 2: values 0..15 low nibbles of its 16 bytes, 16..31 high; weight = d (q - 8)
+  uint32_t q[2][4];
+  float d[2];
+  __device__ __forceinline__ MmaSlices(const UnitQ4_0& un, int, bool keep) {
+    const uint32_t R[9] = {un.r0.x, un.r0.y, un.r0.z, un.r0.w, un.r1.x, un.r1.y, un.r1.z, un.r1.w, un.r2};
+    d[0] = keep ? f16_to_f32(R[0]) : 0.f;
+    d[1] = keep ? f16_to_f32(R[4] >> 16) : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[0][i] = alignbyte(R[i + 1], R[i], 2);
+      q[1][i] = R[5 + i];
+    }
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int b = S >> 2, t = S & 3, dw = 2 * (t & 1), sh = 4 * (t >> 1);
+    slice8((q[b][dw] >> sh) & 0x0F0F0F0Fu, (q[b][dw + 1] >> sh) & 0x0F0F0F0Fu, d[b], -1032.f * d[b], f);
+  }
+};
+
+}  // namespace
+}  // namespace kq
