@@ -17,6 +17,13 @@ LIB_PATH = os.path.join(HERE, "libkq.so")
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is not built; run `python -m gguf_quant_matmul_amd.build`")
 
+# torch's HIP runtime must be the only one in the process.  libkq.so asks for
+# libamdhip64.so.7 and takes whichever copy of that soname is already loaded;
+# torch's own libraries name their bundled copy by another file name, so
+# opening libkq.so first would bring in a second HIP runtime that, once torch
+# holds the GPU, finds no device.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(LIB_PATH)
 
 c_int, c_i64, c_vp, c_cp = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_char_p
