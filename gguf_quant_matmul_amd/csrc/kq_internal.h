@@ -118,6 +118,9 @@ hipError_t launch_qmm(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t
 hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,
                                  int64_t row_bytes, const half_t* x, int64_t rows, const uint32_t* map,
                                  const uint32_t* counts, int64_t cap, void* y, int f16out, hipStream_t s);
+hipError_t launch_seg_mma(int codec, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k, int64_t row_bytes,
+                          const half_t* x, int64_t rows, const uint32_t* map, const uint32_t* counts, int64_t cap,
+                          void* y, int f16out, hipStream_t s);
 hipError_t launch_gather_qmv(int codec, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,
                              int64_t row_bytes, const half_t* x, const uint32_t* ids, int64_t rows, void* y,
                              int f16out, hipStream_t s);

@@ -1,4 +1,7 @@
-// kq_qmm and kq_gather_qmm_seg: quantized GEMM on gfx950 float16 matrix cores.
+// kq_qmm: quantized GEMM on gfx950 float16 matrix cores, and the dispatch of
+// kq_gather_qmm_seg (its matrix-core kernel is in kq_seg.hip; K that is not a
+// whole number of 64-value units takes the plain kernel at the end of this
+// file for both operations).
 //
 // mlx-kquant bindings.cpp page: quantized_matmul docstring (y = x @ dequant(w)
 // transposed, w [N, K]); gather_qmm_seg docstring (expert-sorted rows walked
@@ -23,9 +26,6 @@
 //    contiguous in K, so x is gathered with the same segment map.
 //  * Tiles are ordered so that the workgroups on one XCD (blocks are dealt to
 //    the 8 XCDs round-robin) share activation panels in that XCD's L2.
-//  * The segment variant reads (expert, row_start, num_rows) and the valid
-//    tile count on the device (no host sync after the tile map); MFMAs of
-//    16-row fragments past num_rows are skipped.
 #include <type_traits>
 
 #include "kq_decode.h"
@@ -239,13 +239,10 @@ constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 // s % PD, stored (weights: decoded) to LDS buffer s % 2 during step s - 1, and
 // consumed by the MFMAs of step s.  Activations come from L2 (their panel is
 // shared by the tiles of one XCD) and need a shorter distance than weights.
-template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB, bool SEG, bool F16>
+template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB, bool F16>
 __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restrict__ w, int n, int k,
-                                                          int64_t row_bytes, int64_t expert_stride, int n_experts,
-                                                          const half_t* __restrict__ x, int m_total,
-                                                          const uint32_t* __restrict__ map,
-                                                          const uint32_t* __restrict__ counts, int tiles_total,
-                                                          int per_xcd, void* __restrict__ y) {
+                                                          int64_t row_bytes, const half_t* __restrict__ x, int m_total,
+                                                          int tiles_total, int per_xcd, void* __restrict__ y) {
   static_assert(WM * WN == QMM_THREADS / 64, "8 waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TM = WTM / 16, TN = WTN / 16;  // 16x16 MFMA tiles per wave
@@ -262,21 +259,9 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
   const int nb = (n + BN - 1) / BN;
   const int by = t / nb;
   const int n0 = (t - by * nb) * BN;
-  int m0, mrows;
+  const int m0 = by * BM;
+  const int mrows = min(BM, m_total - m0);
   const uint8_t* wbase = w;
-  if (SEG) {
-    if (by >= (int)counts[0]) return;
-    const uint32_t* mt = map + 3 * (size_t)by;
-    const uint32_t e = mt[0], rs = mt[1], nr = mt[2];
-    if (e >= (uint32_t)n_experts || nr == 0 || nr > 64 || rs >= (uint32_t)m_total || nr > (uint32_t)m_total - rs)
-      return;
-    m0 = (int)rs;
-    mrows = (int)nr;
-    wbase = w + (int64_t)e * expert_stride;
-  } else {
-    m0 = by * BM;
-    mrows = min(BM, m_total - m0);
-  }
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -436,19 +421,19 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
   }
 }
 
-template <int C, bool SEG, int BM, int BN, int WM, int WN, int PDA, int PDB>
-hipError_t launch_t(const uint8_t* w, int64_t n, int64_t k, int64_t rb, int64_t estride, int64_t ne, const half_t* x,
-                    int64_t m, const uint32_t* map, const uint32_t* counts, int64_t tiles_m, void* y, int f16,
+template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB>
+hipError_t launch_t(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m, void* y, int f16,
                     hipStream_t s) {
+  const int64_t tiles_m = (m + BM - 1) / BM;
   const int64_t tiles = tiles_m * ((n + BN - 1) / BN);
   const int64_t per_xcd = (tiles + NXCD - 1) / NXCD;
   const dim3 grid((unsigned)(per_xcd * NXCD));
   if (f16)
-    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, SEG, true>), grid, dim3(QMM_THREADS), 0, s, w, (int)n, (int)k,
-                       rb, estride, (int)ne, x, (int)m, map, counts, (int)tiles, (int)per_xcd, y);
+    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, true>), grid, dim3(QMM_THREADS), 0, s, w, (int)n, (int)k,
+                       rb, x, (int)m, (int)tiles, (int)per_xcd, y);
   else
-    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, SEG, false>), grid, dim3(QMM_THREADS), 0, s, w, (int)n, (int)k,
-                       rb, estride, (int)ne, x, (int)m, map, counts, (int)tiles, (int)per_xcd, y);
+    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, false>), grid, dim3(QMM_THREADS), 0, s, w, (int)n, (int)k,
+                       rb, x, (int)m, (int)tiles, (int)per_xcd, y);
   return hipGetLastError();
 }
 
@@ -456,16 +441,9 @@ template <int C>
 hipError_t launch_dense(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m, void* y,
                         int f16, hipStream_t s) {
   if (m > 128)  // prefill: 256 x 224 tiles (N = 14336 gives 64 tile columns)
-    return launch_t<C, false, 256, 224, 4, 2, 1, 2>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, (m + 255) / 256, y, f16, s);
-  if (m > 64)
-    return launch_t<C, false, 128, 256, 2, 4, 2, 3>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, (m + 127) / 128, y, f16, s);
-  return launch_t<C, false, 64, 256, 2, 4, 2, 4>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, (m + 63) / 64, y, f16, s);
-}
-
-template <int C>
-hipError_t launch_seg(const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t rows,
-                      const uint32_t* map, const uint32_t* counts, int64_t cap, void* y, int f16, hipStream_t s) {
-  return launch_t<C, true, 64, 256, 2, 4, 2, 4>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+    return launch_t<C, 256, 224, 4, 2, 1, 2>(w, n, k, rb, x, m, y, f16, s);
+  if (m > 64) return launch_t<C, 128, 256, 2, 4, 2, 3>(w, n, k, rb, x, m, y, f16, s);
+  return launch_t<C, 64, 256, 2, 4, 2, 4>(w, n, k, rb, x, m, y, f16, s);
 }
 
 template <int C, bool SEG, bool F16>
@@ -552,20 +530,16 @@ hipError_t launch_qmm(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t
 hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb,
                                  const half_t* x, int64_t rows, const uint32_t* map, const uint32_t* counts,
                                  int64_t cap, void* y, int f16, hipStream_t s) {
-  if (k % 64 != 0) {
+  if (k % 64 != 0 || k > (1 << 24)) {  // the segment kernel's buffer offsets are 32-bit
     switch (codec) {
       case Q4_0: return launch_generic<Q4_0, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q8_0: return launch_generic<Q8_0, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+      case Q4_K: return launch_generic<Q4_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+      case Q6_K: return launch_generic<Q6_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
     }
     return hipErrorInvalidValue;
   }
-  switch (codec) {
-    case Q4_0: return launch_seg<Q4_0>(w, ne, n, k, rb, x, rows, map, counts, cap, y, f16, s);
-    case Q8_0: return launch_seg<Q8_0>(w, ne, n, k, rb, x, rows, map, counts, cap, y, f16, s);
-    case Q4_K: return launch_seg<Q4_K>(w, ne, n, k, rb, x, rows, map, counts, cap, y, f16, s);
-    case Q6_K: return launch_seg<Q6_K>(w, ne, n, k, rb, x, rows, map, counts, cap, y, f16, s);
-  }
-  return hipErrorInvalidValue;
+  return launch_seg_mma(codec, w, ne, n, k, rb, x, rows, map, counts, cap, y, f16, s);
 }
 
 }  // namespace kq

@@ -15,6 +15,26 @@ namespace {
 __host__ __device__ constexpr int xpad(int v) { return v + (v >> 6) * 8; }  // padded LDS offset (halves)
 
 // ---------------------------------------------------------------------------
+// Buffer loads: a wave-uniform base and byte count in a resource descriptor,
+// a per-lane offset that stays fixed across the K loop, and a wave-uniform
+// offset that moves with it.  Bytes past the count read as zero.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int64_t nb = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)(uint32_t)nb, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bld16(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bld4(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t bld2(rsrc_t r, int voff, int soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// ---------------------------------------------------------------------------
 // Units.  load(row, u): issue the loads of unit u of a row.
 // dot<M>(...): accumulate the unit's v_dot2 product into acc[0..M).
 // ---------------------------------------------------------------------------
@@ -51,6 +71,13 @@ struct UnitQ4K {
     const uint8_t* qs = blk + 16 + 32 * (u & 3);
     q0 = ld_16B(qs);
     q1 = ld_16B(qs + 16);
+  }
+  // unit u4 + cu of the row at byte rowoff (u4 a multiple of 4, wave-uniform)
+  __device__ __forceinline__ void bload(rsrc_t rs, int rowoff, int cu, int u4) {
+    const int so = (u4 >> 2) * 144;
+    h = bld16(rs, rowoff, so);
+    q0 = bld16(rs, rowoff + 16 + 32 * cu, so);
+    q1 = bld16(rs, rowoff + 32 + 32 * cu, so);
   }
   template <int M>
   __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
@@ -94,6 +121,12 @@ struct Shift16 {
     a = ld_16B_a4(q);
     b = ld_u32(q + 16 - (sh ? 0 : 4));  // sh == 0: re-read the 4th dword, never past the 16 bytes
   }
+  // same from a buffer: va (per lane) and soff (uniform) dword aligned, the
+  // 16 bytes start sh bytes past va + soff
+  __device__ __forceinline__ void bload(rsrc_t rs, int va, int soff, uint32_t sh) {
+    a = bld16(rs, va, soff);
+    b = bld4(rs, va + 16 - (sh ? 0 : 4), soff);
+  }
   __device__ __forceinline__ void get(uint32_t sh, uint32_t o[4]) const {
     o[0] = alignbyte(a.y, a.x, sh);
     o[1] = alignbyte(a.z, a.y, sh);
@@ -114,6 +147,22 @@ struct UnitQ6K {
     qhh.load(blk + 128 + 32 * h + 16 * half, sh);
     scl.load(blk + 192, sh);
     dbits = ld_u16(blk + 208);
+  }
+  // Buffer offsets must each be dword aligned for the dword loads, and a
+  // 210-byte block is not: the uniform offset steps over pairs of blocks, the
+  // odd block and the sub-dword shift go into the per-lane offset (rowoff is
+  // relative to a dword-aligned descriptor base).
+  __device__ __forceinline__ void bload(rsrc_t rs, int rowoff, int cu, int u4) {
+    const int blk = u4 >> 2, so = 420 * (blk >> 1);
+    const int h = (cu >> 1) & 1, half = cu & 1;
+    const int t = rowoff + 210 * (blk & 1);
+    sh = (uint32_t)t & 3u;
+    const int va = t - (int)sh;
+    qa.bload(rs, va + 64 * h + 16 * half, so, sh);
+    qb.bload(rs, va + 64 * h + 32 + 16 * half, so, sh);
+    qhh.bload(rs, va + 128 + 32 * h + 16 * half, so, sh);
+    scl.bload(rs, va + 192, so, sh);
+    dbits = bld2(rs, t + 208, so);
   }
   template <int M>
   __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
@@ -162,6 +211,11 @@ struct UnitQ8_0 {  // two 34-byte blocks, 68 bytes, dword aligned
     r0 = ld_16B_a4(p); r1 = ld_16B_a4(p + 16); r2 = ld_16B_a4(p + 32); r3 = ld_16B_a4(p + 48);
     r4 = ld_u32(p + 64);
   }
+  __device__ __forceinline__ void bload(rsrc_t rs, int rowoff, int cu, int u4) {
+    const int vo = rowoff + 68 * cu, so = 68 * u4;
+    r0 = bld16(rs, vo, so); r1 = bld16(rs, vo + 16, so); r2 = bld16(rs, vo + 32, so); r3 = bld16(rs, vo + 48, so);
+    r4 = bld4(rs, vo + 64, so);
+  }
   template <int M>
   __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
     const uint32_t R[17] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w,
@@ -197,6 +251,11 @@ struct UnitQ4_0 {  // two 18-byte blocks, 36 bytes, dword aligned
     const uint8_t* p = row + 36 * u;
     r0 = ld_16B_a4(p); r1 = ld_16B_a4(p + 16);
     r2 = ld_u32(p + 32);
+  }
+  __device__ __forceinline__ void bload(rsrc_t rs, int rowoff, int cu, int u4) {
+    const int vo = rowoff + 36 * cu, so = 36 * u4;
+    r0 = bld16(rs, vo, so); r1 = bld16(rs, vo + 16, so);
+    r2 = bld4(rs, vo + 32, so);
   }
   template <int M>
   __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {

@@ -274,27 +274,29 @@ def test_tile_map_workload_and_status_flags(kq):
 
 @pytest.mark.parametrize("codec", CODECS)
 def test_gather_qmm_seg_parity(kq, codec):
+    # K in one 512-value chunk or a partial one; K over several chunks with a
+    # ragged last chunk and N over two 192-row blocks with a ragged tail
     torch = _torch()
     rng = np.random.default_rng(17)
-    e, n = 6, 96
-    k = 512 if codec in ("q4_k", "q6_k") else 320
-    ids = np.sort(np.concatenate([rng.integers(0, e - 1, 190), [e - 1] * 3, [e + 2] * 4])).astype(np.uint32)
-    rows = ids.size
-    wf = (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32)
-    w = encode.quantize(codec, wf)
-    x = _x(rows, k, 5)
-    map_, counts, count, status, cap = _tile_map_gpu(kq, ids, e)
-    assert status == 2
-    tiles = host(map_)[:count].view(np.uint32)
-    for tdt in (torch.float16, torch.float32):
-        say(f"seg {codec} e={e} n={n} k={k} rows={rows} {tdt}")
-        y = torch.full((rows, n), float("nan"), dtype=tdt, device="cuda")
-        kq.kq_gather_qmm_seg(codec, dev(w), e, n, k, dev(x), map_[:cap], counts, y)
-        got = host(y).astype(np.float64)
+    kq_ = codec in ("q4_k", "q6_k")
+    for e, n, k in ((6, 96, 512 if kq_ else 320), (3, 200, 1280 if kq_ else 1344)):
+        ids = np.sort(np.concatenate([rng.integers(0, e - 1, 190), [e - 1] * 3, [e + 2] * 4])).astype(np.uint32)
+        rows = ids.size
+        wf = (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32)
+        w = encode.quantize(codec, wf)
+        x = _x(rows, k, 5)
+        map_, counts, count, status, cap = _tile_map_gpu(kq, ids, e)
+        assert status == 2
+        tiles = host(map_)[:count].view(np.uint32)
         ref = matmul.gather_qmm_seg(codec, w, k, x, tiles)
         covered = ids < e
-        assert np.all(np.isnan(got[~covered])), "uncovered rows must stay unwritten"
-        assert_close_rows(got[covered], ref[covered], what=f"seg {codec}")
+        for tdt in (torch.float16, torch.float32):
+            say(f"seg {codec} e={e} n={n} k={k} rows={rows} {tdt}")
+            y = torch.full((rows, n), float("nan"), dtype=tdt, device="cuda")
+            kq.kq_gather_qmm_seg(codec, dev(w), e, n, k, dev(x), map_[:cap], counts, y)
+            got = host(y).astype(np.float64)
+            assert np.all(np.isnan(got[~covered])), "uncovered rows must stay unwritten"
+            assert_close_rows(got[covered], ref[covered], what=f"seg {codec} n={n} k={k}")
 
 
 @pytest.mark.parametrize("codec", CODECS)
