@@ -105,6 +105,23 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t s0, uint32_t s1, uint32_t
   m = j < 4 ? m_lo : m_hi;
 }
 
+// Both sub-blocks 2P and 2P + 1 (P = 0..3) at once.  They sit in bytes
+// 2 (P & 1) and 2 (P & 1) + 1 of each scale dword; for P < 2 the six bits are
+// whole in s0 (scale) and s1 (min), for P >= 2 the low four come from s2 and
+// the top two from s0 / s1.  When P is uniform over a loop, the field offsets
+// and widths are computed once outside it.
+__device__ __forceinline__ void q4k_scale_min_pair(uint32_t s0, uint32_t s1, uint32_t s2, int P, uint32_t& sc0,
+                                                   uint32_t& m0, uint32_t& sc1, uint32_t& m1) {
+  const uint32_t sh = 16u * (uint32_t)(P & 1);
+  const bool hi = P >= 2;
+  const uint32_t a = hi ? s2 : s0, b = hi ? (s2 >> 4) : s1;  // low bits of scale, min
+  const uint32_t w = hi ? 4u : 6u, t = hi ? 2u : 0u;        // their width; width of the top bits
+  sc0 = __builtin_amdgcn_ubfe(a, sh, w) | (__builtin_amdgcn_ubfe(s0, sh + 6u, t) << 4);
+  sc1 = __builtin_amdgcn_ubfe(a, sh + 8u, w) | (__builtin_amdgcn_ubfe(s0, sh + 14u, t) << 4);
+  m0 = __builtin_amdgcn_ubfe(b, sh, w) | (__builtin_amdgcn_ubfe(s1, sh + 6u, t) << 4);
+  m1 = __builtin_amdgcn_ubfe(b, sh + 8u, w) | (__builtin_amdgcn_ubfe(s1, sh + 14u, t) << 4);
+}
+
 // ---------------------------------------------------------------------------
 // launchers (defined in the kernel translation units)
 // ---------------------------------------------------------------------------

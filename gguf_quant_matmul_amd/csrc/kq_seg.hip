@@ -116,10 +116,17 @@ __device__ __forceinline__ void seg_tile(const uint8_t* __restrict__ wbase, int 
     for (int i = 0; i < XPT; ++i) *(u32x4*)(xst + buf * SEG_XBUF + SEG_RPI * i * SEG_XSTRIDE) = xr[i];
   };
 
+  // The loads keep program order (scheduling fences): slot p's loads all go
+  // out before slot p + 1's, as they do in the K loop, so the wait for a
+  // slot is the same on entry as on every iteration.
   load_x(0);
   Unit ring[NS][SEG_RG];
 #pragma unroll
-  for (int p = 0; p < NS; ++p) refill(ring[p], 4 * p);
+  for (int p = 0; p < NS; ++p) {
+    __builtin_amdgcn_sched_barrier(0);
+    refill(ring[p], 4 * p);
+  }
+  __builtin_amdgcn_sched_barrier(0);
   store_x(0);
   __syncthreads();
 
@@ -138,10 +145,13 @@ __device__ __forceinline__ void seg_tile(const uint8_t* __restrict__ wbase, int 
       const int u = ub + 4 * gg + cu;
       const bool valid = u < ue;                    // else this lane adds zeros
       const int uc = valid ? u : max(ue - 1, ub);  // (and reads in-chunk activations)
+      // q4_K reads only u & 3 (lane-uniform): spelled out, its scale fields'
+      // offsets are computed once outside the loop
+      const int us = C == Q4_K ? 4 * (u >> 2) + cu : uc;
       const half_t* xb = cur + r * SEG_XSTRIDE + xpad(MmaSlices<C>::koff(uc) - c0);
-      const MmaSlices<C> sl0(ring[(SEG_GPC * H + gg) % NS][0], uc, valid);
-      const MmaSlices<C> sl1(ring[(SEG_GPC * H + gg) % NS][1], uc, valid);
-      const MmaSlices<C> sl2(ring[(SEG_GPC * H + gg) % NS][2], uc, valid);
+      const MmaSlices<C> sl0(ring[(SEG_GPC * H + gg) % NS][0], us, valid);
+      const MmaSlices<C> sl1(ring[(SEG_GPC * H + gg) % NS][1], us, valid);
+      const MmaSlices<C> sl2(ring[(SEG_GPC * H + gg) % NS][2], us, valid);
       auto step = [&](auto sc) __attribute__((always_inline)) {
         constexpr int S = decltype(sc)::value;
         uint32_t f0[4], f1[4], f2[4];

@@ -317,16 +317,17 @@ template <int C> struct MmaSlices;
 
 template <> struct MmaSlices<Q4_K> {
   // values 0..31: low nibbles of the 32 qs bytes (sub-block 2P), 32..63: high
-  // nibbles (sub-block 2P + 1); weight = d sc q - dmin m
+  // nibbles (sub-block 2P + 1); weight = d sc q - dmin m.  High nibbles are
+  // used in place (16 q, no shift), so their step s1 carries a factor 1/16
+  // (exact: d sc / 16 is a float16 value times a small integer).
   float s0, c0, s1, c1;
   uint32_t qw[8];
   __device__ __forceinline__ MmaSlices(const UnitQ4K& un, int u, bool keep) {
     const float d = keep ? f16_to_f32(un.h.x) : 0.f, dmin = keep ? f16_to_f32(un.h.x >> 16) : 0.f;
     uint32_t sc0, m0, sc1, m1;
-    q4k_scale_min(un.h.y, un.h.z, un.h.w, 2 * (u & 3), sc0, m0);
-    q4k_scale_min(un.h.y, un.h.z, un.h.w, 2 * (u & 3) + 1, sc1, m1);
+    q4k_scale_min_pair(un.h.y, un.h.z, un.h.w, u & 3, sc0, m0, sc1, m1);
     s0 = d * (float)sc0; c0 = -(1024.f * s0 + dmin * (float)m0);
-    s1 = d * (float)sc1; c1 = -(1024.f * s1 + dmin * (float)m1);
+    s1 = (0.0625f * d) * (float)sc1; c1 = -(1024.f * s1 + dmin * (float)m1);
     qw[0] = un.q0.x; qw[1] = un.q0.y; qw[2] = un.q0.z; qw[3] = un.q0.w;
     qw[4] = un.q1.x; qw[5] = un.q1.y; qw[6] = un.q1.z; qw[7] = un.q1.w;
   }
@@ -339,7 +340,7 @@ template <> struct MmaSlices<Q4_K> {
     if (S < 4)
       slice8(qw[2 * t] & 0x0F0F0F0Fu, qw[2 * t + 1] & 0x0F0F0F0Fu, s0, c0, f);
     else
-      slice8((qw[2 * t] >> 4) & 0x0F0F0F0Fu, (qw[2 * t + 1] >> 4) & 0x0F0F0F0Fu, s1, c1, f);
+      slice8(qw[2 * t] & 0xF0F0F0F0u, qw[2 * t + 1] & 0xF0F0F0F0u, s1, c1, f);
   }
 };
 
@@ -405,7 +406,8 @@ template <> struct MmaSlices<Q8_0> {
 };
 
 template <> struct MmaSlices<Q4_0> {
-  // block b = S >> 2: values 0..15 low nibbles of its 16 bytes, 16..31 high; weight = d (q - 8)
+  // block b = S >> 2: values 0..15 low nibbles of its 16 bytes, 16..31 high;
+  // weight = d (q - 8).  High nibbles are used in place (16 q) with step d / 16.
   uint32_t q[2][4];
   float d[2];
   __device__ __forceinline__ MmaSlices(const UnitQ4_0& un, int, bool keep) {
@@ -423,8 +425,11 @@ template <> struct MmaSlices<Q4_0> {
   static constexpr int xstep() { return 8 * S; }
   template <int S>
   __device__ __forceinline__ void get(uint32_t f[4]) const {
-    constexpr int b = S >> 2, t = S & 3, dw = 2 * (t & 1), sh = 4 * (t >> 1);
-    slice8((q[b][dw] >> sh) & 0x0F0F0F0Fu, (q[b][dw + 1] >> sh) & 0x0F0F0F0Fu, d[b], -1032.f * d[b], f);
+    constexpr int b = S >> 2, t = S & 3, dw = 2 * (t & 1);
+    if (t < 2)  // fma(1024 + q, d, -1032 d) = d (q - 8)
+      slice8(q[b][dw] & 0x0F0F0F0Fu, q[b][dw + 1] & 0x0F0F0F0Fu, d[b], -1032.f * d[b], f);
+    else  // fma(1024 + 16 q, d / 16, -72 d) = d (q - 8)
+      slice8(q[b][dw] & 0xF0F0F0F0u, q[b][dw + 1] & 0xF0F0F0F0u, 0.0625f * d[b], -72.f * d[b], f);
   }
 };
 
