@@ -299,6 +299,34 @@ def test_gather_qmm_seg_parity(kq, codec):
             assert_close_rows(got[covered], ref[covered], what=f"seg {codec} n={n} k={k}")
 
 
+@pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0"])
+def test_gather_seg_tail_merge_boundaries(kq, codec):
+    # expert rows 96 (a full tile and a 32-row tail), 97 (a 33-row tail),
+    # 133 (two full tiles and a 5-row tail), 64 (one full tile), 20 and one
+    # out-of-range id block: every tile boundary the expert-segment kernel
+    # treats differently, in one map; N over two 384-row blocks
+    torch = _torch()
+    rng = np.random.default_rng(23)
+    e, n, k = 5, 400, 512
+    sizes = [96, 97, 133, 64, 20]
+    ids = np.concatenate([np.full(c, i, np.uint32) for i, c in enumerate(sizes)] + [np.full(3, e + 1, np.uint32)])
+    rows = ids.size
+    w = encode.quantize(codec, (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32))
+    x = _x(rows, k, 6)
+    map_, counts, count, status, cap = _tile_map_gpu(kq, ids, e)
+    tiles = host(map_)[:count].view(np.uint32)
+    assert [int(t[2]) for t in tiles] == [64, 32, 64, 33, 64, 64, 5, 64, 20]
+    ref = matmul.gather_qmm_seg(codec, w, k, x, tiles)
+    covered = ids < e
+    for tdt in (torch.float16, torch.float32):
+        say(f"seg merge boundaries {codec} {tdt}")
+        y = torch.full((rows, n), float("nan"), dtype=tdt, device="cuda")
+        kq.kq_gather_qmm_seg(codec, dev(w), e, n, k, dev(x), map_[:cap], counts, y)
+        got = host(y).astype(np.float64)
+        assert np.all(np.isnan(got[~covered])), "uncovered rows must stay unwritten"
+        assert_close_rows(got[covered], ref[covered], what=f"seg merge boundaries {codec}")
+
+
 @pytest.mark.parametrize("codec", CODECS)
 def test_gather_qmv_parity(kq, codec):
     # one activation row per routed slot, ids in any order; an id past the
