@@ -300,11 +300,11 @@ def test_gather_qmm_seg_parity(kq, codec):
 
 
 @pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0"])
-def test_gather_seg_tail_merge_boundaries(kq, codec):
+def test_gather_seg_tile_boundaries(kq, codec):
     # expert rows 96 (a full tile and a 32-row tail), 97 (a 33-row tail),
     # 133 (two full tiles and a 5-row tail), 64 (one full tile), 20 and one
-    # out-of-range id block: every tile boundary the expert-segment kernel
-    # treats differently, in one map; N over two 384-row blocks
+    # out-of-range id block: full, partial and single-group tiles of one
+    # expert back to back in one map; N with a ragged last column block
     torch = _torch()
     rng = np.random.default_rng(23)
     e, n, k = 5, 400, 512
@@ -319,12 +319,12 @@ def test_gather_seg_tail_merge_boundaries(kq, codec):
     ref = matmul.gather_qmm_seg(codec, w, k, x, tiles)
     covered = ids < e
     for tdt in (torch.float16, torch.float32):
-        say(f"seg merge boundaries {codec} {tdt}")
+        say(f"seg tile boundaries {codec} {tdt}")
         y = torch.full((rows, n), float("nan"), dtype=tdt, device="cuda")
         kq.kq_gather_qmm_seg(codec, dev(w), e, n, k, dev(x), map_[:cap], counts, y)
         got = host(y).astype(np.float64)
         assert np.all(np.isnan(got[~covered])), "uncovered rows must stay unwritten"
-        assert_close_rows(got[covered], ref[covered], what=f"seg merge boundaries {codec}")
+        assert_close_rows(got[covered], ref[covered], what=f"seg tile boundaries {codec}")
 
 
 @pytest.mark.parametrize("codec", CODECS)
