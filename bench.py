@@ -187,7 +187,23 @@ def measure_rows(torch, kq):
                  f"{cfg.n_experts} experts, {cfg.n}x{cfg.k} {cfg.codec}", "us": round(ms_dec * 1e3, 2),
                  "GB/s": round(alg_dec / ms_dec / 1e6, 1), "hbm_frac": round(alg_dec / ms_dec / 1e6 / HBM_PEAK_GBS, 3),
                  "alg_bytes": alg_dec, "copies": nc})
-    del ws, wq, xd
+    # MoE decode GLU: the same token's slots through kq_moe_glu_gather, these
+    # experts as gate and an up stack drawn the same way (seed + 100); launch i
+    # takes token i's experts and copy i % nc of both stacks
+    del xd
+    wu = gpu_weights(torch, kq, cfg.codec, cfg.seed + 100, cfg.n_experts * cfg.n, cfg.k, "normal")
+    wus = [wu] + [wu.clone() for _ in range(nc - 1)]
+    xg = [torch.from_numpy(np.ascontiguousarray(xtok[i:i + 1])).cuda() for i in range(nl)]
+    gids = dec_ids.view(nl, 1, cfg.top_k)
+    gg = capture(torch, lambda: [kq.kq_moe_glu_gather(cfg.codec, ws[i % nc], wus[i % nc], cfg.n_experts, cfg.n,
+                                                      cfg.k, xg[i], gids[i], yd, "silu") for i in range(nl)])
+    ms_glu = time_graph(torch, gg, nl, 5)
+    alg_glu = 2 * cfg.top_k * cfg.n * wq.shape[1] + cfg.k * 2 + cfg.top_k * cfg.n * 2
+    rows.append({"row": "kq_moe_glu_gather", "workload": f"MoE decode GLU gather (silu) 1 tok top-{cfg.top_k} of "
+                 f"{cfg.n_experts} experts, gate+up {cfg.n}x{cfg.k} {cfg.codec}", "us": round(ms_glu * 1e3, 2),
+                 "GB/s": round(alg_glu / ms_glu / 1e6, 1), "hbm_frac": round(alg_glu / ms_glu / 1e6 / HBM_PEAK_GBS, 3),
+                 "alg_bytes": alg_glu, "copies": nc})
+    del ws, wq, wus, wu, xg
     torch.cuda.empty_cache()
 
     # dequantize (q4_K 4096 x 4096 -> float16)

@@ -236,6 +236,35 @@ int kq_gather_qmv(int codec, const void* w, int64_t n_experts, int64_t n, int64_
                                               ids, rows, y, y_dtype == KQ_F16, (hipStream_t)stream));
 }
 
+int kq_moe_glu_gather(int codec, const void* gate_w, const void* up_w, int64_t n_experts, int64_t n, int64_t k,
+                      const void* x, int64_t tokens, const uint32_t* ids, int64_t top_k, int act, float limit,
+                      void* y, int y_dtype, void* stream) {
+  const char* op = "kq_moe_glu_gather";
+  if (tokens < 0 || tokens >= kMaxDim) return fail(KQ_ERR_ARG, op, "tokens=%lld out of range", (long long)tokens);
+  if (top_k < 0 || top_k >= kMaxDim || (top_k && tokens >= kMaxDim / top_k))
+    return fail(KQ_ERR_ARG, op, "top_k=%lld out of range", (long long)top_k);
+  const int64_t rows = tokens * top_k;
+  int64_t rb;
+  int st = check_matmul(op, codec, gate_w, n, k, x, rows, y, y_dtype, &rb);
+  if (st) return st;
+  if (k % 256)
+    return fail(KQ_ERR_SHAPE, op, "K=%lld is not a multiple of 256 (one activation row per token)", (long long)k);
+  if (n_experts <= 0 || n_experts >= kMaxDim || n_experts * n >= kMaxDim * 64)
+    return fail(KQ_ERR_ARG, op, "n_experts=%lld out of range", (long long)n_experts);
+  if (act != KQ_GLU_SILU && act != KQ_GLU_GELU_TANH && act != KQ_GLU_SILU_LIMIT)
+    return fail(KQ_ERR_ARG, op, "act=%d is not a kq_glu_act", act);
+  if (act == KQ_GLU_SILU_LIMIT && !(limit > 0.f && limit <= 3.0e38f))
+    return fail(KQ_ERR_ARG, op, "limit=%g must be finite and > 0 for KQ_GLU_SILU_LIMIT", (double)limit);
+  if (n == 0 || rows == 0) return KQ_OK;
+  if (!up_w) return fail(KQ_ERR_ARG, op, "null up_w");
+  if (!aligned(up_w, 16)) return fail(KQ_ERR_ALIGN, op, "up_w=%p is not 16-byte aligned", up_w);
+  if (!ids) return fail(KQ_ERR_ARG, op, "null ids");
+  if (!aligned(ids, 4)) return fail(KQ_ERR_ALIGN, op, "ids=%p is not 4-byte aligned", (const void*)ids);
+  return hip_status(op, kq::launch_moe_glu_gather(codec, (const uint8_t*)gate_w, (const uint8_t*)up_w, n_experts, n,
+                                                  k, rb, (const kq::half_t*)x, ids, rows, top_k, act, limit, y,
+                                                  y_dtype == KQ_F16, (hipStream_t)stream));
+}
+
 int kq_quantize(int codec, const float* w, int64_t rows, int64_t k, void* out, void* stream) {
   const char* op = "kq_quantize";
   int64_t rb;

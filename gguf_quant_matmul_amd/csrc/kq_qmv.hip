@@ -64,9 +64,34 @@ __device__ __forceinline__ float lanes_sum(float v) {
 }
 
 // The GEMV of one workgroup: rows [blk * rows_per_block, ...) of w.
-template <int C, int M, int LPR, bool F16>
+// GLU epilogues of the mlx-kquant bindings.cpp page (moe_glu_gather_kq
+// docstring, its act argument), in float32 on the two float32 products g
+// (gate) and u (up):
+//   GLU_SILU        silu(g) * u, silu(g) = g / (1 + exp(-g))
+//   GLU_GELU_TANH   gelu(g) * u with the tanh form of gelu,
+//                   0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)))
+//   GLU_SILU_LIMIT  silu(min(g, limit)) * clip(u, -limit, limit)
+template <int ACT>
+__device__ __forceinline__ float glu_act(float g, float u, float limit) {
+  if constexpr (ACT == GLU_SILU) {
+    return g / (1.f + expf(-g)) * u;
+  } else if constexpr (ACT == GLU_GELU_TANH) {
+    const float c = 0.7978845608028654f;  // sqrt(2 / pi)
+    return 0.5f * g * (1.f + tanhf(c * (g + 0.044715f * g * g * g))) * u;
+  } else {
+    const float gg = fminf(g, limit);
+    return gg / (1.f + expf(-gg)) * fminf(fmaxf(u, -limit), limit);
+  }
+}
+
+// NW = 2: the same rows of a second matrix w2 (M = 1) go through the same
+// pass, sharing each staged activation chunk, and lane 0 of a row stores
+// glu_act<ACT>(row of w, row of w2) instead of both products.
+template <int C, int M, int LPR, bool F16, int NW = 1, int ACT = 0>
 __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, int k, int64_t row_bytes,
-                                         const half_t* __restrict__ x, void* __restrict__ y, int blk) {
+                                         const half_t* __restrict__ x, void* __restrict__ y, int blk,
+                                         const uint8_t* __restrict__ w2 = nullptr, float limit = 0.f) {
+  static_assert(NW == 1 || (NW == 2 && M == 1), "two matrices take one activation row");
   typedef typename UnitOf<C>::T Unit;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int KC = kchunk_max(M);
@@ -82,8 +107,9 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
   const int row = (blk * (QMV_THREADS / 64) + wave) * ROWS_PER_WAVE + rslot;
   const bool row_ok = row < n;
   const uint8_t* wrow = w + (int64_t)(row_ok ? row : 0) * row_bytes;
+  const uint8_t* wrow2 = NW == 2 ? w2 + (int64_t)(row_ok ? row : 0) * row_bytes : nullptr;
 
-  float acc[M];
+  float acc[M], acc2 = 0.f;
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
 
@@ -108,11 +134,12 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
       const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
       xr[i] = *(const u32x4*)(x + (int64_t)m * k + c0 + v);
     }
-    Unit cur[UNROLL];
+    Unit cur[UNROLL], cur2[NW == 2 ? UNROLL : 1];
 #pragma unroll
     for (int j = 0; j < UNROLL; ++j) {
       const int u = ub + uslot + LANES_PER_ROW * j;
       cur[j].load(wrow, u < ue ? u : ue - 1);
+      if constexpr (NW == 2) cur2[j].load(wrow2, u < ue ? u : ue - 1);
     }
     if (c0) __syncthreads();  // previous chunk done with LDS
     // Stage x and its 16-value sums in one pass: pieces 2g and 2g + 1 (8
@@ -135,24 +162,42 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
     const Xv xv{xs, xsum, xstride, sstride, c0};
     for (int g = 0; g < ngroups; ++g) {
       const int u0 = ub + uslot + LANES_PER_ROW * UNROLL * g;
-      Unit nxt[UNROLL];
+      Unit nxt[UNROLL], nxt2[NW == 2 ? UNROLL : 1];
       if (g + 1 < ngroups) {  // uniform across the block
 #pragma unroll
         for (int j = 0; j < UNROLL; ++j) {
           const int u = u0 + LANES_PER_ROW * (UNROLL + j);
           nxt[j].load(wrow, u < ue ? u : ue - 1);
+          if constexpr (NW == 2) nxt2[j].load(wrow2, u < ue ? u : ue - 1);
         }
       }
 #pragma unroll
       for (int j = 0; j < UNROLL; ++j) {
         const int u = u0 + LANES_PER_ROW * j;
-        if (row_ok && u < ue) cur[j].template dot<M>(u, xv, acc);
+        if (row_ok && u < ue) {
+          cur[j].template dot<M>(u, xv, acc);
+          if constexpr (NW == 2) cur2[j].template dot<1>(u, xv, &acc2);
+        }
       }
 #pragma unroll
-      for (int j = 0; j < UNROLL; ++j) cur[j] = nxt[j];
+      for (int j = 0; j < UNROLL; ++j) {
+        cur[j] = nxt[j];
+        if constexpr (NW == 2) cur2[j] = nxt2[j];
+      }
     }
   }
 
+  if constexpr (NW == 2) {
+    const float g = lanes_sum<LPR>(acc[0]), u = lanes_sum<LPR>(acc2);
+    if (row_ok && uslot == 0) {
+      const float v = glu_act<ACT>(g, u, limit);
+      if (F16)
+        ((half_t*)y)[row] = (half_t)v;
+      else
+        ((float*)y)[row] = v;
+    }
+    return;
+  }
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = lanes_sum<LPR>(acc[m]);
   if (row_ok && uslot < M) {
@@ -189,6 +234,24 @@ __global__ __launch_bounds__(QMV_THREADS) void gather_qmv_kernel(const uint8_t* 
   if (e >= (uint32_t)n_experts) return;  // the whole workgroup leaves before any barrier
   void* yr = F16 ? (void*)((half_t*)y + (int64_t)r * n) : (void*)((float*)y + (int64_t)r * n);
   qmv_rows<C, 1, LPR, F16>(w + (int64_t)e * expert_stride, n, k, row_bytes, x + (int64_t)r * k, yr, blockIdx.x);
+}
+
+// MoE GLU gather (mlx-kquant bindings.cpp page, moe_glu_gather_kq
+// docstring): routed slot r of token t = r / top_k gives y[r] =
+// act(x[t] . gate[e]) * (x[t] . up[e]) row by row, e = ids[r]; gate and up
+// rows of the expert share each staged activation chunk.  blockIdx.y is the
+// routed slot; a slot whose id is not below n_experts is left unwritten.
+template <int C, int LPR, bool F16, int ACT>
+__global__ __launch_bounds__(QMV_THREADS) void moe_glu_gather_kernel(
+    const uint8_t* __restrict__ gate_w, const uint8_t* __restrict__ up_w, int n_experts, int64_t expert_stride, int n,
+    int k, int64_t row_bytes, const half_t* __restrict__ x, const uint32_t* __restrict__ ids, int top_k, int row0,
+    float limit, void* __restrict__ y) {
+  const int r = row0 + (int)blockIdx.y;
+  const uint32_t e = ids[r];
+  if (e >= (uint32_t)n_experts) return;  // the whole workgroup leaves before any barrier
+  void* yr = F16 ? (void*)((half_t*)y + (int64_t)r * n) : (void*)((float*)y + (int64_t)r * n);
+  qmv_rows<C, 1, LPR, F16, 2, ACT>(gate_w + (int64_t)e * expert_stride, n, k, row_bytes, x + (int64_t)(r / top_k) * k,
+                                   yr, blockIdx.x, up_w + (int64_t)e * expert_stride, limit);
 }
 
 // Generic GEMV for shapes the unit kernels do not take (q8_0 / q4_0 with an
@@ -466,6 +529,49 @@ hipError_t launch_gather_l(const uint8_t* w, int64_t ne, int64_t n, int64_t k, i
   return hipSuccess;
 }
 
+template <int C, int LPR, int ACT>
+hipError_t launch_glu_l(const uint8_t* gw, const uint8_t* uw, int64_t ne, int64_t n, int64_t k, int64_t rb,
+                        const half_t* x, const uint32_t* ids, int64_t rows, int64_t top_k, float limit, void* y,
+                        int f16, hipStream_t s) {
+  const int kc = (int)(k < kchunk_max(1) ? k : kchunk_max(1));
+  const size_t lds = (size_t)xpad(kc) * 2 + (size_t)(kc / 16) * 4;
+  const unsigned gx = (unsigned)((n + rows_per_block(LPR) - 1) / rows_per_block(LPR));
+  for (int64_t r0 = 0; r0 < rows; r0 += 65535) {  // grid y holds at most 65535 rows per launch
+    const dim3 grid(gx, (unsigned)(rows - r0 < 65535 ? rows - r0 : 65535));
+    if (f16)
+      hipLaunchKernelGGL((moe_glu_gather_kernel<C, LPR, true, ACT>), grid, dim3(QMV_THREADS), lds, s, gw, uw, (int)ne,
+                         n * rb, (int)n, (int)k, rb, x, ids, (int)top_k, (int)r0, limit, y);
+    else
+      hipLaunchKernelGGL((moe_glu_gather_kernel<C, LPR, false, ACT>), grid, dim3(QMV_THREADS), lds, s, gw, uw, (int)ne,
+                         n * rb, (int)n, (int)k, rb, x, ids, (int)top_k, (int)r0, limit, y);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int C, int ACT>
+hipError_t launch_glu_a(const uint8_t* gw, const uint8_t* uw, int64_t ne, int64_t n, int64_t k, int64_t rb,
+                        const half_t* x, const uint32_t* ids, int64_t rows, int64_t top_k, float limit, void* y,
+                        int f16, hipStream_t s) {
+  if (n <= 32768) return launch_glu_l<C, 64, ACT>(gw, uw, ne, n, k, rb, x, ids, rows, top_k, limit, y, f16, s);
+  return launch_glu_l<C, 16, ACT>(gw, uw, ne, n, k, rb, x, ids, rows, top_k, limit, y, f16, s);
+}
+
+template <int C>
+hipError_t launch_glu_c(const uint8_t* gw, const uint8_t* uw, int64_t ne, int64_t n, int64_t k, int64_t rb,
+                        const half_t* x, const uint32_t* ids, int64_t rows, int64_t top_k, int act, float limit,
+                        void* y, int f16, hipStream_t s) {
+  switch (act) {
+    case GLU_SILU: return launch_glu_a<C, GLU_SILU>(gw, uw, ne, n, k, rb, x, ids, rows, top_k, limit, y, f16, s);
+    case GLU_GELU_TANH:
+      return launch_glu_a<C, GLU_GELU_TANH>(gw, uw, ne, n, k, rb, x, ids, rows, top_k, limit, y, f16, s);
+    case GLU_SILU_LIMIT:
+      return launch_glu_a<C, GLU_SILU_LIMIT>(gw, uw, ne, n, k, rb, x, ids, rows, top_k, limit, y, f16, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 template <int C>
 hipError_t launch_gather_c(const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb, const half_t* x,
                            const uint32_t* ids, int64_t rows, void* y, int f16, hipStream_t s) {
@@ -483,6 +589,22 @@ hipError_t launch_gather_qmv(int codec, const uint8_t* w, int64_t n_experts, int
     case Q8_0: return launch_gather_c<Q8_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q4_K: return launch_gather_c<Q4_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q6_K: return launch_gather_c<Q6_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_moe_glu_gather(int codec, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_experts, int64_t n,
+                                 int64_t k, int64_t row_bytes, const half_t* x, const uint32_t* ids, int64_t rows,
+                                 int64_t top_k, int act, float limit, void* y, int f16out, hipStream_t s) {
+  switch (codec) {
+    case Q4_0:
+      return launch_glu_c<Q4_0>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
+    case Q8_0:
+      return launch_glu_c<Q8_0>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
+    case Q4_K:
+      return launch_glu_c<Q4_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
+    case Q6_K:
+      return launch_glu_c<Q6_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
   }
   return hipErrorInvalidValue;
 }

@@ -43,6 +43,8 @@ _SIGS = {
     "kq_expert_tile_map": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp]),
     "kq_gather_qmm_seg": (c_int, [c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_int, c_vp]),
     "kq_gather_qmv": (c_int, [c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_int, c_vp]),
+    "kq_moe_glu_gather": (c_int, [c_int, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_int,
+                                  ctypes.c_float, c_vp, c_int, c_vp]),
     "kq_quantize": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_vp]),
 }
 
@@ -57,6 +59,8 @@ for _name, (_res, _args) in _SIGS.items():
 # ids and enums of include/kq.h
 KQ_Q4_0, KQ_Q8_0, KQ_Q4_K, KQ_Q6_K = 2, 8, 12, 14
 KQ_F32, KQ_F16 = 0, 1
+KQ_GLU_SILU, KQ_GLU_GELU_TANH, KQ_GLU_SILU_LIMIT = 0, 1, 2
+_GLU_ACTS = {"silu": KQ_GLU_SILU, "gelu": KQ_GLU_GELU_TANH, "silu_limit": KQ_GLU_SILU_LIMIT}
 KQ_OK, KQ_ERR_ARG, KQ_ERR_CODEC, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_CAPACITY, KQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 STATUS_NAMES = {0: "KQ_OK", -1: "KQ_ERR_ARG", -2: "KQ_ERR_CODEC", -3: "KQ_ERR_SHAPE", -4: "KQ_ERR_ALIGN",
                 -5: "KQ_ERR_CAPACITY", -6: "KQ_ERR_HIP"}
@@ -178,6 +182,16 @@ def kq_gather_qmv(codec, w, n_experts: int, n: int, k: int, x, ids, y, stream=No
     """w uint8 [E, n, row_bytes]; x float16 [rows, k]; ids int32/uint32 [rows]; y [rows, n]."""
     _check(_lib.kq_gather_qmv(_codec(codec), _ptr(w), n_experts, n, k, _ptr(x), _ptr(ids), x.shape[0], _ptr(y),
                               _dtype_id(y), _stream(stream)))
+
+
+def kq_moe_glu_gather(codec, gate_w, up_w, n_experts: int, n: int, k: int, x, ids, y, act="silu",
+                      limit: float = 0.0, stream=None) -> None:
+    """gate_w, up_w uint8 [E, n, row_bytes]; x float16 [T, k]; ids int32/uint32 [T, R]; y [T * R, n] (or
+    [T, R, n]).  act: 'silu', 'gelu' (tanh form) or 'silu_limit', or a KQ_GLU_* id."""
+    a = _GLU_ACTS[act] if isinstance(act, str) else int(act)
+    top_k = ids.shape[1] if ids.dim() > 1 else 1
+    _check(_lib.kq_moe_glu_gather(_codec(codec), _ptr(gate_w), _ptr(up_w), n_experts, n, k, _ptr(x), x.shape[0],
+                                  _ptr(ids), top_k, a, float(limit), _ptr(y), _dtype_id(y), _stream(stream)))
 
 
 def kq_quantize(codec, w, out, stream=None) -> None:

@@ -52,6 +52,13 @@ typedef enum { KQ_Q4_0 = 2, KQ_Q8_0 = 8, KQ_Q4_K = 12, KQ_Q6_K = 14 } kq_codec;
 /* Output element types. */
 typedef enum { KQ_F32 = 0, KQ_F16 = 1 } kq_dtype;
 
+/* GLU epilogues of kq_moe_glu_gather (the pages' act names in comments). */
+typedef enum {
+  KQ_GLU_SILU = 0,       /* 'silu':       silu(g) * u                          */
+  KQ_GLU_GELU_TANH = 1,  /* 'gelu':       gelu(g) * u, tanh form               */
+  KQ_GLU_SILU_LIMIT = 2  /* 'silu_limit': silu(min(g, L)) * clip(u, -L, L)     */
+} kq_glu_act;
+
 typedef enum {
   KQ_OK = 0,
   KQ_ERR_ARG = -1,      /* null pointer, bad dtype, size out of range       */
@@ -143,6 +150,29 @@ int kq_gather_qmm_seg(int codec, const void* w, int64_t n_experts, int64_t n, in
 int kq_gather_qmv(int codec, const void* w, int64_t n_experts, int64_t n, int64_t k,
                   const void* x, const uint32_t* ids, int64_t rows,
                   void* y, int y_dtype, void* stream);
+
+/* ---- MoE GLU gather (mlx-kquant bindings.cpp page, moe_glu_gather_kq
+ * docstring) ----
+ * The decode-shaped MoE gate/up pair with its GLU epilogue in one launch.
+ * gate_w, up_w [n_experts][N][row_bytes] (same codec and shape); x float16
+ * [tokens][K], one activation row per token shared by its top_k slots; ids
+ * uint32 [tokens][top_k] (device memory).  For slot r = t * top_k + j with
+ * e = ids[r] < n_experts:
+ *   g = sum_k x[t][k] * dequant(gate_w[e])[n][k]
+ *   u = sum_k x[t][k] * dequant(up_w[e])[n][k]
+ *   y[r][n] = act(g, u)
+ * float32 accumulation and epilogue; y [tokens * top_k][N] (the pages'
+ * [T, R, N]).  act is a kq_glu_act; limit is the clamp bound L of
+ * KQ_GLU_SILU_LIMIT (finite and > 0, else KQ_ERR_ARG; ignored by the other
+ * two).  silu(v) = v / (1 + exp(-v)); gelu in its tanh form
+ * 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3))).  Slots with
+ * ids[r] >= n_experts are left unwritten.  K must be a multiple of 256, else
+ * KQ_ERR_SHAPE; ids 4-byte aligned.  The pages' 'swiglu_clamp' act and its
+ * biases belong to the mxfp4/nvfp4 layouts and are not offered. */
+int kq_moe_glu_gather(int codec, const void* gate_w, const void* up_w, int64_t n_experts,
+                      int64_t n, int64_t k, const void* x, int64_t tokens,
+                      const uint32_t* ids, int64_t top_k, int act, float limit,
+                      void* y, int y_dtype, void* stream);
 
 /* ---- encoder (mlx-kquant bindings.cpp page, quantize docstring; no imatrix) ----
  * float32 w [rows][K] -> wire bytes out [rows][row_bytes], round to nearest

@@ -17,6 +17,14 @@ Definitions followed
     oracle emits expert-major, ascending row_start.
   * mlx-kquant ``bindings.cpp`` page, ``gather_qmv_kq`` docstring: one
     activation row per expert slot; row r times expert ``indices[r]``.
+  * mlx-kquant ``bindings.cpp`` page, ``moe_glu_gather_kq`` docstring: the
+    gate and up expert products of one token's activation row, combined by
+    the GLU epilogue act(g) * u.  act 'silu': silu(g) * u; 'gelu' (its tanh
+    approximation): gelu(g) * u; 'silu_limit': silu(min(g, limit)) *
+    clip(u, -limit, limit).  silu(v) = v * sigmoid(v) = v / (1 + exp(-v));
+    the tanh form of gelu is 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
+    (the standard tanh approximation; the page names it, not its formula).
+    Output [T, R, N], slot (t, r) using expert indices[t, r].
   * mlx-kquant ``bindings.cpp`` page, ``gather_qmm_seg`` docstring: for each
     valid tile, rows [row_start, row_start+num_rows) of the expert-sorted x
     times expert ``e``'s dequantized weight, transposed; rows no tile covers
@@ -31,7 +39,11 @@ Pins (tests/test_oracle_matmul.py): exact rational dot products (Python
 tile-map invariants by brute force plus a hand example; the gather equals a
 per-row loop of the nuvec gather definition and reduces to qmm with one expert;
 the gathered GEMV equals exact rational dot products per row and reduces to
-qmm when every row names the same expert.
+qmm when every row names the same expert; the GLU gather's products equal the
+gathered GEMV of each matrix, its activations match library routines
+(``scipy.special.expit`` for the sigmoid, PyTorch's tanh-approximate gelu) at
+the products, and 'silu_limit' with a limit above every |product| equals
+'silu'.
 """
 
 from __future__ import annotations
@@ -109,4 +121,43 @@ def gather_qmv(codec: str, w: np.ndarray, k: int, x: np.ndarray, ids: np.ndarray
     for r, e in enumerate(ids):
         if 0 <= e < n_experts:
             y[r] = qmatmul(codec, w[e], k, x[r:r + 1])[0]
+    return y
+
+
+def glu_act(act: str, g: np.ndarray, u: np.ndarray, limit: float = 0.0) -> np.ndarray:
+    """The GLU epilogue of ``moe_glu_gather_kq`` (its ``act`` argument), in float64."""
+    g = np.asarray(g, dtype=np.float64)
+    u = np.asarray(u, dtype=np.float64)
+    if act == "silu":
+        return g / (1.0 + np.exp(-g)) * u
+    if act == "gelu":
+        return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3))) * u
+    if act == "silu_limit":
+        if not limit > 0:
+            raise ValueError("silu_limit needs limit > 0")
+        gg = np.minimum(g, limit)
+        return gg / (1.0 + np.exp(-gg)) * np.clip(u, -limit, limit)
+    raise ValueError(f"unknown act {act!r}")
+
+
+def moe_glu_gather(codec: str, gate_w: np.ndarray, up_w: np.ndarray, k: int, x: np.ndarray, ids: np.ndarray,
+                   act: str = "silu", limit: float = 0.0, fill=np.nan) -> np.ndarray:
+    """Reference for kq_moe_glu_gather: slot (t, r) is act(x[t] . gate[e], x[t] . up[e]) row by row.
+
+    mlx-kquant ``bindings.cpp`` page, ``moe_glu_gather_kq`` docstring: x [T, K]
+    (one activation row per token, shared by its slots), gate_w and up_w
+    (n_experts, N, bytes_per_row), indices [T, R]; result [T, R, N].  Returned
+    flattened to [T * R, N]; slots whose id is not below E hold ``fill``.
+    """
+    n_experts, n = gate_w.shape[0], gate_w.shape[1]
+    ids = np.asarray(ids, dtype=np.int64).reshape(x.shape[0], -1)
+    top_k = ids.shape[1]
+    y = np.full((x.shape[0] * top_k, n), fill, dtype=np.float64)
+    for t in range(x.shape[0]):
+        for r in range(top_k):
+            e = ids[t, r]
+            if 0 <= e < n_experts:
+                g = qmatmul(codec, gate_w[e], k, x[t:t + 1])[0]
+                u = qmatmul(codec, up_w[e], k, x[t:t + 1])[0]
+                y[t * top_k + r] = glu_act(act, g, u, limit)
     return y

@@ -91,6 +91,26 @@ def _st(ret):
         (lambda: L.kq_gather_qmv(12, A16, 0, 64, 256, A16, A16, 8, A16, 0, None), kq.KQ_ERR_ARG, "n_experts"),
         (lambda: L.kq_gather_qmv(12, A16, 4, 64, 256, A16, None, 8, A16, 0, None), kq.KQ_ERR_ARG, "ids"),
         (lambda: L.kq_gather_qmv(12, A16, 4, 64, 256, A16, A16 + 2, 8, A16, 0, None), kq.KQ_ERR_ALIGN, "ids="),
+        (lambda: L.kq_moe_glu_gather(8, A16, A16, 4, 64, 96, A16, 2, A16, 2, 0, 0.0, A16, 0, None),
+         kq.KQ_ERR_SHAPE, "K=96"),
+        (lambda: L.kq_moe_glu_gather(12, A16, A16, 0, 64, 256, A16, 2, A16, 2, 0, 0.0, A16, 0, None),
+         kq.KQ_ERR_ARG, "n_experts"),
+        (lambda: L.kq_moe_glu_gather(12, A16, A16, 4, 64, 256, A16, 2, A16, 2, 3, 0.0, A16, 0, None),
+         kq.KQ_ERR_ARG, "act=3"),
+        (lambda: L.kq_moe_glu_gather(12, A16, A16, 4, 64, 256, A16, 2, A16, 2, 2, 0.0, A16, 0, None),
+         kq.KQ_ERR_ARG, "limit"),
+        (lambda: L.kq_moe_glu_gather(12, A16, A16, 4, 64, 256, A16, 2, A16, 2, 2, float("inf"), A16, 0, None),
+         kq.KQ_ERR_ARG, "limit"),
+        (lambda: L.kq_moe_glu_gather(12, A16, None, 4, 64, 256, A16, 2, A16, 2, 0, 0.0, A16, 0, None),
+         kq.KQ_ERR_ARG, "up_w"),
+        (lambda: L.kq_moe_glu_gather(12, A16, A16 + 2, 4, 64, 256, A16, 2, A16, 2, 0, 0.0, A16, 0, None),
+         kq.KQ_ERR_ALIGN, "up_w="),
+        (lambda: L.kq_moe_glu_gather(12, A16, A16, 4, 64, 256, A16, 2, None, 2, 0, 0.0, A16, 0, None),
+         kq.KQ_ERR_ARG, "ids"),
+        (lambda: L.kq_moe_glu_gather(12, A16, A16, 4, 64, 256, A16, -1, A16, 2, 0, 0.0, A16, 0, None),
+         kq.KQ_ERR_ARG, "tokens"),
+        (lambda: L.kq_moe_glu_gather(12, A16, A16, 4, 64, 256, A16, 2, A16, -2, 0, 0.0, A16, 0, None),
+         kq.KQ_ERR_ARG, "top_k"),
         (lambda: L.kq_quantize(12, A16, 4, 512, A16 + 4, None), kq.KQ_ERR_ALIGN, "aligned"),
         (lambda: L.kq_quantize(6, A16, 4, 512, A16, None), kq.KQ_ERR_CODEC, "codec"),
     ],
@@ -109,4 +129,6 @@ def test_empty_inputs_are_no_ops():
     assert L.kq_dequantize(14, None, 0, 256, None, 1, None) == 0
     assert L.kq_gather_qmm_seg(12, None, 4, 64, 256, None, 0, None, None, 8, None, 1, None) == 0
     assert L.kq_gather_qmv(12, None, 4, 64, 256, None, None, 0, None, 0, None) == 0
+    assert L.kq_moe_glu_gather(12, None, None, 4, 64, 256, None, 0, None, 8, 0, 0.0, None, 0, None) == 0
+    assert L.kq_moe_glu_gather(12, None, None, 4, 64, 256, None, 3, None, 0, 1, 0.0, None, 0, None) == 0
     assert L.kq_quantize(8, None, 0, 64, None, None) == 0

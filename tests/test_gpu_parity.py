@@ -354,6 +354,35 @@ def test_gather_qmv_parity(kq, codec):
             assert_close_rows(got[live], ref[live], what=f"gather_qmv {codec} n={n} {tdt}")
 
 
+@pytest.mark.parametrize("codec", CODECS)
+def test_moe_glu_gather_parity(kq, codec):
+    # gate and up of each routed slot with the GLU epilogue; one activation
+    # row per token shared by its slots; an id past the expert count leaves
+    # its slot unwritten.  The 40000-row case takes the 16-lanes-per-row
+    # layout.
+    torch = _torch()
+    rng = np.random.default_rng(29)
+    cases = [(5, 100, 512, 3, 4), (3, 33, 256, 2, 1)]
+    if codec == "q4_k":
+        cases.append((2, 40000, 256, 1, 2))
+    for e, n, k, tokens, top_k in cases:
+        gate = encode.quantize(codec, (rng.standard_normal((e, n, k)) * 0.05).astype(np.float32))
+        up = encode.quantize(codec, (rng.standard_normal((e, n, k)) * 0.05).astype(np.float32))
+        x = _x(tokens, k, 11 + n)
+        ids = rng.integers(0, e, (tokens, top_k)).astype(np.uint32)
+        ids.flat[-1] = e + 2
+        live = ids.reshape(-1) < e
+        for act, limit in (("silu", 0.0), ("gelu", 0.0), ("silu_limit", 0.4)):
+            ref = matmul.moe_glu_gather(codec, gate, up, k, x, ids, act, limit)
+            for tdt in (torch.float32, torch.float16):
+                say(f"moe_glu_gather {codec} e={e} n={n} k={k} T={tokens} R={top_k} {act} {tdt}")
+                y = torch.full((tokens * top_k, n), float("nan"), dtype=tdt, device="cuda")
+                kq.kq_moe_glu_gather(codec, dev(gate), dev(up), e, n, k, dev(x), u32(ids), y, act, limit)
+                got = host(y).astype(np.float64)
+                assert np.all(np.isnan(got[~live])), "slots with an out-of-range id must stay unwritten"
+                assert_close_rows(got[live], ref[live], what=f"moe_glu_gather {codec} n={n} {act} {tdt}")
+
+
 def test_gather_qmv_row_equals_qmv_bits(kq):
     # a routed row runs the same kernel as a one-row GEMV on its expert
     torch = _torch()

@@ -120,5 +120,21 @@ def test_moe_seg_workload(kq):
     refd = matmul.gather_qmv(cfg.codec, ref_bytes.reshape(cfg.n_experts, ns.size, rb), cfg.k, xd, ids0)
     errd = assert_close_rows(host(yd)[:, ns].astype(np.float64), refd, what="MoE decode gather_qmv")
     say(f"workload MoE decode gather_qmv (token 0, top-{cfg.top_k}): max row-normalized error {errd:.2e}")
-    del wq, y, yd
+
+    # decode GLU gather: these experts as gate, an up stack drawn the same way
+    # (seed + 100), token 0's slots, silu
+    wudev = dev(W.weight_rows(cfg.seed + 100, rows_w, cfg.k))
+    wu = torch.empty((rows_w, rb), dtype=torch.uint8, device="cuda")
+    kq.kq_quantize(cfg.codec, wudev, wu)
+    del wudev
+    x0 = W.activations(cfg.seed, cfg.tokens, cfg.k)[:1]
+    yg = torch.empty((cfg.top_k, cfg.n), dtype=torch.float16, device="cuda")
+    kq.kq_moe_glu_gather(cfg.codec, wq, wu, cfg.n_experts, cfg.n, cfg.k, dev(x0), u32(ids0[None, :]), yg, "silu")
+    up_bytes = encode.quantize(cfg.codec, W.weight_rows(cfg.seed + 100, rows_w, cfg.k, rows=widx))
+    assert np.array_equal(host(wu[torch.from_numpy(widx).cuda()]), up_bytes)
+    refg = matmul.moe_glu_gather(cfg.codec, ref_bytes.reshape(cfg.n_experts, ns.size, rb),
+                                 up_bytes.reshape(cfg.n_experts, ns.size, rb), cfg.k, x0, ids0[None, :], "silu")
+    errg = assert_close_rows(host(yg)[:, ns].astype(np.float64), refg, what="MoE decode GLU gather")
+    say(f"workload MoE decode GLU gather (token 0, top-{cfg.top_k}, silu): max row-normalized error {errg:.2e}")
+    del wq, wu, y, yd, yg
     torch.cuda.empty_cache()

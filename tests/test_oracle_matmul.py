@@ -168,3 +168,71 @@ def test_gather_qmv_one_expert_is_qmm():
     x = rng.standard_normal((5, k)).astype(np.float16)
     y = matmul.gather_qmv("q6_k", w, k, x, np.ones(5, np.uint32))
     assert np.array_equal(y, matmul.qmatmul("q6_k", w[1], k, x))
+
+
+def _glu_case(codec="q4_k", seed=41, t=2, top_k=3, e=4, n=10, k=512):
+    rng = np.random.default_rng(seed)
+    gate = encode.quantize(codec, (rng.standard_normal((e, n, k)) * 0.05).astype(np.float32))
+    up = encode.quantize(codec, (rng.standard_normal((e, n, k)) * 0.05).astype(np.float32))
+    x = rng.standard_normal((t, k)).astype(np.float16)
+    ids = rng.integers(0, e, (t, top_k)).astype(np.uint32)
+    return gate, up, x, ids, k
+
+
+def _glu_products(codec, gate, up, x, ids, k):
+    # the gate and up products of every slot through the pinned gathered GEMV,
+    # with each token's activation row repeated for its slots
+    xr = np.repeat(x, ids.shape[1], axis=0)
+    flat = ids.reshape(-1)
+    return matmul.gather_qmv(codec, gate, k, xr, flat), matmul.gather_qmv(codec, up, k, xr, flat)
+
+
+def test_moe_glu_gather_silu_matches_expit():
+    from scipy.special import expit
+
+    gate, up, x, ids, k = _glu_case()
+    g, u = _glu_products("q4_k", gate, up, x, ids, k)
+    y = matmul.moe_glu_gather("q4_k", gate, up, k, x, ids, "silu")
+    assert y.shape == (x.shape[0] * ids.shape[1], gate.shape[1])
+    np.testing.assert_allclose(y, g * expit(g) * u, rtol=1e-12, atol=1e-15)
+
+
+def test_moe_glu_gather_gelu_matches_torch_tanh_gelu():
+    import torch
+
+    gate, up, x, ids, k = _glu_case(seed=42)
+    g, u = _glu_products("q4_k", gate, up, x, ids, k)
+    y = matmul.moe_glu_gather("q4_k", gate, up, k, x, ids, "gelu")
+    ref = torch.nn.functional.gelu(torch.from_numpy(g), approximate="tanh").numpy() * u
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-15)
+
+
+def test_moe_glu_gather_silu_limit():
+    from scipy.special import expit
+
+    gate, up, x, ids, k = _glu_case(seed=43)
+    g, u = _glu_products("q4_k", gate, up, x, ids, k)
+    big = 2.0 * max(np.abs(g).max(), np.abs(u).max())
+    # a limit above every product changes nothing
+    np.testing.assert_array_equal(matmul.moe_glu_gather("q4_k", gate, up, k, x, ids, "silu_limit", big),
+                                  matmul.moe_glu_gather("q4_k", gate, up, k, x, ids, "silu"))
+    # a limit inside the range clamps g from above and u on both sides
+    lim = 0.5 * min(g.max(), np.abs(u).max())
+    assert (g > lim).any() and (np.abs(u) > lim).any()  # both clamps are exercised
+    y = matmul.moe_glu_gather("q4_k", gate, up, k, x, ids, "silu_limit", lim)
+    gc = np.where(g > lim, lim, g)
+    uc = np.where(u > lim, lim, np.where(u < -lim, -lim, u))
+    np.testing.assert_allclose(y, gc * expit(gc) * uc, rtol=1e-12, atol=1e-15)
+    with pytest.raises(ValueError):
+        matmul.moe_glu_gather("q4_k", gate, up, k, x, ids, "silu_limit", 0.0)
+
+
+def test_moe_glu_gather_out_of_range_slots_unwritten():
+    gate, up, x, ids, k = _glu_case(seed=44)
+    ids = ids.copy()
+    ids[0, 1] = 7
+    ids[1, 2] = 4
+    y = matmul.moe_glu_gather("q4_k", gate, up, k, x, ids, "silu")
+    bad = np.array([1, 5])
+    assert np.isnan(y[bad]).all()
+    assert np.isfinite(np.delete(y, bad, axis=0)).all()
