@@ -168,6 +168,20 @@ def measure_rows(torch, kq):
     alg = wq.numel() + x.numel() * 2 + y.numel() * 2
     flop = 2 * x.shape[0] * cfg.n * cfg.k
     rows.append({"row": "kq_expert_tile_map", "workload": cfg.name, "us": round(ms_map * 1e3, 2)})
+    # the sorted rows back to token order, score-weighted (sorted-prefill MoE epilogue)
+    inv = torch.from_numpy(r.inv_order.view(np.int32)).cuda()
+    scores = torch.from_numpy(W.routing_scores(cfg.seed, cfg.tokens, cfg.top_k)).cuda()
+    mixed = torch.empty((cfg.tokens, cfg.n), dtype=torch.float16, device="cuda")
+    ymix = [torch.randn_like(y) for _ in range(copies_for(y.numel() * 2))]
+    nmix = max(len(ymix), 16)
+    gmx = capture(torch, lambda: [kq.kq_gather_mix(ymix[i % len(ymix)], inv, scores, mixed) for i in range(nmix)])
+    ms_mix = time_graph(torch, gmx, nmix, 5)
+    alg_mix = y.numel() * 2 + mixed.numel() * 2 + inv.numel() * 4 + scores.numel() * 4
+    rows.append({"row": "kq_gather_mix", "workload": f"MoE unsort + score mix {cfg.tokens} tok x top-{cfg.top_k}, "
+                 f"N={cfg.n} f16", "us": round(ms_mix * 1e3, 2), "GB/s": round(alg_mix / ms_mix / 1e6, 1),
+                 "hbm_frac": round(alg_mix / ms_mix / 1e6 / HBM_PEAK_GBS, 3), "alg_bytes": alg_mix,
+                 "copies": len(ymix)})
+    del ymix
     rows.append({"row": "kq_gather_qmm_seg", "workload": cfg.name, "us": round(ms_seg * 1e3, 2),
                  "GB/s": round(alg / ms_seg / 1e6, 1), "hbm_frac": round(alg / ms_seg / 1e6 / HBM_PEAK_GBS, 3),
                  "TFLOP/s": round(flop / ms_seg / 1e9, 1),

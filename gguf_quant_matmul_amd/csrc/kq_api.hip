@@ -219,6 +219,34 @@ int kq_gather_qmm_seg(int codec, const void* w, int64_t n_experts, int64_t n, in
                                                   y_dtype == KQ_F16, (hipStream_t)stream));
 }
 
+int kq_gather_mix(const void* y, int64_t rows, int64_t n, const uint32_t* inv_order, const float* scores,
+                  int64_t tokens, int64_t top_k, void* out, int dtype, void* stream) {
+  const char* op = "kq_gather_mix";
+  int st = check_dtype(op, dtype);
+  if (st) return st;
+  if (rows < 0 || rows >= kMaxDim) return fail(KQ_ERR_ARG, op, "rows=%lld out of range", (long long)rows);
+  if (n < 0 || n >= kMaxDim) return fail(KQ_ERR_ARG, op, "N=%lld out of range", (long long)n);
+  if (tokens < 0 || tokens >= kMaxDim) return fail(KQ_ERR_ARG, op, "tokens=%lld out of range", (long long)tokens);
+  if (top_k < 0 || top_k >= kMaxDim || (top_k && tokens >= kMaxDim / top_k))
+    return fail(KQ_ERR_ARG, op, "top_k=%lld out of range", (long long)top_k);
+  if (n % 4) return fail(KQ_ERR_SHAPE, op, "N=%lld is not a multiple of 4", (long long)n);
+  if (rows * n >= kMaxElems || tokens * n >= kMaxElems)
+    return fail(KQ_ERR_ARG, op, "tensor too large (rows=%lld tokens=%lld N=%lld)", (long long)rows, (long long)tokens,
+                (long long)n);
+  if (n == 0 || tokens == 0) return KQ_OK;
+  const int vec = 4 * (dtype == KQ_F16 ? 2 : 4);
+  if (!out) return fail(KQ_ERR_ARG, op, "null out");
+  if (!aligned(out, vec)) return fail(KQ_ERR_ALIGN, op, "out=%p is not aligned to 4 elements", out);
+  if (top_k > 0) {
+    if (!inv_order || !scores || (rows > 0 && !y)) return fail(KQ_ERR_ARG, op, "null y, inv_order or scores");
+    if (y && !aligned(y, vec)) return fail(KQ_ERR_ALIGN, op, "y=%p is not aligned to 4 elements", y);
+    if (!aligned(inv_order, 4) || !aligned(scores, 4))
+      return fail(KQ_ERR_ALIGN, op, "inv_order/scores must be 4-byte aligned");
+  }
+  return hip_status(op, kq::launch_gather_mix(y, rows, n, inv_order, scores, tokens, top_k, out, dtype == KQ_F16,
+                                              (hipStream_t)stream));
+}
+
 int kq_gather_qmv(int codec, const void* w, int64_t n_experts, int64_t n, int64_t k, const void* x,
                   const uint32_t* ids, int64_t rows, void* y, int y_dtype, void* stream) {
   const char* op = "kq_gather_qmv";

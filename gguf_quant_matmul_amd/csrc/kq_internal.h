@@ -146,6 +146,8 @@ constexpr int GLU_SILU = 0, GLU_GELU_TANH = 1, GLU_SILU_LIMIT = 2;
 hipError_t launch_moe_glu_gather(int codec, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_experts, int64_t n,
                                  int64_t k, int64_t row_bytes, const half_t* x, const uint32_t* ids, int64_t rows,
                                  int64_t top_k, int act, float limit, void* y, int f16out, hipStream_t s);
+hipError_t launch_gather_mix(const void* y, int64_t rows, int64_t n, const uint32_t* inv_order, const float* scores,
+                             int64_t tokens, int64_t top_k, void* out, int f16, hipStream_t s);
 hipError_t launch_tile_map(const uint32_t* ids, int64_t rows, int64_t n_experts, uint32_t* map,
                            uint32_t* counts, int64_t cap, uint32_t* status, hipStream_t s);
 hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, int64_t row_bytes,

@@ -89,7 +89,72 @@ __global__ __launch_bounds__(TM_THREADS) void tile_map_kernel(const uint32_t* __
   }
 }
 
+// kq_gather_mix (mlx-kquant bindings.cpp page, gather_mix docstring): the
+// unsort and score mix after a sorted-prefill MoE,
+// out[t] = sum_s scores[t, s] * y[inv_order[t * top_k + s]], slots summed in
+// order in float32 (fma), one rounding at the store.  Slots whose row is not
+// below `rows` add nothing.  Each thread takes 4 consecutive columns of one
+// token (one 8-byte float16 or 16-byte float32 load per slot); blockIdx.y is
+// the token.
+constexpr int GM_THREADS = 256;
+
+template <typename T>
+__global__ __launch_bounds__(GM_THREADS) void gather_mix_kernel(const T* __restrict__ y, uint32_t rows, int n,
+                                                                const uint32_t* __restrict__ inv,
+                                                                const float* __restrict__ scores, int top_k, int t0,
+                                                                T* __restrict__ out) {
+  typedef T T4 __attribute__((ext_vector_type(4)));
+  const int64_t t = t0 + (int64_t)blockIdx.y;
+  const int c = (int)(blockIdx.x * GM_THREADS + threadIdx.x) * 4;
+  if (c >= n) return;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  // four slots at a time: their row indices, then their rows, go out together
+  for (int s0 = 0; s0 < top_k; s0 += 4) {
+    uint32_t r[4];
+    float w[4];
+    T4 v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool live = s0 + j < top_k;
+      r[j] = live ? inv[t * top_k + s0 + j] : rows;
+      w[j] = live ? scores[t * top_k + s0 + j] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = r[j] < rows ? *(const T4*)(y + (int64_t)r[j] * n + c) : T4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (r[j] < rows) {  // slots in order; a slot with no row adds nothing
+        a0 = fmaf(w[j], (float)v[j].x, a0);
+        a1 = fmaf(w[j], (float)v[j].y, a1);
+        a2 = fmaf(w[j], (float)v[j].z, a2);
+        a3 = fmaf(w[j], (float)v[j].w, a3);
+      }
+    }
+  }
+  *(T4*)(out + t * n + c) = T4{(T)a0, (T)a1, (T)a2, (T)a3};
+}
+
+template <typename T>
+hipError_t launch_gather_mix_t(const void* y, int64_t rows, int64_t n, const uint32_t* inv, const float* scores,
+                               int64_t tokens, int64_t top_k, void* out, hipStream_t s) {
+  const unsigned gx = (unsigned)((n / 4 + GM_THREADS - 1) / GM_THREADS);
+  for (int64_t t0 = 0; t0 < tokens; t0 += 65535) {  // grid y holds at most 65535 tokens per launch
+    const dim3 grid(gx, (unsigned)(tokens - t0 < 65535 ? tokens - t0 : 65535));
+    hipLaunchKernelGGL((gather_mix_kernel<T>), grid, dim3(GM_THREADS), 0, s, (const T*)y, (uint32_t)rows, (int)n, inv,
+                       scores, (int)top_k, (int)t0, (T*)out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_gather_mix(const void* y, int64_t rows, int64_t n, const uint32_t* inv_order, const float* scores,
+                             int64_t tokens, int64_t top_k, void* out, int f16, hipStream_t s) {
+  if (f16) return launch_gather_mix_t<half_t>(y, rows, n, inv_order, scores, tokens, top_k, out, s);
+  return launch_gather_mix_t<float>(y, rows, n, inv_order, scores, tokens, top_k, out, s);
+}
 
 hipError_t launch_tile_map(const uint32_t* ids, int64_t rows, int64_t n_experts, uint32_t* map, uint32_t* counts,
                            int64_t cap, uint32_t* status, hipStream_t s) {

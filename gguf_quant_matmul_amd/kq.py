@@ -45,6 +45,7 @@ _SIGS = {
     "kq_gather_qmv": (c_int, [c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_int, c_vp]),
     "kq_moe_glu_gather": (c_int, [c_int, c_vp, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_i64, c_int,
                                   ctypes.c_float, c_vp, c_int, c_vp]),
+    "kq_gather_mix": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_i64, c_vp, c_int, c_vp]),
     "kq_quantize": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_vp]),
 }
 
@@ -192,6 +193,16 @@ def kq_moe_glu_gather(codec, gate_w, up_w, n_experts: int, n: int, k: int, x, id
     top_k = ids.shape[1] if ids.dim() > 1 else 1
     _check(_lib.kq_moe_glu_gather(_codec(codec), _ptr(gate_w), _ptr(up_w), n_experts, n, k, _ptr(x), x.shape[0],
                                   _ptr(ids), top_k, a, float(limit), _ptr(y), _dtype_id(y), _stream(stream)))
+
+
+def kq_gather_mix(y, inv_order, scores, out, stream=None) -> None:
+    """y [rows, n] (float16/float32, routing-sorted rows); inv_order int32/uint32 [T * k]; scores float32 [T, k];
+    out [T, n] of y's dtype."""
+    if out.dtype != y.dtype:
+        raise TypeError("out must have y's dtype")
+    tokens, top_k = scores.shape
+    _check(_lib.kq_gather_mix(_ptr(y), y.shape[0], y.shape[1], _ptr(inv_order), _ptr(scores), tokens, top_k,
+                              _ptr(out), _dtype_id(out), _stream(stream)))
 
 
 def kq_quantize(codec, w, out, stream=None) -> None:

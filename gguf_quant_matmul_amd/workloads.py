@@ -15,6 +15,8 @@ never matters):
   * routing: ``default_rng([s, 2])``; per token ``rng.choice(E, top_k,
     replace=False)``; the (token, slot) pairs are ordered by a STABLE sort on
     expert id, so ties keep (token, slot) order.
+  * routing scores: ``default_rng([s, 3])``, Exponential(1) per (token, slot),
+    each token's normalized to sum 1 (like top-k softmax weights), float32.
 """
 
 from __future__ import annotations
@@ -82,6 +84,20 @@ class Routing:
     @property
     def token_of_row(self) -> np.ndarray:
         return self.order // self.top_k
+
+    @property
+    def inv_order(self) -> np.ndarray:
+        """[tokens*top_k] uint32: the sorted row of each flat (token*top_k + slot)."""
+        inv = np.empty(self.order.size, dtype=np.uint32)
+        inv[self.order] = np.arange(self.order.size, dtype=np.uint32)
+        return inv
+
+
+def routing_scores(seed: int, tokens: int, top_k: int) -> np.ndarray:
+    """[tokens, top_k] float32 routing weights: positive, each token's summing to 1."""
+    rng = np.random.default_rng([seed, 3])
+    s = rng.exponential(1.0, (tokens, top_k))
+    return (s / s.sum(axis=1, keepdims=True)).astype(np.float32)
 
 
 def routing(seed: int, tokens: int, top_k: int, n_experts: int) -> Routing:

@@ -136,6 +136,21 @@ int kq_gather_qmm_seg(int codec, const void* w, int64_t n_experts, int64_t n, in
                       const uint32_t* map, const uint32_t* counts, int64_t cap,
                       void* y, int y_dtype, void* stream);
 
+/* ---- unsort and score mix (mlx-kquant bindings.cpp page, gather_mix
+ * docstring) ----
+ * After a sorted-prefill MoE: y [rows][N] holds the expert outputs in
+ * routing-sorted row order, inv_order uint32 [tokens * top_k] the sorted row
+ * of each (token, slot), scores float32 [tokens][top_k] the routing weights.
+ *   out[t][n] = sum_{s < top_k} scores[t][s] * y[inv_order[t * top_k + s]][n]
+ * summed over s in order in float32, rounded once to `dtype` (y and out share
+ * it: KQ_F16 or KQ_F32).  A slot whose inv_order entry is not below `rows`
+ * adds nothing (entries are read on the device).  N must be a multiple of 4,
+ * else KQ_ERR_SHAPE; y and out aligned to 4 elements, inv_order and scores
+ * to 4 bytes. */
+int kq_gather_mix(const void* y, int64_t rows, int64_t n, const uint32_t* inv_order,
+                  const float* scores, int64_t tokens, int64_t top_k, void* out,
+                  int dtype, void* stream);
+
 /* ---- gathered GEMV (mlx-kquant bindings.cpp page, gather_qmv_kq docstring) ----
  * The decode-shaped MoE product: one activation row per (token, slot).
  * w [n_experts][N][row_bytes]; x float16 [rows][K] (the pages' [T, R, K]

@@ -25,6 +25,10 @@ Definitions followed
     the tanh form of gelu is 0.5 v (1 + tanh(sqrt(2/pi) (v + 0.044715 v^3)))
     (the standard tanh approximation; the page names it, not its formula).
     Output [T, R, N], slot (t, r) using expert indices[t, r].
+  * mlx-kquant ``bindings.cpp`` page, ``gather_mix`` docstring: after a
+    sorted-prefill MoE, out[t] = sum_s scores[t, s] * y[inv_order[t*k + s]]
+    (unsort, score multiply and sum over slots).  Reading taken: a slot whose
+    inv_order entry is not below the row count adds nothing.
   * mlx-kquant ``bindings.cpp`` page, ``gather_qmm_seg`` docstring: for each
     valid tile, rows [row_start, row_start+num_rows) of the expert-sorted x
     times expert ``e``'s dequantized weight, transposed; rows no tile covers
@@ -161,3 +165,23 @@ def moe_glu_gather(codec: str, gate_w: np.ndarray, up_w: np.ndarray, k: int, x: 
                 u = qmatmul(codec, up_w[e], k, x[t:t + 1])[0]
                 y[t * top_k + r] = glu_act(act, g, u, limit)
     return y
+
+
+def gather_mix(y: np.ndarray, inv_order: np.ndarray, scores: np.ndarray) -> np.ndarray:
+    """Reference for kq_gather_mix: out[t] = sum_s scores[t, s] * y[inv_order[t * k + s]], in float64.
+
+    mlx-kquant ``bindings.cpp`` page, ``gather_mix`` docstring.  y: [rows, N];
+    inv_order: [T * k]; scores: [T, k].  Slots whose row is not below ``rows``
+    add nothing.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    scores = np.asarray(scores, dtype=np.float64)
+    tokens, top_k = scores.shape
+    inv = np.asarray(inv_order, dtype=np.int64).reshape(tokens, top_k)
+    out = np.zeros((tokens, y.shape[1]), dtype=np.float64)
+    for t in range(tokens):
+        for s in range(top_k):
+            r = inv[t, s]
+            if 0 <= r < y.shape[0]:
+                out[t] += scores[t, s] * y[r]
+    return out

@@ -111,6 +111,13 @@ def _st(ret):
          kq.KQ_ERR_ARG, "tokens"),
         (lambda: L.kq_moe_glu_gather(12, A16, A16, 4, 64, 256, A16, 2, A16, -2, 0, 0.0, A16, 0, None),
          kq.KQ_ERR_ARG, "top_k"),
+        (lambda: L.kq_gather_mix(A16, 8, 6, A16, A16, 2, 4, A16, 1, None), kq.KQ_ERR_SHAPE, "N=6"),
+        (lambda: L.kq_gather_mix(A16, 8, 8, A16, A16, 2, 4, A16, 3, None), kq.KQ_ERR_ARG, "dtype"),
+        (lambda: L.kq_gather_mix(A16, 8, 8, None, A16, 2, 4, A16, 1, None), kq.KQ_ERR_ARG, "inv_order"),
+        (lambda: L.kq_gather_mix(A16, 8, 8, A16, A16, 2, 4, None, 1, None), kq.KQ_ERR_ARG, "out"),
+        (lambda: L.kq_gather_mix(A16 + 4, 8, 8, A16, A16, 2, 4, A16, 1, None), kq.KQ_ERR_ALIGN, "y="),
+        (lambda: L.kq_gather_mix(A16, 8, 8, A16 + 2, A16, 2, 4, A16, 1, None), kq.KQ_ERR_ALIGN, "inv_order"),
+        (lambda: L.kq_gather_mix(A16, 8, 8, A16, A16, -1, 4, A16, 1, None), kq.KQ_ERR_ARG, "tokens"),
         (lambda: L.kq_quantize(12, A16, 4, 512, A16 + 4, None), kq.KQ_ERR_ALIGN, "aligned"),
         (lambda: L.kq_quantize(6, A16, 4, 512, A16, None), kq.KQ_ERR_CODEC, "codec"),
     ],
@@ -130,5 +137,7 @@ def test_empty_inputs_are_no_ops():
     assert L.kq_gather_qmm_seg(12, None, 4, 64, 256, None, 0, None, None, 8, None, 1, None) == 0
     assert L.kq_gather_qmv(12, None, 4, 64, 256, None, None, 0, None, 0, None) == 0
     assert L.kq_moe_glu_gather(12, None, None, 4, 64, 256, None, 0, None, 8, 0, 0.0, None, 0, None) == 0
+    assert L.kq_gather_mix(None, 0, 8, None, None, 0, 4, None, 1, None) == 0
+    assert L.kq_gather_mix(None, 0, 0, None, None, 5, 4, None, 1, None) == 0
     assert L.kq_moe_glu_gather(12, None, None, 4, 64, 256, None, 3, None, 0, 1, 0.0, None, 0, None) == 0
     assert L.kq_quantize(8, None, 0, 64, None, None) == 0

@@ -383,6 +383,36 @@ def test_moe_glu_gather_parity(kq, codec):
                 assert_close_rows(got[live], ref[live], what=f"moe_glu_gather {codec} n={n} {act} {tdt}")
 
 
+def _mix_bound(y, inv, scores, f16):
+    # float32 sum of top_k terms in order, then one rounding to the output type
+    terms = np.abs(scores.astype(np.float64))[:, :, None] * np.abs(
+        np.where((inv < y.shape[0])[:, None], y[np.minimum(inv, y.shape[0] - 1).astype(np.int64)], 0.0)
+    ).reshape(scores.shape[0], scores.shape[1], -1)
+    return scores.shape[1] * 2.0 ** -23 * terms.sum(axis=1)
+
+
+def test_gather_mix_parity(kq):
+    torch = _torch()
+    rng = np.random.default_rng(31)
+    for tokens, top_k, n in ((37, 5, 1028), (3, 1, 4), (70000, 2, 4)):
+        rows = tokens * top_k
+        inv = rng.permutation(rows).astype(np.uint32)
+        inv[:: max(1, rows // 7)] = rows + 5  # some slots name no row
+        scores = rng.standard_normal((tokens, top_k)).astype(np.float32)
+        for f16 in (True, False):
+            dt = np.float16 if f16 else np.float32
+            y = rng.standard_normal((rows, n)).astype(dt)
+            ref = matmul.gather_mix(y, inv, scores)
+            say(f"gather_mix tokens={tokens} top_k={top_k} n={n} f16={f16}")
+            out = torch.full((tokens, n), float("nan"), dtype=torch.float16 if f16 else torch.float32, device="cuda")
+            kq.kq_gather_mix(dev(y), u32(inv), dev(scores), out)
+            got = host(out).astype(np.float64)
+            bound = _mix_bound(y.astype(np.float64), inv, scores, f16)
+            if f16:
+                bound = bound + 2.0 ** -11 * np.abs(ref) + 2.0 ** -24
+            assert np.all(np.abs(got - ref) <= bound), f"gather_mix max excess {np.max(np.abs(got - ref) - bound):.3e}"
+
+
 def test_gather_qmv_row_equals_qmv_bits(kq):
     # a routed row runs the same kernel as a one-row GEMV on its expert
     torch = _torch()

@@ -111,6 +111,20 @@ def test_moe_seg_workload(kq):
     err = assert_close_rows(got, ref, what=cfg.name)
     say(f"workload {cfg.name}: max row-normalized error {err:.2e}")
 
+    # the sorted rows back to token order, weighted by routing scores
+    scores = W.routing_scores(cfg.seed, cfg.tokens, cfg.top_k)
+    inv = r.inv_order
+    mixed = torch.empty((cfg.tokens, cfg.n), dtype=torch.float16, device="cuda")
+    kq.kq_gather_mix(y, u32(inv), dev(scores), mixed)
+    y_host = host(y).astype(np.float64)
+    refm = matmul.gather_mix(y_host, inv, scores)
+    terms = (np.abs(scores.astype(np.float64))[:, :, None] *
+             np.abs(y_host[inv.astype(np.int64)]).reshape(cfg.tokens, cfg.top_k, cfg.n)).sum(axis=1)
+    bound = cfg.top_k * 2.0 ** -23 * terms + 2.0 ** -11 * np.abs(refm) + 2.0 ** -24
+    excess = np.abs(host(mixed).astype(np.float64) - refm) - bound
+    assert np.all(excess <= 0), f"gather_mix max excess {excess.max():.3e}"
+    say(f"workload MoE gather_mix ({cfg.tokens} tok x top-{cfg.top_k}, N={cfg.n}): within the f32-sum + f16 bound")
+
     # decode shape on the same experts: token 0's eight routed rows through
     # kq_gather_qmv, checked on the sampled columns
     ids0 = r.ids[0].astype(np.uint32)
@@ -136,5 +150,5 @@ def test_moe_seg_workload(kq):
                                  up_bytes.reshape(cfg.n_experts, ns.size, rb), cfg.k, x0, ids0[None, :], "silu")
     errg = assert_close_rows(host(yg)[:, ns].astype(np.float64), refg, what="MoE decode GLU gather")
     say(f"workload MoE decode GLU gather (token 0, top-{cfg.top_k}, silu): max row-normalized error {errg:.2e}")
-    del wq, wu, y, yd, yg
+    del wq, wu, y, yd, yg, mixed
     torch.cuda.empty_cache()

@@ -236,3 +236,35 @@ def test_moe_glu_gather_out_of_range_slots_unwritten():
     bad = np.array([1, 5])
     assert np.isnan(y[bad]).all()
     assert np.isfinite(np.delete(y, bad, axis=0)).all()
+
+
+def test_gather_mix_matches_einsum_of_gathered_rows():
+    rng = np.random.default_rng(51)
+    tokens, top_k, n, rows = 6, 3, 8, 18
+    y = rng.standard_normal((rows, n))
+    inv = rng.permutation(rows).astype(np.uint32)
+    scores = rng.random((tokens, top_k)).astype(np.float32)
+    ref = np.einsum("ts,tsn->tn", scores.astype(np.float64), y[inv.astype(np.int64)].reshape(tokens, top_k, n))
+    np.testing.assert_allclose(matmul.gather_mix(y, inv, scores), ref, rtol=1e-13, atol=1e-14)
+
+
+def test_gather_mix_unsorts_the_workload_routing():
+    # per-(token, slot) values placed in routing-sorted row order come back to
+    # their token and slot: the mix is their score-weighted sum per token
+    r = workloads.routing(4, 40, 8, 64)
+    scores = workloads.routing_scores(4, 40, 8)
+    rng = np.random.default_rng(52)
+    v = rng.standard_normal((40, 8, 5))
+    y_sorted = v.reshape(40 * 8, 5)[r.order]
+    out = matmul.gather_mix(y_sorted, r.inv_order, scores)
+    np.testing.assert_allclose(out, (scores[:, :, None].astype(np.float64) * v).sum(axis=1), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(scores.sum(axis=1), 1.0, rtol=1e-6)
+
+
+def test_gather_mix_skips_rows_out_of_range():
+    y = np.arange(12, dtype=np.float64).reshape(3, 4)
+    inv = np.array([2, 9, 0, 1], dtype=np.uint32)
+    scores = np.array([[0.5, 7.0], [1.0, 2.0]], dtype=np.float32)
+    out = matmul.gather_mix(y, inv, scores)
+    np.testing.assert_array_equal(out[0], 0.5 * y[2])
+    np.testing.assert_array_equal(out[1], y[0] + 2.0 * y[1])
