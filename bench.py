@@ -234,6 +234,90 @@ def measure_rows(torch, kq):
                  "alg_bytes": alg})
     del ws, wq, out
     torch.cuda.empty_cache()
+    rows += epilogue_rows(torch, kq)
+    return rows
+
+
+def epilogue_rows(torch, kq):
+    """The fused epilogues on a transformer block's shapes (Llama-3-8B FFN: gate/up 14336x4096, down 4096x14336),
+    prefill (2048 rows, float16 out) and decode (one row, float32 out), each beside the plain matmul of the same
+    weight so the epilogue's cost shows."""
+    from gguf_quant_matmul_amd import workloads as W
+
+    rows = []
+    c4 = W.CFG4_Q4K_GEMM
+    m_pf, k_ffn, n_ffn = c4.m, c4.k, c4.n
+
+    def row(name, workload, fused, plain, nl, flop, alg, extra=None):
+        gf, gp = capture(torch, lambda: [fused(i) for i in range(nl)]), capture(torch, lambda: [plain(i) for i in range(nl)])
+        ms_f, ms_p = time_graph(torch, gf, nl, 5), time_graph(torch, gp, nl, 5)
+        r = {"row": name, "workload": workload, "us": round(ms_f * 1e3, 2), "us_plain_matmul": round(ms_p * 1e3, 2),
+             "GB/s": round(alg / ms_f / 1e6, 1), "hbm_frac": round(alg / ms_f / 1e6 / HBM_PEAK_GBS, 3), "alg_bytes": alg}
+        if flop:
+            r["TFLOP/s"] = round(flop / ms_f / 1e9, 1)
+            r["mfma_frac"] = round(flop / ms_f / 1e9 / MFMA_F16_PEAK_TFLOPS, 3)
+        rows.append(r)
+
+    # GLU: gate = the q4_K prefill weight, up drawn the same way (seed + 100)
+    wg = gpu_weights(torch, kq, c4.codec, c4.seed, n_ffn, k_ffn, c4.dist)
+    wu = gpu_weights(torch, kq, c4.codec, c4.seed + 100, n_ffn, k_ffn, c4.dist)
+    nb = wg.numel()
+    xp = torch.from_numpy(W.gemv_activations(c4)).cuda()
+    yp = torch.empty((m_pf, n_ffn), dtype=torch.float16, device="cuda")
+    row("kq_quantized_matmul_glu", f"q4_K GLU (silu) prefill {m_pf}x{n_ffn}x{k_ffn}, gate+up, f16 out",
+        lambda i: kq.kq_quantized_matmul_glu(c4.codec, wg, wu, n_ffn, k_ffn, xp, yp, "silu"),
+        lambda i: kq.kq_quantized_matmul(c4.codec, wg, n_ffn, k_ffn, xp, yp), 3,
+        2 * 2 * m_pf * n_ffn * k_ffn, 2 * nb + xp.numel() * 2 + yp.numel() * 2)
+    # decode: rotate weight copies so each launch reads from HBM
+    nc = copies_for(2 * nb)
+    wgs, wus = [wg] + [wg.clone() for _ in range(nc - 1)], [wu] + [wu.clone() for _ in range(nc - 1)]
+    x1 = xp[:1].clone()
+    y1 = torch.empty((1, n_ffn), dtype=torch.float32, device="cuda")
+    nl = max(nc, 8)
+    row("kq_quantized_matmul_glu", f"q4_K GLU (silu) decode 1x{n_ffn}x{k_ffn}, gate+up, f32 out",
+        lambda i: kq.kq_quantized_matmul_glu(c4.codec, wgs[i % nc], wus[i % nc], n_ffn, k_ffn, x1, y1, "silu"),
+        lambda i: kq.kq_quantized_matmul(c4.codec, wgs[i % nc], n_ffn, k_ffn, x1, y1), nl,
+        0, 2 * nb + k_ffn * 2 + n_ffn * 4)
+    del wgs, wus, wg, wu, yp
+    torch.cuda.empty_cache()
+
+    # residual: the down projection 4096x14336 with the residual stream updated in place
+    wd = gpu_weights(torch, kq, c4.codec, c4.seed + 200, k_ffn, n_ffn, c4.dist)
+    nb = wd.numel()
+    xd = torch.from_numpy(W.activations(c4.seed + 200, m_pf, n_ffn)).cuda()
+    res = torch.from_numpy(W.activations(c4.seed + 201, m_pf, k_ffn)).cuda()
+    row("kq_quantized_matmul_residual", f"q4_K down proj + residual prefill {m_pf}x{k_ffn}x{n_ffn}, f16 in place",
+        lambda i: kq.kq_quantized_matmul_residual(c4.codec, wd, k_ffn, n_ffn, xd, res, res),
+        lambda i: kq.kq_quantized_matmul(c4.codec, wd, k_ffn, n_ffn, xd, res), 3,
+        2 * m_pf * k_ffn * n_ffn, nb + xd.numel() * 2 + 2 * res.numel() * 2)
+    nc = copies_for(nb)
+    wds = [wd] + [wd.clone() for _ in range(nc - 1)]
+    x1 = xd[:1].clone()
+    r1 = torch.zeros((1, k_ffn), dtype=torch.float32, device="cuda")
+    nl = max(nc, 8)
+    row("kq_quantized_matmul_residual", f"q4_K down proj + residual decode 1x{k_ffn}x{n_ffn}, f32 in place",
+        lambda i: kq.kq_quantized_matmul_residual(c4.codec, wds[i % nc], k_ffn, n_ffn, x1, r1, r1),
+        lambda i: kq.kq_quantized_matmul(c4.codec, wds[i % nc], k_ffn, n_ffn, x1, r1), nl,
+        0, nb + n_ffn * 2 + 2 * k_ffn * 4)
+    del wds, wd, xd, res
+    torch.cuda.empty_cache()
+
+    # bias: q8_0 14336x4096, one row
+    c2 = W.CFG2_GEMV[0]
+    wq = gpu_weights(torch, kq, c2.codec, c2.seed, c2.n, c2.k, c2.dist)
+    nb = wq.numel()
+    nc = copies_for(nb)
+    ws = [wq] + [wq.clone() for _ in range(nc - 1)]
+    x1 = torch.from_numpy(W.gemv_activations(c2)).cuda()
+    bias = torch.from_numpy(np.random.default_rng(c2.seed).standard_normal(c2.n).astype(np.float32)).cuda()
+    y1 = torch.empty((1, c2.n), dtype=torch.float32, device="cuda")
+    nl = max(nc, 8)
+    row("kq_quantized_matmul_qmv_bias", f"q8_0 GEMV + bias 1x{c2.n}x{c2.k}, f32 out",
+        lambda i: kq.kq_quantized_matmul_qmv_bias(c2.codec, ws[i % nc], c2.n, c2.k, x1, bias, y1),
+        lambda i: kq.kq_quantized_matmul(c2.codec, ws[i % nc], c2.n, c2.k, x1, y1), nl,
+        0, nb + c2.k * 2 + 2 * c2.n * 4)
+    del ws, wq
+    torch.cuda.empty_cache()
     return rows
 
 

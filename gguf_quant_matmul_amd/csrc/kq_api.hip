@@ -180,6 +180,76 @@ int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k, const vo
   return kq_qmm(codec, w, n, k, x, m, y, y_dtype, stream);
 }
 
+// [a, a + na) and [b, b + nb) share a byte
+static bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t pa = (uintptr_t)a, pb = (uintptr_t)b;
+  return pa < pb + (uintptr_t)nb && pb < pa + (uintptr_t)na;
+}
+
+int kq_quantized_matmul_residual(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m,
+                                 const void* residual, const void* gate, int64_t gate_rows, void* y, int y_dtype,
+                                 void* stream) {
+  const char* op = "kq_quantized_matmul_residual";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb);
+  if (st) return st;
+  if (gate && (gate_rows <= 0 || gate_rows > m || (m > 0 && m % gate_rows != 0)))
+    return fail(KQ_ERR_SHAPE, op, "gate_rows=%lld must divide M=%lld", (long long)gate_rows, (long long)m);
+  if (n == 0 || m == 0) return KQ_OK;
+  if (!residual) return fail(KQ_ERR_ARG, op, "null residual");
+  const int64_t es = y_dtype == KQ_F32 ? 4 : 2;
+  if (!aligned(residual, es) || (gate && !aligned(gate, es)))
+    return fail(KQ_ERR_ALIGN, op, "residual/gate must be element aligned");
+  const int64_t ybytes = m * n * es;
+  if (residual != y && overlaps(residual, ybytes, y, ybytes))
+    return fail(KQ_ERR_ARG, op, "residual overlaps y without being y");
+  if (gate && overlaps(gate, gate_rows * n * es, y, ybytes)) return fail(KQ_ERR_ARG, op, "gate overlaps y");
+  const kq::Epi epi{residual, gate, nullptr, gate ? (int)(m / gate_rows) : 1};
+  const hipError_t e =
+      m <= 8 ? kq::launch_qmv_epi(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, (int)m, epi, y,
+                                  y_dtype == KQ_F16, (hipStream_t)stream)
+             : kq::launch_qmm_epi(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, m, epi, y,
+                                  y_dtype == KQ_F16, (hipStream_t)stream);
+  return hip_status(op, e);
+}
+
+int kq_quantized_matmul_qmv_bias(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m,
+                                 const void* bias, void* y, int y_dtype, void* stream) {
+  const char* op = "kq_quantized_matmul_qmv_bias";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb);
+  if (st) return st;
+  if (m != 1) return fail(KQ_ERR_SHAPE, op, "M=%lld rows; the bias-fused GEMV takes exactly one", (long long)m);
+  if (n == 0) return KQ_OK;
+  if (!bias) return fail(KQ_ERR_ARG, op, "null bias");
+  const int64_t es = y_dtype == KQ_F32 ? 4 : 2;
+  if (!aligned(bias, es)) return fail(KQ_ERR_ALIGN, op, "bias must be element aligned");
+  if (overlaps(bias, n * es, y, n * es)) return fail(KQ_ERR_ARG, op, "bias overlaps y");
+  const kq::Epi epi{nullptr, nullptr, bias, 1};
+  return hip_status(op, kq::launch_qmv_epi(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, 1, epi, y,
+                                           y_dtype == KQ_F16, (hipStream_t)stream));
+}
+
+int kq_quantized_matmul_glu(int codec, const void* w_gate, const void* w_up, int64_t n, int64_t k, const void* x,
+                            int64_t m, int act, void* y, int y_dtype, void* stream) {
+  const char* op = "kq_quantized_matmul_glu";
+  int64_t rb;
+  int st = check_matmul(op, codec, w_gate, n, k, x, m, y, y_dtype, &rb);
+  if (st) return st;
+  if (act != KQ_GLU_SILU && act != KQ_GLU_GELU_TANH)
+    return fail(KQ_ERR_ARG, op, "act=%d is not KQ_GLU_SILU or KQ_GLU_GELU_TANH", act);
+  if (n == 0 || m == 0) return KQ_OK;
+  if (!w_up) return fail(KQ_ERR_ARG, op, "null w_up");
+  if (!aligned(w_up, 16)) return fail(KQ_ERR_ALIGN, op, "w_up=%p is not 16-byte aligned", w_up);
+  const hipError_t e =
+      m <= kq::QMV_GLU_MAX_M
+          ? kq::launch_qmv_glu(codec, (const uint8_t*)w_gate, (const uint8_t*)w_up, n, k, rb, (const kq::half_t*)x,
+                               (int)m, act, y, y_dtype == KQ_F16, (hipStream_t)stream)
+          : kq::launch_qmm_glu(codec, (const uint8_t*)w_gate, (const uint8_t*)w_up, n, k, rb, (const kq::half_t*)x,
+                               m, act, y, y_dtype == KQ_F16, (hipStream_t)stream);
+  return hip_status(op, e);
+}
+
 int64_t kq_expert_tile_map_capacity(int64_t rows, int64_t n_experts) {
   if (rows < 0 || n_experts < 0) return -1;
   return (rows + 63) / 64 + (n_experts < rows ? n_experts : rows);

@@ -122,6 +122,123 @@ __device__ __forceinline__ void q4k_scale_min_pair(uint32_t s0, uint32_t s1, uin
   m1 = __builtin_amdgcn_ubfe(b, sh + 8u, w) | (__builtin_amdgcn_ubfe(s1, sh + 14u, t) << 4);
 }
 
+// GLU epilogues (kq.h KQ_GLU_* carry the same values)
+constexpr int GLU_SILU = 0, GLU_GELU_TANH = 1, GLU_SILU_LIMIT = 2;
+// activation rows up to which the GLU product runs on the GEMV body
+constexpr int QMV_GLU_MAX_M = 3;
+
+// Matmul epilogue (mlx-kquant bindings.cpp page, quantized_matmul_residual
+// and quantized_matmul_qmv_bias docstrings): per output element
+// y = fma(gate, acc, resid) + bias in float32, rounded once to y's type; a
+// null term is left out.  All three terms are in y's type: resid [M][N],
+// gate [G][N] with row m taking gate row m / gate_div, bias [N].
+struct Epi {
+  const void* resid;
+  const void* gate;
+  const void* bias;
+  int gate_div;
+};
+template <bool F16>
+__device__ __forceinline__ float ld_out(const void* p, int64_t i) {
+  return F16 ? (float)((const half_t*)p)[i] : ((const float*)p)[i];
+}
+template <bool F16>
+__device__ __forceinline__ float epi_apply(const Epi& e, int64_t m, int64_t col, int64_t n, float acc) {
+  const float g = e.gate ? ld_out<F16>(e.gate, (int64_t)((int)m / e.gate_div) * n + col) : 1.f;
+  const float r = e.resid ? ld_out<F16>(e.resid, m * n + col) : 0.f;
+  float v = fmaf(g, acc, r);
+  if (e.bias) v += ld_out<F16>(e.bias, col);
+  return v;
+}
+
+// A finite value beyond the float16 range becomes the largest finite half of
+// its sign; infinities and NaN pass (the float16 store of the GLU product).
+__device__ __forceinline__ float sat_half(float v) {
+  return fabsf(v) <= 3.40282347e38f ? fminf(fmaxf(v, -65504.f), 65504.f) : v;
+}
+// v rounded to y's type (float16 saturating, float32 unchanged)
+template <bool F16>
+__device__ __forceinline__ float round_out(float v) {
+  return F16 ? (float)(half_t)sat_half(v) : v;
+}
+
+// v * sigmoid(t) = v / (1 + 2^(-t log2 e)) from the hardware exp2 and
+// reciprocal (about 1 ulp each): a few float32 ulps in all, far below the
+// float16 rounding the activations of the GLU matmul take.  t -> -inf gives
+// exp2 = inf and a product of 0 (of v's sign); NaN passes.
+__device__ __forceinline__ float sigmoid_mul(float v, float t) {
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * t);
+  return v * __builtin_amdgcn_rcpf(1.f + e);
+}
+
+// GLU epilogues of the mlx-kquant bindings.cpp page (moe_glu_gather_kq
+// docstring, its act argument), in float32 on the two float32 products g
+// (gate) and u (up):
+//   GLU_SILU        silu(g) * u, silu(g) = g sigmoid(g)
+//   GLU_GELU_TANH   gelu(g) * u with the tanh form of gelu,
+//                   0.5 g (1 + tanh(z)), z = sqrt(2/pi) (g + 0.044715 g^3),
+//                   evaluated as g sigmoid(2 z) (the same function:
+//                   0.5 (1 + tanh z) = sigmoid(2 z))
+//   GLU_SILU_LIMIT  silu(min(g, limit)) * clip(u, -limit, limit)
+template <int ACT>
+__device__ __forceinline__ float glu_act(float g, float u, float limit) {
+  if constexpr (ACT == GLU_SILU) {
+    return sigmoid_mul(g, g) * u;
+  } else if constexpr (ACT == GLU_GELU_TANH) {
+    const float c2 = 1.5957691216057308f;  // 2 sqrt(2 / pi)
+    return sigmoid_mul(g, c2 * fmaf(0.044715f * g, g * g, g)) * u;
+  } else {
+    const float gg = fminf(g, limit);
+    return sigmoid_mul(gg, gg) * fminf(fmaxf(u, -limit), limit);
+  }
+}
+
+// The GLU product of quantized_matmul_glu (mlx-kquant bindings.cpp page, its
+// docstring): the activation of the gate product is rounded to y's type, then
+// multiplied by the up product in float32 and rounded again.
+template <int ACT, bool F16>
+__device__ __forceinline__ float glu_rounded(float g, float u) {
+  return round_out<F16>(round_out<F16>(glu_act<ACT>(g, 1.f, 0.f)) * u);
+}
+
+// Output stores of the GEMM kernels.  EP_EPI applies epi_apply (null terms
+// tested per element); EP_RES (y = acc + resid) and EP_RES_GATE (y =
+// fma(gate, acc, resid)) are the same store with the terms known present, so
+// a kernel can load them without branches.  The GLU product is two passes
+// over K: EP_GLU_ACT stores the rounded activation of the gate product in y,
+// EP_GLU_MUL multiplies the up product by it.
+constexpr int EP_PLAIN = 0, EP_EPI = 1, EP_GLU_ACT = 2, EP_GLU_MUL = 3, EP_RES = 4, EP_RES_GATE = 5;
+// The values a store reads (residual and gate, or y's activation), split
+// from the store so that a kernel writing many elements can load them all
+// first: a load placed after a store to y waits for it, y possibly aliasing.
+template <bool F16, int EP>
+__device__ __forceinline__ void epi_load(const void* y, int64_t row, int64_t col, int64_t n, const Epi& e, float& a,
+                                         float& b) {
+  if constexpr (EP == EP_RES || EP == EP_RES_GATE) a = ld_out<F16>(e.resid, row * n + col);
+  if constexpr (EP == EP_RES_GATE) b = ld_out<F16>(e.gate, (int64_t)((int)row / e.gate_div) * n + col);
+  if constexpr (EP == EP_GLU_MUL) a = ld_out<F16>(y, row * n + col);
+}
+template <bool F16, int EP, int ACT>
+__device__ __forceinline__ void store_pre(void* y, int64_t row, int64_t col, int64_t n, const Epi& e, float v, float a,
+                                          float b) {
+  if constexpr (EP == EP_EPI) v = epi_apply<F16>(e, row, col, n, v);
+  if constexpr (EP == EP_RES) v += a;
+  if constexpr (EP == EP_RES_GATE) v = fmaf(b, v, a);
+  if constexpr (EP == EP_GLU_ACT) v = round_out<F16>(glu_act<ACT>(v, 1.f, 0.f));
+  if constexpr (EP == EP_GLU_MUL) v = round_out<F16>(a * v);
+  const int64_t o = row * n + col;
+  if (F16)
+    ((half_t*)y)[o] = (half_t)v;
+  else
+    ((float*)y)[o] = v;
+}
+template <bool F16, int EP, int ACT>
+__device__ __forceinline__ void store_out(void* y, int64_t row, int64_t col, int64_t n, const Epi& e, float v) {
+  float a = 0.f, b = 1.f;
+  epi_load<F16, EP>(y, row, col, n, e, a, b);
+  store_pre<F16, EP, ACT>(y, row, col, n, e, v, a, b);
+}
+
 // ---------------------------------------------------------------------------
 // launchers (defined in the kernel translation units)
 // ---------------------------------------------------------------------------
@@ -141,13 +258,19 @@ hipError_t launch_seg_mma(int codec, const uint8_t* w, int64_t n_experts, int64_
 hipError_t launch_gather_qmv(int codec, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,
                              int64_t row_bytes, const half_t* x, const uint32_t* ids, int64_t rows, void* y,
                              int f16out, hipStream_t s);
-// GLU epilogues of the MoE GLU gather (kq.h KQ_GLU_* carry the same values)
-constexpr int GLU_SILU = 0, GLU_GELU_TANH = 1, GLU_SILU_LIMIT = 2;
 hipError_t launch_moe_glu_gather(int codec, const uint8_t* gate_w, const uint8_t* up_w, int64_t n_experts, int64_t n,
                                  int64_t k, int64_t row_bytes, const half_t* x, const uint32_t* ids, int64_t rows,
                                  int64_t top_k, int act, float limit, void* y, int f16out, hipStream_t s);
 hipError_t launch_gather_mix(const void* y, int64_t rows, int64_t n, const uint32_t* inv_order, const float* scores,
                              int64_t tokens, int64_t top_k, void* out, int f16, hipStream_t s);
+hipError_t launch_qmv_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes, const half_t* x,
+                          int m, const Epi& epi, void* y, int f16out, hipStream_t s);
+hipError_t launch_qmm_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes, const half_t* x,
+                          int64_t m, const Epi& epi, void* y, int f16out, hipStream_t s);
+hipError_t launch_qmv_glu(int codec, const uint8_t* w_gate, const uint8_t* w_up, int64_t n, int64_t k,
+                          int64_t row_bytes, const half_t* x, int m, int act, void* y, int f16out, hipStream_t s);
+hipError_t launch_qmm_glu(int codec, const uint8_t* w_gate, const uint8_t* w_up, int64_t n, int64_t k,
+                          int64_t row_bytes, const half_t* x, int64_t m, int act, void* y, int f16out, hipStream_t s);
 hipError_t launch_tile_map(const uint32_t* ids, int64_t rows, int64_t n_experts, uint32_t* map,
                            uint32_t* counts, int64_t cap, uint32_t* status, hipStream_t s);
 hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, int64_t row_bytes,

@@ -239,10 +239,14 @@ constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
 // s % PD, stored (weights: decoded) to LDS buffer s % 2 during step s - 1, and
 // consumed by the MFMAs of step s.  Activations come from L2 (their panel is
 // shared by the tiles of one XCD) and need a shorter distance than weights.
-template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB, bool F16>
+//
+// EP / ACT / epi: the output store (store_out: plain, the residual epilogue,
+// or one of the two passes of the GLU product).
+template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB, bool F16, int EP = EP_PLAIN, int ACT = 0>
 __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                           int64_t row_bytes, const half_t* __restrict__ x, int m_total,
-                                                          int tiles_total, int per_xcd, void* __restrict__ y) {
+                                                          int tiles_total, int per_xcd, void* __restrict__ y,
+                                                          Epi epi) {
   static_assert(WM * WN == QMM_THREADS / 64, "8 waves");
   constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
   constexpr int TM = WTM / 16, TN = WTN / 16;  // 16x16 MFMA tiles per wave
@@ -399,58 +403,87 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
 
   // 16x16 accumulator layout: lane holds column (lane & 15); register r holds
   // row 4*(lane/16) + r.
+  static_assert(EP != EP_EPI, "the GEMM tile stores take EP_RES / EP_RES_GATE");
+  if constexpr (EP == EP_PLAIN || EP == EP_GLU_ACT) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    if (i >= live_tm) continue;
+    for (int i = 0; i < TM; ++i) {
+      if (i >= live_tm) continue;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = n0 + wc0 + 16 * j + (lane & 15);
-      if (col >= n) continue;
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wc0 + 16 * j + (lane & 15);
+        if (col >= n) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = wr0 + 16 * i + 4 * (lane >> 4) + r;
-        if (row < mrows) {
-          const int64_t o = (int64_t)(m0 + row) * n + col;
-          if (F16)
-            ((half_t*)y)[o] = (half_t)acc[i][j][r];
-          else
-            ((float*)y)[o] = acc[i][j][r];
+        for (int r = 0; r < 4; ++r) {
+          const int row = wr0 + 16 * i + 4 * (lane >> 4) + r;
+          if (row < mrows) store_out<F16, EP, ACT>(y, m0 + row, col, n, epi, acc[i][j][r]);
+        }
+      }
+    }
+  } else {
+    // stores that read: each 16-row group's inputs are loaded before its
+    // stores, unconditionally (indices clamped into the tile; a clamped
+    // element's value is never used), so the loads overlap instead of each
+    // waiting behind a branch
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      if (i >= live_tm) continue;
+      float pa[TN][4], pb[TN][4];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = min(n0 + wc0 + 16 * j + (lane & 15), n - 1);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = min(wr0 + 16 * i + 4 * (lane >> 4) + r, mrows - 1);
+          pa[j][r] = 0.f;
+          pb[j][r] = 1.f;
+          epi_load<F16, EP>(y, m0 + row, col, n, epi, pa[j][r], pb[j][r]);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int col = n0 + wc0 + 16 * j + (lane & 15);
+        if (col >= n) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = wr0 + 16 * i + 4 * (lane >> 4) + r;
+          if (row < mrows) store_pre<F16, EP, ACT>(y, m0 + row, col, n, epi, acc[i][j][r], pa[j][r], pb[j][r]);
         }
       }
     }
   }
 }
 
-template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB>
+template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB, int EP, int ACT>
 hipError_t launch_t(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m, void* y, int f16,
-                    hipStream_t s) {
+                    const Epi& epi, hipStream_t s) {
   const int64_t tiles_m = (m + BM - 1) / BM;
   const int64_t tiles = tiles_m * ((n + BN - 1) / BN);
   const int64_t per_xcd = (tiles + NXCD - 1) / NXCD;
   const dim3 grid((unsigned)(per_xcd * NXCD));
   if (f16)
-    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, true>), grid, dim3(QMM_THREADS), 0, s, w, (int)n, (int)k,
-                       rb, x, (int)m, (int)tiles, (int)per_xcd, y);
+    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, true, EP, ACT>), grid, dim3(QMM_THREADS), 0, s, w,
+                       (int)n, (int)k, rb, x, (int)m, (int)tiles, (int)per_xcd, y, epi);
   else
-    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, false>), grid, dim3(QMM_THREADS), 0, s, w, (int)n, (int)k,
-                       rb, x, (int)m, (int)tiles, (int)per_xcd, y);
+    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, false, EP, ACT>), grid, dim3(QMM_THREADS), 0, s, w,
+                       (int)n, (int)k, rb, x, (int)m, (int)tiles, (int)per_xcd, y, epi);
   return hipGetLastError();
 }
 
-template <int C>
+template <int C, int EP, int ACT>
 hipError_t launch_dense(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m, void* y,
-                        int f16, hipStream_t s) {
+                        int f16, const Epi& epi, hipStream_t s) {
   if (m > 128)  // prefill: 256 x 224 tiles (N = 14336 gives 64 tile columns)
-    return launch_t<C, 256, 224, 4, 2, 1, 2>(w, n, k, rb, x, m, y, f16, s);
-  if (m > 64) return launch_t<C, 128, 256, 2, 4, 2, 3>(w, n, k, rb, x, m, y, f16, s);
-  return launch_t<C, 64, 256, 2, 4, 2, 4>(w, n, k, rb, x, m, y, f16, s);
+    return launch_t<C, 256, 224, 4, 2, 1, 2, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+  if (m > 64) return launch_t<C, 128, 256, 2, 4, 2, 3, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+  return launch_t<C, 64, 256, 2, 4, 2, 4, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
 }
 
-template <int C, bool SEG, bool F16>
+template <int C, bool SEG, bool F16, int EP = EP_PLAIN, int ACT = 0>
 __global__ __launch_bounds__(256) void qmm_generic_kernel(const uint8_t* __restrict__ w, int n, int k, int64_t rb,
                                                           int64_t estride, int n_experts, const half_t* __restrict__ x,
                                                           int m_total, const uint32_t* __restrict__ map,
-                                                          const uint32_t* __restrict__ counts, void* __restrict__ y) {
+                                                          const uint32_t* __restrict__ counts, void* __restrict__ y,
+                                                          Epi epi) {
   const int lane = threadIdx.x & 63;
   const int nb = (n + 3) / 4;
   const int by = (int)(blockIdx.x / nb);
@@ -483,48 +516,76 @@ __global__ __launch_bounds__(256) void qmm_generic_kernel(const uint8_t* __restr
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0) {
-      if (F16)
-        ((half_t*)y)[(int64_t)r * n + col] = (half_t)acc;
-      else
-        ((float*)y)[(int64_t)r * n + col] = acc;
-    }
+    if (lane == 0) store_out<F16, EP, ACT>(y, r, col, n, epi, acc);
   }
 }
 
-template <int C, bool SEG>
+template <int C, bool SEG, int EP = EP_PLAIN, int ACT = 0>
 hipError_t launch_generic(const uint8_t* w, int64_t n, int64_t k, int64_t rb, int64_t estride, int64_t ne,
                           const half_t* x, int64_t m, const uint32_t* map, const uint32_t* counts, int64_t gy, void* y,
-                          int f16, hipStream_t s) {
+                          int f16, hipStream_t s, const Epi& epi = Epi{nullptr, nullptr, nullptr, 1}) {
   const dim3 grid((unsigned)(((n + 3) / 4) * gy));
   if (f16)
-    hipLaunchKernelGGL((qmm_generic_kernel<C, SEG, true>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb, estride,
-                       (int)ne, x, (int)m, map, counts, y);
+    hipLaunchKernelGGL((qmm_generic_kernel<C, SEG, true, EP, ACT>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb,
+                       estride, (int)ne, x, (int)m, map, counts, y, epi);
   else
-    hipLaunchKernelGGL((qmm_generic_kernel<C, SEG, false>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb, estride,
-                       (int)ne, x, (int)m, map, counts, y);
+    hipLaunchKernelGGL((qmm_generic_kernel<C, SEG, false, EP, ACT>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb,
+                       estride, (int)ne, x, (int)m, map, counts, y, epi);
   return hipGetLastError();
+}
+
+// One GEMM pass with output store EP: the matrix-core kernel for K a whole
+// number of 64-value units, else the plain kernel (q4_0 / q8_0 only).
+template <int EP, int ACT>
+hipError_t launch_pass(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m,
+                       void* y, int f16, const Epi& epi, hipStream_t s) {
+  if (k % 64 != 0) {
+    const int64_t gy = (m + 63) / 64;
+    switch (codec) {
+      case Q4_0: return launch_generic<Q4_0, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
+      case Q8_0: return launch_generic<Q8_0, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (codec) {
+    case Q4_0: return launch_dense<Q4_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q8_0: return launch_dense<Q8_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q4_K: return launch_dense<Q4_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q6_K: return launch_dense<Q6_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 hipError_t launch_qmm(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m,
                       void* y, int f16, hipStream_t s) {
-  if (k % 64 != 0) {
-    const int64_t gy = (m + 63) / 64;
-    switch (codec) {
-      case Q4_0: return launch_generic<Q4_0, false>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s);
-      case Q8_0: return launch_generic<Q8_0, false>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s);
-    }
+  return launch_pass<EP_PLAIN, 0>(codec, w, n, k, rb, x, m, y, f16, Epi{nullptr, nullptr, nullptr, 1}, s);
+}
+
+// the GEMM takes a residual with or without a gate (no bias)
+hipError_t launch_qmm_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes, const half_t* x,
+                          int64_t m, const Epi& epi, void* y, int f16out, hipStream_t s) {
+  if (!epi.resid || epi.bias) return hipErrorInvalidValue;
+  if (epi.gate) return launch_pass<EP_RES_GATE, 0>(codec, w, n, k, row_bytes, x, m, y, f16out, epi, s);
+  return launch_pass<EP_RES, 0>(codec, w, n, k, row_bytes, x, m, y, f16out, epi, s);
+}
+
+// The GLU product as two passes on one stream: the gate pass stores the
+// rounded activation in y, the up pass multiplies its product by it; each
+// output element is read and written by the same lane of the same tile.
+hipError_t launch_qmm_glu(int codec, const uint8_t* w_gate, const uint8_t* w_up, int64_t n, int64_t k,
+                          int64_t row_bytes, const half_t* x, int64_t m, int act, void* y, int f16out, hipStream_t s) {
+  const Epi none{nullptr, nullptr, nullptr, 1};
+  hipError_t e;
+  if (act == GLU_SILU)
+    e = launch_pass<EP_GLU_ACT, GLU_SILU>(codec, w_gate, n, k, row_bytes, x, m, y, f16out, none, s);
+  else if (act == GLU_GELU_TANH)
+    e = launch_pass<EP_GLU_ACT, GLU_GELU_TANH>(codec, w_gate, n, k, row_bytes, x, m, y, f16out, none, s);
+  else
     return hipErrorInvalidValue;
-  }
-  switch (codec) {
-    case Q4_0: return launch_dense<Q4_0>(w, n, k, rb, x, m, y, f16, s);
-    case Q8_0: return launch_dense<Q8_0>(w, n, k, rb, x, m, y, f16, s);
-    case Q4_K: return launch_dense<Q4_K>(w, n, k, rb, x, m, y, f16, s);
-    case Q6_K: return launch_dense<Q6_K>(w, n, k, rb, x, m, y, f16, s);
-  }
-  return hipErrorInvalidValue;
+  if (e != hipSuccess) return e;
+  return launch_pass<EP_GLU_MUL, 0>(codec, w_up, n, k, row_bytes, x, m, y, f16out, none, s);
 }
 
 hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb,

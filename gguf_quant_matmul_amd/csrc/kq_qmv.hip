@@ -64,34 +64,17 @@ __device__ __forceinline__ float lanes_sum(float v) {
 }
 
 // The GEMV of one workgroup: rows [blk * rows_per_block, ...) of w.
-// GLU epilogues of the mlx-kquant bindings.cpp page (moe_glu_gather_kq
-// docstring, its act argument), in float32 on the two float32 products g
-// (gate) and u (up):
-//   GLU_SILU        silu(g) * u, silu(g) = g / (1 + exp(-g))
-//   GLU_GELU_TANH   gelu(g) * u with the tanh form of gelu,
-//                   0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3)))
-//   GLU_SILU_LIMIT  silu(min(g, limit)) * clip(u, -limit, limit)
-template <int ACT>
-__device__ __forceinline__ float glu_act(float g, float u, float limit) {
-  if constexpr (ACT == GLU_SILU) {
-    return g / (1.f + expf(-g)) * u;
-  } else if constexpr (ACT == GLU_GELU_TANH) {
-    const float c = 0.7978845608028654f;  // sqrt(2 / pi)
-    return 0.5f * g * (1.f + tanhf(c * (g + 0.044715f * g * g * g))) * u;
-  } else {
-    const float gg = fminf(g, limit);
-    return gg / (1.f + expf(-gg)) * fminf(fmaxf(u, -limit), limit);
-  }
-}
-
-// NW = 2: the same rows of a second matrix w2 (M = 1) go through the same
-// pass, sharing each staged activation chunk, and lane 0 of a row stores
-// glu_act<ACT>(row of w, row of w2) instead of both products.
-template <int C, int M, int LPR, bool F16, int NW = 1, int ACT = 0>
+// NW = 2: the same rows of a second matrix w2 go through the same pass,
+// sharing each staged activation chunk, and activation row m's lane stores
+// glu_act<ACT>(row of w, row of w2) instead of both products (with EPI, the
+// twice-rounded glu_rounded of quantized_matmul_glu).  EPI with NW = 1: the
+// products go through epi_apply before the store.
+template <int C, int M, int LPR, bool F16, int NW = 1, int ACT = 0, bool EPI = false>
 __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, int k, int64_t row_bytes,
                                          const half_t* __restrict__ x, void* __restrict__ y, int blk,
-                                         const uint8_t* __restrict__ w2 = nullptr, float limit = 0.f) {
-  static_assert(NW == 1 || (NW == 2 && M == 1), "two matrices take one activation row");
+                                         const uint8_t* __restrict__ w2 = nullptr, float limit = 0.f,
+                                         Epi epi = Epi{nullptr, nullptr, nullptr, 1}) {
+  static_assert(NW == 1 || NW == 2, "one or two matrices");
   typedef typename UnitOf<C>::T Unit;
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   constexpr int KC = kchunk_max(M);
@@ -109,9 +92,9 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
   const uint8_t* wrow = w + (int64_t)(row_ok ? row : 0) * row_bytes;
   const uint8_t* wrow2 = NW == 2 ? w2 + (int64_t)(row_ok ? row : 0) * row_bytes : nullptr;
 
-  float acc[M], acc2 = 0.f;
+  float acc[M], acc2[M];
 #pragma unroll
-  for (int m = 0; m < M; ++m) acc[m] = 0.f;
+  for (int m = 0; m < M; ++m) acc[m] = acc2[m] = 0.f;
 
   for (int c0 = 0; c0 < k; c0 += KC) {
     const int kc = (k - c0) < KC ? (k - c0) : KC;
@@ -176,7 +159,7 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
         const int u = u0 + LANES_PER_ROW * j;
         if (row_ok && u < ue) {
           cur[j].template dot<M>(u, xv, acc);
-          if constexpr (NW == 2) cur2[j].template dot<1>(u, xv, &acc2);
+          if constexpr (NW == 2) cur2[j].template dot<M>(u, xv, acc2);
         }
       }
 #pragma unroll
@@ -188,13 +171,22 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
   }
 
   if constexpr (NW == 2) {
-    const float g = lanes_sum<LPR>(acc[0]), u = lanes_sum<LPR>(acc2);
-    if (row_ok && uslot == 0) {
-      const float v = glu_act<ACT>(g, u, limit);
+    float v = 0.f;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float g = lanes_sum<LPR>(acc[m]), u = lanes_sum<LPR>(acc2[m]);
+      if (uslot == m) {
+        if constexpr (EPI)
+          v = glu_rounded<ACT, F16>(g, u);
+        else
+          v = glu_act<ACT>(g, u, limit);
+      }
+    }
+    if (row_ok && uslot < M) {
       if (F16)
-        ((half_t*)y)[row] = (half_t)v;
+        ((half_t*)y)[(int64_t)uslot * n + row] = (half_t)v;
       else
-        ((float*)y)[row] = v;
+        ((float*)y)[(int64_t)uslot * n + row] = v;
     }
     return;
   }
@@ -205,6 +197,7 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
 #pragma unroll
     for (int m = 1; m < M; ++m)
       if (uslot == m) v = acc[m];
+    if constexpr (EPI) v = epi_apply<F16>(epi, uslot, row, n, v);
     if (F16)
       ((half_t*)y)[(int64_t)uslot * n + row] = (half_t)v;
     else
@@ -217,6 +210,26 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
                                                           int64_t row_bytes, const half_t* __restrict__ x,
                                                           void* __restrict__ y) {
   qmv_rows<C, M, LPR, F16>(w, n, k, row_bytes, x, y, blockIdx.x);
+}
+
+// GEMV with the matmul epilogue (residual, gate, bias), and the GLU product
+// of two matrices sharing x (mlx-kquant bindings.cpp page,
+// quantized_matmul_residual / _qmv_bias / _glu docstrings), on the dot2 body:
+// the epilogue for every M <= 8, the GLU product for M <= QMV_GLU_MAX_M (two
+// matrices' units for more rows overflow the registers; those take the GEMM).
+template <int C, int M, int LPR, bool F16>
+__global__ __launch_bounds__(QMV_THREADS) void qmv_epi_kernel(const uint8_t* __restrict__ w, int n, int k,
+                                                              int64_t row_bytes, const half_t* __restrict__ x,
+                                                              Epi epi, void* __restrict__ y) {
+  qmv_rows<C, M, LPR, F16, 1, 0, true>(w, n, k, row_bytes, x, y, blockIdx.x, nullptr, 0.f, epi);
+}
+
+template <int C, int M, int LPR, bool F16, int ACT>
+__global__ __launch_bounds__(QMV_THREADS) void qmv_glu_kernel(const uint8_t* __restrict__ w_gate,
+                                                              const uint8_t* __restrict__ w_up, int n, int k,
+                                                              int64_t row_bytes, const half_t* __restrict__ x,
+                                                              void* __restrict__ y) {
+  qmv_rows<C, M, LPR, F16, 2, ACT, true>(w_gate, n, k, row_bytes, x, y, blockIdx.x, w_up);
 }
 
 // Gathered GEMV (mlx-kquant bindings.cpp page, gather_qmv_kq docstring: one
@@ -256,10 +269,11 @@ __global__ __launch_bounds__(QMV_THREADS) void moe_glu_gather_kernel(
 
 // Generic GEMV for shapes the unit kernels do not take (q8_0 / q4_0 with an
 // odd number of blocks per row): one wave per row, 8 values per lane step.
-template <int C, bool F16>
+// EP / ACT / epi: the output store, as in the GEMM (store_out).
+template <int C, bool F16, int EP = EP_PLAIN, int ACT = 0>
 __global__ __launch_bounds__(256) void qmv_generic_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                           int64_t row_bytes, const half_t* __restrict__ x, int m,
-                                                          void* __restrict__ y) {
+                                                          void* __restrict__ y, Epi epi) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
@@ -282,12 +296,7 @@ __global__ __launch_bounds__(256) void qmv_generic_kernel(const uint8_t* __restr
     float s = acc[mm];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-    if (lane == 0 && mm < m) {
-      if (F16)
-        ((half_t*)y)[(int64_t)mm * n + row] = (half_t)s;
-      else
-        ((float*)y)[(int64_t)mm * n + row] = s;
-    }
+    if (lane == 0 && mm < m) store_out<F16, EP, ACT>(y, mm, row, n, epi, s);
   }
 }
 
@@ -484,18 +493,24 @@ hipError_t launch_m(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
   }
 }
 
+template <int C, int EP, int ACT>
+hipError_t launch_generic(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m, void* y,
+                          int f16, const Epi& epi, hipStream_t s) {
+  const dim3 grid((unsigned)((n + 3) / 4));
+  if (f16)
+    hipLaunchKernelGGL((qmv_generic_kernel<C, true, EP, ACT>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb, x, m, y,
+                       epi);
+  else
+    hipLaunchKernelGGL((qmv_generic_kernel<C, false, EP, ACT>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb, x, m, y,
+                       epi);
+  return hipGetLastError();
+}
+
 template <int C>
 hipError_t launch_c(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m, void* y, int f16,
                     hipStream_t s) {
   // The unit kernels need whole 64-value units per row (q8_0 / q4_0: an even block count).
-  if (k % 64 != 0) {
-    const dim3 grid((unsigned)((n + 3) / 4));
-    if (f16)
-      hipLaunchKernelGGL((qmv_generic_kernel<C, true>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb, x, m, y);
-    else
-      hipLaunchKernelGGL((qmv_generic_kernel<C, false>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb, x, m, y);
-    return hipGetLastError();
-  }
+  if (k % 64 != 0) return launch_generic<C, EP_PLAIN, 0>(w, n, k, rb, x, m, y, f16, Epi{nullptr, nullptr, nullptr, 1}, s);
   switch (m) {
     case 1: return launch_m<C, 1>(w, n, k, rb, x, y, f16, s);
     case 2: return launch_m<C, 2>(w, n, k, rb, x, y, f16, s);
@@ -505,6 +520,85 @@ hipError_t launch_c(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
     case 6: return launch_m<C, 6>(w, n, k, rb, x, y, f16, s);
     case 7: return launch_m<C, 7>(w, n, k, rb, x, y, f16, s);
     case 8: return launch_m<C, 8>(w, n, k, rb, x, y, f16, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// mode 0: epilogue; 1..3: GLU with act = mode - 1 (GLU_SILU, GLU_GELU_TANH)
+template <int C, int M, int LPR>
+hipError_t launch_fused_ml(const uint8_t* w, const uint8_t* w2, int64_t n, int64_t k, int64_t rb, const half_t* x,
+                           const Epi& epi, int act, bool glu, void* y, int f16, hipStream_t s) {
+  const int kc = (int)(k < kchunk_max(M) ? k : kchunk_max(M));
+  const size_t lds = (size_t)M * xpad(kc) * 2 + (size_t)M * (kc / 16) * 4;
+  const dim3 grid((unsigned)((n + rows_per_block(LPR) - 1) / rows_per_block(LPR)));
+  if (!glu) {
+    if (f16)
+      hipLaunchKernelGGL((qmv_epi_kernel<C, M, LPR, true>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x,
+                         epi, y);
+    else
+      hipLaunchKernelGGL((qmv_epi_kernel<C, M, LPR, false>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb,
+                         x, epi, y);
+  } else if constexpr (M > QMV_GLU_MAX_M) {
+    return hipErrorInvalidValue;
+  } else if (act == GLU_SILU) {
+    if (f16)
+      hipLaunchKernelGGL((qmv_glu_kernel<C, M, LPR, true, GLU_SILU>), grid, dim3(QMV_THREADS), lds, s, w, w2, (int)n,
+                         (int)k, rb, x, y);
+    else
+      hipLaunchKernelGGL((qmv_glu_kernel<C, M, LPR, false, GLU_SILU>), grid, dim3(QMV_THREADS), lds, s, w, w2, (int)n,
+                         (int)k, rb, x, y);
+  } else {
+    if (f16)
+      hipLaunchKernelGGL((qmv_glu_kernel<C, M, LPR, true, GLU_GELU_TANH>), grid, dim3(QMV_THREADS), lds, s, w, w2,
+                         (int)n, (int)k, rb, x, y);
+    else
+      hipLaunchKernelGGL((qmv_glu_kernel<C, M, LPR, false, GLU_GELU_TANH>), grid, dim3(QMV_THREADS), lds, s, w, w2,
+                         (int)n, (int)k, rb, x, y);
+  }
+  return hipGetLastError();
+}
+
+template <int C, int M>
+hipError_t launch_fused_m(const uint8_t* w, const uint8_t* w2, int64_t n, int64_t k, int64_t rb, const half_t* x,
+                          const Epi& epi, int act, bool glu, void* y, int f16, hipStream_t s) {
+  if (M == 1 && n <= 32768) return launch_fused_ml<C, M, 64>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+  return launch_fused_ml<C, M, 16>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+}
+
+template <int C>
+hipError_t launch_fused_c(const uint8_t* w, const uint8_t* w2, int64_t n, int64_t k, int64_t rb, const half_t* x,
+                          int m, const Epi& epi, int act, bool glu, void* y, int f16, hipStream_t s) {
+  if (k % 64 != 0) {  // odd block count (q8_0 / q4_0): the generic kernel; the GLU in two passes
+    if constexpr (C == Q8_0 || C == Q4_0) {
+      if (!glu) return launch_generic<C, EP_EPI, 0>(w, n, k, rb, x, m, y, f16, epi, s);
+      const hipError_t e =
+          act == GLU_SILU ? launch_generic<C, EP_GLU_ACT, GLU_SILU>(w, n, k, rb, x, m, y, f16, epi, s)
+                          : launch_generic<C, EP_GLU_ACT, GLU_GELU_TANH>(w, n, k, rb, x, m, y, f16, epi, s);
+      if (e != hipSuccess) return e;
+      return launch_generic<C, EP_GLU_MUL, 0>(w2, n, k, rb, x, m, y, f16, epi, s);
+    }
+    return hipErrorInvalidValue;
+  }
+  switch (m) {
+    case 1: return launch_fused_m<C, 1>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+    case 2: return launch_fused_m<C, 2>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+    case 3: return launch_fused_m<C, 3>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+    case 4: return launch_fused_m<C, 4>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+    case 5: return launch_fused_m<C, 5>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+    case 6: return launch_fused_m<C, 6>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+    case 7: return launch_fused_m<C, 7>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+    case 8: return launch_fused_m<C, 8>(w, w2, n, k, rb, x, epi, act, glu, y, f16, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_fused(int codec, const uint8_t* w, const uint8_t* w2, int64_t n, int64_t k, int64_t rb,
+                        const half_t* x, int m, const Epi& epi, int act, bool glu, void* y, int f16, hipStream_t s) {
+  switch (codec) {
+    case Q4_0: return launch_fused_c<Q4_0>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
+    case Q8_0: return launch_fused_c<Q8_0>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
+    case Q4_K: return launch_fused_c<Q4_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
+    case Q6_K: return launch_fused_c<Q6_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
   }
   return hipErrorInvalidValue;
 }
@@ -607,6 +701,18 @@ hipError_t launch_moe_glu_gather(int codec, const uint8_t* gate_w, const uint8_t
       return launch_glu_c<Q6_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_qmv_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes, const half_t* x,
+                          int m, const Epi& epi, void* y, int f16out, hipStream_t s) {
+  return launch_fused(codec, w, nullptr, n, k, row_bytes, x, m, epi, 0, false, y, f16out, s);
+}
+
+hipError_t launch_qmv_glu(int codec, const uint8_t* w_gate, const uint8_t* w_up, int64_t n, int64_t k,
+                          int64_t row_bytes, const half_t* x, int m, int act, void* y, int f16out, hipStream_t s) {
+  if (act != GLU_SILU && act != GLU_GELU_TANH) return hipErrorInvalidValue;
+  return launch_fused(codec, w_gate, w_up, n, k, row_bytes, x, m, Epi{nullptr, nullptr, nullptr, 1}, act, true, y,
+                      f16out, s);
 }
 
 hipError_t launch_qmv(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m, void* y,

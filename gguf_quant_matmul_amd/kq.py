@@ -39,6 +39,10 @@ _SIGS = {
     "kq_qmv": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_int, c_vp]),
     "kq_qmm": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_int, c_vp]),
     "kq_quantized_matmul": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_int, c_vp]),
+    "kq_quantized_matmul_residual": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_int,
+                                             c_vp]),
+    "kq_quantized_matmul_qmv_bias": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_int, c_vp]),
+    "kq_quantized_matmul_glu": (c_int, [c_int, c_vp, c_vp, c_i64, c_i64, c_vp, c_i64, c_int, c_vp, c_int, c_vp]),
     "kq_expert_tile_map_capacity": (c_i64, [c_i64, c_i64]),
     "kq_expert_tile_map": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_vp, c_vp]),
     "kq_gather_qmm_seg": (c_int, [c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_int, c_vp]),
@@ -61,7 +65,8 @@ for _name, (_res, _args) in _SIGS.items():
 KQ_Q4_0, KQ_Q8_0, KQ_Q4_K, KQ_Q6_K = 2, 8, 12, 14
 KQ_F32, KQ_F16 = 0, 1
 KQ_GLU_SILU, KQ_GLU_GELU_TANH, KQ_GLU_SILU_LIMIT = 0, 1, 2
-_GLU_ACTS = {"silu": KQ_GLU_SILU, "gelu": KQ_GLU_GELU_TANH, "silu_limit": KQ_GLU_SILU_LIMIT}
+_GLU_ACTS = {"silu": KQ_GLU_SILU, "gelu": KQ_GLU_GELU_TANH, "gelu_tanh": KQ_GLU_GELU_TANH,
+             "silu_limit": KQ_GLU_SILU_LIMIT}
 KQ_OK, KQ_ERR_ARG, KQ_ERR_CODEC, KQ_ERR_SHAPE, KQ_ERR_ALIGN, KQ_ERR_CAPACITY, KQ_ERR_HIP = 0, -1, -2, -3, -4, -5, -6
 STATUS_NAMES = {0: "KQ_OK", -1: "KQ_ERR_ARG", -2: "KQ_ERR_CODEC", -3: "KQ_ERR_SHAPE", -4: "KQ_ERR_ALIGN",
                 -5: "KQ_ERR_CAPACITY", -6: "KQ_ERR_HIP"}
@@ -165,6 +170,27 @@ def kq_qmm(codec, w, n: int, k: int, x, y, stream=None) -> None:
 def kq_quantized_matmul(codec, w, n: int, k: int, x, y, stream=None) -> None:
     _check(_lib.kq_quantized_matmul(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(y), _dtype_id(y),
                                     _stream(stream)))
+
+
+def kq_quantized_matmul_residual(codec, w, n: int, k: int, x, residual, y, gate=None, stream=None) -> None:
+    """y = residual + gate * (x @ dequant(w)^T).  residual, y [M, n]; gate None, [n] or [G, n] (G rows, one per
+    M / G consecutive rows), all three in y's dtype.  residual may be y itself."""
+    gate_rows = 0 if gate is None else gate.numel() // max(n, 1)
+    _check(_lib.kq_quantized_matmul_residual(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(residual),
+                                             _ptr(gate), gate_rows, _ptr(y), _dtype_id(y), _stream(stream)))
+
+
+def kq_quantized_matmul_qmv_bias(codec, w, n: int, k: int, x, bias, y, stream=None) -> None:
+    """y = x @ dequant(w)^T + bias for one row of x; bias [n] in y's dtype."""
+    _check(_lib.kq_quantized_matmul_qmv_bias(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(bias), _ptr(y),
+                                             _dtype_id(y), _stream(stream)))
+
+
+def kq_quantized_matmul_glu(codec, w_gate, w_up, n: int, k: int, x, y, act="silu", stream=None) -> None:
+    """y = act(x @ dequant(w_gate)^T) * (x @ dequant(w_up)^T); act 'silu' or 'gelu_tanh' (or a KQ_GLU_* id)."""
+    a = _GLU_ACTS[act] if isinstance(act, str) else int(act)
+    _check(_lib.kq_quantized_matmul_glu(_codec(codec), _ptr(w_gate), _ptr(w_up), n, k, _ptr(x), x.shape[0], a,
+                                        _ptr(y), _dtype_id(y), _stream(stream)))
 
 
 def kq_expert_tile_map(sorted_ids, n_experts: int, map_, counts, status=None, stream=None) -> None:

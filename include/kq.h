@@ -52,7 +52,8 @@ typedef enum { KQ_Q4_0 = 2, KQ_Q8_0 = 8, KQ_Q4_K = 12, KQ_Q6_K = 14 } kq_codec;
 /* Output element types. */
 typedef enum { KQ_F32 = 0, KQ_F16 = 1 } kq_dtype;
 
-/* GLU epilogues of kq_moe_glu_gather (the pages' act names in comments). */
+/* GLU epilogues of kq_moe_glu_gather and kq_quantized_matmul_glu (the pages'
+ * act names in comments; kq_quantized_matmul_glu takes the first two). */
 typedef enum {
   KQ_GLU_SILU = 0,       /* 'silu':       silu(g) * u                          */
   KQ_GLU_GELU_TANH = 1,  /* 'gelu':       gelu(g) * u, tanh form               */
@@ -106,6 +107,44 @@ int kq_qmm(int codec, const void* w, int64_t n, int64_t k,
            const void* x, int64_t m, void* y, int y_dtype, void* stream);
 int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k,
                         const void* x, int64_t m, void* y, int y_dtype, void* stream);
+
+/* ---- fused epilogues (mlx-kquant bindings.cpp page: quantized_matmul_residual,
+ *      quantized_matmul_qmv_bias and quantized_matmul_glu docstrings) ----
+ * The product p[m][n] of kq_quantized_matmul (same w, x, M, N, K rules and
+ * the same GEMV / GEMM split) finished in the store, in float32, rounded
+ * once to y_dtype:
+ *
+ * kq_quantized_matmul_residual:  y = residual + gate * p.
+ *   residual [M][N] and gate [gate_rows][N] are in y_dtype; output row m takes
+ *   gate row m / (M / gate_rows), so gate_rows = 1 is one gate for every row
+ *   and gate_rows = B is one row per batch of M / B rows.  gate = NULL drops
+ *   the gate (y = residual + p; gate_rows is then ignored).  gate_rows must
+ *   divide M (KQ_ERR_SHAPE).  residual may be y itself (updated in place);
+ *   otherwise residual and gate must not overlap y (KQ_ERR_ARG).
+ * kq_quantized_matmul_qmv_bias:  y = p + bias, decode only: M must be 1
+ *   (KQ_ERR_SHAPE otherwise).  bias [N] in y_dtype, not overlapping y.
+ * kq_quantized_matmul_glu:  y = act(x @ dequant(w_gate)^T) * (x @ dequant(w_up)^T)
+ *   with act KQ_GLU_SILU or KQ_GLU_GELU_TANH (KQ_ERR_ARG otherwise).  w_gate
+ *   and w_up have the same codec and shape (they may be row slices of one
+ *   wider weight).  The activation of the gate product is rounded to y_dtype,
+ *   then multiplied by the up product in float32 and rounded again; a
+ *   float16 store turns a finite value beyond the float16 range into the
+ *   largest finite half of its sign (infinities and NaN pass).  M <= 3 runs
+ *   both weights through one GEMV pass; larger M runs two GEMM passes on the
+ *   stream (gate, then up), with y as the only buffer between them.
+ *
+ * Element alignment for residual, gate and bias; the rest as in
+ * kq_quantized_matmul. */
+int kq_quantized_matmul_residual(int codec, const void* w, int64_t n, int64_t k,
+                                 const void* x, int64_t m, const void* residual,
+                                 const void* gate, int64_t gate_rows, void* y,
+                                 int y_dtype, void* stream);
+int kq_quantized_matmul_qmv_bias(int codec, const void* w, int64_t n, int64_t k,
+                                 const void* x, int64_t m, const void* bias, void* y,
+                                 int y_dtype, void* stream);
+int kq_quantized_matmul_glu(int codec, const void* w_gate, const void* w_up, int64_t n,
+                            int64_t k, const void* x, int64_t m, int act, void* y,
+                            int y_dtype, void* stream);
 
 /* ---- expert tile map (mlx-kquant bindings.cpp page, expert_tile_map docstring) ----
  * From expert ids sorted ascending (uint32 [rows]), write tiles

@@ -38,6 +38,20 @@ Definitions followed
     ``gather_qmm``: output batch i is x[lhs[i]] times dequantize(w)[rhs[i]]
     transposed.
 
+  * mlx-kquant ``bindings.cpp`` page, ``quantized_matmul_residual``
+    docstring: y = residual + gate * (x @ W^T), gate [N] or one row per batch
+    (x's batch dims, then 1, then N), residual and gate in the output dtype,
+    the fused store rounding once.  Reading taken: the M rows of x are
+    ``gate_rows`` consecutive batches of M / gate_rows rows each.
+  * same page, ``quantized_matmul_qmv_bias`` docstring: x @ W^T + bias for
+    exactly one row of x (other row counts raise), bias of length N.
+  * same page, ``quantized_matmul_glu`` docstring: y = act(x @ Wg^T) *
+    (x @ Wu^T), act 'silu' or 'gelu_tanh'; the sums, the activation and the
+    product in float32 (float64 here), the activation rounded once to y's
+    dtype and the product once more; a float16 store keeps a finite value
+    finite (clamped to the largest half of its sign), NaN and infinities
+    pass.
+
 Pins (tests/test_oracle_matmul.py): exact rational dot products (Python
 ``fractions``) on tiny shapes; one-hot x rows return weight columns exactly;
 tile-map invariants by brute force plus a hand example; the gather equals a
@@ -47,7 +61,12 @@ qmm when every row names the same expert; the GLU gather's products equal the
 gathered GEMV of each matrix, its activations match library routines
 (``scipy.special.expit`` for the sigmoid, PyTorch's tanh-approximate gelu) at
 the products, and 'silu_limit' with a limit above every |product| equals
-'silu'.
+'silu'.  The epilogues: a hand example of per-batch gate rows (constant gate
+rows 1 and 2 on weight rows picked out by one-hot x), the no-gate case
+reducing to the plain product, bias equal to a residual of repeated bias
+rows, the float16 store's saturation on textbook values (65504 the largest
+half, 65520 the first value that rounds to infinity), and the GLU with a
+float32 output equal to the GLU gather's act(g) * u.
 """
 
 from __future__ import annotations
@@ -132,6 +151,11 @@ def glu_act(act: str, g: np.ndarray, u: np.ndarray, limit: float = 0.0) -> np.nd
     """The GLU epilogue of ``moe_glu_gather_kq`` (its ``act`` argument), in float64."""
     g = np.asarray(g, dtype=np.float64)
     u = np.asarray(u, dtype=np.float64)
+    with np.errstate(over="ignore"):  # exp(-g) = inf for very negative g: silu(g) = -0
+        return _glu_act(act, g, u, limit)
+
+
+def _glu_act(act, g, u, limit):
     if act == "silu":
         return g / (1.0 + np.exp(-g)) * u
     if act == "gelu":
@@ -185,3 +209,61 @@ def gather_mix(y: np.ndarray, inv_order: np.ndarray, scores: np.ndarray) -> np.n
             if 0 <= r < y.shape[0]:
                 out[t] += scores[t, s] * y[r]
     return out
+
+
+def round_out(v: np.ndarray, out_dtype: str) -> np.ndarray:
+    """v rounded to the output type, returned as float64: 'f32', or 'f16' with a
+    finite value beyond the float16 range becoming the largest finite half of
+    its sign (infinities and NaN pass), per the quantized_matmul_glu docstring."""
+    v = np.asarray(v, dtype=np.float64)
+    if out_dtype == "f32":
+        return v.astype(np.float32).astype(np.float64)
+    if out_dtype != "f16":
+        raise ValueError(out_dtype)
+    hmax = float(np.finfo(np.float16).max)
+    sat = np.where(np.isfinite(v), np.clip(v, -hmax, hmax), v)
+    return sat.astype(np.float16).astype(np.float64)
+
+
+def quantized_matmul_residual(codec: str, w: np.ndarray, k: int, x: np.ndarray, residual: np.ndarray,
+                              gate: np.ndarray | None = None) -> np.ndarray:
+    """Reference for kq_quantized_matmul_residual: residual + gate * (x @ W^T) in float64.
+
+    residual [M, N]; gate None, [N] or [G, N] with G dividing M: output row m
+    takes gate row m // (M // G) (G consecutive batches of rows).
+    """
+    prod = qmatmul(codec, w, k, x)
+    res = np.asarray(residual, dtype=np.float64).reshape(prod.shape)
+    if gate is None:
+        return res + prod
+    g = np.asarray(gate, dtype=np.float64).reshape(-1, prod.shape[1])
+    m, batches = prod.shape[0], g.shape[0]
+    if batches == 0 or m % batches:
+        raise ValueError(f"{batches} gate rows do not divide {m} rows")
+    return res + g[np.arange(m) // (m // batches)] * prod
+
+
+def quantized_matmul_qmv_bias(codec: str, w: np.ndarray, k: int, x: np.ndarray, bias: np.ndarray) -> np.ndarray:
+    """Reference for kq_quantized_matmul_qmv_bias: x @ W^T + bias, x exactly one row."""
+    if x.shape[0] != 1:
+        raise ValueError("the bias-fused matmul is decode-only: x must have exactly one row")
+    return qmatmul(codec, w, k, x) + np.asarray(bias, dtype=np.float64)[None, :]
+
+
+_GLU_NAMES = {"silu": "silu", "gelu_tanh": "gelu"}
+
+
+def quantized_matmul_glu(codec: str, w_gate: np.ndarray, w_up: np.ndarray, k: int, x: np.ndarray,
+                         act: str = "silu", out_dtype: str = "f32") -> np.ndarray:
+    """Reference for kq_quantized_matmul_glu: round(round(act(x @ Wg^T)) * (x @ Wu^T)).
+
+    The sums and the activation in float64; the activation rounded to
+    ``out_dtype`` ('f32' or 'f16', saturating), the product with the up sum
+    rounded again.  Returns the rounded values as float64.
+    """
+    if act not in _GLU_NAMES:
+        raise ValueError(f"act {act!r} is not 'silu' or 'gelu_tanh'")
+    g = qmatmul(codec, w_gate, k, x)
+    u = qmatmul(codec, w_up, k, x)
+    a = round_out(glu_act(_GLU_NAMES[act], g, np.ones_like(g)), out_dtype)
+    return round_out(a * u, out_dtype)

@@ -118,6 +118,30 @@ def _st(ret):
         (lambda: L.kq_gather_mix(A16 + 4, 8, 8, A16, A16, 2, 4, A16, 1, None), kq.KQ_ERR_ALIGN, "y="),
         (lambda: L.kq_gather_mix(A16, 8, 8, A16 + 2, A16, 2, 4, A16, 1, None), kq.KQ_ERR_ALIGN, "inv_order"),
         (lambda: L.kq_gather_mix(A16, 8, 8, A16, A16, -1, 4, A16, 1, None), kq.KQ_ERR_ARG, "tokens"),
+        (lambda: L.kq_quantized_matmul_residual(12, A16, 64, 256, A16, 4, A16 * 4, A16 * 8, 3, A16, 0, None),
+         kq.KQ_ERR_SHAPE, "gate_rows=3"),
+        (lambda: L.kq_quantized_matmul_residual(12, A16, 64, 256, A16, 4, None, None, 0, A16, 0, None),
+         kq.KQ_ERR_ARG, "null residual"),
+        (lambda: L.kq_quantized_matmul_residual(12, A16, 64, 256, A16, 4, A16 * 4 + 2, None, 0, A16, 0, None),
+         kq.KQ_ERR_ALIGN, "residual"),
+        (lambda: L.kq_quantized_matmul_residual(12, A16, 64, 256, A16, 4, A16 + 256, None, 0, A16, 0, None),
+         kq.KQ_ERR_ARG, "residual overlaps"),
+        (lambda: L.kq_quantized_matmul_residual(12, A16, 64, 256, A16, 4, A16, A16 + 256, 2, A16, 1, None),
+         kq.KQ_ERR_ARG, "gate overlaps"),
+        (lambda: L.kq_quantized_matmul_qmv_bias(8, A16, 64, 256, A16, 2, A16 * 4, A16, 0, None),
+         kq.KQ_ERR_SHAPE, "M=2"),
+        (lambda: L.kq_quantized_matmul_qmv_bias(8, A16, 64, 256, A16, 1, None, A16, 0, None),
+         kq.KQ_ERR_ARG, "null bias"),
+        (lambda: L.kq_quantized_matmul_qmv_bias(8, A16, 64, 256, A16, 1, A16 + 64, A16, 1, None),
+         kq.KQ_ERR_ARG, "bias overlaps"),
+        (lambda: L.kq_quantized_matmul_glu(12, A16, A16, 64, 256, A16, 4, 2, A16, 0, None),
+         kq.KQ_ERR_ARG, "act=2"),
+        (lambda: L.kq_quantized_matmul_glu(12, A16, None, 64, 256, A16, 4, 0, A16, 0, None),
+         kq.KQ_ERR_ARG, "w_up"),
+        (lambda: L.kq_quantized_matmul_glu(12, A16, A16 + 8, 64, 256, A16, 4, 0, A16, 0, None),
+         kq.KQ_ERR_ALIGN, "w_up="),
+        (lambda: L.kq_quantized_matmul_glu(12, A16, A16, 64, 250, A16, 4, 0, A16, 0, None),
+         kq.KQ_ERR_SHAPE, "K=250"),
         (lambda: L.kq_quantize(12, A16, 4, 512, A16 + 4, None), kq.KQ_ERR_ALIGN, "aligned"),
         (lambda: L.kq_quantize(6, A16, 4, 512, A16, None), kq.KQ_ERR_CODEC, "codec"),
     ],
@@ -141,3 +165,6 @@ def test_empty_inputs_are_no_ops():
     assert L.kq_gather_mix(None, 0, 0, None, None, 5, 4, None, 1, None) == 0
     assert L.kq_moe_glu_gather(12, None, None, 4, 64, 256, None, 3, None, 0, 1, 0.0, None, 0, None) == 0
     assert L.kq_quantize(8, None, 0, 64, None, None) == 0
+    assert L.kq_quantized_matmul_residual(12, None, 64, 256, None, 0, None, None, 0, None, 0, None) == 0
+    assert L.kq_quantized_matmul_qmv_bias(8, None, 0, 256, None, 1, None, None, 1, None) == 0
+    assert L.kq_quantized_matmul_glu(14, None, None, 0, 256, None, 3, 1, None, 0, None) == 0

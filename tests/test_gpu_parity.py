@@ -180,6 +180,119 @@ def test_qmm_parity(kq, codec):
             assert_close_rows(host(y).astype(np.float64), ref, what=f"qmm {codec} m={m} n={n} k={k}")
 
 
+# ---------------------------------------------------------------------------
+# fused epilogues: residual / gate, bias, GLU product
+# ---------------------------------------------------------------------------
+
+def _epi_shapes(codec):
+    kk = 256 * 9 if codec in ("q4_k", "q6_k") else 64 * 9
+    shapes = [(1, 37, kk), (3, 300, kk), (8, 45, kk), (130, 200, kk), (260, 131, kk)]
+    if codec in ("q8_0", "q4_0"):
+        shapes += [(4, 45, 2048 + 32), (70, 40, 96)]  # odd block counts: generic kernels
+    return shapes
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_quantized_matmul_residual_parity(kq, codec):
+    # y = residual + gate * p on the GEMV (M <= 8) and GEMM bodies; gate
+    # absent, one row, or one row per batch of consecutive rows; in place
+    # (residual is y) and out of place
+    torch = _torch()
+    for m, n, k in _epi_shapes(codec):
+        w = _weights(codec, n, k, 13 + m)
+        x = _x(m, k, 2 * m + n)
+        rng = np.random.default_rng(m * 1000 + n)
+        batches = [b for b in (2, 4) if m % b == 0][:1]
+        gates = [None, rng.uniform(-2, 2, n)] + [rng.uniform(-2, 2, (b, n)) for b in batches]
+        for tdt, ndt in ((torch.float32, np.float32), (torch.float16, np.float16)):
+            res = rng.standard_normal((m, n)).astype(ndt)
+            for gi, gate in enumerate(gates):
+                g = None if gate is None else gate.astype(ndt)
+                ref = matmul.quantized_matmul_residual(codec, w, k, x, res, g)
+                say(f"residual {codec} m={m} n={n} k={k} gate={gi} {tdt}")
+                y = torch.full((m, n), float("nan"), dtype=tdt, device="cuda")
+                kq.kq_quantized_matmul_residual(codec, dev(w), n, k, dev(x), dev(res), y,
+                                                None if g is None else dev(g))
+                assert_close_rows(host(y).astype(np.float64), ref, what=f"residual {codec} m={m} gate={gi}")
+            say(f"residual in place {codec} m={m} n={n} k={k} {tdt}")
+            y = dev(res)
+            kq.kq_quantized_matmul_residual(codec, dev(w), n, k, dev(x), y, y, dev(gates[1].astype(ndt)))
+            ref = matmul.quantized_matmul_residual(codec, w, k, x, res, gates[1].astype(ndt))
+            assert_close_rows(host(y).astype(np.float64), ref, what=f"residual in place {codec} m={m}")
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_quantized_matmul_qmv_bias_parity(kq, codec):
+    torch = _torch()
+    for n, k in _shapes_qmv(codec) + [(130000, 256 if codec in ("q4_k", "q6_k") else 64)]:
+        w = _weights(codec, n, k, 17 + n)
+        x = _x(1, k, n + 3)
+        bias = np.random.default_rng(n).standard_normal(n)
+        for tdt, ndt in ((torch.float32, np.float32), (torch.float16, np.float16)):
+            b = bias.astype(ndt)
+            say(f"qmv_bias {codec} n={n} k={k} {tdt}")
+            y = torch.full((1, n), float("nan"), dtype=tdt, device="cuda")
+            kq.kq_quantized_matmul_qmv_bias(codec, dev(w), n, k, dev(x), dev(b), y)
+            ref = matmul.quantized_matmul_qmv_bias(codec, w, k, x, b)
+            assert_close_rows(host(y).astype(np.float64), ref, what=f"qmv_bias {codec} n={n} k={k}")
+
+
+@pytest.mark.parametrize("codec", CODECS)
+def test_quantized_matmul_glu_parity(kq, codec):
+    # act(x Wg^T) * (x Wu^T): one GEMV pass for M <= 3, two GEMM passes
+    # above; the activation rounded to y's type before the product.  Gate and
+    # up are row slices of one [2N, row_bytes] weight.
+    torch = _torch()
+    kk = 256 * 5 if codec in ("q4_k", "q6_k") else 64 * 5
+    shapes = [(1, 48, kk), (2, 304, kk), (3, 96, kk), (5, 48, kk), (8, 112, kk), (130, 208, kk), (257, 96, kk)]
+    if codec in ("q8_0", "q4_0"):
+        shapes += [(2, 48, 96), (70, 48, 96)]
+    for m, n, k in shapes:
+        wcat = _weights(codec, 2 * n, k, 23 + m, scale=0.05)
+        wg, wu = wcat[:n], wcat[n:]
+        x = _x(m, k, m + 5 * n)
+        dcat = dev(wcat)
+        rb = wcat.shape[1]
+        assert (n * rb) % 16 == 0
+        for act in ("silu", "gelu_tanh"):
+            for tdt, odt in ((torch.float32, "f32"), (torch.float16, "f16")):
+                say(f"glu {codec} m={m} n={n} k={k} {act} {odt}")
+                y = torch.full((m, n), float("nan"), dtype=tdt, device="cuda")
+                kq.kq_quantized_matmul_glu(codec, dcat[:n], dcat[n:], n, k, dev(x), y, act)
+                ref = matmul.quantized_matmul_glu(codec, wg, wu, k, x, act, odt)
+                assert_close_rows(host(y).astype(np.float64), ref, what=f"glu {codec} m={m} {act} {odt}")
+
+
+@pytest.mark.parametrize("m", [2, 40])
+def test_quantized_matmul_glu_f16_saturates(kq, m):
+    # products beyond the float16 range store the largest finite half of
+    # their sign, on both the GEMV and the GEMM path
+    torch = _torch()
+    n, k = 64, 256
+    w = _weights("q8_0", 2 * n, k, 31, scale=25.0)
+    x = _x(m, k, 77)
+    ref = matmul.quantized_matmul_glu("q8_0", w[:n], w[n:], k, x, "silu", "f16")
+    say(f"glu saturation m={m}")
+    y = torch.empty((m, n), dtype=torch.float16, device="cuda")
+    d = dev(w)
+    kq.kq_quantized_matmul_glu("q8_0", d[:n], d[n:], n, k, dev(x), y, "silu")
+    got = host(y).astype(np.float64)
+    assert np.all(np.isfinite(got))
+    # products clearly past the float16 range (1% beyond the rounding
+    # boundary 65520) must store exactly the largest half of their sign
+    g, u = matmul.qmatmul("q8_0", w[:n], k, x), matmul.qmatmul("q8_0", w[n:], k, x)
+    prod = matmul.round_out(g / (1.0 + np.exp(-g)), "f16") * u
+    far = np.abs(prod) >= 1.01 * 65520.0
+    assert far.sum() > 10
+    assert np.array_equal(got[far], np.sign(prod[far]) * 65504.0)
+    # elsewhere the usual bar, scaled by each row's largest product before the
+    # clamp: the clamp shrinks the row maximum, not the products' own error
+    # (the GEMM's float16 weights put an error of about 2^-12 of the weights'
+    # scale on each sum, and a cancelled gate sum times a large up sum keeps it)
+    scale = np.abs(prod).max(axis=1, keepdims=True)
+    assert np.all(np.abs(got - ref) <= TOL * scale), float((np.abs(got - ref) / scale).max())
+
+
 def test_quantized_matmul_routes_by_m(kq):
     torch = _torch()
     n, k = 64, 512

@@ -268,3 +268,103 @@ def test_gather_mix_skips_rows_out_of_range():
     out = matmul.gather_mix(y, inv, scores)
     np.testing.assert_array_equal(out[0], 0.5 * y[2])
     np.testing.assert_array_equal(out[1], y[0] + 2.0 * y[1])
+
+
+# ---- fused epilogues: residual / gate, bias, GLU product -------------------
+
+def _one_hot_case(codec="q8_0", n=6, k=64, cols=(0, 5, 33, 63)):
+    rng = np.random.default_rng(51)
+    wq = encode.quantize(codec, rng.standard_normal((n, k)).astype(np.float32))
+    x = np.zeros((len(cols), k), np.float16)
+    for i, c in enumerate(cols):
+        x[i, c] = 1
+    wd = codecs.dequantize(codec, wq, k).astype(np.float64)
+    return wq, x, wd, k, list(cols)
+
+
+def test_residual_gate_rows_are_consecutive_batches():
+    # four rows in two batches: rows 0-1 take gate row 0 (all ones), rows 2-3
+    # gate row 1 (all twos); one-hot x makes each product a weight column
+    wq, x, wd, k, cols = _one_hot_case()
+    res = np.full((4, 6), 0.25)
+    gate = np.stack([np.ones(6), np.full(6, 2.0)])
+    y = matmul.quantized_matmul_residual("q8_0", wq, k, x, res, gate)
+    for i, c in enumerate(cols):
+        scale = 1.0 if i < 2 else 2.0
+        assert np.array_equal(y[i], 0.25 + scale * wd[:, c])
+
+
+def test_residual_without_gate_is_the_product_plus_residual():
+    wq, x, wd, k, _ = _one_hot_case()
+    prod = matmul.qmatmul("q8_0", wq, k, x)
+    assert np.array_equal(matmul.quantized_matmul_residual("q8_0", wq, k, x, np.zeros_like(prod)), prod)
+    rng = np.random.default_rng(52)
+    res = rng.standard_normal(prod.shape)
+    ones = np.ones(prod.shape[1])
+    assert np.array_equal(matmul.quantized_matmul_residual("q8_0", wq, k, x, res, ones),
+                          matmul.quantized_matmul_residual("q8_0", wq, k, x, res))
+
+
+def test_residual_one_gate_row_equals_it_repeated_per_row():
+    rng = np.random.default_rng(53)
+    n, k, m = 7, 256, 6
+    wq = encode.quantize("q4_k", rng.standard_normal((n, k)).astype(np.float32))
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    res = rng.standard_normal((m, n))
+    g1 = rng.standard_normal(n)
+    a = matmul.quantized_matmul_residual("q4_k", wq, k, x, res, g1)
+    b = matmul.quantized_matmul_residual("q4_k", wq, k, x, res, np.tile(g1, (m, 1)))
+    c = matmul.quantized_matmul_residual("q4_k", wq, k, x, res, np.tile(g1, (3, 1)))
+    assert np.array_equal(a, b) and np.array_equal(a, c)
+    with pytest.raises(ValueError):
+        matmul.quantized_matmul_residual("q4_k", wq, k, x, res, np.tile(g1, (4, 1)))
+
+
+def test_qmv_bias_is_a_residual_of_repeated_bias_and_one_row_only():
+    rng = np.random.default_rng(54)
+    n, k = 9, 512
+    wq = encode.quantize("q6_k", rng.standard_normal((n, k)).astype(np.float32))
+    x = rng.standard_normal((1, k)).astype(np.float16)
+    bias = rng.standard_normal(n)
+    assert np.array_equal(matmul.quantized_matmul_qmv_bias("q6_k", wq, k, x, bias),
+                          matmul.quantized_matmul_residual("q6_k", wq, k, x, bias[None, :]))
+    with pytest.raises(ValueError):
+        matmul.quantized_matmul_qmv_bias("q6_k", wq, k, np.zeros((2, k), np.float16), bias)
+
+
+def test_round_out_f16_saturates_finite_values_only():
+    v = np.array([65504.0, 65519.0, 65520.0, 1e5, -1e5, np.inf, -np.inf, np.nan, 1.0 + 2.0 ** -11, 0.1])
+    r = matmul.round_out(v, "f16")
+    assert r[:5].tolist() == [65504.0, 65504.0, 65504.0, 65504.0, -65504.0]
+    assert r[5] == np.inf and r[6] == -np.inf and np.isnan(r[7])
+    assert r[8] == 1.0                      # the tie between 1 and 1 + 2^-10 rounds to even
+    assert r[9] == 0.0999755859375          # the float16 nearest 0.1
+    # without saturation 65520 would round to infinity
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float16(65520.0))
+    assert matmul.round_out(np.array([1e5]), "f32")[0] == 1e5
+
+
+@pytest.mark.parametrize("act", ["silu", "gelu_tanh"])
+def test_glu_product_f32_equals_activation_times_up(act):
+    import torch
+    from scipy.special import expit
+
+    rng = np.random.default_rng(55)
+    n, k, m = 12, 512, 5
+    wg = encode.quantize("q4_k", (rng.standard_normal((n, k)) * 0.05).astype(np.float32))
+    wu = encode.quantize("q4_k", (rng.standard_normal((n, k)) * 0.05).astype(np.float32))
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    g, u = matmul.qmatmul("q4_k", wg, k, x), matmul.qmatmul("q4_k", wu, k, x)
+    if act == "silu":
+        a = g * expit(g)
+    else:
+        a = torch.nn.functional.gelu(torch.from_numpy(g), approximate="tanh").numpy()
+    y = matmul.quantized_matmul_glu("q4_k", wg, wu, k, x, act, "f32")
+    np.testing.assert_allclose(y, a * u, rtol=3e-7, atol=1e-30)
+    y16 = matmul.quantized_matmul_glu("q4_k", wg, wu, k, x, act, "f16")
+    assert np.array_equal(y16, y16.astype(np.float16).astype(np.float64))
+    # two float16 roundings: each within half an ulp (2^-11 relative)
+    np.testing.assert_allclose(y16, a * u, rtol=2 * 2.0 ** -11 + 1e-6, atol=2.0 ** -24)
+    with pytest.raises(ValueError):
+        matmul.quantized_matmul_glu("q4_k", wg, wu, k, x, "silu_limit")
