@@ -213,7 +213,8 @@ def test_quantized_matmul_residual_parity(kq, codec):
                 y = torch.full((m, n), float("nan"), dtype=tdt, device="cuda")
                 kq.kq_quantized_matmul_residual(codec, dev(w), n, k, dev(x), dev(res), y,
                                                 None if g is None else dev(g))
-                assert_close_rows(host(y).astype(np.float64), ref, what=f"residual {codec} m={m} gate={gi}")
+                e = assert_close_rows(host(y).astype(np.float64), ref, what=f"residual {codec} m={m} gate={gi}")
+                say(f"  worst row error {e:.2e}")
             say(f"residual in place {codec} m={m} n={n} k={k} {tdt}")
             y = dev(res)
             kq.kq_quantized_matmul_residual(codec, dev(w), n, k, dev(x), y, y, dev(gates[1].astype(ndt)))
@@ -234,7 +235,8 @@ def test_quantized_matmul_qmv_bias_parity(kq, codec):
             y = torch.full((1, n), float("nan"), dtype=tdt, device="cuda")
             kq.kq_quantized_matmul_qmv_bias(codec, dev(w), n, k, dev(x), dev(b), y)
             ref = matmul.quantized_matmul_qmv_bias(codec, w, k, x, b)
-            assert_close_rows(host(y).astype(np.float64), ref, what=f"qmv_bias {codec} n={n} k={k}")
+            e = assert_close_rows(host(y).astype(np.float64), ref, what=f"qmv_bias {codec} n={n} k={k}")
+            say(f"  worst row error {e:.2e}")
 
 
 @pytest.mark.parametrize("codec", CODECS)
@@ -260,7 +262,8 @@ def test_quantized_matmul_glu_parity(kq, codec):
                 y = torch.full((m, n), float("nan"), dtype=tdt, device="cuda")
                 kq.kq_quantized_matmul_glu(codec, dcat[:n], dcat[n:], n, k, dev(x), y, act)
                 ref = matmul.quantized_matmul_glu(codec, wg, wu, k, x, act, odt)
-                assert_close_rows(host(y).astype(np.float64), ref, what=f"glu {codec} m={m} {act} {odt}")
+                e = assert_close_rows(host(y).astype(np.float64), ref, what=f"glu {codec} m={m} {act} {odt}")
+                say(f"  worst row error {e:.2e}")
 
 
 @pytest.mark.parametrize("m", [2, 40])
