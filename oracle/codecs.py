@@ -11,6 +11,9 @@ What the pages fix
   * mlx-kquant ``bindings.cpp`` page, ``dequantize`` docstring: input is
     uint8 wire bytes whose last dim is a multiple of the codec's bytes per
     block; output float dtype defaults to float16.
+  * the same table: q5_k is a 256-value superblock of 5-bit codes in 176
+    bytes ("K-quant superblock"); its layout is not on the pages and takes
+    reading R1 like the others.
   * The q4_K sub-block structure (8 sub-blocks of 32, 6-bit scale and min per
     sub-block, fp16 d and dmin) and the q6_K one (16 sub-blocks of 16, int8
     scales, fp16 d) are stated with the workloads.
@@ -24,7 +27,7 @@ Readings taken where the pages are silent (each is also listed in the design doc)
       honoured, the sign of zero kept, inf/NaN passed through).
   R3  Arithmetic: each value is the exact real number of the formula, rounded
       ONCE to fp32 (RNE).  For q8_0, q4_0 and q6_K the exact value is already
-      an fp32 number.  For q4_K the only rounding is that of
+      an fp32 number.  For q4_K and q5_K the only rounding is that of
       ``(d*sc)*q - (dmin*m)``.
   R4  float16 output is RNE of the fp32 value (so q4_K -> f16 rounds twice, by
       definition).
@@ -50,6 +53,7 @@ GEOMETRY = {
     "q6_k": (256, 6, 210),
     "q8_0": (32, 8, 34),
     "q4_0": (32, 4, 18),
+    "q5_k": (256, 5, 176),
 }
 
 CODECS = tuple(GEOMETRY)
@@ -179,6 +183,28 @@ def fields_q4_k(blk: np.ndarray):
     return d, dmin, sc, m, q  # q: [n, nb, 8, 32]
 
 
+def fields_q5_k(blk: np.ndarray):
+    """q5_K, 176 bytes: [0:2] d, [2:4] dmin (fp16), [4:16] packed scales (as
+    q4_K), [16:48] qh, [48:176] qs.
+
+    Value v lies in sub-block j = v // 32 at position l = v % 32: its low four
+    bits are the nibble of qs[32*(j//2) + l] (low nibble for even j, high for
+    odd j), its fifth bit is bit j of qh[l].
+    value = (d*sc_j)*q - (dmin*m_j), q in 0..31.
+    """
+    d = f16_bits_to_f64(le_u16(blk[..., 0], blk[..., 1]))
+    dmin = f16_bits_to_f64(le_u16(blk[..., 2], blk[..., 3]))
+    sc, m = scale_min_q4_k(blk[..., 4:16])
+    qh = blk[..., 16:48].astype(np.int64)  # [n, nb, 32]
+    qs = blk[..., 48:176].astype(np.int64)  # [n, nb, 128]
+    q = np.empty(qs.shape[:-1] + (8, 32), dtype=np.int64)
+    for j in range(8):
+        byte = qs[..., 32 * (j // 2): 32 * (j // 2) + 32]
+        low4 = (byte & 15) if j % 2 == 0 else (byte >> 4)
+        q[..., j, :] = low4 | (((qh >> j) & 1) << 4)
+    return d, dmin, sc, m, q  # q: [n, nb, 8, 32]
+
+
 def fields_q6_k(blk: np.ndarray):
     """q6_K, 210 bytes: [0:128] ql, [128:192] qh, [192:208] 16 int8 scales, [208:210] d.
 
@@ -238,8 +264,8 @@ def dequantize(codec: str, w: np.ndarray, k: int, dtype=np.float32) -> np.ndarra
             d, scales, q = fields_q6_k(blk)
             step = d[..., None] * scales  # [n, nb, 16], exact in float64
             y = _exact_f32(np.repeat(step, 16, axis=-1) * (q - 32))
-        elif codec == "q4_k":
-            d, dmin, sc, m, q = fields_q4_k(blk)
+        elif codec in ("q4_k", "q5_k"):
+            d, dmin, sc, m, q = fields_q4_k(blk) if codec == "q4_k" else fields_q5_k(blk)
             a = _exact_f32(d[..., None, None] * sc[..., None] * q)  # (d*sc)*q, exact
             b = _exact_f32(np.broadcast_to((dmin[..., None] * m)[..., None], a.shape))
             y = a - b  # float32 - float32: the single IEEE rounding

@@ -1,4 +1,4 @@
-"""Oracle: a plain round-to-nearest encoder for the four codecs (CPU, NumPy).
+"""Oracle: a plain round-to-nearest encoder for the codecs (CPU, NumPy).
 
 Test infrastructure only (see ``oracle/__init__``).  It makes the configs'
 weights; it is not part of the decode contract.
@@ -21,6 +21,8 @@ the same bytes.  ``rint`` rounds half to even; ``f16()`` is RNE to binary16.
          d = f16(max_j scale_j / 63), dmin = f16(max_j min_j / 63);
          sc_j = rint(scale_j/D), m_j = rint(min_j/DM)  (clamped to 0..63);
          q = rint((w + DM*m_j) / (D*sc_j))
+  q5_K : as q4_K with 31 levels: scale_j = (hi - lo)/31, q in 0..31 (the
+         low four bits in qs as q4_K's nibbles, bit 4 in bit j of qh[l])
   q6_K : per 16-value sub-block j: scale_j = amax_j/31;
          d = f16(max_j scale_j / 127); sc_j = rint(scale_j/D) (clamped -128..127);
          q = rint(w/(D*sc_j)) + 32
@@ -28,7 +30,7 @@ Codes are clamped to the codec's range.  Then each code is moved to the
 NEAREST point of the block's decoded grid among {q-1, q, q+1} (distance
 |w - decode(q)| taken in float64; ties go to the lower code), so that every
 code is the nearest grid point.  Where the grid step is zero the code is the
-zero-point code (q8_0: 0, q4_0: 8, q4_K: 0, q6_K: 32).
+zero-point code (q8_0: 0, q4_0: 8, q4_K and q5_K: 0, q6_K: 32).
 
 Pins (tests/test_oracle_encode.py): brute force over every code of the block
 on tiny tensors (the chosen code is a nearest grid point, ties to the lower
@@ -127,12 +129,13 @@ def encode_q4_0(w: np.ndarray) -> np.ndarray:
     return out.reshape(w.shape[:-1] + (row_bytes("q4_0", k),))
 
 
-def encode_q4_k(w: np.ndarray) -> np.ndarray:
-    w2, k = _rows(w, "q4_k")
+def _encode_k_affine(w: np.ndarray, codec: str, qmax: int):
+    """q4_K / q5_K: codes 0..qmax against 6-bit scales and mins (shared steps)."""
+    w2, k = _rows(w, codec)
     x = w2.reshape(w2.shape[0], k // 256, 8, 32)
     lo = np.minimum(F32(0), np.min(x, axis=-1))  # [n, nb, 8]
     hi = np.max(x, axis=-1)
-    scale = _div((hi - lo).astype(F32), F32(15))
+    scale = _div((hi - lo).astype(F32), F32(qmax))
     mins = (-lo).astype(F32)
     dbits = _f16_bits(_div(np.max(scale, axis=-1), F32(63)))
     mbits = _f16_bits(_div(np.max(mins, axis=-1), F32(63)))
@@ -142,28 +145,51 @@ def encode_q4_k(w: np.ndarray) -> np.ndarray:
     m = np.where(DM > 0, np.clip(np.rint(_div(mins, DM)), 0, 63), 0).astype(np.int64)
     S = (D * sc.astype(F32)).astype(F32)[..., None]  # exact: 11 x 6 bits
     MN = (DM * m.astype(F32)).astype(F32)[..., None]
-    q0 = np.clip(np.rint(_div((x + MN).astype(F32), S)), 0, 15)
+    q0 = np.clip(np.rint(_div((x + MN).astype(F32), S)), 0, qmax)
     q0 = np.where(S == 0, 0, q0).astype(np.int64)
 
     def dec(q):
         return ((S * q.astype(F32)).astype(F32) - MN).astype(F32)
 
-    q = np.where(S == 0, 0, _nearest(x, q0, 0, 15, dec))  # [n, nb, 8, 32]
+    q = np.where(S == 0, 0, _nearest(x, q0, 0, qmax, dec))  # [n, nb, 8, 32]
+    return x, k, dbits, mbits, sc, m, q
 
-    out = np.zeros(x.shape[:2] + (144,), dtype=np.uint8)
+
+def _pack_scales(out, dbits, mbits, sc, m):
+    """d, dmin and the 12 packed 6-bit scale/min bytes at [0:16] (q4_K and q5_K)."""
     out[..., 0] = dbits & 255
     out[..., 1] = dbits >> 8
     out[..., 2] = mbits & 255
     out[..., 3] = mbits >> 8
-    s = np.zeros(x.shape[:2] + (12,), dtype=np.int64)
+    s = np.zeros(sc.shape[:-1] + (12,), dtype=np.int64)
     for j in range(4):
         s[..., j] = (sc[..., j] & 63) | ((sc[..., j + 4] >> 4) << 6)
         s[..., j + 4] = (m[..., j] & 63) | ((m[..., j + 4] >> 4) << 6)
         s[..., j + 8] = (sc[..., j + 4] & 15) | ((m[..., j + 4] & 15) << 4)
     out[..., 4:16] = s.astype(np.uint8)
+
+
+def encode_q4_k(w: np.ndarray) -> np.ndarray:
+    x, k, dbits, mbits, sc, m, q = _encode_k_affine(w, "q4_k", 15)
+    out = np.zeros(x.shape[:2] + (144,), dtype=np.uint8)
+    _pack_scales(out, dbits, mbits, sc, m)
     for p in range(4):
         out[..., 16 + 32 * p: 16 + 32 * p + 32] = (q[..., 2 * p, :] | (q[..., 2 * p + 1, :] << 4)).astype(np.uint8)
     return out.reshape(w.shape[:-1] + (row_bytes("q4_k", k),))
+
+
+def encode_q5_k(w: np.ndarray) -> np.ndarray:
+    x, k, dbits, mbits, sc, m, q = _encode_k_affine(w, "q5_k", 31)
+    out = np.zeros(x.shape[:2] + (176,), dtype=np.uint8)
+    _pack_scales(out, dbits, mbits, sc, m)
+    qh = np.zeros(x.shape[:2] + (32,), dtype=np.int64)
+    for j in range(8):
+        qh |= (q[..., j, :] >> 4) << j
+    out[..., 16:48] = qh.astype(np.uint8)
+    for p in range(4):
+        lo, hi = q[..., 2 * p, :] & 15, q[..., 2 * p + 1, :] & 15
+        out[..., 48 + 32 * p: 48 + 32 * p + 32] = (lo | (hi << 4)).astype(np.uint8)
+    return out.reshape(w.shape[:-1] + (row_bytes("q5_k", k),))
 
 
 def encode_q6_k(w: np.ndarray) -> np.ndarray:
@@ -207,6 +233,7 @@ ENCODERS = {
     "q4_0": encode_q4_0,
     "q4_k": encode_q4_k,
     "q6_k": encode_q6_k,
+    "q5_k": encode_q5_k,
 }
 
 
@@ -215,4 +242,4 @@ def quantize(codec: str, w: np.ndarray) -> np.ndarray:
     return ENCODERS[codec](w)
 
 
-assert all(block_bytes(c) == b for c, b in (("q4_k", 144), ("q6_k", 210), ("q8_0", 34), ("q4_0", 18)))
+assert all(block_bytes(c) == b for c, b in (("q4_k", 144), ("q6_k", 210), ("q8_0", 34), ("q4_0", 18), ("q5_k", 176)))

@@ -28,6 +28,8 @@ def test_codec_table_byte_totals():
     assert codecs.GEOMETRY["q6_k"] == (256, 6, 210)
     assert codecs.GEOMETRY["q8_0"] == (32, 8, 34)
     assert codecs.GEOMETRY["q4_0"] == (32, 4, 18)
+    assert codecs.GEOMETRY["q5_k"] == (256, 5, 176)  # the same table's q5_k row
+    assert 2 + 2 + 12 + 32 + 128 == 176              # d, dmin, scales, qh, qs
     # The layout reading must account for every byte of the block.
     assert 2 + 2 + 12 + 128 == 144          # d, dmin, scales, qs
     assert 128 + 64 + 16 + 2 == 210         # ql, qh, scales, d
@@ -75,7 +77,8 @@ def _load_golden(name):
     return codec, np.frombuffer(raw, dtype=np.uint8), values
 
 
-@pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt"])
+@pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt",
+                                  "q5_k_block.txt"])
 @pytest.mark.parametrize("dtype", [np.float32, np.float16])
 def test_golden_hand_decoded_blocks(name, dtype):
     codec, blk, values = _load_golden(name)
@@ -126,6 +129,27 @@ def _hand_pack(codec, rng, nblocks):
             j, l = divmod(v, 32)
             out[:, 16 + 32 * (j // 2) + l] |= (q[:, v] << (4 * (j % 2))).astype(np.uint8)
         return out, dict(d=d, dm=dm, sc=sc, m=m, q=q)
+    if codec == "q5_k":
+        q = rng.integers(0, 32, size=(nblocks, 256))
+        sc = rng.integers(0, 64, size=(nblocks, 8))
+        m = rng.integers(0, 64, size=(nblocks, 8))
+        d = rng.integers(0, 0x7C00, size=nblocks)
+        dm = rng.integers(0, 0x7C00, size=nblocks)
+        out = np.zeros((nblocks, 176), np.uint8)
+        out[:, 0], out[:, 1], out[:, 2], out[:, 3] = d & 255, d >> 8, dm & 255, dm >> 8
+        for j in range(8):  # the 6-bit scale/min packing of q4_K
+            if j < 4:
+                out[:, 4 + j] |= sc[:, j].astype(np.uint8)
+                out[:, 8 + j] |= m[:, j].astype(np.uint8)
+            else:
+                out[:, 12 + (j - 4)] |= ((sc[:, j] & 15) | ((m[:, j] & 15) << 4)).astype(np.uint8)
+                out[:, 4 + (j - 4)] |= ((sc[:, j] >> 4) << 6).astype(np.uint8)
+                out[:, 8 + (j - 4)] |= ((m[:, j] >> 4) << 6).astype(np.uint8)
+        for v in range(256):
+            j, l = divmod(v, 32)
+            out[:, 48 + 32 * (j // 2) + l] |= ((q[:, v] & 15) << (4 * (j % 2))).astype(np.uint8)
+            out[:, 16 + l] |= ((q[:, v] >> 4) << j).astype(np.uint8)
+        return out, dict(d=d, dm=dm, sc=sc, m=m, q=q)
     if codec == "q6_k":
         q = rng.integers(0, 64, size=(nblocks, 256))
         sc = rng.integers(-128, 128, size=(nblocks, 16))
@@ -169,6 +193,7 @@ def _affine(codec, f):
       q8_0 : code q+128 (8 bits), scale d,      bias -128 d
       q4_0 : code q (4 bits),     scale d,      bias -8 d
       q4_K : code q (4 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 32)
+      q5_K : code q (5 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 32)
       q6_K : code q (6 bits),     scale d*sc_j, bias -32 d*sc_j  (groups of 16)
     Evaluated in exact rational arithmetic, rounded to fp32 at the end.
     """
@@ -181,7 +206,7 @@ def _affine(codec, f):
         elif codec == "q4_0":
             d = half(f["d"][i])
             params = [(d, -8 * d, int(q)) for q in f["q"][i]]
-        elif codec == "q4_k":
+        elif codec in ("q4_k", "q5_k"):
             d, dm = half(f["d"][i]), half(f["dm"][i])
             params = [(d * int(f["sc"][i][v // 32]), -dm * int(f["m"][i][v // 32]), int(f["q"][i][v])) for v in range(256)]
         elif codec == "q6_k":
@@ -199,6 +224,10 @@ def test_hand_packed_codes_decode_to_affine_closed_form(codec):
     # fields decoded by the oracle match what was packed
     if codec == "q4_k":
         d, dmin, sc, m, q = codecs.fields_q4_k(blocks[:, None, :])
+        assert np.array_equal(sc[:, 0], fields["sc"]) and np.array_equal(m[:, 0], fields["m"])
+        assert np.array_equal(q[:, 0].reshape(24, 256), fields["q"])
+    elif codec == "q5_k":
+        d, dmin, sc, m, q = codecs.fields_q5_k(blocks[:, None, :])
         assert np.array_equal(sc[:, 0], fields["sc"]) and np.array_equal(m[:, 0], fields["m"])
         assert np.array_equal(q[:, 0].reshape(24, 256), fields["q"])
     elif codec == "q6_k":

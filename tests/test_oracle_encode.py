@@ -25,6 +25,10 @@ def _all_codes_block(codec, blk, c):
         b[..., 2:18] = np.uint8(c | (c << 4))
     elif codec == "q4_k":
         b[..., 16:144] = np.uint8(c | (c << 4))
+    elif codec == "q5_k":
+        lo, h1 = c & 15, c >> 4
+        b[..., 16:48] = np.uint8(255 * h1)
+        b[..., 48:176] = np.uint8(lo | (lo << 4))
     elif codec == "q6_k":
         lo, h2 = c & 15, c >> 4
         b[..., 0:128] = np.uint8(lo | (lo << 4))
@@ -32,7 +36,8 @@ def _all_codes_block(codec, blk, c):
     return b
 
 
-CODE_RANGE = {"q8_0": range(-128, 128), "q4_0": range(16), "q4_k": range(16), "q6_k": range(64)}
+CODE_RANGE = {"q8_0": range(-128, 128), "q4_0": range(16), "q4_k": range(16), "q6_k": range(64),
+              "q5_k": range(32)}
 
 
 def _codes(codec, blk):
@@ -42,6 +47,8 @@ def _codes(codec, blk):
         return codecs.fields_q4_0(blk)[1].reshape(blk.shape[0], -1)
     if codec == "q4_k":
         return codecs.fields_q4_k(blk)[4].reshape(blk.shape[0], -1)
+    if codec == "q5_k":
+        return codecs.fields_q5_k(blk)[4].reshape(blk.shape[0], -1)
     return codecs.fields_q6_k(blk)[2].reshape(blk.shape[0], -1)
 
 
