@@ -235,6 +235,63 @@ def measure_rows(torch, kq):
     del ws, wq, out
     torch.cuda.empty_cache()
     rows += epilogue_rows(torch, kq)
+    rows += q5k_rows(torch, kq)
+    return rows
+
+
+def q5k_rows(torch, kq):
+    """q5_K on the decode GEMV, prefill GEMM and MoE segment shapes."""
+    from gguf_quant_matmul_amd import workloads as W
+
+    rows = []
+    cfg = W.Q5K_GEMV
+    wq = gpu_weights(torch, kq, cfg.codec, cfg.seed, cfg.n, cfg.k, cfg.dist)
+    nb = wq.numel()
+    nc = copies_for(nb)
+    ws = [wq] + [wq.clone() for _ in range(nc - 1)]
+    x = torch.from_numpy(W.gemv_activations(cfg)).cuda()
+    y = torch.empty((cfg.m, cfg.n), dtype=torch.float32, device="cuda")
+    nl = max(nc, 8)
+    g = capture(torch, lambda: [kq.kq_qmv(cfg.codec, ws[i % nc], cfg.n, cfg.k, x, y) for i in range(nl)])
+    ms = time_graph(torch, g, nl, 5)
+    alg = nb + x.numel() * 2 + y.numel() * 4
+    rows.append({"row": "kq_qmv", "workload": cfg.name, "us": round(ms * 1e3, 2), "GB/s": round(alg / ms / 1e6, 1),
+                 "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3), "alg_bytes": alg, "copies": nc})
+    del ws
+    cfg = W.Q5K_GEMM
+    xm = torch.from_numpy(W.gemv_activations(cfg)).cuda()
+    ym = torch.empty((cfg.m, cfg.n), dtype=torch.float16, device="cuda")
+    g = capture(torch, lambda: [kq.kq_qmm(cfg.codec, wq, cfg.n, cfg.k, xm, ym) for _ in range(3)])
+    ms = time_graph(torch, g, 3, 5)
+    flop = 2 * cfg.m * cfg.n * cfg.k
+    rows.append({"row": "kq_qmm", "workload": cfg.name, "us": round(ms * 1e3, 2),
+                 "TFLOP/s": round(flop / ms / 1e9, 1), "mfma_frac": round(flop / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 3)})
+    del wq, xm, ym
+    # the MoE segment workload with q5_K experts
+    c5 = W.CFG5_MOE_SEG
+    we = gpu_weights(torch, kq, "q5_k", c5.seed, c5.n_experts * c5.n, c5.k, "normal")
+    nc = copies_for(we.numel())
+    wes = [we] + [we.clone() for _ in range(nc - 1)]
+    r = W.routing(c5.seed, c5.tokens, c5.top_k, c5.n_experts)
+    xs = torch.from_numpy(W.activations(c5.seed, c5.tokens, c5.k)[r.token_of_row]).cuda()
+    ids = torch.from_numpy(r.sorted_ids.view(np.int32)).cuda()
+    cap = kq.kq_expert_tile_map_capacity(ids.numel(), c5.n_experts)
+    map_ = torch.empty((cap, 3), dtype=torch.int32, device="cuda")
+    counts = torch.empty((1,), dtype=torch.int32, device="cuda")
+    kq.kq_expert_tile_map(ids, c5.n_experts, map_, counts)
+    ys = torch.empty((xs.shape[0], c5.n), dtype=torch.float16, device="cuda")
+    nl = max(nc, 6)
+    gs = capture(torch, lambda: [kq.kq_gather_qmm_seg("q5_k", wes[i % nc], c5.n_experts, c5.n, c5.k, xs, map_,
+                                                      counts, ys) for i in range(nl)])
+    ms = time_graph(torch, gs, nl, 5)
+    alg = we.numel() + xs.numel() * 2 + ys.numel() * 2
+    flop = 2 * xs.shape[0] * c5.n * c5.k
+    rows.append({"row": "kq_gather_qmm_seg", "workload": c5.name.replace("MoE", "q5_K MoE"),
+                 "us": round(ms * 1e3, 2), "GB/s": round(alg / ms / 1e6, 1),
+                 "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3), "TFLOP/s": round(flop / ms / 1e9, 1),
+                 "mfma_frac": round(flop / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 3), "alg_bytes": alg, "copies": nc})
+    del wes, we
+    torch.cuda.empty_cache()
     return rows
 
 

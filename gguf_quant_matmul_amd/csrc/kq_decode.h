@@ -63,6 +63,28 @@ __device__ __forceinline__ void decode8<Q4_K>(const uint8_t* __restrict__ row, i
 }
 
 template <>
+__device__ __forceinline__ void decode8<Q5_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  const uint8_t* blk = row + (v0 / 256) * 176;  // 16-byte aligned: rows are multiples of 176 bytes
+  const int vi = (int)(v0 % 256);
+  const int j = vi / 32, l0 = vi % 32;
+  const u32x4 h = ld_16B(blk);
+  const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
+  uint32_t sc, m;
+  q4k_scale_min(h.y, h.z, h.w, j, sc, m);
+  const float dsc = d * (float)sc;   // exact
+  const float dm = dmin * (float)m;  // exact
+  const u32x2 c = *(const u32x2*)(blk + 48 + 32 * (j / 2) + l0);
+  const u32x2 hb = *(const u32x2*)(blk + 16 + l0);
+  const int sh = (j & 1) ? 4 : 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo = (((i < 4 ? c.x : c.y) >> (8 * (i & 3) + sh))) & 15u;
+    const uint32_t hi = (((i < 4 ? hb.x : hb.y) >> (8 * (i & 3) + j))) & 1u;
+    out[i] = dsc * (float)(lo | (hi << 4)) - dm;  // one rounding
+  }
+}
+
+template <>
 __device__ __forceinline__ void decode8<Q6_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
   const uint8_t* blk = row + (v0 / 256) * 210;
   const int vi = (int)(v0 % 256);

@@ -2,7 +2,7 @@
 //
 // mlx-kquant bindings.cpp page, dequantize docstring.  Each value is the
 // codec formula evaluated exactly and rounded once to float32:
-//   q4_K  (d*sc)*q - dmin*m : d*sc (<= 17 bits) and (d*sc)*q (<= 21 bits)
+//   q4_K, q5_K  (d*sc)*q - dmin*m : d*sc (<= 17 bits) and (d*sc)*q (<= 22 bits)
 //         and dmin*m are exact in float32, so the subtraction is the only
 //         rounding (an FMA gives the same bits);
 //   q6_K  (d*sc)*(q-32), q8_0 d*q, q4_0 d*(q-8): exact products.
@@ -66,6 +66,7 @@ hipError_t launch_dequantize(int codec, const uint8_t* w, int64_t rows, int64_t 
     case Q4_0: return launch_c<Q4_0>(w, rows, k, rb, out, f16, s);
     case Q8_0: return launch_c<Q8_0>(w, rows, k, rb, out, f16, s);
     case Q4_K: return launch_c<Q4_K>(w, rows, k, rb, out, f16, s);
+    case Q5_K: return launch_c<Q5_K>(w, rows, k, rb, out, f16, s);
     case Q6_K: return launch_c<Q6_K>(w, rows, k, rb, out, f16, s);
   }
   return hipErrorInvalidValue;

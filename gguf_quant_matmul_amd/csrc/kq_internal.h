@@ -8,6 +8,9 @@
 //   q4_K 144 B: [0:2] d, [2:4] dmin, [4:16] twelve bytes of 6-bit (sc, m)
 //         pairs, [16:144] qs; sub-block j = v/32, byte qs[32*(j/2) + v%32],
 //         low nibble for even j; value = (d*sc_j)*q - dmin*m_j
+//   q5_K 176 B: [0:16] as q4_K, [16:48] qh, [48:176] qs; the low four bits
+//         as q4_K's nibbles (at qs), the fifth bit of value l of sub-block j
+//         is bit j of qh[l]; value = (d*sc_j)*q - dmin*m_j, q in 0..31
 //   q6_K 210 B: [0:128] ql, [128:192] qh, [192:208] int8 scales, [208:210] d;
 //         v -> h=v/128, c=(v%128)/32, l=v%32: low 4 bits from
 //         ql[64h + l + 32(c&1)] (low nibble if c<2), high 2 bits
@@ -19,15 +22,17 @@
 
 namespace kq {
 
-enum Codec : int { Q4_0 = 2, Q8_0 = 8, Q4_K = 12, Q6_K = 14 };
+enum Codec : int { Q4_0 = 2, Q8_0 = 8, Q4_K = 12, Q5_K = 13, Q6_K = 14 };
 
 template <int C> struct Geo;
 template <> struct Geo<Q4_0> { static constexpr int BV = 32;  static constexpr int BB = 18; };
 template <> struct Geo<Q8_0> { static constexpr int BV = 32;  static constexpr int BB = 34; };
 template <> struct Geo<Q4_K> { static constexpr int BV = 256; static constexpr int BB = 144; };
+template <> struct Geo<Q5_K> { static constexpr int BV = 256; static constexpr int BB = 176; };
 template <> struct Geo<Q6_K> { static constexpr int BV = 256; static constexpr int BB = 210; };
 
 static_assert(Geo<Q4_K>::BB == 2 + 2 + 12 + 128, "q4_K superblock bytes");
+static_assert(Geo<Q5_K>::BB == 2 + 2 + 12 + 32 + 128, "q5_K superblock bytes");
 static_assert(Geo<Q6_K>::BB == 128 + 64 + 16 + 2, "q6_K superblock bytes");
 static_assert(Geo<Q8_0>::BB == 2 + 32 && Geo<Q4_0>::BB == 2 + 16, "block bytes");
 

@@ -113,6 +113,46 @@ template <> struct HalfUnit<Q4_K> {
   }
 };
 
+template <> struct HalfUnit<Q5_K> {
+  // q4_K's half unit with 5-bit codes: the fifth bits of positions l in
+  // [16hh, 16hh+16) are bits 2P (sub-block 2P) and 2P + 1 of qh[l].
+  u32x4 h, q, e;
+  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
+    const uint8_t* blk = row + (u >> 2) * 176;
+    h = ld_16B(blk);
+    e = ld_16B(blk + 16 + 16 * hh);
+    q = ld_16B(blk + 48 + 32 * (u & 3) + 16 * hh);
+  }
+  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+    const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3), sc0, m0);
+    q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3) + 1, sc1, m1);
+    // as q4_K: fma((1024 + q), s, -(1024 s + dmin m)) rounded once to float16
+    const float s0 = d * (float)sc0, c0 = -(1024.f * s0 + dmin * (float)m0);
+    const float s1 = d * (float)sc1, c1 = -(1024.f * s1 + dmin * (float)m1);
+    const uint32_t qw[4] = {q.x, q.y, q.z, q.w}, qe[4] = {e.x, e.y, e.z, e.w};
+    const int j0 = 2 * (u & 3);
+    uint32_t lo[8], hi[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qhs = qe[i] >> j0;
+      const uint32_t l = (qw[i] & 0x0F0F0F0Fu) | ((qhs << 4) & 0x10101010u);
+      const uint32_t t = ((qw[i] >> 4) & 0x0F0F0F0Fu) | ((qhs << 3) & 0x10101010u);
+      const half2_t l01 = as_h2(pair01(l)), l23 = as_h2(pair23(l));
+      const half2_t t01 = as_h2(pair01(t)), t23 = as_h2(pair23(t));
+      lo[2 * i] = pack_h2(fmaf((float)l01.x, s0, c0), fmaf((float)l01.y, s0, c0));
+      lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, s0, c0), fmaf((float)l23.y, s0, c0));
+      hi[2 * i] = pack_h2(fmaf((float)t01.x, s1, c1), fmaf((float)t01.y, s1, c1));
+      hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, s1, c1), fmaf((float)t23.y, s1, c1));
+    }
+    st_chunk(dst, sw, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    st_chunk(dst, sw, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
+    st_chunk(dst, sw, 4 + 2 * hh, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    st_chunk(dst, sw, 5 + 2 * hh, u32x4{hi[4], hi[5], hi[6], hi[7]});
+  }
+};
+
 template <> struct HalfUnit<Q6_K> {
   // unit u = (superblock s, h, half); half hh takes c = hh (low nibbles) and
   // c = hh + 2 (high nibbles) of ql[64h + 32hh + 16half + i].
@@ -551,6 +591,7 @@ hipError_t launch_pass(int codec, const uint8_t* w, int64_t n, int64_t k, int64_
     case Q4_0: return launch_dense<Q4_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q8_0: return launch_dense<Q8_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q4_K: return launch_dense<Q4_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q5_K: return launch_dense<Q5_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q6_K: return launch_dense<Q6_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
   }
   return hipErrorInvalidValue;
@@ -596,6 +637,7 @@ hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t ne, int64_
       case Q4_0: return launch_generic<Q4_0, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q8_0: return launch_generic<Q8_0, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q4_K: return launch_generic<Q4_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+      case Q5_K: return launch_generic<Q5_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q6_K: return launch_generic<Q6_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
     }
     return hipErrorInvalidValue;

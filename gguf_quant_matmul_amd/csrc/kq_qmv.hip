@@ -598,6 +598,7 @@ hipError_t launch_fused(int codec, const uint8_t* w, const uint8_t* w2, int64_t 
     case Q4_0: return launch_fused_c<Q4_0>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q8_0: return launch_fused_c<Q8_0>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q4_K: return launch_fused_c<Q4_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
+    case Q5_K: return launch_fused_c<Q5_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q6_K: return launch_fused_c<Q6_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
   }
   return hipErrorInvalidValue;
@@ -682,6 +683,7 @@ hipError_t launch_gather_qmv(int codec, const uint8_t* w, int64_t n_experts, int
     case Q4_0: return launch_gather_c<Q4_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q8_0: return launch_gather_c<Q8_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q4_K: return launch_gather_c<Q4_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+    case Q5_K: return launch_gather_c<Q5_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q6_K: return launch_gather_c<Q6_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
   }
   return hipErrorInvalidValue;
@@ -697,6 +699,8 @@ hipError_t launch_moe_glu_gather(int codec, const uint8_t* gate_w, const uint8_t
       return launch_glu_c<Q8_0>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
     case Q4_K:
       return launch_glu_c<Q4_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
+    case Q5_K:
+      return launch_glu_c<Q5_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
     case Q6_K:
       return launch_glu_c<Q6_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
   }
@@ -721,6 +725,7 @@ hipError_t launch_qmv(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t
     case Q4_0: return launch_c<Q4_0>(w, n, k, rb, x, m, y, f16, s);
     case Q8_0: return launch_c<Q8_0>(w, n, k, rb, x, m, y, f16, s);
     case Q4_K: return launch_c<Q4_K>(w, n, k, rb, x, m, y, f16, s);
+    case Q5_K: return launch_c<Q5_K>(w, n, k, rb, x, m, y, f16, s);
     case Q6_K: return launch_c<Q6_K>(w, n, k, rb, x, m, y, f16, s);
   }
   return hipErrorInvalidValue;

@@ -12,13 +12,14 @@
 //          d = f16(max scale/63), dmin = f16(max min/63);
 //          sc = rint(scale/D), m = rint(min/DM) (0..63);
 //          q = rint((w + DM*m)/(D*sc))
+//   q5_K : as q4_K with scale = (hi - lo)/31 and q in 0..31
 //   q6_K : per 16 values scale = amax/31; d = f16(max scale/127);
 //          sc = rint(scale/D) (-128..127); q = rint(w/(D*sc)) + 32
 // Codes are clamped to the codec's range, then moved to the nearest point of
 // the block's decoded grid among q-1, q, q+1 (distance |w - decode(q)| in
 // float64, ties to the lower code).  A zero grid step gives the zero-point
-// code (q8_0 0, q4_0 8, q4_K 0, q6_K 32).  One thread per block (q8_0, q4_0)
-// or superblock (q4_K, q6_K); not a hot path.
+// code (q8_0 0, q4_0 8, q4_K and q5_K 0, q6_K 32).  One thread per block
+// (q8_0, q4_0) or superblock (q4_K, q5_K, q6_K); not a hot path.
 #include "kq_internal.h"
 
 #pragma clang fp contract(off)
@@ -95,8 +96,14 @@ __global__ __launch_bounds__(256) void quant_q4_0(const float* __restrict__ w, i
     st_u16(o + 2 + i, (uint32_t)(q[i] | (q[i + 16] << 4)) | ((uint32_t)(q[i + 1] | (q[i + 17] << 4)) << 8));
 }
 
-__global__ __launch_bounds__(256) void quant_q4_k(const float* __restrict__ w, int64_t nsb, int kb, int64_t row_bytes,
-                                                  uint8_t* __restrict__ out) {
+// q4_K (QMAX 15, 144-byte superblocks) and q5_K (QMAX 31, 176 bytes: the
+// same header, then qh[32] with bit j of qh[l] the fifth bit of value l of
+// sub-block j, then the low nibbles laid out as q4_K's qs)
+template <int QMAX>
+__global__ __launch_bounds__(256) void quant_k_affine(const float* __restrict__ w, int64_t nsb, int kb,
+                                                      int64_t row_bytes, uint8_t* __restrict__ out) {
+  constexpr bool Q5 = QMAX == 31;
+  constexpr int BB = Q5 ? 176 : 144, QS = Q5 ? 48 : 16;
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (g >= nsb) return;
   const int64_t r = g / kb, b = g % kb;
@@ -107,7 +114,7 @@ __global__ __launch_bounds__(256) void quant_q4_k(const float* __restrict__ w, i
     float lo = x[32 * j], hi = x[32 * j];
     for (int i = 1; i < 32; ++i) { lo = fminf(lo, x[32 * j + i]); hi = fmaxf(hi, x[32 * j + i]); }
     lo = fminf(0.f, lo);
-    scale[j] = (hi - lo) / 15.f;
+    scale[j] = (hi - lo) / (float)QMAX;
     mins[j] = -lo;
     smax = j ? fmaxf(smax, scale[j]) : scale[j];
     mmax = j ? fmaxf(mmax, mins[j]) : mins[j];
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(256) void quant_q4_k(const float* __restrict__ w, i
     sc[j] = D > 0.f ? (int)clampf(rintf(scale[j] / D), 0.f, 63.f) : 0;
     m[j] = DM > 0.f ? (int)clampf(rintf(mins[j] / DM), 0.f, 63.f) : 0;
   }
-  uint8_t* o = out + r * row_bytes + b * 144;  // 16-byte aligned
+  uint8_t* o = out + r * row_bytes + b * BB;  // 16-byte aligned
   uint32_t s[12];
   for (int j = 0; j < 4; ++j) {
     s[j] = (uint32_t)((sc[j] & 63) | ((sc[j + 4] >> 4) << 6));
@@ -132,6 +139,8 @@ __global__ __launch_bounds__(256) void quant_q4_k(const float* __restrict__ w, i
   hdr.z = s[4] | (s[5] << 8) | (s[6] << 16) | (s[7] << 24);
   hdr.w = s[8] | (s[9] << 8) | (s[10] << 16) | (s[11] << 24);
   *(u32x4*)o = hdr;
+  uint32_t qh[8];
+  for (int i = 0; i < 8; ++i) qh[i] = 0;
   for (int p = 0; p < 4; ++p) {  // sub-block pair (2p low nibbles, 2p+1 high nibbles)
     uint32_t word[8];
     for (int i = 0; i < 8; ++i) word[i] = 0;
@@ -144,14 +153,19 @@ __global__ __launch_bounds__(256) void quant_q4_k(const float* __restrict__ w, i
           q = 0;
         } else {
           const float v = x[32 * j + l];
-          const int q0 = (int)clampf(rintf((v + MN) / S), 0.f, 15.f);
-          q = nearest(v, q0, 0, 15, [S, MN](int c) { return S * (float)c - MN; });
+          const int q0 = (int)clampf(rintf((v + MN) / S), 0.f, (float)QMAX);
+          q = nearest(v, q0, 0, QMAX, [S, MN](int c) { return S * (float)c - MN; });
         }
-        word[l >> 2] |= (uint32_t)q << (8 * (l & 3) + 4 * half);
+        word[l >> 2] |= (uint32_t)(q & 15) << (8 * (l & 3) + 4 * half);
+        if (Q5) qh[l >> 2] |= (uint32_t)(q >> 4) << (8 * (l & 3) + j);
       }
     }
-    *(u32x4*)(o + 16 + 32 * p) = u32x4{word[0], word[1], word[2], word[3]};
-    *(u32x4*)(o + 16 + 32 * p + 16) = u32x4{word[4], word[5], word[6], word[7]};
+    *(u32x4*)(o + QS + 32 * p) = u32x4{word[0], word[1], word[2], word[3]};
+    *(u32x4*)(o + QS + 32 * p + 16) = u32x4{word[4], word[5], word[6], word[7]};
+  }
+  if (Q5) {
+    *(u32x4*)(o + 16) = u32x4{qh[0], qh[1], qh[2], qh[3]};
+    *(u32x4*)(o + 32) = u32x4{qh[4], qh[5], qh[6], qh[7]};
   }
 }
 
@@ -204,14 +218,15 @@ __global__ __launch_bounds__(256) void quant_q6_k(const float* __restrict__ w, i
 
 hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, int64_t rb, uint8_t* out,
                            hipStream_t s) {
-  const int bv = (codec == Q4_K || codec == Q6_K) ? 256 : 32;
+  const int bv = (codec == Q4_K || codec == Q5_K || codec == Q6_K) ? 256 : 32;
   const int kb = (int)(k / bv);
   const int64_t nblk = rows * kb;
   const dim3 grid((unsigned)((nblk + 255) / 256)), block(256);
   switch (codec) {
     case Q8_0: hipLaunchKernelGGL(quant_q8_0, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q4_0: hipLaunchKernelGGL(quant_q4_0, grid, block, 0, s, w, nblk, kb, rb, out); break;
-    case Q4_K: hipLaunchKernelGGL(quant_q4_k, grid, block, 0, s, w, nblk, kb, rb, out); break;
+    case Q4_K: hipLaunchKernelGGL(quant_k_affine<15>, grid, block, 0, s, w, nblk, kb, rb, out); break;
+    case Q5_K: hipLaunchKernelGGL(quant_k_affine<31>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q6_K: hipLaunchKernelGGL(quant_q6_k, grid, block, 0, s, w, nblk, kb, rb, out); break;
     default: return hipErrorInvalidValue;
   }

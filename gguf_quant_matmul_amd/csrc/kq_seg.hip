@@ -51,6 +51,12 @@ constexpr int SEG_NXCD = 8;
 // CU (two waves per SIMD), so the other one covers what latency two slots
 // leave open.
 template <int C> struct SegSlots { static constexpr int value = 2; };
+// Workgroups per CU the register budget is sized for.  q5_K's units carry
+// the 32 qh bytes as well (20 registers a unit against q4_K's 12): at two
+// waves per SIMD its ring spills, so it takes one wave per SIMD and the whole
+// register file (the 2-slot ring at one wave per SIMD measured within a few
+// percent of two waves for q4_K).
+template <int C> struct SegOcc { static constexpr int value = C == Q5_K ? 1 : 2; };
 
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -145,9 +151,9 @@ __device__ __forceinline__ void seg_tile(const uint8_t* __restrict__ wbase, int 
       const int u = ub + 4 * gg + cu;
       const bool valid = u < ue;                    // else this lane adds zeros
       const int uc = valid ? u : max(ue - 1, ub);  // (and reads in-chunk activations)
-      // q4_K reads only u & 3 (lane-uniform): spelled out, its scale fields'
-      // offsets are computed once outside the loop
-      const int us = C == Q4_K ? 4 * (u >> 2) + cu : uc;
+      // q4_K and q5_K read only u & 3 (lane-uniform): spelled out, their
+      // scale fields' offsets are computed once outside the loop
+      const int us = (C == Q4_K || C == Q5_K) ? 4 * (u >> 2) + cu : uc;
       const half_t* xb = cur + r * SEG_XSTRIDE + xpad(MmaSlices<C>::koff(uc) - c0);
       const MmaSlices<C> sl0(ring[(SEG_GPC * H + gg) % NS][0], us, valid);
       const MmaSlices<C> sl1(ring[(SEG_GPC * H + gg) % NS][1], us, valid);
@@ -208,7 +214,7 @@ __device__ __forceinline__ void seg_tile(const uint8_t* __restrict__ wbase, int 
 }
 
 template <int C, bool F16>
-__global__ __launch_bounds__(SEG_THREADS, 2) void seg_mma_kernel(const uint8_t* __restrict__ w, int n, int k,
+__global__ __launch_bounds__(SEG_THREADS, SegOcc<C>::value) void seg_mma_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                               int64_t row_bytes, int64_t expert_stride, int n_experts,
                                                               const half_t* __restrict__ x, int m_total,
                                                               const uint32_t* __restrict__ map,
@@ -269,6 +275,7 @@ hipError_t launch_seg_mma(int codec, const uint8_t* w, int64_t n_experts, int64_
     case Q4_0: return launch_seg_mma_c<Q4_0>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q8_0: return launch_seg_mma_c<Q8_0>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q4_K: return launch_seg_mma_c<Q4_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
+    case Q5_K: return launch_seg_mma_c<Q5_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q6_K: return launch_seg_mma_c<Q6_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
   }
   return hipErrorInvalidValue;

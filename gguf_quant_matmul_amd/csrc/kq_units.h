@@ -111,6 +111,69 @@ struct UnitQ4K {
   }
 };
 
+// q5_K: q4_K's unit (the 32 qs bytes of sub-block pair P = u % 4) plus the
+// 32 qh bytes, whose bits 2P and 2P + 1 are the fifth bits of the two
+// sub-blocks' values.
+struct UnitQ5K {
+  u32x4 h, q0, q1, e0, e1;
+  __device__ __forceinline__ void load(const uint8_t* row, int u) {
+    const uint8_t* blk = row + (u >> 2) * 176;
+    h = ld_16B(blk);
+    e0 = ld_16B(blk + 16);
+    e1 = ld_16B(blk + 32);
+    const uint8_t* qs = blk + 48 + 32 * (u & 3);
+    q0 = ld_16B(qs);
+    q1 = ld_16B(qs + 16);
+  }
+  __device__ __forceinline__ void bload(rsrc_t rs, int rowoff, int cu, int u4) {
+    const int so = (u4 >> 2) * 176;
+    h = bld16(rs, rowoff, so);
+    e0 = bld16(rs, rowoff + 16, so);
+    e1 = bld16(rs, rowoff + 32, so);
+    q0 = bld16(rs, rowoff + 48 + 32 * cu, so);
+    q1 = bld16(rs, rowoff + 64 + 32 * cu, so);
+  }
+  // 5-bit code bytes of dword i: low nibbles (sub-block 2P) or high (2P + 1)
+  static __device__ __forceinline__ uint32_t lo5(uint32_t qw, uint32_t qhs) {
+    return (qw & 0x0F0F0F0Fu) | ((qhs << 4) & 0x10101010u);
+  }
+  static __device__ __forceinline__ uint32_t hi5(uint32_t qw, uint32_t qhs) {
+    return ((qw >> 4) & 0x0F0F0F0Fu) | ((qhs << 3) & 0x10101010u);
+  }
+  template <int M>
+  __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
+    const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
+    const int j0 = 2 * (u & 3);
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min(h.y, h.z, h.w, j0, sc0, m0);
+    q4k_scale_min(h.y, h.z, h.w, j0 + 1, sc1, m1);
+    const float dsc0 = d * (float)sc0, dm0 = dmin * (float)m0;
+    const float dsc1 = d * (float)sc1, dm1 = dmin * (float)m1;
+    const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    const uint32_t qe[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+    uint32_t lo[16], hi[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t qhs = qe[i] >> j0;
+      const uint32_t l = lo5(qw[i], qhs), hh = hi5(qw[i], qhs);
+      lo[2 * i] = pair01(l); lo[2 * i + 1] = pair23(l);
+      hi[2 * i] = pair01(hh); hi[2 * i + 1] = pair23(hh);
+    }
+    const int base = 64 * u;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float s0 = 0.f, s1 = 0.f;
+      s0 = dot16(lo, xv.pairs(m, base), s0);
+      s0 = dot16(lo + 8, xv.pairs(m, base + 16), s0);
+      s1 = dot16(hi, xv.pairs(m, base + 32), s1);
+      s1 = dot16(hi + 8, xv.pairs(m, base + 48), s1);
+      const float4_t xs = *(const float4_t*)&xv.xsum[m * xv.sstride + ((base - xv.c0) >> 4)];
+      const float x0 = xs.x + xs.y, x1 = xs.z + xs.w;
+      acc[m] += dsc0 * (s0 - 1024.f * x0) - dm0 * x0 + dsc1 * (s1 - 1024.f * x1) - dm1 * x1;
+    }
+  }
+};
+
 // 16 bytes at a 2-byte aligned address: dwords loaded from the dword-aligned
 // address below it, then shifted by (addr & 3) bytes.
 struct Shift16 {
@@ -288,6 +351,7 @@ struct UnitQ4_0 {  // two 18-byte blocks, 36 bytes, dword aligned
 
 template <int C> struct UnitOf;
 template <> struct UnitOf<Q4_K> { typedef UnitQ4K T; };
+template <> struct UnitOf<Q5_K> { typedef UnitQ5K T; };
 template <> struct UnitOf<Q6_K> { typedef UnitQ6K T; };
 template <> struct UnitOf<Q8_0> { typedef UnitQ8_0 T; };
 template <> struct UnitOf<Q4_0> { typedef UnitQ4_0 T; };
@@ -350,6 +414,37 @@ template <> struct MmaSlices<Q4_K> {
       slice8(qw[2 * t] & 0x0F0F0F0Fu, qw[2 * t + 1] & 0x0F0F0F0Fu, s0, c0, f);
     else
       slice8(qw[2 * t] & 0xF0F0F0F0u, qw[2 * t + 1] & 0xF0F0F0F0u, s1, c1, f);
+  }
+};
+
+template <> struct MmaSlices<Q5_K> {
+  // q4_K's slices with 5-bit codes: values 0..31 sub-block 2P (low nibbles,
+  // fifth bit from bit 2P of qh), 32..63 sub-block 2P + 1 (high nibbles, bit
+  // 2P + 1); weight = d sc q - dmin m.  qhs holds qh >> 2P.
+  float s0, c0, s1, c1;
+  uint32_t qw[8], qhs[8];
+  __device__ __forceinline__ MmaSlices(const UnitQ5K& un, int u, bool keep) {
+    const float d = keep ? f16_to_f32(un.h.x) : 0.f, dmin = keep ? f16_to_f32(un.h.x >> 16) : 0.f;
+    uint32_t sc0, m0, sc1, m1;
+    q4k_scale_min_pair(un.h.y, un.h.z, un.h.w, u & 3, sc0, m0, sc1, m1);
+    s0 = d * (float)sc0; c0 = -(1024.f * s0 + dmin * (float)m0);
+    s1 = d * (float)sc1; c1 = -(1024.f * s1 + dmin * (float)m1);
+    qw[0] = un.q0.x; qw[1] = un.q0.y; qw[2] = un.q0.z; qw[3] = un.q0.w;
+    qw[4] = un.q1.x; qw[5] = un.q1.y; qw[6] = un.q1.z; qw[7] = un.q1.w;
+    const int j0 = 2 * (u & 3);
+    qhs[0] = un.e0.x >> j0; qhs[1] = un.e0.y >> j0; qhs[2] = un.e0.z >> j0; qhs[3] = un.e0.w >> j0;
+    qhs[4] = un.e1.x >> j0; qhs[5] = un.e1.y >> j0; qhs[6] = un.e1.z >> j0; qhs[7] = un.e1.w >> j0;
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int t = S & 3;
+    if (S < 4)
+      slice8(UnitQ5K::lo5(qw[2 * t], qhs[2 * t]), UnitQ5K::lo5(qw[2 * t + 1], qhs[2 * t + 1]), s0, c0, f);
+    else
+      slice8(UnitQ5K::hi5(qw[2 * t], qhs[2 * t]), UnitQ5K::hi5(qw[2 * t + 1], qhs[2 * t + 1]), s1, c1, f);
   }
 };
 

@@ -133,6 +133,11 @@ CFG3_Q6K_LMHEAD = GemvConfig("q6_K lm-head GEMV 128256x4096", "q6_k", 128256, 40
 CFG4_Q4K_GEMM = GemvConfig("q4_K prefill GEMM 2048x14336x4096", "q4_k", 14336, 4096, 2048, 3, "normal", "f16")
 
 
+# q5_K on the q4_K decode and prefill shapes (a widening of the codec set; seed 5)
+Q5K_GEMV = GemvConfig("q5_K GEMV 14336x4096 M=1", "q5_k", 14336, 4096, 1, 5, "normal", "f32")
+Q5K_GEMM = GemvConfig("q5_K prefill GEMM 2048x14336x4096", "q5_k", 14336, 4096, 2048, 5, "normal", "f16")
+
+
 @dataclass(frozen=True)
 class MoeConfig:
     name: str

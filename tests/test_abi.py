@@ -37,7 +37,10 @@ def test_codec_registry():
     assert kq.kq_codec_info("q6_k") == (256, 210)
     assert kq.kq_codec_info("q8_0") == (32, 34)
     assert kq.kq_codec_info("q4_0") == (32, 18)
+    assert kq.kq_codec_info("q5_k") == (256, 176)
     assert kq.kq_codec_from_name("Q4_K") == kq.KQ_Q4_K
+    assert kq.kq_codec_from_name("q5_k") == kq.KQ_Q5_K == 13
+    assert kq.kq_row_bytes("q5_k", 4096) == 2816
     assert kq.kq_row_bytes("q6_k", 4096) == 3360
     assert kq.kq_row_bytes("q8_0", 4096) == 4352
     with pytest.raises(kq.KQError) as e:

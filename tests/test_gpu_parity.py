@@ -16,7 +16,8 @@ from oracle import codecs, encode, matmul
 
 pytestmark = pytest.mark.gpu
 
-CODECS = ("q4_k", "q6_k", "q8_0", "q4_0")
+CODECS = ("q4_k", "q6_k", "q8_0", "q4_0", "q5_k")
+SUPER = ("q4_k", "q5_k", "q6_k")  # 256-value superblocks
 
 
 @pytest.fixture(scope="module")
@@ -52,7 +53,7 @@ def _random_wire(codec, n, k, rng):
     w = rng.integers(0, 256, size=(n, rb), dtype=np.uint8)
     bb = codecs.block_bytes(codec)
     blk = w.reshape(n, -1, bb)
-    offs = {"q8_0": [0], "q4_0": [0], "q4_k": [0, 2], "q6_k": [208]}[codec]
+    offs = {"q8_0": [0], "q4_0": [0], "q4_k": [0, 2], "q5_k": [0, 2], "q6_k": [208]}[codec]
     for o in offs:
         hi = blk[..., o + 1]
         bad = (hi & 0x7C) == 0x7C
@@ -66,7 +67,7 @@ def _random_wire(codec, n, k, rng):
 def test_dequantize_bit_exact(kq, codec, out_dtype, kind):
     torch = _torch()
     rng = np.random.default_rng(zlib.crc32(repr((codec, kind)).encode()))
-    k = 256 * 5 if codec in ("q4_k", "q6_k") else 32 * 7
+    k = 256 * 5 if codec in SUPER else 32 * 7
     n = 67
     w = _weights(codec, n, k, 1) if kind == "encoded" else _random_wire(codec, n, k, rng)
     dt = np.float32 if out_dtype == "f32" else np.float16
@@ -115,7 +116,8 @@ def test_dequantize_f16_rounds_via_f32(kq):
     assert np.array_equal(got.view(np.uint16), ref.view(np.uint16))
 
 
-@pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt"])
+@pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt",
+                                  "q5_k_block.txt"])
 def test_dequantize_golden_blocks(kq, name):
     from test_oracle_codecs import _load_golden
 
@@ -140,7 +142,7 @@ def test_dequantize_golden_blocks(kq, name):
 # ---------------------------------------------------------------------------
 
 def _shapes_qmv(codec):
-    if codec in ("q4_k", "q6_k"):
+    if codec in SUPER:
         return [(37, 512), (300, 256 * 17)]   # 17 superblocks: q6_K rows only 2-byte aligned
     return [(37, 96), (300, 4160), (45, 2048 + 32)]  # 96 and 2080: odd block counts -> generic kernel
 
@@ -166,7 +168,7 @@ def test_qmv_parity(kq, codec, m):
 @pytest.mark.parametrize("codec", CODECS)
 def test_qmm_parity(kq, codec):
     torch = _torch()
-    shapes = [(1, 37, 512), (130, 200, 512), (257, 131, 256 * 9 if codec in ("q4_k", "q6_k") else 64 * 9)]
+    shapes = [(1, 37, 512), (130, 200, 512), (257, 131, 256 * 9 if codec in SUPER else 64 * 9)]
     if codec in ("q8_0", "q4_0"):
         shapes.append((70, 40, 96))  # odd block count -> generic kernel
     for m, n, k in shapes:
@@ -185,7 +187,7 @@ def test_qmm_parity(kq, codec):
 # ---------------------------------------------------------------------------
 
 def _epi_shapes(codec):
-    kk = 256 * 9 if codec in ("q4_k", "q6_k") else 64 * 9
+    kk = 256 * 9 if codec in SUPER else 64 * 9
     shapes = [(1, 37, kk), (3, 300, kk), (8, 45, kk), (130, 200, kk), (260, 131, kk)]
     if codec in ("q8_0", "q4_0"):
         shapes += [(4, 45, 2048 + 32), (70, 40, 96)]  # odd block counts: generic kernels
@@ -225,7 +227,7 @@ def test_quantized_matmul_residual_parity(kq, codec):
 @pytest.mark.parametrize("codec", CODECS)
 def test_quantized_matmul_qmv_bias_parity(kq, codec):
     torch = _torch()
-    for n, k in _shapes_qmv(codec) + [(130000, 256 if codec in ("q4_k", "q6_k") else 64)]:
+    for n, k in _shapes_qmv(codec) + [(130000, 256 if codec in SUPER else 64)]:
         w = _weights(codec, n, k, 17 + n)
         x = _x(1, k, n + 3)
         bias = np.random.default_rng(n).standard_normal(n)
@@ -245,7 +247,7 @@ def test_quantized_matmul_glu_parity(kq, codec):
     # above; the activation rounded to y's type before the product.  Gate and
     # up are row slices of one [2N, row_bytes] weight.
     torch = _torch()
-    kk = 256 * 5 if codec in ("q4_k", "q6_k") else 64 * 5
+    kk = 256 * 5 if codec in SUPER else 64 * 5
     shapes = [(1, 48, kk), (2, 304, kk), (3, 96, kk), (5, 48, kk), (8, 112, kk), (130, 208, kk), (257, 96, kk)]
     if codec in ("q8_0", "q4_0"):
         shapes += [(2, 48, 96), (70, 48, 96)]
@@ -394,7 +396,7 @@ def test_gather_qmm_seg_parity(kq, codec):
     # ragged last chunk and N over two 192-row blocks with a ragged tail
     torch = _torch()
     rng = np.random.default_rng(17)
-    kq_ = codec in ("q4_k", "q6_k")
+    kq_ = codec in SUPER
     for e, n, k in ((6, 96, 512 if kq_ else 320), (3, 200, 1280 if kq_ else 1344)):
         ids = np.sort(np.concatenate([rng.integers(0, e - 1, 190), [e - 1] * 3, [e + 2] * 4])).astype(np.uint32)
         rows = ids.size
@@ -415,7 +417,7 @@ def test_gather_qmm_seg_parity(kq, codec):
             assert_close_rows(got[covered], ref[covered], what=f"seg {codec} n={n} k={k}")
 
 
-@pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0"])
+@pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0", "q5_k"])
 def test_gather_seg_tile_boundaries(kq, codec):
     # expert rows 96 (a full tile and a 32-row tail), 97 (a 33-row tail),
     # 133 (two full tiles and a 5-row tail), 64 (one full tile), 20 and one
