@@ -12,8 +12,10 @@ What the pages fix
     uint8 wire bytes whose last dim is a multiple of the codec's bytes per
     block; output float dtype defaults to float16.
   * the same table: q5_k is a 256-value superblock of 5-bit codes in 176
-    bytes ("K-quant superblock"); its layout is not on the pages and takes
-    reading R1 like the others.
+    bytes ("K-quant superblock"); q4_1 32 values, 4 bits, 20 bytes ("block
+    scale + min"); q5_0 32 values, 5 bits, 22 bytes ("block scale"); q5_1 32
+    values, 5 bits, 24 bytes ("block scale + min").  Their layouts are not on
+    the pages and take reading R1 like the others.
   * The q4_K sub-block structure (8 sub-blocks of 32, 6-bit scale and min per
     sub-block, fp16 d and dmin) and the q6_K one (16 sub-blocks of 16, int8
     scales, fp16 d) are stated with the workloads.
@@ -26,9 +28,10 @@ Readings taken where the pages are silent (each is also listed in the design doc)
   R2  fp16 fields are little-endian IEEE binary16, decoded exactly (subnormals
       honoured, the sign of zero kept, inf/NaN passed through).
   R3  Arithmetic: each value is the exact real number of the formula, rounded
-      ONCE to fp32 (RNE).  For q8_0, q4_0 and q6_K the exact value is already
-      an fp32 number.  For q4_K and q5_K the only rounding is that of
-      ``(d*sc)*q - (dmin*m)``.
+      ONCE to fp32 (RNE).  For q8_0, q4_0, q5_0 and q6_K the exact value is
+      already an fp32 number.  For q4_K and q5_K the only rounding is that of
+      ``(d*sc)*q - (dmin*m)``; for q4_1 and q5_1 that of ``d*q + m`` (exact in
+      float64: its bits span at most 2^-24 .. 2^21).
   R4  float16 output is RNE of the fp32 value (so q4_K -> f16 rounds twice, by
       definition).
 
@@ -54,6 +57,9 @@ GEOMETRY = {
     "q8_0": (32, 8, 34),
     "q4_0": (32, 4, 18),
     "q5_k": (256, 5, 176),
+    "q4_1": (32, 4, 20),
+    "q5_0": (32, 5, 22),
+    "q5_1": (32, 5, 24),
 }
 
 CODECS = tuple(GEOMETRY)
@@ -145,6 +151,27 @@ def fields_q4_0(blk: np.ndarray):
     qs = blk[..., 2:18].astype(np.int64)  # [n, nb, 16]
     q = np.concatenate([qs & 15, qs >> 4], axis=-1)  # [n, nb, 32]
     return d, q
+
+
+def fields_legacy(codec: str, blk: np.ndarray):
+    """q4_1 (20 B: d, m, qs[16]), q5_0 (22 B: d, qh[4], qs[16]), q5_1 (24 B:
+    d, m, qh[4], qs[16]); d and m fp16, qh a little-endian uint32.
+
+    Value v < 16 is the low nibble of qs[v], v >= 16 the high nibble of
+    qs[v - 16]; for the 5-bit codecs bit v of qh is its fifth bit.
+    value = d*q + m (q4_1, q5_1) or d*(q - 16) (q5_0).  Returns d, m (None
+    for q5_0) and q [.., 32].
+    """
+    d = f16_bits_to_f64(le_u16(blk[..., 0], blk[..., 1]))
+    m = f16_bits_to_f64(le_u16(blk[..., 2], blk[..., 3])) if codec in ("q4_1", "q5_1") else None
+    o = {"q4_1": 4, "q5_0": 6, "q5_1": 8}[codec]
+    qs = blk[..., o:o + 16].astype(np.int64)
+    q = np.concatenate([qs & 15, qs >> 4], axis=-1)  # [.., 32]
+    if codec != "q4_1":
+        h = o - 4
+        qh = sum(blk[..., h + i].astype(np.int64) << (8 * i) for i in range(4))
+        q = q | (((qh[..., None] >> np.arange(32)) & 1) << 4)
+    return d, m, q
 
 
 def scale_min_q4_k(s: np.ndarray):
@@ -264,6 +291,12 @@ def dequantize(codec: str, w: np.ndarray, k: int, dtype=np.float32) -> np.ndarra
             d, scales, q = fields_q6_k(blk)
             step = d[..., None] * scales  # [n, nb, 16], exact in float64
             y = _exact_f32(np.repeat(step, 16, axis=-1) * (q - 32))
+        elif codec in ("q4_1", "q5_1"):
+            d, m, q = fields_legacy(codec, blk)
+            y = (d[..., None] * q + m[..., None]).astype(np.float32)  # exact in float64, one rounding
+        elif codec == "q5_0":
+            d, _, q = fields_legacy(codec, blk)
+            y = _exact_f32(d[..., None] * (q - 16))
         elif codec in ("q4_k", "q5_k"):
             d, dmin, sc, m, q = fields_q4_k(blk) if codec == "q4_k" else fields_q5_k(blk)
             a = _exact_f32(d[..., None, None] * sc[..., None] * q)  # (d*sc)*q, exact

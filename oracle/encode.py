@@ -16,6 +16,9 @@ the same bytes.  ``rint`` rounds half to even; ``f16()`` is RNE to binary16.
 
   q8_0 : d = f16(amax/127); q = rint(w/D)                      (D = float(d))
   q4_0 : d = f16(amax/7);   q = rint(w/D) + 8
+  q4_1 : d = f16((max w - min w)/15), m = f16(min w); q = rint((w - M)/D)
+  q5_0 : d = f16(amax/15);  q = rint(w/D) + 16
+  q5_1 : d = f16((max w - min w)/31), m = f16(min w); q = rint((w - M)/D)
   q4_K : per 32-value sub-block j: lo = min(0, min w), hi = max(w),
          scale_j = (hi - lo)/15, min_j = -lo;
          d = f16(max_j scale_j / 63), dmin = f16(max_j min_j / 63);
@@ -30,7 +33,8 @@ Codes are clamped to the codec's range.  Then each code is moved to the
 NEAREST point of the block's decoded grid among {q-1, q, q+1} (distance
 |w - decode(q)| taken in float64; ties go to the lower code), so that every
 code is the nearest grid point.  Where the grid step is zero the code is the
-zero-point code (q8_0: 0, q4_0: 8, q4_K and q5_K: 0, q6_K: 32).
+zero-point code (q8_0: 0, q4_0: 8, q4_1 and q5_1: 0, q5_0: 16, q4_K and
+q5_K: 0, q6_K: 32).
 
 Pins (tests/test_oracle_encode.py): brute force over every code of the block
 on tiny tensors (the chosen code is a nearest grid point, ties to the lower
@@ -127,6 +131,66 @@ def encode_q4_0(w: np.ndarray) -> np.ndarray:
     out[..., 1] = dbits >> 8
     out[..., 2:] = (q[..., :16] | (q[..., 16:] << 4)).astype(np.uint8)
     return out.reshape(w.shape[:-1] + (row_bytes("q4_0", k),))
+
+
+def _legacy_pack(codec, dbits, mbits, q):
+    """Blocks of the legacy layouts (d, [m], [qh], qs) from codes q [.., 32]."""
+    bb = block_bytes(codec)
+    out = np.zeros(q.shape[:-1] + (bb,), dtype=np.uint8)
+    out[..., 0] = dbits & 255
+    out[..., 1] = dbits >> 8
+    o = 2
+    if mbits is not None:
+        out[..., 2] = mbits & 255
+        out[..., 3] = mbits >> 8
+        o = 4
+    if codec != "q4_1":
+        qh = np.zeros(q.shape[:-1], dtype=np.int64)
+        for v in range(32):
+            qh |= (q[..., v] >> 4) << v
+        for i in range(4):
+            out[..., o + i] = (qh >> (8 * i)) & 255
+        o += 4
+    out[..., o:o + 16] = ((q[..., :16] & 15) | ((q[..., 16:] & 15) << 4)).astype(np.uint8)
+    return out
+
+
+def encode_affine_min(w: np.ndarray, codec: str) -> np.ndarray:
+    """q4_1 / q5_1: codes 0..qmax against the block minimum."""
+    qmax = 15 if codec == "q4_1" else 31
+    w2, k = _rows(w, codec)
+    x = w2.reshape(w2.shape[0], k // 32, 32)
+    lo, hi = np.min(x, axis=-1), np.max(x, axis=-1)
+    dbits = _f16_bits(_div((hi - lo).astype(F32), F32(qmax)))
+    mbits = _f16_bits(lo)
+    D = _f16_value(dbits)[..., None]
+    M = _f16_value(mbits)[..., None]
+    q0 = np.clip(np.rint(_div((x - M).astype(F32), D)), 0, qmax)
+    q0 = np.where(D == 0, 0, q0).astype(np.int64)
+
+    def dec(q):
+        return ((D * q.astype(F32)).astype(F32) + M).astype(F32)
+
+    q = np.where(D == 0, 0, _nearest(x, q0, 0, qmax, dec))
+    out = _legacy_pack(codec, dbits, mbits, q)
+    return out.reshape(w.shape[:-1] + (row_bytes(codec, k),))
+
+
+def encode_q5_0(w: np.ndarray) -> np.ndarray:
+    w2, k = _rows(w, "q5_0")
+    x = w2.reshape(w2.shape[0], k // 32, 32)
+    amax = np.max(np.abs(x), axis=-1)
+    dbits = _f16_bits(_div(amax, F32(15)))
+    D = _f16_value(dbits)[..., None]
+    q0 = np.clip(np.rint(_div(x, D)) + 16, 0, 31)
+    q0 = np.where(D == 0, 16, q0).astype(np.int64)
+
+    def dec(q):
+        return (D * (q - 16).astype(F32)).astype(F32)
+
+    q = np.where(D == 0, 16, _nearest(x, q0, 0, 31, dec))
+    out = _legacy_pack("q5_0", dbits, None, q)
+    return out.reshape(w.shape[:-1] + (row_bytes("q5_0", k),))
 
 
 def _encode_k_affine(w: np.ndarray, codec: str, qmax: int):
@@ -234,6 +298,9 @@ ENCODERS = {
     "q4_k": encode_q4_k,
     "q6_k": encode_q6_k,
     "q5_k": encode_q5_k,
+    "q4_1": lambda w: encode_affine_min(w, "q4_1"),
+    "q5_0": encode_q5_0,
+    "q5_1": lambda w: encode_affine_min(w, "q5_1"),
 }
 
 
@@ -242,4 +309,5 @@ def quantize(codec: str, w: np.ndarray) -> np.ndarray:
     return ENCODERS[codec](w)
 
 
-assert all(block_bytes(c) == b for c, b in (("q4_k", 144), ("q6_k", 210), ("q8_0", 34), ("q4_0", 18), ("q5_k", 176)))
+assert all(block_bytes(c) == b for c, b in (("q4_k", 144), ("q6_k", 210), ("q8_0", 34), ("q4_0", 18), ("q5_k", 176),
+                                              ("q4_1", 20), ("q5_0", 22), ("q5_1", 24)))

@@ -30,6 +30,9 @@ def test_codec_table_byte_totals():
     assert codecs.GEOMETRY["q4_0"] == (32, 4, 18)
     assert codecs.GEOMETRY["q5_k"] == (256, 5, 176)  # the same table's q5_k row
     assert 2 + 2 + 12 + 32 + 128 == 176              # d, dmin, scales, qh, qs
+    assert codecs.GEOMETRY["q4_1"] == (32, 4, 20) and 2 + 2 + 16 == 20          # d, m, qs
+    assert codecs.GEOMETRY["q5_0"] == (32, 5, 22) and 2 + 4 + 16 == 22          # d, qh, qs
+    assert codecs.GEOMETRY["q5_1"] == (32, 5, 24) and 2 + 2 + 4 + 16 == 24      # d, m, qh, qs
     # The layout reading must account for every byte of the block.
     assert 2 + 2 + 12 + 128 == 144          # d, dmin, scales, qs
     assert 128 + 64 + 16 + 2 == 210         # ql, qh, scales, d
@@ -78,7 +81,7 @@ def _load_golden(name):
 
 
 @pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt",
-                                  "q5_k_block.txt"])
+                                  "q5_k_block.txt", "q4_1_block.txt", "q5_0_block.txt", "q5_1_block.txt"])
 @pytest.mark.parametrize("dtype", [np.float32, np.float16])
 def test_golden_hand_decoded_blocks(name, dtype):
     codec, blk, values = _load_golden(name)
@@ -129,6 +132,24 @@ def _hand_pack(codec, rng, nblocks):
             j, l = divmod(v, 32)
             out[:, 16 + 32 * (j // 2) + l] |= (q[:, v] << (4 * (j % 2))).astype(np.uint8)
         return out, dict(d=d, dm=dm, sc=sc, m=m, q=q)
+    if codec in ("q4_1", "q5_0", "q5_1"):
+        bits = 4 if codec == "q4_1" else 5
+        q = rng.integers(0, 1 << bits, size=(nblocks, 32))
+        d = rng.integers(0, 0x7C00, size=nblocks) | (rng.integers(0, 2, size=nblocks) << 15)
+        mm = rng.integers(0, 0x7C00, size=nblocks) | (rng.integers(0, 2, size=nblocks) << 15)
+        out = np.zeros((nblocks, codecs.block_bytes(codec)), np.uint8)
+        out[:, 0], out[:, 1] = d & 255, d >> 8
+        o = 2
+        if codec != "q5_0":
+            out[:, 2], out[:, 3] = mm & 255, mm >> 8
+            o = 4
+        if bits == 5:  # fifth bits: bit v of the little-endian uint32 at o
+            for v in range(32):
+                out[:, o + v // 8] |= ((q[:, v] >> 4) << (v % 8)).astype(np.uint8)
+            o += 4
+        for v in range(32):
+            out[:, o + (v % 16)] |= ((q[:, v] & 15) << (4 * (v // 16))).astype(np.uint8)
+        return out, dict(d=d, m=mm, q=q)
     if codec == "q5_k":
         q = rng.integers(0, 32, size=(nblocks, 256))
         sc = rng.integers(0, 64, size=(nblocks, 8))
@@ -194,6 +215,9 @@ def _affine(codec, f):
       q4_0 : code q (4 bits),     scale d,      bias -8 d
       q4_K : code q (4 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 32)
       q5_K : code q (5 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 32)
+      q4_1 : code q (4 bits),     scale d,      bias m
+      q5_0 : code q (5 bits),     scale d,      bias -16 d
+      q5_1 : code q (5 bits),     scale d,      bias m
       q6_K : code q (6 bits),     scale d*sc_j, bias -32 d*sc_j  (groups of 16)
     Evaluated in exact rational arithmetic, rounded to fp32 at the end.
     """
@@ -206,6 +230,12 @@ def _affine(codec, f):
         elif codec == "q4_0":
             d = half(f["d"][i])
             params = [(d, -8 * d, int(q)) for q in f["q"][i]]
+        elif codec in ("q4_1", "q5_1"):
+            d, mm = half(f["d"][i]), half(f["m"][i])
+            params = [(d, mm, int(q)) for q in f["q"][i]]
+        elif codec == "q5_0":
+            d = half(f["d"][i])
+            params = [(d, -16 * d, int(q)) for q in f["q"][i]]
         elif codec in ("q4_k", "q5_k"):
             d, dm = half(f["d"][i]), half(f["dm"][i])
             params = [(d * int(f["sc"][i][v // 32]), -dm * int(f["m"][i][v // 32]), int(f["q"][i][v])) for v in range(256)]
@@ -230,6 +260,9 @@ def test_hand_packed_codes_decode_to_affine_closed_form(codec):
         d, dmin, sc, m, q = codecs.fields_q5_k(blocks[:, None, :])
         assert np.array_equal(sc[:, 0], fields["sc"]) and np.array_equal(m[:, 0], fields["m"])
         assert np.array_equal(q[:, 0].reshape(24, 256), fields["q"])
+    elif codec in ("q4_1", "q5_0", "q5_1"):
+        d, m, q = codecs.fields_legacy(codec, blocks[:, None, :])
+        assert np.array_equal(q[:, 0], fields["q"])
     elif codec == "q6_k":
         d, scales, q = codecs.fields_q6_k(blocks[:, None, :])
         assert np.array_equal(scales[:, 0], fields["sc"]) and np.array_equal(q[:, 0], fields["q"])
