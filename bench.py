@@ -235,16 +235,14 @@ def measure_rows(torch, kq):
     del ws, wq, out
     torch.cuda.empty_cache()
     rows += epilogue_rows(torch, kq)
-    rows += q5k_rows(torch, kq)
+    rows += codec_rows(torch, kq)
     return rows
 
 
-def q5k_rows(torch, kq):
-    """q5_K on the decode GEMV, prefill GEMM and MoE segment shapes."""
+def cold_gemv_row(torch, kq, cfg):
+    """One GEMV workload over rotated weight copies; returns (row, weights)."""
     from gguf_quant_matmul_amd import workloads as W
 
-    rows = []
-    cfg = W.Q5K_GEMV
     wq = gpu_weights(torch, kq, cfg.codec, cfg.seed, cfg.n, cfg.k, cfg.dist)
     nb = wq.numel()
     nc = copies_for(nb)
@@ -255,9 +253,22 @@ def q5k_rows(torch, kq):
     g = capture(torch, lambda: [kq.kq_qmv(cfg.codec, ws[i % nc], cfg.n, cfg.k, x, y) for i in range(nl)])
     ms = time_graph(torch, g, nl, 5)
     alg = nb + x.numel() * 2 + y.numel() * 4
-    rows.append({"row": "kq_qmv", "workload": cfg.name, "us": round(ms * 1e3, 2), "GB/s": round(alg / ms / 1e6, 1),
-                 "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3), "alg_bytes": alg, "copies": nc})
     del ws
+    return {"row": "kq_qmv", "workload": cfg.name, "us": round(ms * 1e3, 2), "GB/s": round(alg / ms / 1e6, 1),
+            "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3), "alg_bytes": alg, "copies": nc}, wq
+
+
+def codec_rows(torch, kq):
+    """q5_K on the decode GEMV, prefill GEMM and MoE segment shapes; the legacy
+    32-value codecs on the 14336x4096 GEMV."""
+    from gguf_quant_matmul_amd import workloads as W
+
+    rows = []
+    for cfg in W.LEGACY_GEMV:
+        r, _ = cold_gemv_row(torch, kq, cfg)
+        rows.append(r)
+    r, wq = cold_gemv_row(torch, kq, W.Q5K_GEMV)
+    rows.append(r)
     cfg = W.Q5K_GEMM
     xm = torch.from_numpy(W.gemv_activations(cfg)).cuda()
     ym = torch.empty((cfg.m, cfg.n), dtype=torch.float16, device="cuda")

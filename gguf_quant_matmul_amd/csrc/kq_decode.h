@@ -42,6 +42,40 @@ __device__ __forceinline__ void decode8<Q4_0>(const uint8_t* __restrict__ row, i
   }
 }
 
+// q4_1, q5_0, q5_1: d*q + m by one fma (the exact value rounded once), or
+// d*(q - 16) (exact)
+template <int C>
+__device__ __forceinline__ void decode8_leg(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  using L = Leg<C>;
+  const uint8_t* blk = row + (v0 / 32) * L::BB;  // 2-byte aligned
+  const int vb = (int)(v0 % 32);
+  const float d = f16_to_f32(ld_u16(blk));
+  const float m = L::MIN ? f16_to_f32(ld_u16(blk + 2)) : 0.f;
+  const uint32_t qh = L::QH >= 0 ? (ld_u16(blk + (L::QH >= 0 ? L::QH : 0)) |
+                                    (ld_u16(blk + (L::QH >= 0 ? L::QH : 0) + 2) << 16))
+                                 : 0u;
+  const u32x2 c = ld8_a2(blk + L::QS + (vb & 15));
+  const int sh = vb >= 16 ? 4 : 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t lo4 = ((i < 4 ? c.x : c.y) >> (8 * (i & 3) + sh)) & 15u;
+    const int q = (int)(lo4 | (((qh >> (vb + i)) & 1u) << 4));
+    out[i] = L::MIN ? fmaf(d, (float)q, m) : d * (float)(q - L::ZP);
+  }
+}
+template <>
+__device__ __forceinline__ void decode8<Q4_1>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  decode8_leg<Q4_1>(row, v0, out);
+}
+template <>
+__device__ __forceinline__ void decode8<Q5_0>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  decode8_leg<Q5_0>(row, v0, out);
+}
+template <>
+__device__ __forceinline__ void decode8<Q5_1>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  decode8_leg<Q5_1>(row, v0, out);
+}
+
 template <>
 __device__ __forceinline__ void decode8<Q4_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
   const uint8_t* blk = row + (v0 / 256) * 144;  // 16-byte aligned: rows are multiples of 144 bytes

@@ -5,7 +5,8 @@
 //   q4_K, q5_K  (d*sc)*q - dmin*m : d*sc (<= 17 bits) and (d*sc)*q (<= 22 bits)
 //         and dmin*m are exact in float32, so the subtraction is the only
 //         rounding (an FMA gives the same bits);
-//   q6_K  (d*sc)*(q-32), q8_0 d*q, q4_0 d*(q-8): exact products.
+//   q6_K  (d*sc)*(q-32), q8_0 d*q, q4_0 d*(q-8), q5_0 d*(q-16): exact products;
+//   q4_1, q5_1  d*q + m: one fma (the exact value rounded once).
 // float16 output is the RNE conversion of that float32 value.
 //
 // One thread produces 8 consecutive values of a row, so each thread's store
@@ -67,6 +68,9 @@ hipError_t launch_dequantize(int codec, const uint8_t* w, int64_t rows, int64_t 
     case Q8_0: return launch_c<Q8_0>(w, rows, k, rb, out, f16, s);
     case Q4_K: return launch_c<Q4_K>(w, rows, k, rb, out, f16, s);
     case Q5_K: return launch_c<Q5_K>(w, rows, k, rb, out, f16, s);
+    case Q4_1: return launch_c<Q4_1>(w, rows, k, rb, out, f16, s);
+    case Q5_0: return launch_c<Q5_0>(w, rows, k, rb, out, f16, s);
+    case Q5_1: return launch_c<Q5_1>(w, rows, k, rb, out, f16, s);
     case Q6_K: return launch_c<Q6_K>(w, rows, k, rb, out, f16, s);
   }
   return hipErrorInvalidValue;

@@ -8,6 +8,10 @@
 //   q4_K 144 B: [0:2] d, [2:4] dmin, [4:16] twelve bytes of 6-bit (sc, m)
 //         pairs, [16:144] qs; sub-block j = v/32, byte qs[32*(j/2) + v%32],
 //         low nibble for even j; value = (d*sc_j)*q - dmin*m_j
+//   q4_1  20 B: [0:2] d, [2:4] m, [4:20] qs (nibbles as q4_0); value = d*q + m
+//   q5_0  22 B: [0:2] d, [2:6] qh (uint32), [6:22] qs; fifth bit of value v
+//         is bit v of qh; value = d*(q-16)
+//   q5_1  24 B: [0:2] d, [2:4] m, [4:8] qh, [8:24] qs; value = d*q + m
 //   q5_K 176 B: [0:16] as q4_K, [16:48] qh, [48:176] qs; the low four bits
 //         as q4_K's nibbles (at qs), the fifth bit of value l of sub-block j
 //         is bit j of qh[l]; value = (d*sc_j)*q - dmin*m_j, q in 0..31
@@ -22,11 +26,14 @@
 
 namespace kq {
 
-enum Codec : int { Q4_0 = 2, Q8_0 = 8, Q4_K = 12, Q5_K = 13, Q6_K = 14 };
+enum Codec : int { Q4_0 = 2, Q4_1 = 3, Q5_0 = 6, Q5_1 = 7, Q8_0 = 8, Q4_K = 12, Q5_K = 13, Q6_K = 14 };
 
 template <int C> struct Geo;
 template <> struct Geo<Q4_0> { static constexpr int BV = 32;  static constexpr int BB = 18; };
 template <> struct Geo<Q8_0> { static constexpr int BV = 32;  static constexpr int BB = 34; };
+template <> struct Geo<Q4_1> { static constexpr int BV = 32;  static constexpr int BB = 20; };
+template <> struct Geo<Q5_0> { static constexpr int BV = 32;  static constexpr int BB = 22; };
+template <> struct Geo<Q5_1> { static constexpr int BV = 32;  static constexpr int BB = 24; };
 template <> struct Geo<Q4_K> { static constexpr int BV = 256; static constexpr int BB = 144; };
 template <> struct Geo<Q5_K> { static constexpr int BV = 256; static constexpr int BB = 176; };
 template <> struct Geo<Q6_K> { static constexpr int BV = 256; static constexpr int BB = 210; };
@@ -46,6 +53,16 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The legacy 32-value codecs with a minimum or a fifth bit (q4_1, q5_0, q5_1):
+// block bytes, whether an fp16 minimum follows d, the byte offsets of qh
+// (-1: none) and qs, and the code offset of a codec without a minimum.
+template <int C> struct Leg;
+template <> struct Leg<Q4_1> { static constexpr int BB = 20, QH = -1, QS = 4, ZP = 0; static constexpr bool MIN = true; };
+template <> struct Leg<Q5_0> { static constexpr int BB = 22, QH = 2, QS = 6, ZP = 16; static constexpr bool MIN = false; };
+template <> struct Leg<Q5_1> { static constexpr int BB = 24, QH = 4, QS = 8, ZP = 0; static constexpr bool MIN = true; };
+template <int C> constexpr bool is_leg() { return C == Q4_1 || C == Q5_0 || C == Q5_1; }
+template <int C> constexpr bool is_block32() { return C == Q4_0 || C == Q8_0 || is_leg<C>(); }
 
 // ---------------------------------------------------------------------------
 // small device helpers
@@ -125,6 +142,22 @@ __device__ __forceinline__ void q4k_scale_min_pair(uint32_t s0, uint32_t s1, uin
   sc1 = __builtin_amdgcn_ubfe(a, sh + 8u, w) | (__builtin_amdgcn_ubfe(s0, sh + 14u, t) << 4);
   m0 = __builtin_amdgcn_ubfe(b, sh, w) | (__builtin_amdgcn_ubfe(s1, sh + 6u, t) << 4);
   m1 = __builtin_amdgcn_ubfe(b, sh + 8u, w) | (__builtin_amdgcn_ubfe(s1, sh + 14u, t) << 4);
+}
+
+// Bit 4 of byte b of the result is bit b of t (b < 4): the fifth bits of
+// four consecutive values of a legacy block moved next to their nibbles.
+__device__ __forceinline__ uint32_t spread4(uint32_t t) { return (((t & 0xFu) * 0x00204081u) & 0x01010101u) << 4; }
+// 5-bit (or 4-bit) code bytes of qs dword i (values 4i..4i+3 low nibbles,
+// 16+4i.. high nibbles) of a legacy block with fifth bits qh
+template <int C>
+__device__ __forceinline__ uint32_t leg_lo(uint32_t qs, uint32_t qh, int i) {
+  if constexpr (Leg<C>::QH < 0) return qs & 0x0F0F0F0Fu;
+  else return (qs & 0x0F0F0F0Fu) | spread4(qh >> (4 * i));
+}
+template <int C>
+__device__ __forceinline__ uint32_t leg_hi(uint32_t qs, uint32_t qh, int i) {
+  if constexpr (Leg<C>::QH < 0) return (qs >> 4) & 0x0F0F0F0Fu;
+  else return ((qs >> 4) & 0x0F0F0F0Fu) | spread4(qh >> (16 + 4 * i));
 }
 
 // GLU epilogues (kq.h KQ_GLU_* carry the same values)

@@ -262,6 +262,76 @@ template <> struct HalfUnit<Q4_0> {
   }
 };
 
+// q4_1, q5_0, q5_1: half hh = block hh (low nibbles values 0..15, segment
+// 2hh; high nibbles 16..31, segment 2hh+1).  The block's dwords are read from
+// the dword-aligned address below it (q5_0's odd block sits 2 bytes past one:
+// sh = 2); NWB dwords cover it without reading past the unit.
+template <int C>
+struct HalfUnitLeg {
+  using L = Leg<C>;
+  static constexpr int NWB = L::BB % 4 ? (L::BB + 2 + 3) / 4 : L::BB / 4;
+  uint32_t R[NWB];
+  uint32_t sh;
+  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
+    const uint8_t* p = row + 2 * L::BB * u + L::BB * hh;
+    sh = L::BB % 4 ? (uint32_t)((uintptr_t)p & 3) : 0u;
+    const uint8_t* a = p - sh;
+#pragma unroll
+    for (int i = 0; i < NWB; ++i) R[i] = ld_u32(a + 4 * i);
+  }
+  // the 4 bytes at block byte offset O (even)
+  template <int O>
+  __device__ __forceinline__ uint32_t at() const {
+    if constexpr (L::BB % 4 == 0) {
+      if constexpr (O % 4 == 0) return R[O / 4];
+      else return alignbyte(R[O / 4 + 1], R[O / 4], 2);
+    } else if constexpr (O % 4 == 0) {
+      return sh ? alignbyte(R[O / 4 + 1], R[O / 4], 2) : R[O / 4];
+    } else {
+      return sh ? R[(O + 2) / 4] : alignbyte(R[O / 4 + 1], R[O / 4], 2);
+    }
+  }
+  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
+    constexpr int qso = L::QS, qho = L::QH >= 0 ? L::QH : 0;
+    const uint32_t w0 = at<0>();
+    const uint32_t qh = L::QH >= 0 ? at<qho>() : 0u;
+    const uint32_t q[4] = {at<qso>(), at<qso + 4>(), at<qso + 8>(), at<qso + 12>()};
+    uint32_t lo[8], hi[8];
+    if constexpr (L::MIN) {
+      // fma((1024 + q), d, m - 1024 d) in float32, rounded once to float16
+      const float d = f16_to_f32(w0), c = fmaf(-1024.f, d, f16_to_f32(w0 >> 16));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t l01 = as_h2(pair01(leg_lo<C>(q[i], qh, i))), l23 = as_h2(pair23(leg_lo<C>(q[i], qh, i)));
+        const half2_t t01 = as_h2(pair01(leg_hi<C>(q[i], qh, i))), t23 = as_h2(pair23(leg_hi<C>(q[i], qh, i)));
+        lo[2 * i] = pack_h2(fmaf((float)l01.x, d, c), fmaf((float)l01.y, d, c));
+        lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, d, c), fmaf((float)l23.y, d, c));
+        hi[2 * i] = pack_h2(fmaf((float)t01.x, d, c), fmaf((float)t01.y, d, c));
+        hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, d, c), fmaf((float)t23.y, d, c));
+      }
+    } else {
+      // (1024 + q - 1024 - ZP) is the exact code; times d, one rounding
+      const half2_t d = h2(__builtin_bit_cast(half_t, (uint16_t)(w0 & 0xFFFFu)));
+      const half2_t k = h2((half_t)(1024.f + L::ZP));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t l = leg_lo<C>(q[i], qh, i), t = leg_hi<C>(q[i], qh, i);
+        lo[2 * i] = as_u32((as_h2(pair01(l)) - k) * d);
+        lo[2 * i + 1] = as_u32((as_h2(pair23(l)) - k) * d);
+        hi[2 * i] = as_u32((as_h2(pair01(t)) - k) * d);
+        hi[2 * i + 1] = as_u32((as_h2(pair23(t)) - k) * d);
+      }
+    }
+    st_chunk(dst, sw, 4 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    st_chunk(dst, sw, 4 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
+    st_chunk(dst, sw, 4 * hh + 2, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    st_chunk(dst, sw, 4 * hh + 3, u32x4{hi[4], hi[5], hi[6], hi[7]});
+  }
+};
+template <> struct HalfUnit<Q4_1> : HalfUnitLeg<Q4_1> {};
+template <> struct HalfUnit<Q5_0> : HalfUnitLeg<Q5_0> {};
+template <> struct HalfUnit<Q5_1> : HalfUnitLeg<Q5_1> {};
+
 constexpr int QMM_THREADS = 512;
 
 // Tile of the (tiles_m x nb, n fastest) grid run by this block: block b runs
@@ -584,12 +654,18 @@ hipError_t launch_pass(int codec, const uint8_t* w, int64_t n, int64_t k, int64_
     switch (codec) {
       case Q4_0: return launch_generic<Q4_0, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
       case Q8_0: return launch_generic<Q8_0, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
+      case Q4_1: return launch_generic<Q4_1, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
+      case Q5_0: return launch_generic<Q5_0, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
+      case Q5_1: return launch_generic<Q5_1, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
     }
     return hipErrorInvalidValue;
   }
   switch (codec) {
     case Q4_0: return launch_dense<Q4_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q8_0: return launch_dense<Q8_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q4_1: return launch_dense<Q4_1, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q5_0: return launch_dense<Q5_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q5_1: return launch_dense<Q5_1, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q4_K: return launch_dense<Q4_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q5_K: return launch_dense<Q5_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q6_K: return launch_dense<Q6_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
@@ -636,6 +712,9 @@ hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t ne, int64_
     switch (codec) {
       case Q4_0: return launch_generic<Q4_0, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q8_0: return launch_generic<Q8_0, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+      case Q4_1: return launch_generic<Q4_1, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+      case Q5_0: return launch_generic<Q5_0, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+      case Q5_1: return launch_generic<Q5_1, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q4_K: return launch_generic<Q4_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q5_K: return launch_generic<Q5_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q6_K: return launch_generic<Q6_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);

@@ -568,8 +568,8 @@ hipError_t launch_fused_m(const uint8_t* w, const uint8_t* w2, int64_t n, int64_
 template <int C>
 hipError_t launch_fused_c(const uint8_t* w, const uint8_t* w2, int64_t n, int64_t k, int64_t rb, const half_t* x,
                           int m, const Epi& epi, int act, bool glu, void* y, int f16, hipStream_t s) {
-  if (k % 64 != 0) {  // odd block count (q8_0 / q4_0): the generic kernel; the GLU in two passes
-    if constexpr (C == Q8_0 || C == Q4_0) {
+  if (k % 64 != 0) {  // odd block count (32-value codecs): the generic kernel; the GLU in two passes
+    if constexpr (is_block32<C>()) {
       if (!glu) return launch_generic<C, EP_EPI, 0>(w, n, k, rb, x, m, y, f16, epi, s);
       const hipError_t e =
           act == GLU_SILU ? launch_generic<C, EP_GLU_ACT, GLU_SILU>(w, n, k, rb, x, m, y, f16, epi, s)
@@ -597,6 +597,9 @@ hipError_t launch_fused(int codec, const uint8_t* w, const uint8_t* w2, int64_t 
   switch (codec) {
     case Q4_0: return launch_fused_c<Q4_0>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q8_0: return launch_fused_c<Q8_0>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
+    case Q4_1: return launch_fused_c<Q4_1>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
+    case Q5_0: return launch_fused_c<Q5_0>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
+    case Q5_1: return launch_fused_c<Q5_1>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q4_K: return launch_fused_c<Q4_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q5_K: return launch_fused_c<Q5_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q6_K: return launch_fused_c<Q6_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
@@ -682,6 +685,9 @@ hipError_t launch_gather_qmv(int codec, const uint8_t* w, int64_t n_experts, int
   switch (codec) {
     case Q4_0: return launch_gather_c<Q4_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q8_0: return launch_gather_c<Q8_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+    case Q4_1: return launch_gather_c<Q4_1>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+    case Q5_0: return launch_gather_c<Q5_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+    case Q5_1: return launch_gather_c<Q5_1>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q4_K: return launch_gather_c<Q4_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q5_K: return launch_gather_c<Q5_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q6_K: return launch_gather_c<Q6_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
@@ -697,6 +703,12 @@ hipError_t launch_moe_glu_gather(int codec, const uint8_t* gate_w, const uint8_t
       return launch_glu_c<Q4_0>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
     case Q8_0:
       return launch_glu_c<Q8_0>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
+    case Q4_1:
+      return launch_glu_c<Q4_1>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
+    case Q5_0:
+      return launch_glu_c<Q5_0>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
+    case Q5_1:
+      return launch_glu_c<Q5_1>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
     case Q4_K:
       return launch_glu_c<Q4_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
     case Q5_K:
@@ -724,6 +736,9 @@ hipError_t launch_qmv(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t
   switch (codec) {
     case Q4_0: return launch_c<Q4_0>(w, n, k, rb, x, m, y, f16, s);
     case Q8_0: return launch_c<Q8_0>(w, n, k, rb, x, m, y, f16, s);
+    case Q4_1: return launch_c<Q4_1>(w, n, k, rb, x, m, y, f16, s);
+    case Q5_0: return launch_c<Q5_0>(w, n, k, rb, x, m, y, f16, s);
+    case Q5_1: return launch_c<Q5_1>(w, n, k, rb, x, m, y, f16, s);
     case Q4_K: return launch_c<Q4_K>(w, n, k, rb, x, m, y, f16, s);
     case Q5_K: return launch_c<Q5_K>(w, n, k, rb, x, m, y, f16, s);
     case Q6_K: return launch_c<Q6_K>(w, n, k, rb, x, m, y, f16, s);

@@ -12,14 +12,18 @@
 //          d = f16(max scale/63), dmin = f16(max min/63);
 //          sc = rint(scale/D), m = rint(min/DM) (0..63);
 //          q = rint((w + DM*m)/(D*sc))
+//   q4_1 : d = f16((max w - min w)/15), m = f16(min w); q = rint((w - M)/D)
+//   q5_0 : d = f16(amax/15);             q = rint(w/D) + 16
+//   q5_1 : d = f16((max w - min w)/31), m = f16(min w); q = rint((w - M)/D)
 //   q5_K : as q4_K with scale = (hi - lo)/31 and q in 0..31
 //   q6_K : per 16 values scale = amax/31; d = f16(max scale/127);
 //          sc = rint(scale/D) (-128..127); q = rint(w/(D*sc)) + 32
 // Codes are clamped to the codec's range, then moved to the nearest point of
 // the block's decoded grid among q-1, q, q+1 (distance |w - decode(q)| in
 // float64, ties to the lower code).  A zero grid step gives the zero-point
-// code (q8_0 0, q4_0 8, q4_K and q5_K 0, q6_K 32).  One thread per block
-// (q8_0, q4_0) or superblock (q4_K, q5_K, q6_K); not a hot path.
+// code (q8_0 0, q4_0 8, q4_1 and q5_1 0, q5_0 16, q4_K and q5_K 0, q6_K 32).
+// One thread per block (32-value codecs) or superblock (q4_K, q5_K, q6_K);
+// not a hot path.
 #include "kq_internal.h"
 
 #pragma clang fp contract(off)
@@ -94,6 +98,59 @@ __global__ __launch_bounds__(256) void quant_q4_0(const float* __restrict__ w, i
   st_u16(o, db);
   for (int i = 0; i < 16; i += 2)
     st_u16(o + 2 + i, (uint32_t)(q[i] | (q[i + 16] << 4)) | ((uint32_t)(q[i + 1] | (q[i + 17] << 4)) << 8));
+}
+
+// q4_1, q5_0, q5_1: d, [m], [qh as a little-endian uint32], qs; blocks are
+// 2-byte aligned, so every store is 2 bytes.
+template <int C>
+__global__ __launch_bounds__(256) void quant_leg(const float* __restrict__ w, int64_t nblocks, int kb,
+                                                 int64_t row_bytes, uint8_t* __restrict__ out) {
+  using L = Leg<C>;
+  constexpr int QMAX = C == Q4_1 ? 15 : 31;
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= nblocks) return;
+  const int64_t r = g / kb, b = g % kb;
+  const float* x = w + (r * kb + b) * 32;
+  uint32_t db, mb = 0;
+  float D, M = 0.f;
+  if constexpr (L::MIN) {
+    float lo = x[0], hi = x[0];
+    for (int i = 1; i < 32; ++i) { lo = fminf(lo, x[i]); hi = fmaxf(hi, x[i]); }
+    db = f16_bits((hi - lo) / (float)QMAX);
+    mb = f16_bits(lo);
+    D = f16_val(db);
+    M = f16_val(mb);
+  } else {
+    float amax = 0.f;
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    db = f16_bits(amax / 15.f);
+    D = f16_val(db);
+  }
+  int q[32];
+  for (int i = 0; i < 32; ++i) {
+    const float v = x[i];
+    if (D == 0.f) {
+      q[i] = L::ZP;
+    } else if constexpr (L::MIN) {
+      const int q0 = (int)clampf(rintf((v - M) / D), 0.f, (float)QMAX);
+      q[i] = nearest(v, q0, 0, QMAX, [D, M](int c) { return D * (float)c + M; });
+    } else {
+      const int q0 = (int)clampf(rintf(v / D) + 16.f, 0.f, 31.f);
+      q[i] = nearest(v, q0, 0, 31, [D](int c) { return D * (float)(c - 16); });
+    }
+  }
+  uint8_t* o = out + r * row_bytes + b * L::BB;
+  st_u16(o, db);
+  if constexpr (L::MIN) st_u16(o + 2, mb);
+  if constexpr (L::QH >= 0) {
+    uint32_t qh = 0;
+    for (int i = 0; i < 32; ++i) qh |= (uint32_t)(q[i] >> 4) << i;
+    st_u16(o + L::QH, qh & 0xFFFFu);
+    st_u16(o + L::QH + 2, qh >> 16);
+  }
+  for (int i = 0; i < 16; i += 2)
+    st_u16(o + L::QS + i, (uint32_t)((q[i] & 15) | ((q[i + 16] & 15) << 4)) |
+                              ((uint32_t)((q[i + 1] & 15) | ((q[i + 17] & 15) << 4)) << 8));
 }
 
 // q4_K (QMAX 15, 144-byte superblocks) and q5_K (QMAX 31, 176 bytes: the
@@ -225,6 +282,9 @@ hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, i
   switch (codec) {
     case Q8_0: hipLaunchKernelGGL(quant_q8_0, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q4_0: hipLaunchKernelGGL(quant_q4_0, grid, block, 0, s, w, nblk, kb, rb, out); break;
+    case Q4_1: hipLaunchKernelGGL(quant_leg<Q4_1>, grid, block, 0, s, w, nblk, kb, rb, out); break;
+    case Q5_0: hipLaunchKernelGGL(quant_leg<Q5_0>, grid, block, 0, s, w, nblk, kb, rb, out); break;
+    case Q5_1: hipLaunchKernelGGL(quant_leg<Q5_1>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q4_K: hipLaunchKernelGGL(quant_k_affine<15>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q5_K: hipLaunchKernelGGL(quant_k_affine<31>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q6_K: hipLaunchKernelGGL(quant_q6_k, grid, block, 0, s, w, nblk, kb, rb, out); break;

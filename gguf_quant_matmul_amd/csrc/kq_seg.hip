@@ -276,6 +276,9 @@ hipError_t launch_seg_mma(int codec, const uint8_t* w, int64_t n_experts, int64_
     case Q8_0: return launch_seg_mma_c<Q8_0>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q4_K: return launch_seg_mma_c<Q4_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q5_K: return launch_seg_mma_c<Q5_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
+    case Q4_1: return launch_seg_mma_c<Q4_1>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
+    case Q5_0: return launch_seg_mma_c<Q5_0>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
+    case Q5_1: return launch_seg_mma_c<Q5_1>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q6_K: return launch_seg_mma_c<Q6_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
   }
   return hipErrorInvalidValue;

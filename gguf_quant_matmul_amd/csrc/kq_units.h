@@ -349,12 +349,81 @@ struct UnitQ4_0 {  // two 18-byte blocks, 36 bytes, dword aligned
   }
 };
 
+// q4_1, q5_0, q5_1: a unit is two blocks (40, 44 or 48 bytes), dword
+// aligned in a row of whole units.
+template <int C>
+struct UnitLeg {
+  using L = Leg<C>;
+  static constexpr int UB = 2 * L::BB, NWD = UB / 4;
+  u32x4 a, b;
+  uint32_t t0, t1, t2 = 0, t3 = 0;  // dwords 8 .. NWD-1
+  __device__ __forceinline__ void load(const uint8_t* row, int u) {
+    const uint8_t* p = row + UB * u;
+    a = ld_16B_a4(p); b = ld_16B_a4(p + 16);
+    t0 = ld_u32(p + 32); t1 = ld_u32(p + 36);
+    if constexpr (NWD > 10) t2 = ld_u32(p + 40);
+    if constexpr (NWD > 11) t3 = ld_u32(p + 44);
+  }
+  __device__ __forceinline__ void bload(rsrc_t rs, int rowoff, int cu, int u4) {
+    const int vo = rowoff + UB * cu, so = UB * u4;
+    a = bld16(rs, vo, so); b = bld16(rs, vo + 16, so);
+    t0 = bld4(rs, vo + 32, so); t1 = bld4(rs, vo + 36, so);
+    if constexpr (NWD > 10) t2 = bld4(rs, vo + 40, so);
+    if constexpr (NWD > 11) t3 = bld4(rs, vo + 44, so);
+  }
+  // the 4 bytes at unit byte offset O (even)
+  template <int O>
+  __device__ __forceinline__ uint32_t at() const {
+    const uint32_t R[12] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, t0, t1, t2, t3};
+    if constexpr (O % 4 == 0) return R[O / 4];
+    else return alignbyte(R[O / 4 + 1], R[O / 4], 2);
+  }
+  // block B's d, m and code dwords (lo: values 0..15, hi: 16..31)
+  template <int B>
+  __device__ __forceinline__ void block(float& d, float& m, uint32_t lo[4], uint32_t hi[4]) const {
+    constexpr int base = B * L::BB, qso = base + L::QS, qho = base + (L::QH >= 0 ? L::QH : 0);
+    const uint32_t w0 = at<base>();
+    d = f16_to_f32(w0);
+    m = L::MIN ? f16_to_f32(w0 >> 16) : 0.f;
+    const uint32_t qh = L::QH >= 0 ? at<qho>() : 0u;
+    const uint32_t q[4] = {at<qso>(), at<qso + 4>(), at<qso + 8>(), at<qso + 12>()};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { lo[i] = leg_lo<C>(q[i], qh, i); hi[i] = leg_hi<C>(q[i], qh, i); }
+  }
+  template <int M>
+  __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
+    float d0, m0, d1, m1;
+    uint32_t lo0[4], hi0[4], lo1[4], hi1[4];
+    block<0>(d0, m0, lo0, hi0);
+    block<1>(d1, m1, lo1, hi1);
+    uint32_t pl0[8], ph0[8], pl1[8], ph1[8];
+    pairs16(lo0, pl0); pairs16(hi0, ph0); pairs16(lo1, pl1); pairs16(hi1, ph1);
+    constexpr float K = 1024.f + (float)L::ZP;  // the float16 code offset
+    const int base = 64 * u;
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) {
+      float s0 = dot16(pl0, xv.pairs(mm, base), 0.f);
+      s0 = dot16(ph0, xv.pairs(mm, base + 16), s0);
+      float s1 = dot16(pl1, xv.pairs(mm, base + 32), 0.f);
+      s1 = dot16(ph1, xv.pairs(mm, base + 48), s1);
+      const float4_t xs = *(const float4_t*)&xv.xsum[mm * xv.sstride + ((base - xv.c0) >> 4)];
+      const float x0 = xs.x + xs.y, x1 = xs.z + xs.w;
+      float t = d0 * (s0 - K * x0) + d1 * (s1 - K * x1);
+      if constexpr (L::MIN) t += m0 * x0 + m1 * x1;
+      acc[mm] += t;
+    }
+  }
+};
+
 template <int C> struct UnitOf;
 template <> struct UnitOf<Q4_K> { typedef UnitQ4K T; };
 template <> struct UnitOf<Q5_K> { typedef UnitQ5K T; };
 template <> struct UnitOf<Q6_K> { typedef UnitQ6K T; };
 template <> struct UnitOf<Q8_0> { typedef UnitQ8_0 T; };
 template <> struct UnitOf<Q4_0> { typedef UnitQ4_0 T; };
+template <> struct UnitOf<Q4_1> { typedef UnitLeg<Q4_1> T; };
+template <> struct UnitOf<Q5_0> { typedef UnitLeg<Q5_0> T; };
+template <> struct UnitOf<Q5_1> { typedef UnitLeg<Q5_1> T; };
 
 // ---------------------------------------------------------------------------
 // Matrix-core operand slices of a unit.
@@ -536,6 +605,44 @@ template <> struct MmaSlices<Q4_0> {
       slice8(q[b][dw] & 0xF0F0F0F0u, q[b][dw + 1] & 0xF0F0F0F0u, 0.0625f * d[b], -72.f * d[b], f);
   }
 };
+
+// q4_1, q5_0, q5_1: block b = S >> 2 (values 32 b ..): slices t < 2 are the
+// low-nibble codes (values 8t..), t >= 2 the high ones; weight =
+// fma(1024 + q, d, m - 1024 d) or fma(1024 + q, d, -(1024 + 16) d).
+template <int C>
+struct MmaSlicesLeg {
+  using L = Leg<C>;
+  uint32_t lo[2][4], hi[2][4];
+  float s[2], c[2];
+  __device__ __forceinline__ MmaSlicesLeg(const UnitLeg<C>& un, int, bool keep) {
+    float d0, m0, d1, m1;
+    un.template block<0>(d0, m0, lo[0], hi[0]);
+    un.template block<1>(d1, m1, lo[1], hi[1]);
+    s[0] = keep ? d0 : 0.f;
+    s[1] = keep ? d1 : 0.f;
+    if constexpr (L::MIN) {
+      c[0] = keep ? fmaf(-1024.f, d0, m0) : 0.f;
+      c[1] = keep ? fmaf(-1024.f, d1, m1) : 0.f;
+    } else {
+      c[0] = -(1024.f + L::ZP) * s[0];
+      c[1] = -(1024.f + L::ZP) * s[1];
+    }
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int b = S >> 2, t = S & 3, dw = 2 * (t & 1);
+    if (t < 2)
+      slice8(lo[b][dw], lo[b][dw + 1], s[b], c[b], f);
+    else
+      slice8(hi[b][dw], hi[b][dw + 1], s[b], c[b], f);
+  }
+};
+template <> struct MmaSlices<Q4_1> : MmaSlicesLeg<Q4_1> { using MmaSlicesLeg<Q4_1>::MmaSlicesLeg; };
+template <> struct MmaSlices<Q5_0> : MmaSlicesLeg<Q5_0> { using MmaSlicesLeg<Q5_0>::MmaSlicesLeg; };
+template <> struct MmaSlices<Q5_1> : MmaSlicesLeg<Q5_1> { using MmaSlicesLeg<Q5_1>::MmaSlicesLeg; };
 
 }  // namespace
 }  // namespace kq

@@ -41,6 +41,8 @@ def test_codec_registry():
     assert kq.kq_codec_from_name("Q4_K") == kq.KQ_Q4_K
     assert kq.kq_codec_from_name("q5_k") == kq.KQ_Q5_K == 13
     assert kq.kq_row_bytes("q5_k", 4096) == 2816
+    for name, cid, geo in (("q4_1", 3, (32, 20)), ("q5_0", 6, (32, 22)), ("q5_1", 7, (32, 24))):
+        assert kq.kq_codec_from_name(name) == cid and kq.kq_codec_info(name) == geo
     assert kq.kq_row_bytes("q6_k", 4096) == 3360
     assert kq.kq_row_bytes("q8_0", 4096) == 4352
     with pytest.raises(kq.KQError) as e:
@@ -146,7 +148,7 @@ def _st(ret):
         (lambda: L.kq_quantized_matmul_glu(12, A16, A16, 64, 250, A16, 4, 0, A16, 0, None),
          kq.KQ_ERR_SHAPE, "K=250"),
         (lambda: L.kq_quantize(12, A16, 4, 512, A16 + 4, None), kq.KQ_ERR_ALIGN, "aligned"),
-        (lambda: L.kq_quantize(6, A16, 4, 512, A16, None), kq.KQ_ERR_CODEC, "codec"),
+        (lambda: L.kq_quantize(9, A16, 4, 512, A16, None), kq.KQ_ERR_CODEC, "codec"),
     ],
 )
 def test_argument_errors_return_before_launch(call, status, msg):

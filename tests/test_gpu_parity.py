@@ -16,7 +16,7 @@ from oracle import codecs, encode, matmul
 
 pytestmark = pytest.mark.gpu
 
-CODECS = ("q4_k", "q6_k", "q8_0", "q4_0", "q5_k")
+CODECS = ("q4_k", "q6_k", "q8_0", "q4_0", "q5_k", "q4_1", "q5_0", "q5_1")
 SUPER = ("q4_k", "q5_k", "q6_k")  # 256-value superblocks
 
 
@@ -53,7 +53,8 @@ def _random_wire(codec, n, k, rng):
     w = rng.integers(0, 256, size=(n, rb), dtype=np.uint8)
     bb = codecs.block_bytes(codec)
     blk = w.reshape(n, -1, bb)
-    offs = {"q8_0": [0], "q4_0": [0], "q4_k": [0, 2], "q5_k": [0, 2], "q6_k": [208]}[codec]
+    offs = {"q8_0": [0], "q4_0": [0], "q4_k": [0, 2], "q5_k": [0, 2], "q6_k": [208], "q4_1": [0, 2], "q5_0": [0],
+            "q5_1": [0, 2]}[codec]
     for o in offs:
         hi = blk[..., o + 1]
         bad = (hi & 0x7C) == 0x7C
@@ -117,7 +118,7 @@ def test_dequantize_f16_rounds_via_f32(kq):
 
 
 @pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt",
-                                  "q5_k_block.txt"])
+                                  "q5_k_block.txt", "q4_1_block.txt", "q5_0_block.txt", "q5_1_block.txt"])
 def test_dequantize_golden_blocks(kq, name):
     from test_oracle_codecs import _load_golden
 
@@ -169,7 +170,7 @@ def test_qmv_parity(kq, codec, m):
 def test_qmm_parity(kq, codec):
     torch = _torch()
     shapes = [(1, 37, 512), (130, 200, 512), (257, 131, 256 * 9 if codec in SUPER else 64 * 9)]
-    if codec in ("q8_0", "q4_0"):
+    if codec not in SUPER:
         shapes.append((70, 40, 96))  # odd block count -> generic kernel
     for m, n, k in shapes:
         w = _weights(codec, n, k, 11 + m)
@@ -189,7 +190,7 @@ def test_qmm_parity(kq, codec):
 def _epi_shapes(codec):
     kk = 256 * 9 if codec in SUPER else 64 * 9
     shapes = [(1, 37, kk), (3, 300, kk), (8, 45, kk), (130, 200, kk), (260, 131, kk)]
-    if codec in ("q8_0", "q4_0"):
+    if codec not in SUPER:
         shapes += [(4, 45, 2048 + 32), (70, 40, 96)]  # odd block counts: generic kernels
     return shapes
 
@@ -249,7 +250,7 @@ def test_quantized_matmul_glu_parity(kq, codec):
     torch = _torch()
     kk = 256 * 5 if codec in SUPER else 64 * 5
     shapes = [(1, 48, kk), (2, 304, kk), (3, 96, kk), (5, 48, kk), (8, 112, kk), (130, 208, kk), (257, 96, kk)]
-    if codec in ("q8_0", "q4_0"):
+    if codec not in SUPER:
         shapes += [(2, 48, 96), (70, 48, 96)]
     for m, n, k in shapes:
         wcat = _weights(codec, 2 * n, k, 23 + m, scale=0.05)
@@ -417,7 +418,7 @@ def test_gather_qmm_seg_parity(kq, codec):
             assert_close_rows(got[covered], ref[covered], what=f"seg {codec} n={n} k={k}")
 
 
-@pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0", "q5_k"])
+@pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0", "q5_k", "q4_1", "q5_0", "q5_1"])
 def test_gather_seg_tile_boundaries(kq, codec):
     # expert rows 96 (a full tile and a 32-row tail), 97 (a 33-row tail),
     # 133 (two full tiles and a 5-row tail), 64 (one full tile), 20 and one
