@@ -305,6 +305,8 @@ hipError_t launch_qmv_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int
                           int m, const Epi& epi, void* y, int f16out, hipStream_t s);
 hipError_t launch_qmm_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes, const half_t* x,
                           int64_t m, const Epi& epi, void* y, int f16out, hipStream_t s);
+hipError_t launch_qmm_glu_mul(int codec, const uint8_t* w_up, int64_t n, int64_t k, int64_t row_bytes,
+                              const half_t* x, int64_t m, void* y, int f16out, hipStream_t s);
 hipError_t launch_qmv_glu(int codec, const uint8_t* w_gate, const uint8_t* w_up, int64_t n, int64_t k,
                           int64_t row_bytes, const half_t* x, int m, int act, void* y, int f16out, hipStream_t s);
 hipError_t launch_qmm_glu(int codec, const uint8_t* w_gate, const uint8_t* w_up, int64_t n, int64_t k,

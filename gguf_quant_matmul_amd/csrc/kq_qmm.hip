@@ -1,708 +1,14 @@
-// kq_qmm: quantized GEMM on gfx950 float16 matrix cores, and the dispatch of
-// kq_gather_qmm_seg (its matrix-core kernel is in kq_seg.hip; K that is not a
-// whole number of 64-value units takes the plain kernel at the end of this
-// file for both operations).
-//
-// mlx-kquant bindings.cpp page: quantized_matmul docstring (y = x @ dequant(w)
-// transposed, w [N, K]); gather_qmm_seg docstring (expert-sorted rows walked
-// tile by tile from a (expert, row_start, num_rows) map with <= 64 rows per
-// tile, dead rows of a partial tile skipped, uncovered rows unwritten).
-//
-// Design.
-//  * A workgroup of 8 waves (2 per SIMD, so one wave's decode overlaps the
-//    other's matrix work) computes a BM x BN output tile, walking K 64 values
-//    (one "unit") per step.  Each step stages the x tile (BM x 64 float16) and
-//    DECODES the weight tile (BN rows x 64 values) from wire bytes into LDS as
-//    float16; the waves then run v_mfma_f32_16x16x32_f16 with float32
-//    accumulators.  LDS is double-buffered and the next step's wire bytes and
-//    activations are loaded into registers before the current step's MFMAs,
-//    so global latency hides behind matrix work; one barrier per step.
-//  * Every decoded weight is rounded to float16 once, from its exact value
-//    (q4_K: one float32 FMA, then RNE; q6_K: exact integer code*scale times
-//    d; q8_0 / q4_0: d times the code), never through a rounded per-block
-//    scale, which would put one correlated error on a whole sub-block.
-//  * Within a 64-value step only the agreement of x and W on k matters to
-//    the contraction: a q6_K unit's four 16-value segments are not
-//    contiguous in K, so x is gathered with the same segment map.
-//  * Tiles are ordered so that the workgroups on one XCD (blocks are dealt to
-//    the 8 XCDs round-robin) share activation panels in that XCD's L2.
-#include <type_traits>
-
-#include "kq_decode.h"
+// kq_qmm: the plain quantized GEMM and the kq_gather_qmm_seg dispatch (the
+// segment kernel is in kq_seg.hip; K that is not a whole number of 64-value
+// units takes the plain kernel for both)
+// (the kernel and its launchers: kq_qmm_impl.h).
+#include "kq_qmm_impl.h"
 
 namespace kq {
-namespace {
-
-constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK;  // halves: 128-byte rows of eight 16-byte chunks
-// Chunk c of row r lives at chunk c ^ (r & 7): the MFMA operand reads (16 rows
-// x 16 bytes at one column) then touch every bank once (a plain or 16-byte
-// padded row stride makes them conflict, measured with SQ_LDS_BANK_CONFLICT).
-__device__ __forceinline__ void st_chunk(half_t* row, int sw, int c, u32x4 v) { *(u32x4*)(row + 8 * (c ^ sw)) = v; }
-constexpr int NXCD = 8;
-
-// Row offset of segment t (16 values) of unit u.
-template <int C>
-__device__ __forceinline__ int seg_off(int u, int t) {
-  if (C == Q6_K) return 256 * (u >> 2) + 128 * ((u >> 1) & 1) + 32 * t + 16 * (u & 1);
-  return 64 * u + 16 * t;
-}
-
-__device__ __forceinline__ half2_t h2(half_t a) { return half2_t{a, a}; }
-
-// 16 bytes at a 2-byte-aligned address: dwords from the dword-aligned address
-// below it (never past the 16 bytes), shifted by sh = addr & 3 bytes.
-struct Raw16 {
-  u32x4 a;
-  uint32_t b;
-  __device__ __forceinline__ void load(const uint8_t* p, uint32_t sh) {
-    const uint8_t* q = p - sh;
-    a = ld_16B_a4(q);
-    b = ld_u32(q + 16 - (sh ? 0 : 4));
-  }
-  __device__ __forceinline__ void get(uint32_t sh, uint32_t o[4]) const {
-    o[0] = alignbyte(a.y, a.x, sh);
-    o[1] = alignbyte(a.z, a.y, sh);
-    o[2] = alignbyte(a.w, a.z, sh);
-    o[3] = alignbyte(b, a.w, sh);
-  }
-};
-
-// Half of unit u of one weight row: load() issues its global loads into
-// registers, store() decodes them into 32 float16 values: segment t (16
-// values) is LDS chunks 2t and 2t+1 of the row at dst (swizzle sw = row & 7).
-template <int C> struct HalfUnit;
-
-template <> struct HalfUnit<Q4_K> {
-  // half hh: qs bytes 16hh..16hh+15 of sub-block pair P = u%4: positions
-  // l in [16hh, 16hh+16) of sub-blocks 2P (low nibbles, segment hh) and 2P+1
-  // (high nibbles, segment 2+hh).
-  u32x4 h, q;
-  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
-    const uint8_t* blk = row + (u >> 2) * 144;
-    h = ld_16B(blk);
-    q = ld_16B(blk + 16 + 32 * (u & 3) + 16 * hh);
-  }
-  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
-    const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
-    uint32_t sc0, m0, sc1, m1;
-    q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3), sc0, m0);
-    q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3) + 1, sc1, m1);
-    // Codes come as float16 (1024 + q) from one byte permute per pair; the
-    // weight is fma((1024 + q), s, -(1024 s + dmin m)) in float32 (s and
-    // dmin m exact, the constant rounded once in float32, about 2^-24 of
-    // 1024 s) and rounded once to float16 (v_fma_mix).
-    const float s0 = d * (float)sc0, c0 = -(1024.f * s0 + dmin * (float)m0);
-    const float s1 = d * (float)sc1, c1 = -(1024.f * s1 + dmin * (float)m1);
-    const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t l = qw[i] & 0x0F0F0F0Fu, t = (qw[i] >> 4) & 0x0F0F0F0Fu;
-      const half2_t l01 = as_h2(pair01(l)), l23 = as_h2(pair23(l));
-      const half2_t t01 = as_h2(pair01(t)), t23 = as_h2(pair23(t));
-      lo[2 * i] = pack_h2(fmaf((float)l01.x, s0, c0), fmaf((float)l01.y, s0, c0));
-      lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, s0, c0), fmaf((float)l23.y, s0, c0));
-      hi[2 * i] = pack_h2(fmaf((float)t01.x, s1, c1), fmaf((float)t01.y, s1, c1));
-      hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, s1, c1), fmaf((float)t23.y, s1, c1));
-    }
-    st_chunk(dst, sw, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    st_chunk(dst, sw, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
-    st_chunk(dst, sw, 4 + 2 * hh, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    st_chunk(dst, sw, 5 + 2 * hh, u32x4{hi[4], hi[5], hi[6], hi[7]});
-  }
-};
-
-template <> struct HalfUnit<Q5_K> {
-  // q4_K's half unit with 5-bit codes: the fifth bits of positions l in
-  // [16hh, 16hh+16) are bits 2P (sub-block 2P) and 2P + 1 of qh[l].
-  u32x4 h, q, e;
-  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
-    const uint8_t* blk = row + (u >> 2) * 176;
-    h = ld_16B(blk);
-    e = ld_16B(blk + 16 + 16 * hh);
-    q = ld_16B(blk + 48 + 32 * (u & 3) + 16 * hh);
-  }
-  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
-    const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
-    uint32_t sc0, m0, sc1, m1;
-    q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3), sc0, m0);
-    q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3) + 1, sc1, m1);
-    // as q4_K: fma((1024 + q), s, -(1024 s + dmin m)) rounded once to float16
-    const float s0 = d * (float)sc0, c0 = -(1024.f * s0 + dmin * (float)m0);
-    const float s1 = d * (float)sc1, c1 = -(1024.f * s1 + dmin * (float)m1);
-    const uint32_t qw[4] = {q.x, q.y, q.z, q.w}, qe[4] = {e.x, e.y, e.z, e.w};
-    const int j0 = 2 * (u & 3);
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t qhs = qe[i] >> j0;
-      const uint32_t l = (qw[i] & 0x0F0F0F0Fu) | ((qhs << 4) & 0x10101010u);
-      const uint32_t t = ((qw[i] >> 4) & 0x0F0F0F0Fu) | ((qhs << 3) & 0x10101010u);
-      const half2_t l01 = as_h2(pair01(l)), l23 = as_h2(pair23(l));
-      const half2_t t01 = as_h2(pair01(t)), t23 = as_h2(pair23(t));
-      lo[2 * i] = pack_h2(fmaf((float)l01.x, s0, c0), fmaf((float)l01.y, s0, c0));
-      lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, s0, c0), fmaf((float)l23.y, s0, c0));
-      hi[2 * i] = pack_h2(fmaf((float)t01.x, s1, c1), fmaf((float)t01.y, s1, c1));
-      hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, s1, c1), fmaf((float)t23.y, s1, c1));
-    }
-    st_chunk(dst, sw, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    st_chunk(dst, sw, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
-    st_chunk(dst, sw, 4 + 2 * hh, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    st_chunk(dst, sw, 5 + 2 * hh, u32x4{hi[4], hi[5], hi[6], hi[7]});
-  }
-};
-
-template <> struct HalfUnit<Q6_K> {
-  // unit u = (superblock s, h, half); half hh takes c = hh (low nibbles) and
-  // c = hh + 2 (high nibbles) of ql[64h + 32hh + 16half + i].
-  Raw16 rq, rh, rs;
-  uint32_t dbits, sh;
-  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
-    const uint8_t* blk = row + (u >> 2) * 210;
-    const int h = (u >> 1) & 1, half = u & 1;
-    sh = (uint32_t)((uintptr_t)blk & 3);
-    rq.load(blk + 64 * h + 32 * hh + 16 * half, sh);
-    rh.load(blk + 128 + 32 * h + 16 * half, sh);
-    rs.load(blk + 192, sh);
-    dbits = ld_u16(blk + 208);
-  }
-  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
-    const int h = (u >> 1) & 1, half = u & 1;
-    uint32_t Q[4], H[4], S[4];
-    rq.get(sh, Q);
-    rh.get(sh, H);
-    rs.get(sh, S);
-    // scales[8h + 2c + half]: c = hh in dword 2h (byte half + 2hh), c = hh+2 in dword 2h+1
-    const uint32_t slo = h ? S[2] : S[0], shi = h ? S[3] : S[1];
-    const int bsh = 8 * (half + 2 * hh);
-    // value = ((q - 32) * sc) * d: (q - 32) * sc is an integer of magnitude
-    // <= 4096 (exact in float16 up to 2048), so each weight rounds by itself.
-    const half2_t sa = h2((half_t)(float)(int)(int8_t)(slo >> bsh));
-    const half2_t sb = h2((half_t)(float)(int)(int8_t)(shi >> bsh));
-    const half2_t dd = h2(__builtin_bit_cast(half_t, (uint16_t)dbits));
-    const half2_t k1056 = h2((half_t)1056.f);
-    const int hs = 2 * hh;
-    uint32_t a[8], b[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t ca = (Q[i] & 0x0F0F0F0Fu) | (((H[i] >> hs) << 4) & 0x30303030u);
-      const uint32_t cb = ((Q[i] >> 4) & 0x0F0F0F0Fu) | (((H[i] >> (hs + 4)) << 4) & 0x30303030u);
-      a[2 * i] = as_u32(((as_h2(pair01(ca)) - k1056) * sa) * dd);
-      a[2 * i + 1] = as_u32(((as_h2(pair23(ca)) - k1056) * sa) * dd);
-      b[2 * i] = as_u32(((as_h2(pair01(cb)) - k1056) * sb) * dd);
-      b[2 * i + 1] = as_u32(((as_h2(pair23(cb)) - k1056) * sb) * dd);
-    }
-    st_chunk(dst, sw, 2 * hh, u32x4{a[0], a[1], a[2], a[3]});
-    st_chunk(dst, sw, 2 * hh + 1, u32x4{a[4], a[5], a[6], a[7]});
-    st_chunk(dst, sw, 2 * hh + 4, u32x4{b[0], b[1], b[2], b[3]});
-    st_chunk(dst, sw, 2 * hh + 5, u32x4{b[4], b[5], b[6], b[7]});
-  }
-};
-
-template <> struct HalfUnit<Q8_0> {
-  // unit u = two blocks at 68u; half hh = block hh (34 bytes) -> segments 2hh, 2hh+1.
-  // Nine dwords from the dword below the block cover it (sh = 0 or 2).
-  u32x4 r0, r1;
-  uint32_t r8, sh;
-  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
-    const uint8_t* p = row + 68 * u + 34 * hh;
-    sh = (uint32_t)((uintptr_t)p & 3);
-    const uint8_t* a = p - sh;
-    r0 = ld_16B_a4(a);
-    r1 = ld_16B_a4(a + 16);
-    r8 = ld_u32(a + 32);
-  }
-  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
-    const uint32_t R[9] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w, r8};
-    const half2_t d = h2(__builtin_bit_cast(half_t, (uint16_t)(sh ? (R[0] >> 16) : (R[0] & 0xFFFFu))));
-    const half2_t k1152 = h2((half_t)1152.f);
-    uint32_t o[16];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c = (sh ? R[i + 1] : alignbyte(R[i + 1], R[i], 2)) ^ 0x80808080u;
-      o[2 * i] = as_u32((as_h2(pair01(c)) - k1152) * d);  // exact code, one rounding
-      o[2 * i + 1] = as_u32((as_h2(pair23(c)) - k1152) * d);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) st_chunk(dst, sw, 4 * hh + i, u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]});
-  }
-};
-
-template <> struct HalfUnit<Q4_0> {
-  // unit u = two blocks at 36u; half hh = block hh (18 bytes): low nibbles are
-  // values 0..15 (segment 2hh), high nibbles 16..31 (segment 2hh+1).
-  u32x4 r0;
-  uint32_t r4, sh;
-  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
-    const uint8_t* p = row + 36 * u + 18 * hh;
-    sh = (uint32_t)((uintptr_t)p & 3);
-    const uint8_t* a = p - sh;
-    r0 = ld_16B_a4(a);
-    r4 = ld_u32(a + 16);
-  }
-  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
-    const uint32_t R[5] = {r0.x, r0.y, r0.z, r0.w, r4};
-    const half2_t d = h2(__builtin_bit_cast(half_t, (uint16_t)(sh ? (R[0] >> 16) : (R[0] & 0xFFFFu))));
-    const half2_t k1032 = h2((half_t)1032.f);
-    uint32_t lo[8], hi[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t q = sh ? R[i + 1] : alignbyte(R[i + 1], R[i], 2);
-      const uint32_t l = q & 0x0F0F0F0Fu, t = (q >> 4) & 0x0F0F0F0Fu;
-      lo[2 * i] = as_u32((as_h2(pair01(l)) - k1032) * d);
-      lo[2 * i + 1] = as_u32((as_h2(pair23(l)) - k1032) * d);
-      hi[2 * i] = as_u32((as_h2(pair01(t)) - k1032) * d);
-      hi[2 * i + 1] = as_u32((as_h2(pair23(t)) - k1032) * d);
-    }
-    st_chunk(dst, sw, 4 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    st_chunk(dst, sw, 4 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
-    st_chunk(dst, sw, 4 * hh + 2, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    st_chunk(dst, sw, 4 * hh + 3, u32x4{hi[4], hi[5], hi[6], hi[7]});
-  }
-};
-
-// q4_1, q5_0, q5_1: half hh = block hh (low nibbles values 0..15, segment
-// 2hh; high nibbles 16..31, segment 2hh+1).  The block's dwords are read from
-// the dword-aligned address below it (q5_0's odd block sits 2 bytes past one:
-// sh = 2); NWB dwords cover it without reading past the unit.
-template <int C>
-struct HalfUnitLeg {
-  using L = Leg<C>;
-  static constexpr int NWB = L::BB % 4 ? (L::BB + 2 + 3) / 4 : L::BB / 4;
-  uint32_t R[NWB];
-  uint32_t sh;
-  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
-    const uint8_t* p = row + 2 * L::BB * u + L::BB * hh;
-    sh = L::BB % 4 ? (uint32_t)((uintptr_t)p & 3) : 0u;
-    const uint8_t* a = p - sh;
-#pragma unroll
-    for (int i = 0; i < NWB; ++i) R[i] = ld_u32(a + 4 * i);
-  }
-  // the 4 bytes at block byte offset O (even)
-  template <int O>
-  __device__ __forceinline__ uint32_t at() const {
-    if constexpr (L::BB % 4 == 0) {
-      if constexpr (O % 4 == 0) return R[O / 4];
-      else return alignbyte(R[O / 4 + 1], R[O / 4], 2);
-    } else if constexpr (O % 4 == 0) {
-      return sh ? alignbyte(R[O / 4 + 1], R[O / 4], 2) : R[O / 4];
-    } else {
-      return sh ? R[(O + 2) / 4] : alignbyte(R[O / 4 + 1], R[O / 4], 2);
-    }
-  }
-  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
-    constexpr int qso = L::QS, qho = L::QH >= 0 ? L::QH : 0;
-    const uint32_t w0 = at<0>();
-    const uint32_t qh = L::QH >= 0 ? at<qho>() : 0u;
-    const uint32_t q[4] = {at<qso>(), at<qso + 4>(), at<qso + 8>(), at<qso + 12>()};
-    uint32_t lo[8], hi[8];
-    if constexpr (L::MIN) {
-      // fma((1024 + q), d, m - 1024 d) in float32, rounded once to float16
-      const float d = f16_to_f32(w0), c = fmaf(-1024.f, d, f16_to_f32(w0 >> 16));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half2_t l01 = as_h2(pair01(leg_lo<C>(q[i], qh, i))), l23 = as_h2(pair23(leg_lo<C>(q[i], qh, i)));
-        const half2_t t01 = as_h2(pair01(leg_hi<C>(q[i], qh, i))), t23 = as_h2(pair23(leg_hi<C>(q[i], qh, i)));
-        lo[2 * i] = pack_h2(fmaf((float)l01.x, d, c), fmaf((float)l01.y, d, c));
-        lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, d, c), fmaf((float)l23.y, d, c));
-        hi[2 * i] = pack_h2(fmaf((float)t01.x, d, c), fmaf((float)t01.y, d, c));
-        hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, d, c), fmaf((float)t23.y, d, c));
-      }
-    } else {
-      // (1024 + q - 1024 - ZP) is the exact code; times d, one rounding
-      const half2_t d = h2(__builtin_bit_cast(half_t, (uint16_t)(w0 & 0xFFFFu)));
-      const half2_t k = h2((half_t)(1024.f + L::ZP));
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t l = leg_lo<C>(q[i], qh, i), t = leg_hi<C>(q[i], qh, i);
-        lo[2 * i] = as_u32((as_h2(pair01(l)) - k) * d);
-        lo[2 * i + 1] = as_u32((as_h2(pair23(l)) - k) * d);
-        hi[2 * i] = as_u32((as_h2(pair01(t)) - k) * d);
-        hi[2 * i + 1] = as_u32((as_h2(pair23(t)) - k) * d);
-      }
-    }
-    st_chunk(dst, sw, 4 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    st_chunk(dst, sw, 4 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
-    st_chunk(dst, sw, 4 * hh + 2, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    st_chunk(dst, sw, 4 * hh + 3, u32x4{hi[4], hi[5], hi[6], hi[7]});
-  }
-};
-template <> struct HalfUnit<Q4_1> : HalfUnitLeg<Q4_1> {};
-template <> struct HalfUnit<Q5_0> : HalfUnitLeg<Q5_0> {};
-template <> struct HalfUnit<Q5_1> : HalfUnitLeg<Q5_1> {};
-
-constexpr int QMM_THREADS = 512;
-
-// Tile of the (tiles_m x nb, n fastest) grid run by this block: block b runs
-// on XCD b % 8, and XCD x takes the contiguous tile range
-// [x * per_xcd, (x+1) * per_xcd), so its workgroups share x panels in its L2.
-__device__ __forceinline__ int xcd_tile(int per_xcd) {
-  return (int)(blockIdx.x % NXCD) * per_xcd + (int)(blockIdx.x / NXCD);
-}
-
-constexpr int gcd_c(int a, int b) { return b ? gcd_c(b, a % b) : a; }
-constexpr int lcm_c(int a, int b) { return a / gcd_c(a, b) * b; }
-
-// PDA / PDB: prefetch distances in K-steps for activations and weights.  The
-// loads for step s are issued at the start of step s - PD into register slot
-// s % PD, stored (weights: decoded) to LDS buffer s % 2 during step s - 1, and
-// consumed by the MFMAs of step s.  Activations come from L2 (their panel is
-// shared by the tiles of one XCD) and need a shorter distance than weights.
-//
-// EP / ACT / epi: the output store (store_out: plain, the residual epilogue,
-// or one of the two passes of the GLU product).
-template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB, bool F16, int EP = EP_PLAIN, int ACT = 0>
-__global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restrict__ w, int n, int k,
-                                                          int64_t row_bytes, const half_t* __restrict__ x, int m_total,
-                                                          int tiles_total, int per_xcd, void* __restrict__ y,
-                                                          Epi epi) {
-  static_assert(WM * WN == QMM_THREADS / 64, "8 waves");
-  constexpr int WTM = BM / WM, WTN = BN / WN;  // wave tile
-  constexpr int TM = WTM / 16, TN = WTN / 16;  // 16x16 MFMA tiles per wave
-  static_assert(TM >= 1 && TN >= 1 && WTM % 16 == 0 && WTN % 16 == 0, "wave tile");
-  static_assert(PDA >= 1 && PDB >= 1, "prefetch distance");
-  constexpr int A_CHUNKS = BM * 8, A_PER_T = (A_CHUNKS + QMM_THREADS - 1) / QMM_THREADS;
-  constexpr int B_HALVES = BN * 2, B_PER_T = (B_HALVES + QMM_THREADS - 1) / QMM_THREADS;
-  constexpr int UNR = lcm_c(lcm_c(PDA, PDB), 2);
-  __shared__ __attribute__((aligned(16))) half_t As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) half_t Bs[2][BN * LDS_STRIDE];
-
-  const int t = xcd_tile(per_xcd);
-  if (t >= tiles_total) return;
-  const int nb = (n + BN - 1) / BN;
-  const int by = t / nb;
-  const int n0 = (t - by * nb) * BN;
-  const int m0 = by * BM;
-  const int mrows = min(BM, m_total - m0);
-  const uint8_t* wbase = w;
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int wr0 = wm * WTM, wc0 = wn * WTN;
-  // 16-row fragments of this wave that hold live rows (the rest skip their MFMAs)
-  const int live_tm = min(TM, max(0, (mrows - wr0 + 15) / 16));
-
-  float4_t acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-  u32x4 areg[PDA][A_PER_T];
-  HalfUnit<C> braw[PDB][B_PER_T];
-
-  // Activation chunks: 8 per tile row (4 segments x 2 halves of 8 values).
-  // Rows past the tile read a clamped valid row; their outputs are never
-  // stored, so no predicate sits in the K loop.
-  const half_t* xrow[A_PER_T];
-#pragma unroll
-  for (int i = 0; i < A_PER_T; ++i) {
-    const int c = min(tid + i * QMM_THREADS, A_CHUNKS - 1), r = c >> 3;
-    xrow[i] = x + (int64_t)min(m0 + r, m_total - 1) * k + 8 * (c & 1);
-  }
-  // Weight half-units: wave w decodes rows [w * RPW, (w+1) * RPW), two lanes
-  // (halves) per row, so every wave has the same decode work.  Spare lanes
-  // redo the wave's last row (same values to the same LDS bytes), so no lane
-  // is masked off.  Rows past N read a clamped valid row (finite values,
-  // outputs never stored).
-  constexpr int RPW = BN / 8;  // rows per wave
-  static_assert(BN % 8 == 0 && 2 * RPW <= 64 && B_PER_T == 1, "one half-unit per lane");
-  const int brow0 = wave * RPW + min(lane >> 1, RPW - 1);
-  const uint8_t* const wrow0 = wbase + (int64_t)min(n0 + brow0, n - 1) * row_bytes;
-
-  auto issue_a = [&](int slot, int u) {
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int part = (tid + i * QMM_THREADS) & 7;
-      areg[slot][i] = *(const u32x4*)(xrow[i] + seg_off<C>(u, part >> 1));
-    }
-  };
-  auto issue_b = [&](int slot, int u) { braw[slot][0].load(wrow0, u, lane & 1); };
-  auto stage = [&](int sa, int sb, int buf, int u) {
-#pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int c = tid + i * QMM_THREADS;
-      if (A_CHUNKS % QMM_THREADS == 0 || c < A_CHUNKS) {
-        const int r = c >> 3, part = c & 7;
-        st_chunk(&As[buf][r * LDS_STRIDE], r & 7, part, areg[sa][i]);
-      }
-    }
-    braw[sb][0].store(u, lane & 1, &Bs[buf][brow0 * LDS_STRIDE], brow0 & 7);
-  };
-  // All fragment reads of a 32-wide K slice are issued before its MFMAs, in
-  // the order the MFMAs consume them, so one LDS round trip per slice is
-  // exposed instead of one per A fragment.  Full tiles take a copy without
-  // the dead-fragment test.
-  auto mfma_slice = [&](int buf, int ks, auto full) {
-    constexpr bool FULL = decltype(full)::value;
-    const int kk = 8 * ((4 * ks + (lane >> 4)) ^ (lane & 7));
-    half8_t a[TM], b[TN];
-    a[0] = *(const half8_t*)(&As[buf][(wr0 + (lane & 15)) * LDS_STRIDE + kk]);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = *(const half8_t*)(&Bs[buf][(wc0 + 16 * j + (lane & 15)) * LDS_STRIDE + kk]);
-#pragma unroll
-    for (int i = 1; i < TM; ++i) a[i] = *(const half8_t*)(&As[buf][(wr0 + 16 * i + (lane & 15)) * LDS_STRIDE + kk]);
-    asm volatile("" ::: "memory");  // keep every read above the MFMAs (the scheduler would sink them)
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (FULL || i < live_tm) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    }
-  };
-  const bool full_rows = live_tm == TM;
-  auto mfma_step = [&](int buf) {
-    if (full_rows) {
-#pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) mfma_slice(buf, ks, std::true_type{});
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) mfma_slice(buf, ks, std::false_type{});
-    }
-  };
-
-  // Waves w and w+4 share a SIMD: the first four stage the next step before
-  // their MFMAs, the other four after, so one wave's decode runs while its
-  // partner's MFMAs occupy the matrix unit.  The steady-state loop body has no
-  // branches (step indices are clamped instead: a clamped extra load or stage
-  // is harmless), so the compiler keeps PD steps of loads in flight.
-  const int units = k / BK;
-  const int last = units - 1;
-#pragma unroll
-  for (int s = 0; s < PDA; ++s) issue_a(s, min(s, last));
-#pragma unroll
-  for (int s = 0; s < PDB; ++s) issue_b(s, min(s, last));
-  stage(0, 0, 0, 0);
-  __syncthreads();
-  const int units_main = units - units % UNR;
-  auto kloop = [&](auto sf) {
-    constexpr bool SF = decltype(sf)::value;
-    for (int u0 = 0; u0 < units_main; u0 += UNR) {
-#pragma unroll
-      for (int du = 0; du < UNR; ++du) {
-        const int u = u0 + du;
-        issue_a(du % PDA, min(u + PDA, last));
-        issue_b(du % PDB, min(u + PDB, last));
-        if (SF) stage((du + 1) % PDA, (du + 1) % PDB, (du + 1) & 1, min(u + 1, last));
-        mfma_step(du & 1);
-        if (!SF) stage((du + 1) % PDA, (du + 1) % PDB, (du + 1) & 1, min(u + 1, last));
-        __syncthreads();
-      }
-    }
-    // leftover steps (units not a multiple of UNR): slot = du % PD still holds
-    // because units_main is a multiple of both distances
-#pragma unroll
-    for (int du = 0; du < UNR; ++du) {
-      const int u = units_main + du;
-      if (u < units) {
-        issue_a(du % PDA, min(u + PDA, last));
-        issue_b(du % PDB, min(u + PDB, last));
-        if (SF) stage((du + 1) % PDA, (du + 1) % PDB, (du + 1) & 1, min(u + 1, last));
-        mfma_step(du & 1);
-        if (!SF) stage((du + 1) % PDA, (du + 1) % PDB, (du + 1) & 1, min(u + 1, last));
-        __syncthreads();
-      }
-    }
-  };
-  if (wave < 4)
-    kloop(std::true_type{});
-  else
-    kloop(std::false_type{});
-
-  // 16x16 accumulator layout: lane holds column (lane & 15); register r holds
-  // row 4*(lane/16) + r.
-  static_assert(EP != EP_EPI, "the GEMM tile stores take EP_RES / EP_RES_GATE");
-  if constexpr (EP == EP_PLAIN || EP == EP_GLU_ACT) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (i >= live_tm) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wc0 + 16 * j + (lane & 15);
-        if (col >= n) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wr0 + 16 * i + 4 * (lane >> 4) + r;
-          if (row < mrows) store_out<F16, EP, ACT>(y, m0 + row, col, n, epi, acc[i][j][r]);
-        }
-      }
-    }
-  } else {
-    // stores that read: each 16-row group's inputs are loaded before its
-    // stores, unconditionally (indices clamped into the tile; a clamped
-    // element's value is never used), so the loads overlap instead of each
-    // waiting behind a branch
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (i >= live_tm) continue;
-      float pa[TN][4], pb[TN][4];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = min(n0 + wc0 + 16 * j + (lane & 15), n - 1);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = min(wr0 + 16 * i + 4 * (lane >> 4) + r, mrows - 1);
-          pa[j][r] = 0.f;
-          pb[j][r] = 1.f;
-          epi_load<F16, EP>(y, m0 + row, col, n, epi, pa[j][r], pb[j][r]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        const int col = n0 + wc0 + 16 * j + (lane & 15);
-        if (col >= n) continue;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = wr0 + 16 * i + 4 * (lane >> 4) + r;
-          if (row < mrows) store_pre<F16, EP, ACT>(y, m0 + row, col, n, epi, acc[i][j][r], pa[j][r], pb[j][r]);
-        }
-      }
-    }
-  }
-}
-
-template <int C, int BM, int BN, int WM, int WN, int PDA, int PDB, int EP, int ACT>
-hipError_t launch_t(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m, void* y, int f16,
-                    const Epi& epi, hipStream_t s) {
-  const int64_t tiles_m = (m + BM - 1) / BM;
-  const int64_t tiles = tiles_m * ((n + BN - 1) / BN);
-  const int64_t per_xcd = (tiles + NXCD - 1) / NXCD;
-  const dim3 grid((unsigned)(per_xcd * NXCD));
-  if (f16)
-    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, true, EP, ACT>), grid, dim3(QMM_THREADS), 0, s, w,
-                       (int)n, (int)k, rb, x, (int)m, (int)tiles, (int)per_xcd, y, epi);
-  else
-    hipLaunchKernelGGL((qmm_kernel<C, BM, BN, WM, WN, PDA, PDB, false, EP, ACT>), grid, dim3(QMM_THREADS), 0, s, w,
-                       (int)n, (int)k, rb, x, (int)m, (int)tiles, (int)per_xcd, y, epi);
-  return hipGetLastError();
-}
-
-template <int C, int EP, int ACT>
-hipError_t launch_dense(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m, void* y,
-                        int f16, const Epi& epi, hipStream_t s) {
-  if (m > 128)  // prefill: 256 x 224 tiles (N = 14336 gives 64 tile columns)
-    return launch_t<C, 256, 224, 4, 2, 1, 2, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-  if (m > 64) return launch_t<C, 128, 256, 2, 4, 2, 3, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-  return launch_t<C, 64, 256, 2, 4, 2, 4, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-}
-
-template <int C, bool SEG, bool F16, int EP = EP_PLAIN, int ACT = 0>
-__global__ __launch_bounds__(256) void qmm_generic_kernel(const uint8_t* __restrict__ w, int n, int k, int64_t rb,
-                                                          int64_t estride, int n_experts, const half_t* __restrict__ x,
-                                                          int m_total, const uint32_t* __restrict__ map,
-                                                          const uint32_t* __restrict__ counts, void* __restrict__ y,
-                                                          Epi epi) {
-  const int lane = threadIdx.x & 63;
-  const int nb = (n + 3) / 4;
-  const int by = (int)(blockIdx.x / nb);
-  const int col = (int)(blockIdx.x % nb) * 4 + (threadIdx.x >> 6);
-  if (col >= n) return;
-  int r0, r1;
-  const uint8_t* wb = w;
-  if (SEG) {
-    const int tile = by;
-    if (tile >= (int)counts[0]) return;
-    const uint32_t* mt = map + 3 * (size_t)tile;
-    const uint32_t e = mt[0], rs = mt[1], nr = mt[2];
-    if (e >= (uint32_t)n_experts || nr == 0 || nr > 64 || rs >= (uint32_t)m_total || nr > (uint32_t)m_total - rs)
-      return;
-    r0 = (int)rs; r1 = (int)(rs + nr);
-    wb = w + (int64_t)e * estride;
-  } else {
-    r0 = by * 64;
-    r1 = min(m_total, r0 + 64);
-  }
-  const uint8_t* wrow = wb + (int64_t)col * rb;
-  for (int r = r0; r < r1; ++r) {
-    float acc = 0.f;
-    for (int g = lane; g < k / 8; g += 64) {
-      float v[8];
-      decode8<C>(wrow, (int64_t)g * 8, v);
-      const half8_t xv = *(const half8_t*)(x + (int64_t)r * k + 8 * g);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc += v[i] * (float)xv[i];
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-    if (lane == 0) store_out<F16, EP, ACT>(y, r, col, n, epi, acc);
-  }
-}
-
-template <int C, bool SEG, int EP = EP_PLAIN, int ACT = 0>
-hipError_t launch_generic(const uint8_t* w, int64_t n, int64_t k, int64_t rb, int64_t estride, int64_t ne,
-                          const half_t* x, int64_t m, const uint32_t* map, const uint32_t* counts, int64_t gy, void* y,
-                          int f16, hipStream_t s, const Epi& epi = Epi{nullptr, nullptr, nullptr, 1}) {
-  const dim3 grid((unsigned)(((n + 3) / 4) * gy));
-  if (f16)
-    hipLaunchKernelGGL((qmm_generic_kernel<C, SEG, true, EP, ACT>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb,
-                       estride, (int)ne, x, (int)m, map, counts, y, epi);
-  else
-    hipLaunchKernelGGL((qmm_generic_kernel<C, SEG, false, EP, ACT>), grid, dim3(256), 0, s, w, (int)n, (int)k, rb,
-                       estride, (int)ne, x, (int)m, map, counts, y, epi);
-  return hipGetLastError();
-}
-
-// One GEMM pass with output store EP: the matrix-core kernel for K a whole
-// number of 64-value units, else the plain kernel (q4_0 / q8_0 only).
-template <int EP, int ACT>
-hipError_t launch_pass(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m,
-                       void* y, int f16, const Epi& epi, hipStream_t s) {
-  if (k % 64 != 0) {
-    const int64_t gy = (m + 63) / 64;
-    switch (codec) {
-      case Q4_0: return launch_generic<Q4_0, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
-      case Q8_0: return launch_generic<Q8_0, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
-      case Q4_1: return launch_generic<Q4_1, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
-      case Q5_0: return launch_generic<Q5_0, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
-      case Q5_1: return launch_generic<Q5_1, false, EP, ACT>(w, n, k, rb, 0, 1, x, m, nullptr, nullptr, gy, y, f16, s, epi);
-    }
-    return hipErrorInvalidValue;
-  }
-  switch (codec) {
-    case Q4_0: return launch_dense<Q4_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-    case Q8_0: return launch_dense<Q8_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-    case Q4_1: return launch_dense<Q4_1, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-    case Q5_0: return launch_dense<Q5_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-    case Q5_1: return launch_dense<Q5_1, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-    case Q4_K: return launch_dense<Q4_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-    case Q5_K: return launch_dense<Q5_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-    case Q6_K: return launch_dense<Q6_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-}  // namespace
 
 hipError_t launch_qmm(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m,
                       void* y, int f16, hipStream_t s) {
   return launch_pass<EP_PLAIN, 0>(codec, w, n, k, rb, x, m, y, f16, Epi{nullptr, nullptr, nullptr, 1}, s);
-}
-
-// the GEMM takes a residual with or without a gate (no bias)
-hipError_t launch_qmm_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes, const half_t* x,
-                          int64_t m, const Epi& epi, void* y, int f16out, hipStream_t s) {
-  if (!epi.resid || epi.bias) return hipErrorInvalidValue;
-  if (epi.gate) return launch_pass<EP_RES_GATE, 0>(codec, w, n, k, row_bytes, x, m, y, f16out, epi, s);
-  return launch_pass<EP_RES, 0>(codec, w, n, k, row_bytes, x, m, y, f16out, epi, s);
-}
-
-// The GLU product as two passes on one stream: the gate pass stores the
-// rounded activation in y, the up pass multiplies its product by it; each
-// output element is read and written by the same lane of the same tile.
-hipError_t launch_qmm_glu(int codec, const uint8_t* w_gate, const uint8_t* w_up, int64_t n, int64_t k,
-                          int64_t row_bytes, const half_t* x, int64_t m, int act, void* y, int f16out, hipStream_t s) {
-  const Epi none{nullptr, nullptr, nullptr, 1};
-  hipError_t e;
-  if (act == GLU_SILU)
-    e = launch_pass<EP_GLU_ACT, GLU_SILU>(codec, w_gate, n, k, row_bytes, x, m, y, f16out, none, s);
-  else if (act == GLU_GELU_TANH)
-    e = launch_pass<EP_GLU_ACT, GLU_GELU_TANH>(codec, w_gate, n, k, row_bytes, x, m, y, f16out, none, s);
-  else
-    return hipErrorInvalidValue;
-  if (e != hipSuccess) return e;
-  return launch_pass<EP_GLU_MUL, 0>(codec, w_up, n, k, row_bytes, x, m, y, f16out, none, s);
 }
 
 hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb,
