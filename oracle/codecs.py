@@ -14,8 +14,9 @@ What the pages fix
   * the same table: q5_k is a 256-value superblock of 5-bit codes in 176
     bytes ("K-quant superblock"); q4_1 32 values, 4 bits, 20 bytes ("block
     scale + min"); q5_0 32 values, 5 bits, 22 bytes ("block scale"); q5_1 32
-    values, 5 bits, 24 bytes ("block scale + min").  Their layouts are not on
-    the pages and take reading R1 like the others.
+    values, 5 bits, 24 bytes ("block scale + min"); q2_k 256 values, 2 bits,
+    84 bytes ("K-quant superblock").  Their layouts are not on the pages and
+    take reading R1 like the others.
   * The q4_K sub-block structure (8 sub-blocks of 32, 6-bit scale and min per
     sub-block, fp16 d and dmin) and the q6_K one (16 sub-blocks of 16, int8
     scales, fp16 d) are stated with the workloads.
@@ -29,8 +30,8 @@ Readings taken where the pages are silent (each is also listed in the design doc)
       honoured, the sign of zero kept, inf/NaN passed through).
   R3  Arithmetic: each value is the exact real number of the formula, rounded
       ONCE to fp32 (RNE).  For q8_0, q4_0, q5_0 and q6_K the exact value is
-      already an fp32 number.  For q4_K and q5_K the only rounding is that of
-      ``(d*sc)*q - (dmin*m)``; for q4_1 and q5_1 that of ``d*q + m`` (exact in
+      already an fp32 number.  For q2_K, q4_K and q5_K the only rounding is
+      that of ``(d*sc)*q - (dmin*m)``; for q4_1 and q5_1 that of ``d*q + m`` (exact in
       float64: its bits span at most 2^-24 .. 2^21).
   R4  float16 output is RNE of the fp32 value (so q4_K -> f16 rounds twice, by
       definition).
@@ -60,6 +61,7 @@ GEOMETRY = {
     "q4_1": (32, 4, 20),
     "q5_0": (32, 5, 22),
     "q5_1": (32, 5, 24),
+    "q2_k": (256, 2, 84),
 }
 
 CODECS = tuple(GEOMETRY)
@@ -232,6 +234,26 @@ def fields_q5_k(blk: np.ndarray):
     return d, dmin, sc, m, q  # q: [n, nb, 8, 32]
 
 
+def fields_q2_k(blk: np.ndarray):
+    """q2_K, 84 bytes: [0:16] scales (sub-block j of 16 values: scale = low
+    nibble of byte j, min = high nibble), [16:80] qs, [80:82] d, [82:84] dmin.
+
+    Value v: h = v // 128, c = (v % 128) // 32, l = v % 32; its code is bits
+    2c..2c+1 of qs[32h + l].  value = (d*sc_j)*q - (dmin*m_j), j = v // 16.
+    """
+    sc = (blk[..., 0:16] & 15).astype(np.int64)
+    m = (blk[..., 0:16] >> 4).astype(np.int64)
+    qs = blk[..., 16:80].astype(np.int64)
+    d = f16_bits_to_f64(le_u16(blk[..., 80], blk[..., 81]))
+    dmin = f16_bits_to_f64(le_u16(blk[..., 82], blk[..., 83]))
+    q = np.empty(qs.shape[:-1] + (256,), dtype=np.int64)
+    for v in range(256):
+        h, r = divmod(v, 128)
+        c, l = divmod(r, 32)
+        q[..., v] = (qs[..., 32 * h + l] >> (2 * c)) & 3
+    return d, dmin, sc, m, q  # sc, m: [.., 16]; q: [.., 256]
+
+
 def fields_q6_k(blk: np.ndarray):
     """q6_K, 210 bytes: [0:128] ql, [128:192] qh, [192:208] 16 int8 scales, [208:210] d.
 
@@ -297,6 +319,12 @@ def dequantize(codec: str, w: np.ndarray, k: int, dtype=np.float32) -> np.ndarra
         elif codec == "q5_0":
             d, _, q = fields_legacy(codec, blk)
             y = _exact_f32(d[..., None] * (q - 16))
+        elif codec == "q2_k":
+            d, dmin, sc, m, q = fields_q2_k(blk)
+            step = np.repeat(d[..., None] * sc, 16, axis=-1)  # [n, nb, 256]
+            a = _exact_f32(step * q)
+            b = _exact_f32(np.repeat(dmin[..., None] * m, 16, axis=-1))
+            y = a - b  # float32 - float32: the single IEEE rounding
         elif codec in ("q4_k", "q5_k"):
             d, dmin, sc, m, q = fields_q4_k(blk) if codec == "q4_k" else fields_q5_k(blk)
             a = _exact_f32(d[..., None, None] * sc[..., None] * q)  # (d*sc)*q, exact

@@ -26,6 +26,10 @@ the same bytes.  ``rint`` rounds half to even; ``f16()`` is RNE to binary16.
          q = rint((w + DM*m_j) / (D*sc_j))
   q5_K : as q4_K with 31 levels: scale_j = (hi - lo)/31, q in 0..31 (the
          low four bits in qs as q4_K's nibbles, bit 4 in bit j of qh[l])
+  q2_K : per 16-value sub-block j: lo = min(0, min w), hi = max(w),
+         scale_j = (hi - lo)/3, min_j = -lo; d = f16(max scale_j / 15),
+         dmin = f16(max min_j / 15); sc_j = rint(scale_j/D), m_j =
+         rint(min_j/DM) (0..15); q = rint((w + DM*m_j) / (D*sc_j)) (0..3)
   q6_K : per 16-value sub-block j: scale_j = amax_j/31;
          d = f16(max_j scale_j / 127); sc_j = rint(scale_j/D) (clamped -128..127);
          q = rint(w/(D*sc_j)) + 32
@@ -34,7 +38,7 @@ NEAREST point of the block's decoded grid among {q-1, q, q+1} (distance
 |w - decode(q)| taken in float64; ties go to the lower code), so that every
 code is the nearest grid point.  Where the grid step is zero the code is the
 zero-point code (q8_0: 0, q4_0: 8, q4_1 and q5_1: 0, q5_0: 16, q4_K and
-q5_K: 0, q6_K: 32).
+q5_K: 0, q2_K: 0, q6_K: 32).
 
 Pins (tests/test_oracle_encode.py): brute force over every code of the block
 on tiny tensors (the chosen code is a nearest grid point, ties to the lower
@@ -256,6 +260,43 @@ def encode_q5_k(w: np.ndarray) -> np.ndarray:
     return out.reshape(w.shape[:-1] + (row_bytes("q5_k", k),))
 
 
+def encode_q2_k(w: np.ndarray) -> np.ndarray:
+    w2, k = _rows(w, "q2_k")
+    x = w2.reshape(w2.shape[0], k // 256, 16, 16)
+    lo = np.minimum(F32(0), np.min(x, axis=-1))  # [n, nb, 16]
+    hi = np.max(x, axis=-1)
+    scale = _div((hi - lo).astype(F32), F32(3))
+    mins = (-lo).astype(F32)
+    dbits = _f16_bits(_div(np.max(scale, axis=-1), F32(15)))
+    mbits = _f16_bits(_div(np.max(mins, axis=-1), F32(15)))
+    D = _f16_value(dbits)[..., None]
+    DM = _f16_value(mbits)[..., None]
+    sc = np.where(D > 0, np.clip(np.rint(_div(scale, D)), 0, 15), 0).astype(np.int64)
+    m = np.where(DM > 0, np.clip(np.rint(_div(mins, DM)), 0, 15), 0).astype(np.int64)
+    S = (D * sc.astype(F32)).astype(F32)[..., None]  # exact: 11 x 4 bits
+    MN = (DM * m.astype(F32)).astype(F32)[..., None]
+    q0 = np.clip(np.rint(_div((x + MN).astype(F32), S)), 0, 3)
+    q0 = np.where(S == 0, 0, q0).astype(np.int64)
+
+    def dec(q):
+        return ((S * q.astype(F32)).astype(F32) - MN).astype(F32)
+
+    q = np.where(S == 0, 0, _nearest(x, q0, 0, 3, dec)).reshape(x.shape[:2] + (256,))
+    out = np.zeros(x.shape[:2] + (84,), dtype=np.uint8)
+    out[..., 0:16] = (sc | (m << 4)).astype(np.uint8)
+    qs = np.zeros(x.shape[:2] + (64,), dtype=np.int64)
+    for v in range(256):
+        h, r = divmod(v, 128)
+        c, l = divmod(r, 32)
+        qs[..., 32 * h + l] |= q[..., v] << (2 * c)
+    out[..., 16:80] = qs.astype(np.uint8)
+    out[..., 80] = dbits & 255
+    out[..., 81] = dbits >> 8
+    out[..., 82] = mbits & 255
+    out[..., 83] = mbits >> 8
+    return out.reshape(w.shape[:-1] + (row_bytes("q2_k", k),))
+
+
 def encode_q6_k(w: np.ndarray) -> np.ndarray:
     w2, k = _rows(w, "q6_k")
     x = w2.reshape(w2.shape[0], k // 256, 16, 16)
@@ -301,6 +342,7 @@ ENCODERS = {
     "q4_1": lambda w: encode_affine_min(w, "q4_1"),
     "q5_0": encode_q5_0,
     "q5_1": lambda w: encode_affine_min(w, "q5_1"),
+    "q2_k": encode_q2_k,
 }
 
 
@@ -310,4 +352,5 @@ def quantize(codec: str, w: np.ndarray) -> np.ndarray:
 
 
 assert all(block_bytes(c) == b for c, b in (("q4_k", 144), ("q6_k", 210), ("q8_0", 34), ("q4_0", 18), ("q5_k", 176),
-                                              ("q4_1", 20), ("q5_0", 22), ("q5_1", 24)))
+                                              ("q4_1", 20), ("q5_0", 22), ("q5_1", 24),
+                                              ("q2_k", 84)))

@@ -33,6 +33,7 @@ def test_codec_table_byte_totals():
     assert codecs.GEOMETRY["q4_1"] == (32, 4, 20) and 2 + 2 + 16 == 20          # d, m, qs
     assert codecs.GEOMETRY["q5_0"] == (32, 5, 22) and 2 + 4 + 16 == 22          # d, qh, qs
     assert codecs.GEOMETRY["q5_1"] == (32, 5, 24) and 2 + 2 + 4 + 16 == 24      # d, m, qh, qs
+    assert codecs.GEOMETRY["q2_k"] == (256, 2, 84) and 16 + 64 + 2 + 2 == 84    # scales, qs, d, dmin
     # The layout reading must account for every byte of the block.
     assert 2 + 2 + 12 + 128 == 144          # d, dmin, scales, qs
     assert 128 + 64 + 16 + 2 == 210         # ql, qh, scales, d
@@ -81,7 +82,8 @@ def _load_golden(name):
 
 
 @pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt",
-                                  "q5_k_block.txt", "q4_1_block.txt", "q5_0_block.txt", "q5_1_block.txt"])
+                                  "q5_k_block.txt", "q4_1_block.txt", "q5_0_block.txt", "q5_1_block.txt",
+                                  "q2_k_block.txt"])
 @pytest.mark.parametrize("dtype", [np.float32, np.float16])
 def test_golden_hand_decoded_blocks(name, dtype):
     codec, blk, values = _load_golden(name)
@@ -150,6 +152,20 @@ def _hand_pack(codec, rng, nblocks):
         for v in range(32):
             out[:, o + (v % 16)] |= ((q[:, v] & 15) << (4 * (v // 16))).astype(np.uint8)
         return out, dict(d=d, m=mm, q=q)
+    if codec == "q2_k":
+        q = rng.integers(0, 4, size=(nblocks, 256))
+        sc = rng.integers(0, 16, size=(nblocks, 16))
+        m = rng.integers(0, 16, size=(nblocks, 16))
+        d = rng.integers(0, 0x7C00, size=nblocks)
+        dm = rng.integers(0, 0x7C00, size=nblocks)
+        out = np.zeros((nblocks, 84), np.uint8)
+        out[:, 0:16] = (sc | (m << 4)).astype(np.uint8)
+        for v in range(256):
+            h, r = divmod(v, 128)
+            c, l = divmod(r, 32)
+            out[:, 16 + 32 * h + l] |= (q[:, v] << (2 * c)).astype(np.uint8)
+        out[:, 80], out[:, 81], out[:, 82], out[:, 83] = d & 255, d >> 8, dm & 255, dm >> 8
+        return out, dict(d=d, dm=dm, sc=sc, m=m, q=q)
     if codec == "q5_k":
         q = rng.integers(0, 32, size=(nblocks, 256))
         sc = rng.integers(0, 64, size=(nblocks, 8))
@@ -215,6 +231,7 @@ def _affine(codec, f):
       q4_0 : code q (4 bits),     scale d,      bias -8 d
       q4_K : code q (4 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 32)
       q5_K : code q (5 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 32)
+      q2_K : code q (2 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 16)
       q4_1 : code q (4 bits),     scale d,      bias m
       q5_0 : code q (5 bits),     scale d,      bias -16 d
       q5_1 : code q (5 bits),     scale d,      bias m
@@ -236,6 +253,9 @@ def _affine(codec, f):
         elif codec == "q5_0":
             d = half(f["d"][i])
             params = [(d, -16 * d, int(q)) for q in f["q"][i]]
+        elif codec == "q2_k":
+            d, dm = half(f["d"][i]), half(f["dm"][i])
+            params = [(d * int(f["sc"][i][v // 16]), -dm * int(f["m"][i][v // 16]), int(f["q"][i][v])) for v in range(256)]
         elif codec in ("q4_k", "q5_k"):
             d, dm = half(f["d"][i]), half(f["dm"][i])
             params = [(d * int(f["sc"][i][v // 32]), -dm * int(f["m"][i][v // 32]), int(f["q"][i][v])) for v in range(256)]
@@ -260,6 +280,10 @@ def test_hand_packed_codes_decode_to_affine_closed_form(codec):
         d, dmin, sc, m, q = codecs.fields_q5_k(blocks[:, None, :])
         assert np.array_equal(sc[:, 0], fields["sc"]) and np.array_equal(m[:, 0], fields["m"])
         assert np.array_equal(q[:, 0].reshape(24, 256), fields["q"])
+    elif codec == "q2_k":
+        d, dmin, sc, m, q = codecs.fields_q2_k(blocks[:, None, :])
+        assert np.array_equal(sc[:, 0], fields["sc"]) and np.array_equal(m[:, 0], fields["m"])
+        assert np.array_equal(q[:, 0], fields["q"])
     elif codec in ("q4_1", "q5_0", "q5_1"):
         d, m, q = codecs.fields_legacy(codec, blocks[:, None, :])
         assert np.array_equal(q[:, 0], fields["q"])
