@@ -36,6 +36,7 @@ const char* codec_name(int c) {
     case KQ_Q8_0: return "q8_0";
     case KQ_Q4_K: return "q4_k";
     case KQ_Q5_K: return "q5_k";
+    case KQ_Q2_K: return "q2_k";
     case KQ_Q4_1: return "q4_1";
     case KQ_Q5_0: return "q5_0";
     case KQ_Q5_1: return "q5_1";
@@ -50,6 +51,7 @@ bool geometry(int c, int* bv, int* bb) {
     case KQ_Q8_0: *bv = 32; *bb = 34; return true;
     case KQ_Q4_K: *bv = 256; *bb = 144; return true;
     case KQ_Q5_K: *bv = 256; *bb = 176; return true;
+    case KQ_Q2_K: *bv = 256; *bb = 84; return true;
     case KQ_Q4_1: *bv = 32; *bb = 20; return true;
     case KQ_Q5_0: *bv = 32; *bb = 22; return true;
     case KQ_Q5_1: *bv = 32; *bb = 24; return true;
@@ -118,13 +120,13 @@ int kq_codec_from_name(const char* name, int* codec) {
   low[i] = 0;
   static const struct { const char* n; int c; } table[] = {
       {"q4_0", KQ_Q4_0}, {"q8_0", KQ_Q8_0}, {"q4_k", KQ_Q4_K}, {"q5_k", KQ_Q5_K}, {"q6_k", KQ_Q6_K},
-      {"q4_1", KQ_Q4_1}, {"q5_0", KQ_Q5_0}, {"q5_1", KQ_Q5_1}};
+      {"q4_1", KQ_Q4_1}, {"q5_0", KQ_Q5_0}, {"q5_1", KQ_Q5_1}, {"q2_k", KQ_Q2_K}};
   for (const auto& t : table)
     if (!name[i] && strcmp(low, t.n) == 0) {
       *codec = t.c;
       return KQ_OK;
     }
-  return fail(KQ_ERR_CODEC, "kq_codec_from_name", "unknown codec '%s' (known: q4_0, q4_1, q5_0, q5_1, q8_0, q4_k, q5_k, q6_k)", name);
+  return fail(KQ_ERR_CODEC, "kq_codec_from_name", "unknown codec '%s' (known: q4_0, q4_1, q5_0, q5_1, q8_0, q2_k, q4_k, q5_k, q6_k)", name);
 }
 
 int kq_codec_info(int codec, int* block_values, int* block_bytes) {

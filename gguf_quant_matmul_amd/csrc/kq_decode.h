@@ -77,6 +77,23 @@ __device__ __forceinline__ void decode8<Q5_1>(const uint8_t* __restrict__ row, i
 }
 
 template <>
+__device__ __forceinline__ void decode8<Q2_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  const uint8_t* blk = row + (v0 / 256) * 84;  // 4-byte aligned: rows are multiples of 84 bytes
+  const int vi = (int)(v0 % 256);
+  const int h = vi / 128, c = (vi % 128) / 32, l0 = vi % 32;
+  const uint32_t sb = blk[vi / 16];
+  const uint32_t dd = ld_u32(blk + 80);
+  const float dsc = f16_to_f32(dd) * (float)(sb & 15u);        // exact
+  const float dm = f16_to_f32(dd >> 16) * (float)(sb >> 4);    // exact
+  const u32x2 q = *(const u32x2*)(blk + 16 + 32 * h + l0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t code = ((i < 4 ? q.x : q.y) >> (8 * (i & 3) + 2 * c)) & 3u;
+    out[i] = dsc * (float)code - dm;  // one rounding
+  }
+}
+
+template <>
 __device__ __forceinline__ void decode8<Q4_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
   const uint8_t* blk = row + (v0 / 256) * 144;  // 16-byte aligned: rows are multiples of 144 bytes
   const int vi = (int)(v0 % 256);

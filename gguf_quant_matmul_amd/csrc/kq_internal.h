@@ -12,6 +12,10 @@
 //   q5_0  22 B: [0:2] d, [2:6] qh (uint32), [6:22] qs; fifth bit of value v
 //         is bit v of qh; value = d*(q-16)
 //   q5_1  24 B: [0:2] d, [2:4] m, [4:8] qh, [8:24] qs; value = d*q + m
+//   q2_K  84 B: [0:16] scales (byte j: sub-block j of 16 values, scale in the
+//         low nibble, min in the high), [16:80] qs, [80:82] d, [82:84] dmin;
+//         v -> h=v/128, c=(v%128)/32, l=v%32: code = (qs[32h+l] >> 2c) & 3;
+//         value = (d*sc_j)*q - dmin*m_j, j = v/16
 //   q5_K 176 B: [0:16] as q4_K, [16:48] qh, [48:176] qs; the low four bits
 //         as q4_K's nibbles (at qs), the fifth bit of value l of sub-block j
 //         is bit j of qh[l]; value = (d*sc_j)*q - dmin*m_j, q in 0..31
@@ -26,7 +30,7 @@
 
 namespace kq {
 
-enum Codec : int { Q4_0 = 2, Q4_1 = 3, Q5_0 = 6, Q5_1 = 7, Q8_0 = 8, Q4_K = 12, Q5_K = 13, Q6_K = 14 };
+enum Codec : int { Q4_0 = 2, Q4_1 = 3, Q5_0 = 6, Q5_1 = 7, Q8_0 = 8, Q2_K = 10, Q4_K = 12, Q5_K = 13, Q6_K = 14 };
 
 template <int C> struct Geo;
 template <> struct Geo<Q4_0> { static constexpr int BV = 32;  static constexpr int BB = 18; };
@@ -35,6 +39,7 @@ template <> struct Geo<Q4_1> { static constexpr int BV = 32;  static constexpr i
 template <> struct Geo<Q5_0> { static constexpr int BV = 32;  static constexpr int BB = 22; };
 template <> struct Geo<Q5_1> { static constexpr int BV = 32;  static constexpr int BB = 24; };
 template <> struct Geo<Q4_K> { static constexpr int BV = 256; static constexpr int BB = 144; };
+template <> struct Geo<Q2_K> { static constexpr int BV = 256; static constexpr int BB = 84; };
 template <> struct Geo<Q5_K> { static constexpr int BV = 256; static constexpr int BB = 176; };
 template <> struct Geo<Q6_K> { static constexpr int BV = 256; static constexpr int BB = 210; };
 

@@ -117,6 +117,42 @@ template <> struct HalfUnit<Q4_K> {
   }
 };
 
+template <> struct HalfUnit<Q2_K> {
+  // unit u' = u % 4 (half h = u' / 2, shifts c0 = 2 (u' % 2), c0 + 1); half
+  // hh takes shift c0 + hh: segment 2hh (positions 0..15, sub-block 4u' +
+  // 2hh) and 2hh + 1 (16..31, sub-block 4u' + 2hh + 1).
+  u32x4 q0, q1;
+  uint32_t sc, dd;
+  __device__ __forceinline__ void load(const uint8_t* row, int u, int) {
+    const uint8_t* blk = row + (u >> 2) * 84;
+    const int up = u & 3;
+    q0 = ld_16B_a4(blk + 16 + 32 * (up >> 1));
+    q1 = ld_16B_a4(blk + 32 + 32 * (up >> 1));
+    sc = ld_u32(blk + 4 * up);
+    dd = ld_u32(blk + 80);
+  }
+  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+    const float d = f16_to_f32(dd), dmin = f16_to_f32(dd >> 16);
+    const int shift = 2 * (2 * (u & 1) + hh);
+    const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {  // segment 2hh + g
+      const uint32_t b = (sc >> (8 * (2 * hh + g))) & 0xFFu;
+      const float s = d * (float)(b & 15u), c = -(1024.f * s + dmin * (float)(b >> 4));
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = (qw[4 * g + i] >> shift) & 0x03030303u;
+        const half2_t c01 = as_h2(pair01(code)), c23 = as_h2(pair23(code));
+        o[2 * i] = pack_h2(fmaf((float)c01.x, s, c), fmaf((float)c01.y, s, c));
+        o[2 * i + 1] = pack_h2(fmaf((float)c23.x, s, c), fmaf((float)c23.y, s, c));
+      }
+      st_chunk(dst, sw, 4 * hh + 2 * g, u32x4{o[0], o[1], o[2], o[3]});
+      st_chunk(dst, sw, 4 * hh + 2 * g + 1, u32x4{o[4], o[5], o[6], o[7]});
+    }
+  }
+};
+
 template <> struct HalfUnit<Q5_K> {
   // q4_K's half unit with 5-bit codes: the fifth bits of positions l in
   // [16hh, 16hh+16) are bits 2P (sub-block 2P) and 2P + 1 of qh[l].
@@ -670,6 +706,7 @@ hipError_t launch_pass(int codec, const uint8_t* w, int64_t n, int64_t k, int64_
     case Q4_1: return launch_dense<Q4_1, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q5_0: return launch_dense<Q5_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q5_1: return launch_dense<Q5_1, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q2_K: return launch_dense<Q2_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q4_K: return launch_dense<Q4_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q5_K: return launch_dense<Q5_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q6_K: return launch_dense<Q6_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);

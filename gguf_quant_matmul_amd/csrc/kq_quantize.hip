@@ -16,13 +16,18 @@
 //   q5_0 : d = f16(amax/15);             q = rint(w/D) + 16
 //   q5_1 : d = f16((max w - min w)/31), m = f16(min w); q = rint((w - M)/D)
 //   q5_K : as q4_K with scale = (hi - lo)/31 and q in 0..31
+//   q2_K : per 16 values lo = min(0, min w), hi = max w, scale = (hi-lo)/3,
+//          min = -lo; d = f16(max scale/15), dmin = f16(max min/15);
+//          sc = rint(scale/D), m = rint(min/DM) (0..15);
+//          q = rint((w + DM*m)/(D*sc)) (0..3)
 //   q6_K : per 16 values scale = amax/31; d = f16(max scale/127);
 //          sc = rint(scale/D) (-128..127); q = rint(w/(D*sc)) + 32
 // Codes are clamped to the codec's range, then moved to the nearest point of
 // the block's decoded grid among q-1, q, q+1 (distance |w - decode(q)| in
 // float64, ties to the lower code).  A zero grid step gives the zero-point
-// code (q8_0 0, q4_0 8, q4_1 and q5_1 0, q5_0 16, q4_K and q5_K 0, q6_K 32).
-// One thread per block (32-value codecs) or superblock (q4_K, q5_K, q6_K);
+// code (q8_0 0, q4_0 8, q4_1 and q5_1 0, q5_0 16, q2_K, q4_K and q5_K 0,
+// q6_K 32).  One thread per block (32-value codecs) or superblock (q2_K,
+// q4_K, q5_K, q6_K);
 // not a hot path.
 #include "kq_internal.h"
 
@@ -226,6 +231,52 @@ __global__ __launch_bounds__(256) void quant_k_affine(const float* __restrict__ 
   }
 }
 
+__global__ __launch_bounds__(256) void quant_q2_k(const float* __restrict__ w, int64_t nsb, int kb, int64_t row_bytes,
+                                                  uint8_t* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= nsb) return;
+  const int64_t r = g / kb, b = g % kb;
+  const float* x = w + (r * kb + b) * 256;
+  float scale[16], mins[16];
+  float smax = 0.f, mmax = 0.f;
+  for (int j = 0; j < 16; ++j) {
+    float lo = x[16 * j], hi = x[16 * j];
+    for (int i = 1; i < 16; ++i) { lo = fminf(lo, x[16 * j + i]); hi = fmaxf(hi, x[16 * j + i]); }
+    lo = fminf(0.f, lo);
+    scale[j] = (hi - lo) / 3.f;
+    mins[j] = -lo;
+    smax = j ? fmaxf(smax, scale[j]) : scale[j];
+    mmax = j ? fmaxf(mmax, mins[j]) : mins[j];
+  }
+  const uint32_t db = f16_bits(smax / 15.f), mb = f16_bits(mmax / 15.f);
+  const float D = f16_val(db), DM = f16_val(mb);
+  uint8_t* o = out + r * row_bytes + b * 84;  // 4-byte aligned
+  uint32_t sw[4] = {0, 0, 0, 0}, qw[16];
+  for (int i = 0; i < 16; ++i) qw[i] = 0;
+  for (int j = 0; j < 16; ++j) {
+    const int sc = D > 0.f ? (int)clampf(rintf(scale[j] / D), 0.f, 15.f) : 0;
+    const int m = DM > 0.f ? (int)clampf(rintf(mins[j] / DM), 0.f, 15.f) : 0;
+    sw[j >> 2] |= (uint32_t)(sc | (m << 4)) << (8 * (j & 3));
+    const float S = D * (float)sc, MN = DM * (float)m;
+    for (int i = 0; i < 16; ++i) {
+      const int v = 16 * j + i;
+      int q;
+      if (S == 0.f) {
+        q = 0;
+      } else {
+        const float xv = x[v];
+        const int q0 = (int)clampf(rintf((xv + MN) / S), 0.f, 3.f);
+        q = nearest(xv, q0, 0, 3, [S, MN](int c) { return S * (float)c - MN; });
+      }
+      const int h = v / 128, c = (v % 128) / 32, l = v % 32, p = 32 * h + l;
+      qw[p >> 2] |= (uint32_t)q << (8 * (p & 3) + 2 * c);
+    }
+  }
+  for (int i = 0; i < 4; ++i) *(uint32_t*)(o + 4 * i) = sw[i];
+  for (int i = 0; i < 16; ++i) *(uint32_t*)(o + 16 + 4 * i) = qw[i];
+  *(uint32_t*)(o + 80) = db | (mb << 16);
+}
+
 __global__ __launch_bounds__(256) void quant_q6_k(const float* __restrict__ w, int64_t nsb, int kb, int64_t row_bytes,
                                                   uint8_t* __restrict__ out) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -275,7 +326,7 @@ __global__ __launch_bounds__(256) void quant_q6_k(const float* __restrict__ w, i
 
 hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, int64_t rb, uint8_t* out,
                            hipStream_t s) {
-  const int bv = (codec == Q4_K || codec == Q5_K || codec == Q6_K) ? 256 : 32;
+  const int bv = (codec == Q2_K || codec == Q4_K || codec == Q5_K || codec == Q6_K) ? 256 : 32;
   const int kb = (int)(k / bv);
   const int64_t nblk = rows * kb;
   const dim3 grid((unsigned)((nblk + 255) / 256)), block(256);
@@ -285,6 +336,7 @@ hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, i
     case Q4_1: hipLaunchKernelGGL(quant_leg<Q4_1>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q5_0: hipLaunchKernelGGL(quant_leg<Q5_0>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q5_1: hipLaunchKernelGGL(quant_leg<Q5_1>, grid, block, 0, s, w, nblk, kb, rb, out); break;
+    case Q2_K: hipLaunchKernelGGL(quant_q2_k, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q4_K: hipLaunchKernelGGL(quant_k_affine<15>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q5_K: hipLaunchKernelGGL(quant_k_affine<31>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q6_K: hipLaunchKernelGGL(quant_q6_k, grid, block, 0, s, w, nblk, kb, rb, out); break;

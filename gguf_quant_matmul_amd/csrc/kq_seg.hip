@@ -274,6 +274,7 @@ hipError_t launch_seg_mma(int codec, const uint8_t* w, int64_t n_experts, int64_
   switch (codec) {
     case Q4_0: return launch_seg_mma_c<Q4_0>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q8_0: return launch_seg_mma_c<Q8_0>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
+    case Q2_K: return launch_seg_mma_c<Q2_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q4_K: return launch_seg_mma_c<Q4_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q5_K: return launch_seg_mma_c<Q5_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q4_1: return launch_seg_mma_c<Q4_1>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);

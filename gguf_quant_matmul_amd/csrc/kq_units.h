@@ -174,6 +174,63 @@ struct UnitQ5K {
   }
 };
 
+// q2_K: unit u' = u % 4 of a superblock is half h = u' / 2 with code shifts
+// 2 c0 (values 0..31) and 2 c0 + 2 (32..63), c0 = 2 (u' % 2): the 32 qs
+// bytes of half h, the scale bytes of sub-blocks 4u'..4u'+3 and d, dmin.
+// Sub-block t of the unit (16 values) is shift c0 + t / 2, qs dwords
+// 4 (t % 2) .. 4 (t % 2) + 3.
+struct UnitQ2K {
+  u32x4 q0, q1;
+  uint32_t sc, dd;
+  __device__ __forceinline__ void load(const uint8_t* row, int u) {
+    const uint8_t* blk = row + (u >> 2) * 84;  // dword aligned
+    const int up = u & 3;
+    q0 = ld_16B_a4(blk + 16 + 32 * (up >> 1));
+    q1 = ld_16B_a4(blk + 32 + 32 * (up >> 1));
+    sc = ld_u32(blk + 4 * up);
+    dd = ld_u32(blk + 80);
+  }
+  __device__ __forceinline__ void bload(rsrc_t rs, int rowoff, int cu, int u4) {
+    const int so = (u4 >> 2) * 84;
+    q0 = bld16(rs, rowoff + 16 + 32 * (cu >> 1), so);
+    q1 = bld16(rs, rowoff + 32 + 32 * (cu >> 1), so);
+    sc = bld4(rs, rowoff + 4 * cu, so);
+    dd = bld4(rs, rowoff + 80, so);
+  }
+  template <int M>
+  __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
+    const float d = f16_to_f32(dd), dmin = f16_to_f32(dd >> 16);
+    const int c0 = 2 * (u & 1);
+    const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    float dsc[4], dm[4];
+    uint32_t p[4][8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t b = (sc >> (8 * t)) & 0xFFu;
+      dsc[t] = d * (float)(b & 15u);
+      dm[t] = dmin * (float)(b >> 4);
+      const int shift = 2 * (c0 + (t >> 1));
+      uint32_t c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = (qw[4 * (t & 1) + i] >> shift) & 0x03030303u;
+      pairs16(c, p[t]);
+    }
+    const int base = 64 * u;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float4_t xs = *(const float4_t*)&xv.xsum[m * xv.sstride + ((base - xv.c0) >> 4)];
+      const float x[4] = {xs.x, xs.y, xs.z, xs.w};
+      float tot = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const float st = dot16(p[t], xv.pairs(m, base + 16 * t), 0.f);
+        tot += dsc[t] * (st - 1024.f * x[t]) - dm[t] * x[t];
+      }
+      acc[m] += tot;
+    }
+  }
+};
+
 // 16 bytes at a 2-byte aligned address: dwords loaded from the dword-aligned
 // address below it, then shifted by (addr & 3) bytes.
 struct Shift16 {
@@ -417,6 +474,7 @@ struct UnitLeg {
 
 template <int C> struct UnitOf;
 template <> struct UnitOf<Q4_K> { typedef UnitQ4K T; };
+template <> struct UnitOf<Q2_K> { typedef UnitQ2K T; };
 template <> struct UnitOf<Q5_K> { typedef UnitQ5K T; };
 template <> struct UnitOf<Q6_K> { typedef UnitQ6K T; };
 template <> struct UnitOf<Q8_0> { typedef UnitQ8_0 T; };
@@ -483,6 +541,35 @@ template <> struct MmaSlices<Q4_K> {
       slice8(qw[2 * t] & 0x0F0F0F0Fu, qw[2 * t + 1] & 0x0F0F0F0Fu, s0, c0, f);
     else
       slice8(qw[2 * t] & 0xF0F0F0F0u, qw[2 * t + 1] & 0xF0F0F0F0u, s1, c1, f);
+  }
+};
+
+template <> struct MmaSlices<Q2_K> {
+  // slice S: sub-block t = S / 2 (its own scale and min), qs dwords
+  // 4 (t % 2) + 2 (S % 2) and the next, code shift 2 c0 + 2 (S / 4); the
+  // codes are kept shifted by 2 c0 so that the rest is compile-time.
+  // weight = fma(1024 + q, d sc, -(1024 d sc + dmin m))
+  uint32_t qs[8];
+  float s[4], c[4];
+  __device__ __forceinline__ MmaSlices(const UnitQ2K& un, int u, bool keep) {
+    const float d = keep ? f16_to_f32(un.dd) : 0.f, dmin = keep ? f16_to_f32(un.dd >> 16) : 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t b = (un.sc >> (8 * t)) & 0xFFu;
+      s[t] = d * (float)(b & 15u);
+      c[t] = -(1024.f * s[t] + dmin * (float)(b >> 4));
+    }
+    const int sh = 4 * (u & 1);
+    qs[0] = un.q0.x >> sh; qs[1] = un.q0.y >> sh; qs[2] = un.q0.z >> sh; qs[3] = un.q0.w >> sh;
+    qs[4] = un.q1.x >> sh; qs[5] = un.q1.y >> sh; qs[6] = un.q1.z >> sh; qs[7] = un.q1.w >> sh;
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int t = S >> 1, i0 = 4 * (t & 1) + 2 * (S & 1), sh = 2 * (S >> 2);
+    slice8((qs[i0] >> sh) & 0x03030303u, (qs[i0 + 1] >> sh) & 0x03030303u, s[t], c[t], f);
   }
 };
 

@@ -23,7 +23,7 @@
  *  - Activations x are float16, row-major [M][K].
  *  - w and x must be 16-byte aligned, y/out 16-byte aligned, map/counts/ids
  *    4-byte aligned: otherwise KQ_ERR_ALIGN.
- *  - K must be a positive multiple of the codec's block (256 for q4_K, q5_K and
+ *  - K must be a positive multiple of the codec's block (256 for q2_K, q4_K, q5_K and
  *    q6_K, 32 for the others): otherwise KQ_ERR_SHAPE.  Sizes must be
  *    below 2^31 (element counts below 2^40).
  *  - On any error nothing is launched and outputs are untouched; the return
@@ -42,18 +42,19 @@ extern "C" {
 
 /* Codec ids: GGML's type numbers for these codecs (the names are the
  * authority: "q4_0", "q4_1", "q5_0", "q5_1", "q8_0", "q4_k", "q5_k",
- * "q6_k").  Geometry per the mlx-kquant README "Codec reference" table:
+ * "q2_k", "q6_k").  Geometry per the mlx-kquant README "Codec reference" table:
  *   q4_0  32 values,  4 bits,  18 bytes per block (scale)
  *   q4_1  32 values,  4 bits,  20 bytes per block (scale + min)
  *   q5_0  32 values,  5 bits,  22 bytes per block (scale)
  *   q5_1  32 values,  5 bits,  24 bytes per block (scale + min)
  *   q8_0  32 values,  8 bits,  34 bytes per block
+ *   q2_K 256 values,  2 bits,  84 bytes per superblock
  *   q4_K 256 values,  4 bits, 144 bytes per superblock
  *   q5_K 256 values,  5 bits, 176 bytes per superblock
  *   q6_K 256 values,  6 bits, 210 bytes per superblock */
 typedef enum {
   KQ_Q4_0 = 2, KQ_Q4_1 = 3, KQ_Q5_0 = 6, KQ_Q5_1 = 7, KQ_Q8_0 = 8,
-  KQ_Q4_K = 12, KQ_Q5_K = 13, KQ_Q6_K = 14
+  KQ_Q2_K = 10, KQ_Q4_K = 12, KQ_Q5_K = 13, KQ_Q6_K = 14
 } kq_codec;
 
 /* Output element types. */
