@@ -15,7 +15,7 @@ What the pages fix
     bytes ("K-quant superblock"); q4_1 32 values, 4 bits, 20 bytes ("block
     scale + min"); q5_0 32 values, 5 bits, 22 bytes ("block scale"); q5_1 32
     values, 5 bits, 24 bytes ("block scale + min"); q2_k 256 values, 2 bits,
-    84 bytes ("K-quant superblock").  Their layouts are not on the pages and
+    84 bytes, and q3_k 256 values, 3 bits, 110 bytes ("K-quant superblock").  Their layouts are not on the pages and
     take reading R1 like the others.
   * The q4_K sub-block structure (8 sub-blocks of 32, 6-bit scale and min per
     sub-block, fp16 d and dmin) and the q6_K one (16 sub-blocks of 16, int8
@@ -30,7 +30,8 @@ Readings taken where the pages are silent (each is also listed in the design doc)
       honoured, the sign of zero kept, inf/NaN passed through).
   R3  Arithmetic: each value is the exact real number of the formula, rounded
       ONCE to fp32 (RNE).  For q8_0, q4_0, q5_0 and q6_K the exact value is
-      already an fp32 number.  For q2_K, q4_K and q5_K the only rounding is
+      already an fp32 number, as is q3_K's ``d*sc*q``.  For q2_K, q4_K and
+      q5_K the only rounding is
       that of ``(d*sc)*q - (dmin*m)``; for q4_1 and q5_1 that of ``d*q + m`` (exact in
       float64: its bits span at most 2^-24 .. 2^21).
   R4  float16 output is RNE of the fp32 value (so q4_K -> f16 rounds twice, by
@@ -62,6 +63,7 @@ GEOMETRY = {
     "q5_0": (32, 5, 22),
     "q5_1": (32, 5, 24),
     "q2_k": (256, 2, 84),
+    "q3_k": (256, 3, 110),
 }
 
 CODECS = tuple(GEOMETRY)
@@ -254,6 +256,45 @@ def fields_q2_k(blk: np.ndarray):
     return d, dmin, sc, m, q  # sc, m: [.., 16]; q: [.., 256]
 
 
+def scales_q3_k(s: np.ndarray) -> np.ndarray:
+    """The 12 packed scale bytes of a q3_K superblock -> 16 signed scales.
+
+    Scale j (6 bits, stored with +32): its low four bits are the low nibble of
+    s[j] for j < 8 and the high nibble of s[j - 8] for j >= 8; its top two
+    bits are bits 2(j // 4) .. 2(j // 4) + 1 of s[8 + j % 4].
+    """
+    s = s.astype(np.int64)
+    out = np.empty(s.shape[:-1] + (16,), dtype=np.int64)
+    for j in range(16):
+        low4 = (s[..., j] & 15) if j < 8 else (s[..., j - 8] >> 4)
+        high2 = (s[..., 8 + j % 4] >> (2 * (j // 4))) & 3
+        out[..., j] = (low4 | (high2 << 4)) - 32
+    return out
+
+
+def fields_q3_k(blk: np.ndarray):
+    """q3_K, 110 bytes: [0:32] hmask, [32:96] qs, [96:108] packed scales,
+    [108:110] d.
+
+    Value v: h = v // 128, c = (v % 128) // 32, l = v % 32; low two bits =
+    bits 2c..2c+1 of qs[32h + l], high bit = bit 4h + c of hmask[l]; the code
+    is low2 - 4 when the high bit is clear, low2 when it is set (-4..3).
+    value = d*sc_j*q, j = v // 16.
+    """
+    hm = blk[..., 0:32].astype(np.int64)
+    qs = blk[..., 32:96].astype(np.int64)
+    sc = scales_q3_k(blk[..., 96:108])
+    d = f16_bits_to_f64(le_u16(blk[..., 108], blk[..., 109]))
+    q = np.empty(qs.shape[:-1] + (256,), dtype=np.int64)
+    for v in range(256):
+        h, r = divmod(v, 128)
+        c, l = divmod(r, 32)
+        low2 = (qs[..., 32 * h + l] >> (2 * c)) & 3
+        hbit = (hm[..., l] >> (4 * h + c)) & 1
+        q[..., v] = low2 - 4 * (1 - hbit)
+    return d, sc, q  # sc [.., 16] signed; q [.., 256] in -4..3
+
+
 def fields_q6_k(blk: np.ndarray):
     """q6_K, 210 bytes: [0:128] ql, [128:192] qh, [192:208] 16 int8 scales, [208:210] d.
 
@@ -319,6 +360,9 @@ def dequantize(codec: str, w: np.ndarray, k: int, dtype=np.float32) -> np.ndarra
         elif codec == "q5_0":
             d, _, q = fields_legacy(codec, blk)
             y = _exact_f32(d[..., None] * (q - 16))
+        elif codec == "q3_k":
+            d, sc, q = fields_q3_k(blk)
+            y = _exact_f32(np.repeat(d[..., None] * sc, 16, axis=-1) * q)
         elif codec == "q2_k":
             d, dmin, sc, m, q = fields_q2_k(blk)
             step = np.repeat(d[..., None] * sc, 16, axis=-1)  # [n, nb, 256]

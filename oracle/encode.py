@@ -30,6 +30,10 @@ the same bytes.  ``rint`` rounds half to even; ``f16()`` is RNE to binary16.
          scale_j = (hi - lo)/3, min_j = -lo; d = f16(max scale_j / 15),
          dmin = f16(max min_j / 15); sc_j = rint(scale_j/D), m_j =
          rint(min_j/DM) (0..15); q = rint((w + DM*m_j) / (D*sc_j)) (0..3)
+  q3_K : per 16-value sub-block j: scale_j = amax_j/3;
+         d = f16(max_j |scale_j| / 31); sc_j = rint(scale_j/D) (-32..31);
+         q = rint(w/(D*sc_j)) (-4..3), stored as q + 4 split into two low
+         bits and a high bit
   q6_K : per 16-value sub-block j: scale_j = amax_j/31;
          d = f16(max_j scale_j / 127); sc_j = rint(scale_j/D) (clamped -128..127);
          q = rint(w/(D*sc_j)) + 32
@@ -38,7 +42,7 @@ NEAREST point of the block's decoded grid among {q-1, q, q+1} (distance
 |w - decode(q)| taken in float64; ties go to the lower code), so that every
 code is the nearest grid point.  Where the grid step is zero the code is the
 zero-point code (q8_0: 0, q4_0: 8, q4_1 and q5_1: 0, q5_0: 16, q4_K and
-q5_K: 0, q2_K: 0, q6_K: 32).
+q5_K: 0, q2_K: 0, q3_K: 0 (stored 4), q6_K: 32).
 
 Pins (tests/test_oracle_encode.py): brute force over every code of the block
 on tiny tensors (the chosen code is a nearest grid point, ties to the lower
@@ -297,6 +301,47 @@ def encode_q2_k(w: np.ndarray) -> np.ndarray:
     return out.reshape(w.shape[:-1] + (row_bytes("q2_k", k),))
 
 
+def encode_q3_k(w: np.ndarray) -> np.ndarray:
+    w2, k = _rows(w, "q3_k")
+    x = w2.reshape(w2.shape[0], k // 256, 16, 16)
+    amax = np.max(np.abs(x), axis=-1)  # [n, nb, 16]
+    scale = _div(amax, F32(3))
+    dbits = _f16_bits(_div(np.max(scale, axis=-1), F32(31)))
+    D = _f16_value(dbits)[..., None]
+    sc = np.where(D > 0, np.clip(np.rint(_div(scale, D)), -32, 31), 0).astype(np.int64)
+    S = (D * sc.astype(F32)).astype(F32)[..., None]  # exact: 11 x 6 bits
+    q0 = np.clip(np.rint(_div(x, S)), -4, 3)
+    q0 = np.where(S == 0, 0, q0).astype(np.int64)
+
+    def dec(q):
+        return (S * q.astype(F32)).astype(F32)
+
+    q = np.where(S == 0, 0, _nearest(x, q0, -4, 3, dec)).reshape(x.shape[:2] + (256,))
+    u = q + 4  # 0..7: bit 2 is the hmask bit
+    out = np.zeros(x.shape[:2] + (110,), dtype=np.uint8)
+    hm = np.zeros(x.shape[:2] + (32,), dtype=np.int64)
+    qs = np.zeros(x.shape[:2] + (64,), dtype=np.int64)
+    for v in range(256):
+        h, r = divmod(v, 128)
+        c, l = divmod(r, 32)
+        qs[..., 32 * h + l] |= (u[..., v] & 3) << (2 * c)
+        hm[..., l] |= (u[..., v] >> 2) << (4 * h + c)
+    out[..., 0:32] = hm.astype(np.uint8)
+    out[..., 32:96] = qs.astype(np.uint8)
+    st = sc + 32  # 0..63
+    sb = np.zeros(x.shape[:2] + (12,), dtype=np.int64)
+    for j in range(16):
+        if j < 8:
+            sb[..., j] |= st[..., j] & 15
+        else:
+            sb[..., j - 8] |= (st[..., j] & 15) << 4
+        sb[..., 8 + j % 4] |= (st[..., j] >> 4) << (2 * (j // 4))
+    out[..., 96:108] = sb.astype(np.uint8)
+    out[..., 108] = dbits & 255
+    out[..., 109] = dbits >> 8
+    return out.reshape(w.shape[:-1] + (row_bytes("q3_k", k),))
+
+
 def encode_q6_k(w: np.ndarray) -> np.ndarray:
     w2, k = _rows(w, "q6_k")
     x = w2.reshape(w2.shape[0], k // 256, 16, 16)
@@ -343,6 +388,7 @@ ENCODERS = {
     "q5_0": encode_q5_0,
     "q5_1": lambda w: encode_affine_min(w, "q5_1"),
     "q2_k": encode_q2_k,
+    "q3_k": encode_q3_k,
 }
 
 
@@ -353,4 +399,4 @@ def quantize(codec: str, w: np.ndarray) -> np.ndarray:
 
 assert all(block_bytes(c) == b for c, b in (("q4_k", 144), ("q6_k", 210), ("q8_0", 34), ("q4_0", 18), ("q5_k", 176),
                                               ("q4_1", 20), ("q5_0", 22), ("q5_1", 24),
-                                              ("q2_k", 84)))
+                                              ("q2_k", 84), ("q3_k", 110)))

@@ -34,6 +34,7 @@ def test_codec_table_byte_totals():
     assert codecs.GEOMETRY["q5_0"] == (32, 5, 22) and 2 + 4 + 16 == 22          # d, qh, qs
     assert codecs.GEOMETRY["q5_1"] == (32, 5, 24) and 2 + 2 + 4 + 16 == 24      # d, m, qh, qs
     assert codecs.GEOMETRY["q2_k"] == (256, 2, 84) and 16 + 64 + 2 + 2 == 84    # scales, qs, d, dmin
+    assert codecs.GEOMETRY["q3_k"] == (256, 3, 110) and 32 + 64 + 12 + 2 == 110  # hmask, qs, scales, d
     # The layout reading must account for every byte of the block.
     assert 2 + 2 + 12 + 128 == 144          # d, dmin, scales, qs
     assert 128 + 64 + 16 + 2 == 210         # ql, qh, scales, d
@@ -83,7 +84,7 @@ def _load_golden(name):
 
 @pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt",
                                   "q5_k_block.txt", "q4_1_block.txt", "q5_0_block.txt", "q5_1_block.txt",
-                                  "q2_k_block.txt"])
+                                  "q2_k_block.txt", "q3_k_block.txt"])
 @pytest.mark.parametrize("dtype", [np.float32, np.float16])
 def test_golden_hand_decoded_blocks(name, dtype):
     codec, blk, values = _load_golden(name)
@@ -152,6 +153,23 @@ def _hand_pack(codec, rng, nblocks):
         for v in range(32):
             out[:, o + (v % 16)] |= ((q[:, v] & 15) << (4 * (v // 16))).astype(np.uint8)
         return out, dict(d=d, m=mm, q=q)
+    if codec == "q3_k":
+        q = rng.integers(-4, 4, size=(nblocks, 256))
+        sc = rng.integers(-32, 32, size=(nblocks, 16))
+        d = rng.integers(0, 0x7C00, size=nblocks) | (rng.integers(0, 2, size=nblocks) << 15)
+        out = np.zeros((nblocks, 110), np.uint8)
+        for v in range(256):
+            h, r = divmod(v, 128)
+            c, l = divmod(r, 32)
+            u = q[:, v] + 4
+            out[:, 32 + 32 * h + l] |= ((u & 3) << (2 * c)).astype(np.uint8)
+            out[:, l] |= ((u >> 2) << (4 * h + c)).astype(np.uint8)
+        st = sc + 32
+        for j in range(16):
+            out[:, 96 + (j % 8)] |= ((st[:, j] & 15) << (4 * (j // 8))).astype(np.uint8)
+            out[:, 104 + (j % 4)] |= ((st[:, j] >> 4) << (2 * (j // 4))).astype(np.uint8)
+        out[:, 108], out[:, 109] = d & 255, d >> 8
+        return out, dict(d=d, sc=sc, q=q)
     if codec == "q2_k":
         q = rng.integers(0, 4, size=(nblocks, 256))
         sc = rng.integers(0, 16, size=(nblocks, 16))
@@ -232,6 +250,7 @@ def _affine(codec, f):
       q4_K : code q (4 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 32)
       q5_K : code q (5 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 32)
       q2_K : code q (2 bits),     scale d*sc_j, bias -dmin*m_j   (groups of 16)
+      q3_K : code q+4 (3 bits),   scale d*sc_j, bias -4 d*sc_j   (groups of 16)
       q4_1 : code q (4 bits),     scale d,      bias m
       q5_0 : code q (5 bits),     scale d,      bias -16 d
       q5_1 : code q (5 bits),     scale d,      bias m
@@ -253,6 +272,10 @@ def _affine(codec, f):
         elif codec == "q5_0":
             d = half(f["d"][i])
             params = [(d, -16 * d, int(q)) for q in f["q"][i]]
+        elif codec == "q3_k":
+            d = half(f["d"][i])
+            params = [(d * int(f["sc"][i][v // 16]), -4 * d * int(f["sc"][i][v // 16]), int(f["q"][i][v]) + 4)
+                      for v in range(256)]
         elif codec == "q2_k":
             d, dm = half(f["d"][i]), half(f["dm"][i])
             params = [(d * int(f["sc"][i][v // 16]), -dm * int(f["m"][i][v // 16]), int(f["q"][i][v])) for v in range(256)]
@@ -280,6 +303,9 @@ def test_hand_packed_codes_decode_to_affine_closed_form(codec):
         d, dmin, sc, m, q = codecs.fields_q5_k(blocks[:, None, :])
         assert np.array_equal(sc[:, 0], fields["sc"]) and np.array_equal(m[:, 0], fields["m"])
         assert np.array_equal(q[:, 0].reshape(24, 256), fields["q"])
+    elif codec == "q3_k":
+        d, sc, q = codecs.fields_q3_k(blocks[:, None, :])
+        assert np.array_equal(sc[:, 0], fields["sc"]) and np.array_equal(q[:, 0], fields["q"])
     elif codec == "q2_k":
         d, dmin, sc, m, q = codecs.fields_q2_k(blocks[:, None, :])
         assert np.array_equal(sc[:, 0], fields["sc"]) and np.array_equal(m[:, 0], fields["m"])

@@ -32,6 +32,10 @@ def _all_codes_block(codec, blk, c):
             b[..., o - 4:o] = np.uint8(255 * (c >> 4))
     elif codec == "q2_k":
         b[..., 16:80] = np.uint8(c * 0x55)
+    elif codec == "q3_k":
+        u = c + 4
+        b[..., 0:32] = np.uint8(255 * (u >> 2))
+        b[..., 32:96] = np.uint8((u & 3) * 0x55)
     elif codec == "q5_k":
         lo, h1 = c & 15, c >> 4
         b[..., 16:48] = np.uint8(255 * h1)
@@ -45,7 +49,7 @@ def _all_codes_block(codec, blk, c):
 
 CODE_RANGE = {"q8_0": range(-128, 128), "q4_0": range(16), "q4_k": range(16), "q6_k": range(64),
               "q5_k": range(32), "q4_1": range(16), "q5_0": range(32), "q5_1": range(32),
-              "q2_k": range(4)}
+              "q2_k": range(4), "q3_k": range(-4, 4)}
 
 
 def _codes(codec, blk):
@@ -59,6 +63,8 @@ def _codes(codec, blk):
         return codecs.fields_q5_k(blk)[4].reshape(blk.shape[0], -1)
     if codec == "q2_k":
         return codecs.fields_q2_k(blk)[4].reshape(blk.shape[0], -1)
+    if codec == "q3_k":
+        return codecs.fields_q3_k(blk)[2].reshape(blk.shape[0], -1)
     if codec in ("q4_1", "q5_0", "q5_1"):
         return codecs.fields_legacy(codec, blk)[2].reshape(blk.shape[0], -1)
     return codecs.fields_q6_k(blk)[2].reshape(blk.shape[0], -1)
