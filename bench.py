@@ -260,11 +260,11 @@ def cold_gemv_row(torch, kq, cfg):
 
 def codec_rows(torch, kq):
     """q5_K on the decode GEMV, prefill GEMM and MoE segment shapes; the legacy
-    32-value codecs and q2_K on the 14336x4096 GEMV."""
+    32-value codecs, q2_K and q3_K on the 14336x4096 GEMV."""
     from gguf_quant_matmul_amd import workloads as W
 
     rows = []
-    for cfg in W.LEGACY_GEMV + (W.Q2K_GEMV,):
+    for cfg in W.LEGACY_GEMV + (W.Q2K_GEMV, W.Q3K_GEMV):
         r, _ = cold_gemv_row(torch, kq, cfg)
         rows.append(r)
     r, wq = cold_gemv_row(torch, kq, W.Q5K_GEMV)

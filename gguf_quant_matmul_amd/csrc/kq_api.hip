@@ -37,6 +37,7 @@ const char* codec_name(int c) {
     case KQ_Q4_K: return "q4_k";
     case KQ_Q5_K: return "q5_k";
     case KQ_Q2_K: return "q2_k";
+    case KQ_Q3_K: return "q3_k";
     case KQ_Q4_1: return "q4_1";
     case KQ_Q5_0: return "q5_0";
     case KQ_Q5_1: return "q5_1";
@@ -52,6 +53,7 @@ bool geometry(int c, int* bv, int* bb) {
     case KQ_Q4_K: *bv = 256; *bb = 144; return true;
     case KQ_Q5_K: *bv = 256; *bb = 176; return true;
     case KQ_Q2_K: *bv = 256; *bb = 84; return true;
+    case KQ_Q3_K: *bv = 256; *bb = 110; return true;
     case KQ_Q4_1: *bv = 32; *bb = 20; return true;
     case KQ_Q5_0: *bv = 32; *bb = 22; return true;
     case KQ_Q5_1: *bv = 32; *bb = 24; return true;
@@ -120,13 +122,13 @@ int kq_codec_from_name(const char* name, int* codec) {
   low[i] = 0;
   static const struct { const char* n; int c; } table[] = {
       {"q4_0", KQ_Q4_0}, {"q8_0", KQ_Q8_0}, {"q4_k", KQ_Q4_K}, {"q5_k", KQ_Q5_K}, {"q6_k", KQ_Q6_K},
-      {"q4_1", KQ_Q4_1}, {"q5_0", KQ_Q5_0}, {"q5_1", KQ_Q5_1}, {"q2_k", KQ_Q2_K}};
+      {"q4_1", KQ_Q4_1}, {"q5_0", KQ_Q5_0}, {"q5_1", KQ_Q5_1}, {"q2_k", KQ_Q2_K}, {"q3_k", KQ_Q3_K}};
   for (const auto& t : table)
     if (!name[i] && strcmp(low, t.n) == 0) {
       *codec = t.c;
       return KQ_OK;
     }
-  return fail(KQ_ERR_CODEC, "kq_codec_from_name", "unknown codec '%s' (known: q4_0, q4_1, q5_0, q5_1, q8_0, q2_k, q4_k, q5_k, q6_k)", name);
+  return fail(KQ_ERR_CODEC, "kq_codec_from_name", "unknown codec '%s' (known: q4_0, q4_1, q5_0, q5_1, q8_0, q2_k, q3_k, q4_k, q5_k, q6_k)", name);
 }
 
 int kq_codec_info(int codec, int* block_values, int* block_bytes) {
@@ -253,7 +255,7 @@ int kq_quantized_matmul_glu(int codec, const void* w_gate, const void* w_up, int
   if (!w_up) return fail(KQ_ERR_ARG, op, "null w_up");
   if (!aligned(w_up, 16)) return fail(KQ_ERR_ALIGN, op, "w_up=%p is not 16-byte aligned", w_up);
   const hipError_t e =
-      m <= kq::QMV_GLU_MAX_M
+      m <= kq::qmv_glu_max_m(codec)
           ? kq::launch_qmv_glu(codec, (const uint8_t*)w_gate, (const uint8_t*)w_up, n, k, rb, (const kq::half_t*)x,
                                (int)m, act, y, y_dtype == KQ_F16, (hipStream_t)stream)
           : kq::launch_qmm_glu(codec, (const uint8_t*)w_gate, (const uint8_t*)w_up, n, k, rb, (const kq::half_t*)x,

@@ -94,6 +94,24 @@ __device__ __forceinline__ void decode8<Q2_K>(const uint8_t* __restrict__ row, i
 }
 
 template <>
+__device__ __forceinline__ void decode8<Q3_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
+  const uint8_t* blk = row + (v0 / 256) * 110;  // 2-byte aligned
+  const int vi = (int)(v0 % 256);
+  const int h = vi / 128, c = (vi % 128) / 32, l0 = vi % 32, j = vi / 16;
+  const uint32_t lo4 = (j < 8 ? blk[96 + j] : (blk[96 + j - 8] >> 4)) & 15u;
+  const uint32_t hi2 = (blk[104 + (j & 3)] >> (2 * (j >> 2))) & 3u;
+  const float dsc = f16_to_f32(ld_u16(blk + 108)) * (float)((int)(lo4 | (hi2 << 4)) - 32);  // exact
+  const u32x2 q = ld8_a2(blk + 32 + 32 * h + l0);
+  const u32x2 hm = ld8_a2(blk + l0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t low2 = ((i < 4 ? q.x : q.y) >> (8 * (i & 3) + 2 * c)) & 3u;
+    const uint32_t hb = ((i < 4 ? hm.x : hm.y) >> (8 * (i & 3) + 4 * h + c)) & 1u;
+    out[i] = dsc * (float)((int)(low2 | (hb << 2)) - 4);  // exact
+  }
+}
+
+template <>
 __device__ __forceinline__ void decode8<Q4_K>(const uint8_t* __restrict__ row, int64_t v0, float out[8]) {
   const uint8_t* blk = row + (v0 / 256) * 144;  // 16-byte aligned: rows are multiples of 144 bytes
   const int vi = (int)(v0 % 256);

@@ -67,6 +67,7 @@ hipError_t launch_dequantize(int codec, const uint8_t* w, int64_t rows, int64_t 
     case Q4_0: return launch_c<Q4_0>(w, rows, k, rb, out, f16, s);
     case Q8_0: return launch_c<Q8_0>(w, rows, k, rb, out, f16, s);
     case Q2_K: return launch_c<Q2_K>(w, rows, k, rb, out, f16, s);
+    case Q3_K: return launch_c<Q3_K>(w, rows, k, rb, out, f16, s);
     case Q4_K: return launch_c<Q4_K>(w, rows, k, rb, out, f16, s);
     case Q5_K: return launch_c<Q5_K>(w, rows, k, rb, out, f16, s);
     case Q4_1: return launch_c<Q4_1>(w, rows, k, rb, out, f16, s);

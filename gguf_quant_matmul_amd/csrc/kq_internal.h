@@ -16,6 +16,10 @@
 //         low nibble, min in the high), [16:80] qs, [80:82] d, [82:84] dmin;
 //         v -> h=v/128, c=(v%128)/32, l=v%32: code = (qs[32h+l] >> 2c) & 3;
 //         value = (d*sc_j)*q - dmin*m_j, j = v/16
+//   q3_K 110 B: [0:32] hmask, [32:96] qs, [96:108] 16 packed 6-bit scales
+//         (stored + 32), [108:110] d; v -> h, c, l as q2_K: u = low2 |
+//         hbit << 2 with low2 = (qs[32h+l] >> 2c) & 3, hbit = bit 4h+c of
+//         hmask[l]; value = d*sc_j*(u - 4)
 //   q5_K 176 B: [0:16] as q4_K, [16:48] qh, [48:176] qs; the low four bits
 //         as q4_K's nibbles (at qs), the fifth bit of value l of sub-block j
 //         is bit j of qh[l]; value = (d*sc_j)*q - dmin*m_j, q in 0..31
@@ -30,7 +34,7 @@
 
 namespace kq {
 
-enum Codec : int { Q4_0 = 2, Q4_1 = 3, Q5_0 = 6, Q5_1 = 7, Q8_0 = 8, Q2_K = 10, Q4_K = 12, Q5_K = 13, Q6_K = 14 };
+enum Codec : int { Q4_0 = 2, Q4_1 = 3, Q5_0 = 6, Q5_1 = 7, Q8_0 = 8, Q2_K = 10, Q3_K = 11, Q4_K = 12, Q5_K = 13, Q6_K = 14 };
 
 template <int C> struct Geo;
 template <> struct Geo<Q4_0> { static constexpr int BV = 32;  static constexpr int BB = 18; };
@@ -40,6 +44,7 @@ template <> struct Geo<Q5_0> { static constexpr int BV = 32;  static constexpr i
 template <> struct Geo<Q5_1> { static constexpr int BV = 32;  static constexpr int BB = 24; };
 template <> struct Geo<Q4_K> { static constexpr int BV = 256; static constexpr int BB = 144; };
 template <> struct Geo<Q2_K> { static constexpr int BV = 256; static constexpr int BB = 84; };
+template <> struct Geo<Q3_K> { static constexpr int BV = 256; static constexpr int BB = 110; };
 template <> struct Geo<Q5_K> { static constexpr int BV = 256; static constexpr int BB = 176; };
 template <> struct Geo<Q6_K> { static constexpr int BV = 256; static constexpr int BB = 210; };
 
@@ -165,10 +170,21 @@ __device__ __forceinline__ uint32_t leg_hi(uint32_t qs, uint32_t qh, int i) {
   else return ((qs >> 4) & 0x0F0F0F0Fu) | spread4(qh >> (16 + 4 * i));
 }
 
+// q3_K: signed scale t of the four sub-blocks 4u' + t (u' = unit % 4) from the
+// scale dwords A (bytes 4 (u' % 2) .. of the 12, low nibbles for u' < 2, high
+// for u' >= 2) and B (bytes 8..11, bits 2u'..2u'+1 of byte t)
+__device__ __forceinline__ int q3k_scale(uint32_t A, uint32_t B, int up, int t) {
+  const uint32_t lo4 = (A >> (8 * t + 4 * (up >> 1))) & 15u;
+  const uint32_t hi2 = (B >> (8 * t + 2 * up)) & 3u;
+  return (int)(lo4 | (hi2 << 4)) - 32;
+}
+
 // GLU epilogues (kq.h KQ_GLU_* carry the same values)
 constexpr int GLU_SILU = 0, GLU_GELU_TANH = 1, GLU_SILU_LIMIT = 2;
-// activation rows up to which the GLU product runs on the GEMV body
+// activation rows up to which the GLU product runs on the GEMV body (two
+// matrices' q3_K units fill the registers from two rows on)
 constexpr int QMV_GLU_MAX_M = 3;
+__host__ __device__ constexpr int qmv_glu_max_m(int codec) { return codec == Q3_K ? 1 : QMV_GLU_MAX_M; }
 
 // Matmul epilogue (mlx-kquant bindings.cpp page, quantized_matmul_residual
 // and quantized_matmul_qmv_bias docstrings): per output element

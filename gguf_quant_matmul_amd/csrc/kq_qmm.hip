@@ -22,6 +22,7 @@ hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t ne, int64_
       case Q5_0: return launch_generic<Q5_0, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q5_1: return launch_generic<Q5_1, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q2_K: return launch_generic<Q2_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
+      case Q3_K: return launch_generic<Q3_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q4_K: return launch_generic<Q4_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q5_K: return launch_generic<Q5_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);
       case Q6_K: return launch_generic<Q6_K, true>(w, n, k, rb, n * rb, ne, x, rows, map, counts, cap, y, f16, s);

@@ -153,6 +153,46 @@ template <> struct HalfUnit<Q2_K> {
   }
 };
 
+template <> struct HalfUnit<Q3_K> {
+  // unit u' = u % 4 (half h = u' / 2, shifts c0 = 2 (u' % 2), c0 + 1); half
+  // hh takes positions l in [16hh, 16hh+16) at both shifts: sub-block 4u' +
+  // hh (segment hh) and 4u' + 2 + hh (segment 2 + hh).  110-byte blocks are
+  // 2-byte aligned; each span is read from the dword below it and stays in
+  // the block (the scales from [92, 108)).
+  Raw16 rq, rh, rs;
+  uint32_t dbits, sh;
+  __device__ __forceinline__ void load(const uint8_t* row, int u, int hh) {
+    const uint8_t* blk = row + (u >> 2) * 110;
+    sh = (uint32_t)((uintptr_t)blk & 3);
+    rq.load(blk + 32 + 32 * ((u >> 1) & 1) + 16 * hh, sh);
+    rh.load(blk + 16 * hh, sh);
+    rs.load(blk + 92, sh);
+    dbits = ld_u16(blk + 108);
+  }
+  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+    const int up = u & 3, h = up >> 1, c0 = 2 * (up & 1);
+    uint32_t Q[4], H[4], S[4];
+    rq.get(sh, Q); rh.get(sh, H); rs.get(sh, S);
+    const float d = f16_to_f32(dbits);
+    const uint32_t A = (up & 1) ? S[2] : S[1], B = S[3];
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {  // shift c0 + g: sub-block 2g + hh, segment 2g + hh
+      const float s = d * (float)q3k_scale(A, B, up, 2 * g + hh), c = -1028.f * s;
+      const int c2 = c0 + g;
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = ((Q[i] >> (2 * c2)) & 0x03030303u) | (((H[i] >> (4 * h + c2)) & 0x01010101u) << 2);
+        const half2_t c01 = as_h2(pair01(code)), c23 = as_h2(pair23(code));
+        o[2 * i] = pack_h2(fmaf((float)c01.x, s, c), fmaf((float)c01.y, s, c));
+        o[2 * i + 1] = pack_h2(fmaf((float)c23.x, s, c), fmaf((float)c23.y, s, c));
+      }
+      st_chunk(dst, sw, 4 * g + 2 * hh, u32x4{o[0], o[1], o[2], o[3]});
+      st_chunk(dst, sw, 4 * g + 2 * hh + 1, u32x4{o[4], o[5], o[6], o[7]});
+    }
+  }
+};
+
 template <> struct HalfUnit<Q5_K> {
   // q4_K's half unit with 5-bit codes: the fifth bits of positions l in
   // [16hh, 16hh+16) are bits 2P (sub-block 2P) and 2P + 1 of qh[l].
@@ -707,6 +747,7 @@ hipError_t launch_pass(int codec, const uint8_t* w, int64_t n, int64_t k, int64_
     case Q5_0: return launch_dense<Q5_0, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q5_1: return launch_dense<Q5_1, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q2_K: return launch_dense<Q2_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    case Q3_K: return launch_dense<Q3_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q4_K: return launch_dense<Q4_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q5_K: return launch_dense<Q5_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
     case Q6_K: return launch_dense<Q6_K, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);

@@ -16,6 +16,7 @@ hipError_t launch_fused(int codec, const uint8_t* w, const uint8_t* w2, int64_t 
     case Q5_0: return launch_fused_c<Q5_0>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q5_1: return launch_fused_c<Q5_1>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q2_K: return launch_fused_c<Q2_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
+    case Q3_K: return launch_fused_c<Q3_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q4_K: return launch_fused_c<Q4_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q5_K: return launch_fused_c<Q5_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);
     case Q6_K: return launch_fused_c<Q6_K>(w, w2, n, k, rb, x, m, epi, act, glu, y, f16, s);

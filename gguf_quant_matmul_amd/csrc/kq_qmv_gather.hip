@@ -14,6 +14,7 @@ hipError_t launch_gather_qmv(int codec, const uint8_t* w, int64_t n_experts, int
     case Q5_0: return launch_gather_c<Q5_0>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q5_1: return launch_gather_c<Q5_1>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q2_K: return launch_gather_c<Q2_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
+    case Q3_K: return launch_gather_c<Q3_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q4_K: return launch_gather_c<Q4_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q5_K: return launch_gather_c<Q5_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
     case Q6_K: return launch_gather_c<Q6_K>(w, n_experts, n, k, row_bytes, x, ids, rows, y, f16out, s);
@@ -37,6 +38,8 @@ hipError_t launch_moe_glu_gather(int codec, const uint8_t* gate_w, const uint8_t
       return launch_glu_c<Q5_1>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
     case Q2_K:
       return launch_glu_c<Q2_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
+    case Q3_K:
+      return launch_glu_c<Q3_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
     case Q4_K:
       return launch_glu_c<Q4_K>(gate_w, up_w, n_experts, n, k, row_bytes, x, ids, rows, top_k, act, limit, y, f16out, s);
     case Q5_K:

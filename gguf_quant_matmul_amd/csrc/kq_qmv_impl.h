@@ -542,7 +542,7 @@ hipError_t launch_fused_ml(const uint8_t* w, const uint8_t* w2, int64_t n, int64
     else
       hipLaunchKernelGGL((qmv_epi_kernel<C, M, LPR, false>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb,
                          x, epi, y);
-  } else if constexpr (M > QMV_GLU_MAX_M) {
+  } else if constexpr (M > qmv_glu_max_m(C)) {
     return hipErrorInvalidValue;
   } else if (act == GLU_SILU) {
     if (f16)

@@ -20,14 +20,16 @@
 //          min = -lo; d = f16(max scale/15), dmin = f16(max min/15);
 //          sc = rint(scale/D), m = rint(min/DM) (0..15);
 //          q = rint((w + DM*m)/(D*sc)) (0..3)
+//   q3_K : per 16 values scale = amax/3; d = f16(max scale/31);
+//          sc = rint(scale/D) (-32..31); q = rint(w/(D*sc)) (-4..3)
 //   q6_K : per 16 values scale = amax/31; d = f16(max scale/127);
 //          sc = rint(scale/D) (-128..127); q = rint(w/(D*sc)) + 32
 // Codes are clamped to the codec's range, then moved to the nearest point of
 // the block's decoded grid among q-1, q, q+1 (distance |w - decode(q)| in
 // float64, ties to the lower code).  A zero grid step gives the zero-point
-// code (q8_0 0, q4_0 8, q4_1 and q5_1 0, q5_0 16, q2_K, q4_K and q5_K 0,
-// q6_K 32).  One thread per block (32-value codecs) or superblock (q2_K,
-// q4_K, q5_K, q6_K);
+// code (q8_0 0, q4_0 8, q4_1 and q5_1 0, q5_0 16, q2_K, q3_K, q4_K and q5_K
+// 0, q6_K 32).  One thread per block (32-value codecs) or superblock (the K
+// codecs);
 // not a hot path.
 #include "kq_internal.h"
 
@@ -277,6 +279,55 @@ __global__ __launch_bounds__(256) void quant_q2_k(const float* __restrict__ w, i
   *(uint32_t*)(o + 80) = db | (mb << 16);
 }
 
+__global__ __launch_bounds__(256) void quant_q3_k(const float* __restrict__ w, int64_t nsb, int kb, int64_t row_bytes,
+                                                  uint8_t* __restrict__ out) {
+  const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (g >= nsb) return;
+  const int64_t r = g / kb, b = g % kb;
+  const float* x = w + (r * kb + b) * 256;
+  float scale[16];
+  float smax = 0.f;
+  for (int j = 0; j < 16; ++j) {
+    float amax = 0.f;
+    for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[16 * j + i]));
+    scale[j] = amax / 3.f;
+    smax = j ? fmaxf(smax, scale[j]) : scale[j];
+  }
+  const uint32_t db = f16_bits(smax / 31.f);
+  const float D = f16_val(db);
+  uint8_t* o = out + r * row_bytes + b * 110;  // 2-byte aligned
+  uint32_t hm[8], qw[16], sb[3] = {0, 0, 0};
+  for (int i = 0; i < 8; ++i) hm[i] = 0;
+  for (int i = 0; i < 16; ++i) qw[i] = 0;
+  for (int j = 0; j < 16; ++j) {
+    const int sc = D > 0.f ? (int)clampf(rintf(scale[j] / D), -32.f, 31.f) : 0;
+    const uint32_t st = (uint32_t)(sc + 32);
+    const int lb = j & 7;
+    sb[lb >> 2] |= (st & 15u) << (8 * (lb & 3) + 4 * (j >> 3));
+    sb[2] |= (st >> 4) << (8 * (j & 3) + 2 * (j >> 2));
+    const float S = D * (float)sc;
+    for (int i = 0; i < 16; ++i) {
+      const int v = 16 * j + i;
+      int q;
+      if (S == 0.f) {
+        q = 0;
+      } else {
+        const float xv = x[v];
+        const int q0 = (int)clampf(rintf(xv / S), -4.f, 3.f);
+        q = nearest(xv, q0, -4, 3, [S](int c) { return S * (float)c; });
+      }
+      const uint32_t u = (uint32_t)(q + 4);
+      const int h = v / 128, c = (v % 128) / 32, l = v % 32, p = 32 * h + l;
+      qw[p >> 2] |= (u & 3u) << (8 * (p & 3) + 2 * c);
+      hm[l >> 2] |= (u >> 2) << (8 * (l & 3) + 4 * h + c);
+    }
+  }
+  for (int i = 0; i < 8; ++i) { st_u16(o + 4 * i, hm[i] & 0xFFFFu); st_u16(o + 4 * i + 2, hm[i] >> 16); }
+  for (int i = 0; i < 16; ++i) { st_u16(o + 32 + 4 * i, qw[i] & 0xFFFFu); st_u16(o + 32 + 4 * i + 2, qw[i] >> 16); }
+  for (int i = 0; i < 3; ++i) { st_u16(o + 96 + 4 * i, sb[i] & 0xFFFFu); st_u16(o + 96 + 4 * i + 2, sb[i] >> 16); }
+  st_u16(o + 108, db);
+}
+
 __global__ __launch_bounds__(256) void quant_q6_k(const float* __restrict__ w, int64_t nsb, int kb, int64_t row_bytes,
                                                   uint8_t* __restrict__ out) {
   const int64_t g = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -326,7 +377,7 @@ __global__ __launch_bounds__(256) void quant_q6_k(const float* __restrict__ w, i
 
 hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, int64_t rb, uint8_t* out,
                            hipStream_t s) {
-  const int bv = (codec == Q2_K || codec == Q4_K || codec == Q5_K || codec == Q6_K) ? 256 : 32;
+  const int bv = (codec == Q2_K || codec == Q3_K || codec == Q4_K || codec == Q5_K || codec == Q6_K) ? 256 : 32;
   const int kb = (int)(k / bv);
   const int64_t nblk = rows * kb;
   const dim3 grid((unsigned)((nblk + 255) / 256)), block(256);
@@ -337,6 +388,7 @@ hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, i
     case Q5_0: hipLaunchKernelGGL(quant_leg<Q5_0>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q5_1: hipLaunchKernelGGL(quant_leg<Q5_1>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q2_K: hipLaunchKernelGGL(quant_q2_k, grid, block, 0, s, w, nblk, kb, rb, out); break;
+    case Q3_K: hipLaunchKernelGGL(quant_q3_k, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q4_K: hipLaunchKernelGGL(quant_k_affine<15>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q5_K: hipLaunchKernelGGL(quant_k_affine<31>, grid, block, 0, s, w, nblk, kb, rb, out); break;
     case Q6_K: hipLaunchKernelGGL(quant_q6_k, grid, block, 0, s, w, nblk, kb, rb, out); break;

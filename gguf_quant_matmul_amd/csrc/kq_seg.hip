@@ -52,11 +52,12 @@ constexpr int SEG_NXCD = 8;
 // leave open.
 template <int C> struct SegSlots { static constexpr int value = 2; };
 // Workgroups per CU the register budget is sized for.  q5_K's units carry
-// the 32 qh bytes as well (20 registers a unit against q4_K's 12): at two
-// waves per SIMD its ring spills, so it takes one wave per SIMD and the whole
-// register file (the 2-slot ring at one wave per SIMD measured within a few
-// percent of two waves for q4_K).
-template <int C> struct SegOcc { static constexpr int value = C == Q5_K ? 1 : 2; };
+// the 32 qh bytes as well (20 registers a unit against q4_K's 12), q3_K's
+// five 2-byte-aligned spans (27): at two waves per SIMD their rings spill,
+// so they take one wave per SIMD and the whole register file (the 2-slot
+// ring at one wave per SIMD measured within a few percent of two waves for
+// q4_K).
+template <int C> struct SegOcc { static constexpr int value = (C == Q5_K || C == Q3_K) ? 1 : 2; };
 
 template <int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -275,6 +276,7 @@ hipError_t launch_seg_mma(int codec, const uint8_t* w, int64_t n_experts, int64_
     case Q4_0: return launch_seg_mma_c<Q4_0>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q8_0: return launch_seg_mma_c<Q8_0>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q2_K: return launch_seg_mma_c<Q2_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
+    case Q3_K: return launch_seg_mma_c<Q3_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q4_K: return launch_seg_mma_c<Q4_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q5_K: return launch_seg_mma_c<Q5_K>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);
     case Q4_1: return launch_seg_mma_c<Q4_1>(w, n_experts, n, k, row_bytes, x, rows, map, counts, cap, y, f16out, s);

@@ -472,9 +472,83 @@ struct UnitLeg {
   }
 };
 
+// q3_K: unit u' = u % 4 is half h = u' / 2 at code shifts c0 = 2 (u' % 2)
+// and c0 + 1, as q2_K: the 32 qs bytes of half h, the 32 hmask bytes (bits
+// 4h + c), the scale bytes and d.  Blocks are 2-byte aligned (110 bytes):
+// every span is read from the dword below it (Shift16) and placed so that
+// the read stays inside the block; the scales come from the span [92, 108).
+struct UnitQ3K {
+  Shift16 qa, qb, ha, hb, sc;
+  uint32_t dbits, sh;
+  __device__ __forceinline__ void load(const uint8_t* row, int u) {
+    const uint8_t* blk = row + (u >> 2) * 110;
+    const int h = (u >> 1) & 1;
+    sh = (uint32_t)((uintptr_t)blk & 3);
+    qa.load(blk + 32 + 32 * h, sh);
+    qb.load(blk + 48 + 32 * h, sh);
+    ha.load(blk, sh);
+    hb.load(blk + 16, sh);
+    sc.load(blk + 92, sh);
+    dbits = ld_u16(blk + 108);
+  }
+  // as q6_K: the uniform offset steps over pairs of blocks (220 bytes), the
+  // odd block and the sub-dword shift go into the per-lane offset
+  __device__ __forceinline__ void bload(rsrc_t rs, int rowoff, int cu, int u4) {
+    const int blk = u4 >> 2, so = 220 * (blk >> 1);
+    const int h = (cu >> 1) & 1;
+    const int t = rowoff + 110 * (blk & 1);
+    sh = (uint32_t)t & 3u;
+    const int va = t - (int)sh;
+    qa.bload(rs, va + 32 + 32 * h, so, sh);
+    qb.bload(rs, va + 48 + 32 * h, so, sh);
+    ha.bload(rs, va, so, sh);
+    hb.bload(rs, va + 16, so, sh);
+    sc.bload(rs, va + 92, so, sh);
+    dbits = bld2(rs, t + 108, so);
+  }
+  // the unit's four signed sub-block scales times d, and its 3-bit codes
+  // (u = q + 4) of sub-block t as four dwords
+  __device__ __forceinline__ void fields(int u, float s[4], uint32_t cw[4][4]) const {
+    const int up = u & 3, h = up >> 1, c0 = 2 * (up & 1);
+    uint32_t Q[8], H[8], S[4];
+    qa.get(sh, Q); qb.get(sh, Q + 4); ha.get(sh, H); hb.get(sh, H + 4); sc.get(sh, S);
+    const float d = f16_to_f32(dbits);
+    const uint32_t A = (up & 1) ? S[2] : S[1], B = S[3];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      s[t] = d * (float)q3k_scale(A, B, up, t);
+      const int c = c0 + (t >> 1);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = 4 * (t & 1) + i;
+        cw[t][i] = ((Q[k] >> (2 * c)) & 0x03030303u) | (((H[k] >> (4 * h + c)) & 0x01010101u) << 2);
+      }
+    }
+  }
+  template <int M>
+  __device__ __forceinline__ void dot(int u, const Xv& xv, float acc[M]) const {
+    float s[4];
+    uint32_t cw[4][4], p[4][8];
+    fields(u, s, cw);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) pairs16(cw[t], p[t]);
+    const int base = 64 * u;
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float4_t xs = *(const float4_t*)&xv.xsum[m * xv.sstride + ((base - xv.c0) >> 4)];
+      const float x[4] = {xs.x, xs.y, xs.z, xs.w};
+      float tot = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) tot += s[t] * (dot16(p[t], xv.pairs(m, base + 16 * t), 0.f) - 1028.f * x[t]);
+      acc[m] += tot;
+    }
+  }
+};
+
 template <int C> struct UnitOf;
 template <> struct UnitOf<Q4_K> { typedef UnitQ4K T; };
 template <> struct UnitOf<Q2_K> { typedef UnitQ2K T; };
+template <> struct UnitOf<Q3_K> { typedef UnitQ3K T; };
 template <> struct UnitOf<Q5_K> { typedef UnitQ5K T; };
 template <> struct UnitOf<Q6_K> { typedef UnitQ6K T; };
 template <> struct UnitOf<Q8_0> { typedef UnitQ8_0 T; };
@@ -570,6 +644,25 @@ template <> struct MmaSlices<Q2_K> {
   __device__ __forceinline__ void get(uint32_t f[4]) const {
     constexpr int t = S >> 1, i0 = 4 * (t & 1) + 2 * (S & 1), sh = 2 * (S >> 2);
     slice8((qs[i0] >> sh) & 0x03030303u, (qs[i0 + 1] >> sh) & 0x03030303u, s[t], c[t], f);
+  }
+};
+
+template <> struct MmaSlices<Q3_K> {
+  // slice S: sub-block t = S / 2, code dwords 2 (S % 2) .. of it; weight =
+  // fma(1024 + u, d sc, -1028 d sc) = d sc (u - 4)
+  uint32_t cw[4][4];
+  float s[4];
+  __device__ __forceinline__ MmaSlices(const UnitQ3K& un, int u, bool keep) {
+    un.fields(u, s, cw);
+    if (!keep) s[0] = s[1] = s[2] = s[3] = 0.f;
+  }
+  static __device__ __forceinline__ int koff(int u) { return 64 * u; }
+  template <int S>
+  static constexpr int xstep() { return 8 * S; }
+  template <int S>
+  __device__ __forceinline__ void get(uint32_t f[4]) const {
+    constexpr int t = S >> 1, i = 2 * (S & 1);
+    slice8(cw[t][i], cw[t][i + 1], s[t], -1028.f * s[t], f);
   }
 };
 

@@ -62,7 +62,8 @@ for _name, (_res, _args) in _SIGS.items():
     _fn.argtypes = _args
 
 # ids and enums of include/kq.h
-KQ_Q4_0, KQ_Q4_1, KQ_Q5_0, KQ_Q5_1, KQ_Q8_0, KQ_Q2_K, KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 2, 3, 6, 7, 8, 10, 12, 13, 14
+KQ_Q4_0, KQ_Q4_1, KQ_Q5_0, KQ_Q5_1, KQ_Q8_0 = 2, 3, 6, 7, 8
+KQ_Q2_K, KQ_Q3_K, KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 10, 11, 12, 13, 14
 KQ_F32, KQ_F16 = 0, 1
 KQ_GLU_SILU, KQ_GLU_GELU_TANH, KQ_GLU_SILU_LIMIT = 0, 1, 2
 _GLU_ACTS = {"silu": KQ_GLU_SILU, "gelu": KQ_GLU_GELU_TANH, "gelu_tanh": KQ_GLU_GELU_TANH,

@@ -136,8 +136,9 @@ CFG4_Q4K_GEMM = GemvConfig("q4_K prefill GEMM 2048x14336x4096", "q4_k", 14336, 4
 # q5_K on the q4_K decode and prefill shapes (a widening of the codec set; seed 5)
 Q5K_GEMV = GemvConfig("q5_K GEMV 14336x4096 M=1", "q5_k", 14336, 4096, 1, 5, "normal", "f32")
 Q5K_GEMM = GemvConfig("q5_K prefill GEMM 2048x14336x4096", "q5_k", 14336, 4096, 2048, 5, "normal", "f16")
-# q2_K on the same GEMV shape (seed 7)
+# q2_K and q3_K on the same GEMV shape (seeds 7, 8)
 Q2K_GEMV = GemvConfig("q2_K GEMV 14336x4096 M=1", "q2_k", 14336, 4096, 1, 7, "normal", "f32")
+Q3K_GEMV = GemvConfig("q3_K GEMV 14336x4096 M=1", "q3_k", 14336, 4096, 1, 8, "normal", "f32")
 # the legacy 32-value codecs on the q8_0 / q4_0 GEMV shape (seed 6)
 LEGACY_GEMV = tuple(GemvConfig(f"{c} GEMV 14336x4096 M=1", c, 14336, 4096, 1, 6, "normal", "f32")
                     for c in ("q4_1", "q5_0", "q5_1"))

@@ -23,8 +23,8 @@
  *  - Activations x are float16, row-major [M][K].
  *  - w and x must be 16-byte aligned, y/out 16-byte aligned, map/counts/ids
  *    4-byte aligned: otherwise KQ_ERR_ALIGN.
- *  - K must be a positive multiple of the codec's block (256 for q2_K, q4_K, q5_K and
- *    q6_K, 32 for the others): otherwise KQ_ERR_SHAPE.  Sizes must be
+ *  - K must be a positive multiple of the codec's block (256 for the
+ *    K-quants q2_K .. q6_K, 32 for the others): otherwise KQ_ERR_SHAPE.  Sizes must be
  *    below 2^31 (element counts below 2^40).
  *  - On any error nothing is launched and outputs are untouched; the return
  *    value is a kq_status and kq_last_error() describes it.
@@ -42,19 +42,20 @@ extern "C" {
 
 /* Codec ids: GGML's type numbers for these codecs (the names are the
  * authority: "q4_0", "q4_1", "q5_0", "q5_1", "q8_0", "q4_k", "q5_k",
- * "q2_k", "q6_k").  Geometry per the mlx-kquant README "Codec reference" table:
+ * "q2_k", "q3_k", "q6_k").  Geometry per the mlx-kquant README "Codec reference" table:
  *   q4_0  32 values,  4 bits,  18 bytes per block (scale)
  *   q4_1  32 values,  4 bits,  20 bytes per block (scale + min)
  *   q5_0  32 values,  5 bits,  22 bytes per block (scale)
  *   q5_1  32 values,  5 bits,  24 bytes per block (scale + min)
  *   q8_0  32 values,  8 bits,  34 bytes per block
  *   q2_K 256 values,  2 bits,  84 bytes per superblock
+ *   q3_K 256 values,  3 bits, 110 bytes per superblock
  *   q4_K 256 values,  4 bits, 144 bytes per superblock
  *   q5_K 256 values,  5 bits, 176 bytes per superblock
  *   q6_K 256 values,  6 bits, 210 bytes per superblock */
 typedef enum {
   KQ_Q4_0 = 2, KQ_Q4_1 = 3, KQ_Q5_0 = 6, KQ_Q5_1 = 7, KQ_Q8_0 = 8,
-  KQ_Q2_K = 10, KQ_Q4_K = 12, KQ_Q5_K = 13, KQ_Q6_K = 14
+  KQ_Q2_K = 10, KQ_Q3_K = 11, KQ_Q4_K = 12, KQ_Q5_K = 13, KQ_Q6_K = 14
 } kq_codec;
 
 /* Output element types. */
@@ -137,9 +138,10 @@ int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k,
  *   wider weight).  The activation of the gate product is rounded to y_dtype,
  *   then multiplied by the up product in float32 and rounded again; a
  *   float16 store turns a finite value beyond the float16 range into the
- *   largest finite half of its sign (infinities and NaN pass).  M <= 3 runs
- *   both weights through one GEMV pass; larger M runs two GEMM passes on the
- *   stream (gate, then up), with y as the only buffer between them.
+ *   largest finite half of its sign (infinities and NaN pass).  M <= 3
+ *   (q3_K: M = 1) runs both weights through one GEMV pass; larger M runs two
+ *   GEMM passes on the stream (gate, then up), with y as the only buffer
+ *   between them.
  *
  * Element alignment for residual, gate and bias; the rest as in
  * kq_quantized_matmul. */

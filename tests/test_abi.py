@@ -41,7 +41,8 @@ def test_codec_registry():
     assert kq.kq_codec_from_name("Q4_K") == kq.KQ_Q4_K
     assert kq.kq_codec_from_name("q5_k") == kq.KQ_Q5_K == 13
     assert kq.kq_row_bytes("q5_k", 4096) == 2816
-    for name, cid, geo in (("q4_1", 3, (32, 20)), ("q5_0", 6, (32, 22)), ("q5_1", 7, (32, 24)), ("q2_k", 10, (256, 84))):
+    for name, cid, geo in (("q4_1", 3, (32, 20)), ("q5_0", 6, (32, 22)), ("q5_1", 7, (32, 24)), ("q2_k", 10, (256, 84)),
+                             ("q3_k", 11, (256, 110))):
         assert kq.kq_codec_from_name(name) == cid and kq.kq_codec_info(name) == geo
     assert kq.kq_row_bytes("q6_k", 4096) == 3360
     assert kq.kq_row_bytes("q8_0", 4096) == 4352

@@ -16,8 +16,8 @@ from oracle import codecs, encode, matmul
 
 pytestmark = pytest.mark.gpu
 
-CODECS = ("q4_k", "q6_k", "q8_0", "q4_0", "q5_k", "q4_1", "q5_0", "q5_1", "q2_k")
-SUPER = ("q4_k", "q5_k", "q6_k", "q2_k")  # 256-value superblocks
+CODECS = ("q4_k", "q6_k", "q8_0", "q4_0", "q5_k", "q4_1", "q5_0", "q5_1", "q2_k", "q3_k")
+SUPER = ("q4_k", "q5_k", "q6_k", "q2_k", "q3_k")  # 256-value superblocks
 
 
 @pytest.fixture(scope="module")
@@ -54,7 +54,7 @@ def _random_wire(codec, n, k, rng):
     bb = codecs.block_bytes(codec)
     blk = w.reshape(n, -1, bb)
     offs = {"q8_0": [0], "q4_0": [0], "q4_k": [0, 2], "q5_k": [0, 2], "q6_k": [208], "q4_1": [0, 2], "q5_0": [0],
-            "q5_1": [0, 2], "q2_k": [80, 82]}[codec]
+            "q5_1": [0, 2], "q2_k": [80, 82], "q3_k": [108]}[codec]
     for o in offs:
         hi = blk[..., o + 1]
         bad = (hi & 0x7C) == 0x7C
@@ -119,7 +119,7 @@ def test_dequantize_f16_rounds_via_f32(kq):
 
 @pytest.mark.parametrize("name", ["q4_k_block.txt", "q6_k_block.txt", "q8_0_block.txt", "q4_0_block.txt",
                                   "q5_k_block.txt", "q4_1_block.txt", "q5_0_block.txt", "q5_1_block.txt",
-                                  "q2_k_block.txt"])
+                                  "q2_k_block.txt", "q3_k_block.txt"])
 def test_dequantize_golden_blocks(kq, name):
     from test_oracle_codecs import _load_golden
 
@@ -419,7 +419,7 @@ def test_gather_qmm_seg_parity(kq, codec):
             assert_close_rows(got[covered], ref[covered], what=f"seg {codec} n={n} k={k}")
 
 
-@pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0", "q5_k", "q4_1", "q5_0", "q5_1", "q2_k"])
+@pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0", "q5_k", "q4_1", "q5_0", "q5_1", "q2_k", "q3_k"])
 def test_gather_seg_tile_boundaries(kq, codec):
     # expert rows 96 (a full tile and a 32-row tail), 97 (a 33-row tail),
     # 133 (two full tiles and a 5-row tail), 64 (one full tile), 20 and one
