@@ -46,6 +46,7 @@ def assert_close_rows(y, ref, tol=TOL, what=""):
     err = row_rel_err(y, ref)
     assert np.all(np.isfinite(y)), f"{what}: non-finite output"
     assert err.max() <= tol, f"{what}: row-normalized max error {err.max():.3e} > {tol} (row {int(err.argmax())})"
+    say(f"  {what}: worst row error {err.max():.2e}")
     return float(err.max())
 
 
