@@ -507,8 +507,9 @@ def main():
         ev[i][2].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms1 = float(np.mean([a.elapsed_time(b) for a, b, _ in ev])) / n_cold
-    ms4 = float(np.mean([b.elapsed_time(c) for _, b, c in ev]))
+    per1 = np.array([a.elapsed_time(b) for a, b, _ in ev]) / n_cold  # per-launch ms, one value per step
+    per4 = np.array([b.elapsed_time(c) for _, b, c in ev])
+    ms1, ms4 = float(per1.mean()), float(per4.mean())
     stream_ms = ms1
 
     gbs = alg1 / ms1 / 1e6
@@ -537,9 +538,13 @@ def main():
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic("qmv"),
             "kernel": "kq_qmv q4_K (qmv_kernel<12,1,false>)", "alg_bytes_per_launch": alg1,
             "mean_launch_us": round(ms1 * 1e3, 3),
+            "median_launch_us": round(float(np.median(per1)) * 1e3, 3),
+            "p90_launch_us": round(float(np.percentile(per1, 90)) * 1e3, 3),
         },
         "qmm": {
             "value": round(tflops, 1), "unit": "TFLOP/s", "mean_launch_us": round(ms4 * 1e3, 2),
+            "median_launch_us": round(float(np.median(per4)) * 1e3, 2),
+            "p90_launch_us": round(float(np.percentile(per4, 90)) * 1e3, 2),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic("qmm"),
                          "kernel": "kq_qmm q4_K (qmm_kernel)", "alg_flop_per_launch": flop4,
@@ -547,7 +552,8 @@ def main():
         },
         "timing": "HIP graphs: one replay = 64 GEMVs over distinct cold weight copies (back to back on one "
                   "stream), one replay = one GEMM; HIP events around each replay; per-launch time = replay "
-                  "time / launches (includes the GPU-side gap between consecutive kernels)",
+                  "time / launches (includes the GPU-side gap between consecutive kernels); mean, median and "
+                  "p90 over the timed steps",
         "device": dev_name,
     }
     del w1s, w1, w4, x4, y4

@@ -53,3 +53,47 @@ def assert_close_rows(y, ref, tol=TOL, what=""):
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+def glu_bound(g, u, act, f16, tol=TOL):
+    """Per-element bound for the GLU product act(g) * u from the matmul bar.
+
+    g and u are the fp64 oracle gate and up products [M, N].  Each may err by
+    tol times its row's largest magnitude (the matmul bar), eg and eu.  The
+    activation then moves by at most da = the larger of |act(g +- eg) -
+    act(g)| and |act'(g)| eg (the endpoints cover its exponential tails), and
+    the product by da (|u| + eu) + |act(g)| eu.  Added: for a float16 output
+    the two roundings the op defines (the activation, then the product: 2^-11
+    each, relative) and float16's smallest subnormal step; for float32 a few
+    ulps; and a floor at float32 resolution of the row's largest product.
+    """
+    from oracle import matmul
+
+    name = {"silu": "silu", "gelu_tanh": "gelu", "gelu": "gelu"}[act]
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    one = np.ones_like(g)
+    a = matmul.glu_act(name, g, one)
+    h = 1e-6 * np.maximum(1.0, np.abs(g))
+    slope = (matmul.glu_act(name, g + h, one) - matmul.glu_act(name, g - h, one)) / (2 * h)
+    eg = tol * np.max(np.abs(g), axis=1, keepdims=True)
+    eu = tol * np.max(np.abs(u), axis=1, keepdims=True)
+    da = np.maximum.reduce([np.abs(matmul.glu_act(name, g + eg, one) - a),
+                            np.abs(matmul.glu_act(name, g - eg, one) - a), np.abs(slope) * eg])
+    b = da * (np.abs(u) + eu) + np.abs(a) * eu
+    rel = 2.0 ** -11 if f16 else 2.0 ** -22
+    floor = 2.0 ** -22 * np.max(np.abs(a * u), axis=1, keepdims=True) + (2.0 ** -24 if f16 else 0.0)
+    return b + rel * (2 * np.abs(a) * np.abs(u) + np.abs(a * u)) + floor + 1e-30
+
+
+def assert_glu_close(y, ref, g, u, act, f16, what=""):
+    """y within glu_bound of the oracle's GLU product ref; reports the largest
+    fraction of the bound used and the row-normalized error."""
+    y = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    bound = glu_bound(g, u, act, f16)
+    frac = np.abs(y - ref) / bound
+    i = np.unravel_index(int(frac.argmax()), frac.shape)
+    assert frac.max() <= 1.0, f"{what}: error {abs(y[i] - ref[i]):.3e} at {i} exceeds its bound {bound[i]:.3e}"
+    say(f"  {what}: bound use {frac.max():.2f}, row-normalized error {row_rel_err(y, ref).max():.2e}")
+    return float(frac.max())

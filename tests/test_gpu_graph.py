@@ -57,3 +57,52 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for got, want in zip((yv, ym, ys, map_, counts), ref):
             assert torch.equal(got, want), f"replay {rep} differs"
+
+
+def test_graph_replays_fused_and_other_codecs():
+    # the two-pass GLU GEMM (the up pass reads what the gate pass stored), the
+    # residual epilogue on the GEMV body and the GEMVs of other codecs
+    import torch
+
+    from gguf_quant_matmul_amd import kq
+
+    rng = np.random.default_rng(78)
+    n, k = 160, 1024
+
+    def wq(codec, shape):
+        return dev(encode.quantize(codec, (rng.standard_normal(shape + (k,)) * 0.05).astype(np.float32)))
+
+    wg, wu, wr, wl, w2 = wq("q5_k", (n,)), wq("q5_k", (n,)), wq("q3_k", (n,)), wq("q4_1", (n,)), wq("q2_k", (n,))
+    xm = dev(rng.standard_normal((130, k)).astype(np.float16))
+    xr = dev(rng.standard_normal((5, k)).astype(np.float16))
+    res = dev(rng.standard_normal((5, n)).astype(np.float32))
+    gate = dev(rng.standard_normal(n).astype(np.float32))
+    y_glu = torch.zeros((130, n), dtype=torch.float16, device="cuda")
+    y_res = torch.zeros((5, n), dtype=torch.float32, device="cuda")
+    y_l = torch.zeros((5, n), dtype=torch.float32, device="cuda")
+    y_2 = torch.zeros((130, n), dtype=torch.float16, device="cuda")
+    outs = (y_glu, y_res, y_l, y_2)
+
+    def work():
+        kq.kq_quantized_matmul_glu("q5_k", wg, wu, n, k, xm, y_glu, "gelu_tanh")
+        kq.kq_quantized_matmul_residual("q3_k", wr, n, k, xr, res, y_res, gate)
+        kq.kq_qmv("q4_1", wl, n, k, xr, y_l)
+        kq.kq_qmm("q2_k", w2, n, k, xm, y_2)
+
+    work()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        work()
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for t in outs:
+            t.zero_()
+        _ = (xm.float() @ xm.float().T).sum()  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got, want), f"replay {rep} differs"

@@ -11,7 +11,7 @@ import zlib
 import numpy as np
 import pytest
 
-from _gpu import TOL, assert_close_rows, dev, host, say, u32
+from _gpu import TOL, assert_close_rows, assert_glu_close, dev, host, say, u32
 from oracle import codecs, encode, matmul
 
 pytestmark = pytest.mark.gpu
@@ -259,6 +259,7 @@ def test_quantized_matmul_glu_parity(kq, codec):
         x = _x(m, k, m + 5 * n)
         dcat = dev(wcat)
         rb = wcat.shape[1]
+        g, u = matmul.qmatmul(codec, wg, k, x), matmul.qmatmul(codec, wu, k, x)
         assert (n * rb) % 16 == 0
         for act in ("silu", "gelu_tanh"):
             for tdt, odt in ((torch.float32, "f32"), (torch.float16, "f16")):
@@ -266,8 +267,7 @@ def test_quantized_matmul_glu_parity(kq, codec):
                 y = torch.full((m, n), float("nan"), dtype=tdt, device="cuda")
                 kq.kq_quantized_matmul_glu(codec, dcat[:n], dcat[n:], n, k, dev(x), y, act)
                 ref = matmul.quantized_matmul_glu(codec, wg, wu, k, x, act, odt)
-                e = assert_close_rows(host(y).astype(np.float64), ref, what=f"glu {codec} m={m} {act} {odt}")
-                say(f"  worst row error {e:.2e}")
+                assert_glu_close(host(y), ref, g, u, act, odt == "f16", what=f"glu {codec} m={m} {act} {odt}")
 
 
 @pytest.mark.parametrize("m", [2, 40])

@@ -1,5 +1,7 @@
-"""GPU parity at the five workloads' full sizes, in the launch configuration the
-benchmark times, checked on sampled outputs the oracle computes one by one.
+"""GPU parity at the workloads' full sizes (the five configurations, the other
+codecs' rows and the fused epilogues' prefill rows), in the launch
+configuration the benchmark times, checked on sampled outputs the oracle
+computes one by one.
 
 For each workload: the float32 weights are drawn (seeded, see
 gguf_quant_matmul_amd/workloads.py), encoded on the GPU by kq_quantize, and the
@@ -12,7 +14,7 @@ the sampled rows.
 import numpy as np
 import pytest
 
-from _gpu import assert_close_rows, dev, host, say, u32
+from _gpu import assert_close_rows, assert_glu_close, dev, host, say, u32
 from gguf_quant_matmul_amd import workloads as W
 from oracle import codecs, encode, matmul
 
@@ -32,7 +34,8 @@ def _sample(n, count, seed):
     return np.array(sorted(s))
 
 
-GEMV_CFGS = [W.CFG1_Q4K_GEMV, *W.CFG2_GEMV, W.CFG3_Q6K_LMHEAD, W.CFG4_Q4K_GEMM]
+GEMV_CFGS = [W.CFG1_Q4K_GEMV, *W.CFG2_GEMV, W.CFG3_Q6K_LMHEAD, W.CFG4_Q4K_GEMM,
+             W.Q5K_GEMV, W.Q5K_GEMM, *W.LEGACY_GEMV, W.Q2K_GEMV, W.Q3K_GEMV]
 
 
 @pytest.mark.parametrize("cfg", GEMV_CFGS, ids=[c.name for c in GEMV_CFGS])
@@ -151,4 +154,61 @@ def test_moe_seg_workload(kq):
     errg = assert_close_rows(host(yg)[:, ns].astype(np.float64), refg, what="MoE decode GLU gather")
     say(f"workload MoE decode GLU gather (token 0, top-{cfg.top_k}, silu): max row-normalized error {errg:.2e}")
     del wq, wu, y, yd, yg, mixed
+    torch.cuda.empty_cache()
+
+
+def _gpu_encode(kq, codec, seed, n, k, dist="normal"):
+    import torch
+
+    wdev = dev(W.weight_rows(seed, n, k, dist))
+    wq = torch.empty((n, codecs.row_bytes(codec, k)), dtype=torch.uint8, device="cuda")
+    kq.kq_quantize(codec, wdev, wq)
+    del wdev
+    return wq
+
+
+def test_glu_prefill_workload(kq):
+    # the GLU bench row: q4_K gate (the GEMM workload's weights) and up (seed
+    # + 100), 2048 x 14336 x 4096, float16 out, silu
+    import torch
+
+    c = W.CFG4_Q4K_GEMM
+    say("workload GLU prefill: weights")
+    wg = _gpu_encode(kq, c.codec, c.seed, c.n, c.k)
+    wu = _gpu_encode(kq, c.codec, c.seed + 100, c.n, c.k)
+    x = W.gemv_activations(c)
+    y = torch.empty((c.m, c.n), dtype=torch.float16, device="cuda")
+    say("workload GLU prefill: kernel")
+    kq.kq_quantized_matmul_glu(c.codec, wg, wu, c.n, c.k, dev(x), y, "silu")
+    ns = _sample(c.n, 32, 11)
+    g_rows = encode.quantize(c.codec, W.weight_rows(c.seed, c.n, c.k, rows=ns))
+    u_rows = encode.quantize(c.codec, W.weight_rows(c.seed + 100, c.n, c.k, rows=ns))
+    assert np.array_equal(host(wg[torch.from_numpy(ns).cuda()]), g_rows)
+    ref = matmul.quantized_matmul_glu(c.codec, g_rows, u_rows, c.k, x, "silu", "f16")
+    g, u = matmul.qmatmul(c.codec, g_rows, c.k, x), matmul.qmatmul(c.codec, u_rows, c.k, x)
+    assert_glu_close(host(y)[:, ns], ref, g, u, "silu", True, what="GLU prefill")
+    del wg, wu, y
+    torch.cuda.empty_cache()
+
+
+def test_residual_prefill_workload(kq):
+    # the residual bench row: the q4_K down projection 4096 x 14336 (seed + 200)
+    # over activations [2048, 14336] (seed + 200), residual [2048, 4096]
+    # (seed + 201) updated in place, float16
+    import torch
+
+    c = W.CFG4_Q4K_GEMM
+    n, k = c.k, c.n
+    say("workload residual prefill: weights")
+    wd = _gpu_encode(kq, c.codec, c.seed + 200, n, k)
+    x = W.activations(c.seed + 200, c.m, k)
+    res = W.activations(c.seed + 201, c.m, n)
+    y = dev(res)
+    say("workload residual prefill: kernel")
+    kq.kq_quantized_matmul_residual(c.codec, wd, n, k, dev(x), y, y)
+    ns = _sample(n, 32, 12)
+    w_rows = encode.quantize(c.codec, W.weight_rows(c.seed + 200, n, k, rows=ns))
+    ref = matmul.quantized_matmul_residual(c.codec, w_rows, k, x, res[:, ns])
+    assert_close_rows(host(y)[:, ns].astype(np.float64), ref, what="residual prefill")
+    del wd, y
     torch.cuda.empty_cache()
