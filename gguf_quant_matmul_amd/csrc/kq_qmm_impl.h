@@ -28,9 +28,9 @@
 //    contiguous in K, so x is gathered with the same segment map.
 //  * Tiles are ordered so that the workgroups on one XCD (blocks are dealt to
 //    the 8 XCDs round-robin) share activation panels in that XCD's L2.
-#include <type_traits>
 #pragma once
 
+#include <type_traits>
 
 #include "kq_decode.h"
 
@@ -662,7 +662,11 @@ hipError_t launch_t(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
 template <int C, int EP, int ACT>
 hipError_t launch_dense(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int64_t m, void* y,
                         int f16, const Epi& epi, hipStream_t s) {
-  if (m > 128)  // prefill: 256 x 224 tiles (N = 14336 gives 64 tile columns)
+  // prefill: 256 x 224 tiles (N = 14336 gives 64 tile columns) while they
+  // give every CU at least one; fewer (N = 4096: 152) leave CUs idle for the
+  // whole K walk, and 128 x 256 tiles fill them
+  constexpr int64_t kCUs = 256;
+  if (m > 128 && ((m + 255) / 256) * ((n + 223) / 224) >= kCUs)
     return launch_t<C, 256, 224, 4, 2, 1, 2, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
   if (m > 64) return launch_t<C, 128, 256, 2, 4, 2, 3, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
   return launch_t<C, 64, 256, 2, 4, 2, 4, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
