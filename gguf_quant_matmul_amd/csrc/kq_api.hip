@@ -170,7 +170,8 @@ int kq_qmv(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_
   int64_t rb;
   int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb);
   if (st) return st;
-  if (m > 8) return fail(KQ_ERR_SHAPE, op, "M=%lld rows; the GEMV takes 1..8 (use kq_qmm)", (long long)m);
+  if (m > kq::QMV_MAX_M)
+    return fail(KQ_ERR_SHAPE, op, "M=%lld rows; the GEMV takes 1..%d (use kq_qmm)", (long long)m, kq::QMV_MAX_M);
   if (n == 0 || m == 0) return KQ_OK;
   return hip_status(op, kq::launch_qmv(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, (int)m, y,
                                        y_dtype == KQ_F16, (hipStream_t)stream));
@@ -189,7 +190,7 @@ int kq_qmm(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_
 
 int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                         int y_dtype, void* stream) {
-  if (m >= 0 && m <= 8) return kq_qmv(codec, w, n, k, x, m, y, y_dtype, stream);
+  if (m >= 0 && m <= kq::QMV_MAX_M) return kq_qmv(codec, w, n, k, x, m, y, y_dtype, stream);
   return kq_qmm(codec, w, n, k, x, m, y, y_dtype, stream);
 }
 

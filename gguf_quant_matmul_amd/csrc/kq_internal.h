@@ -181,6 +181,8 @@ __device__ __forceinline__ int q3k_scale(uint32_t A, uint32_t B, int up, int t) 
 
 // GLU epilogues (kq.h KQ_GLU_* carry the same values)
 constexpr int GLU_SILU = 0, GLU_GELU_TANH = 1, GLU_SILU_LIMIT = 2;
+// activation rows the GEMV takes (the matrix-core GEMV's A operand has 16)
+constexpr int QMV_MAX_M = 16;
 // activation rows up to which the GLU product runs on the GEMV body (two
 // matrices' q3_K units fill the registers from two rows on)
 constexpr int QMV_GLU_MAX_M = 3;

@@ -1,6 +1,6 @@
 // kq_qmv_impl.h -- decode-shaped quantized GEMV kernels and launchers, shared
 // by kq_qmv.hip, kq_qmv_fused.hip and kq_qmv_gather.hip:
-// y[m][n] = sum_k x[m][k] * W[n][k], 1 <= M <= 8 activation rows, float32
+// y[m][n] = sum_k x[m][k] * W[n][k], 1 <= M <= 16 activation rows, float32
 // accumulation.
 //
 // mlx-kquant bindings.cpp page, quantized_matmul docstring (transpose=True
@@ -281,13 +281,15 @@ __global__ __launch_bounds__(256) void qmv_generic_kernel(const uint8_t* __restr
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
-  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float acc[QMV_MAX_M];
+#pragma unroll
+  for (int mm = 0; mm < QMV_MAX_M; ++mm) acc[mm] = 0.f;
   const uint8_t* wrow = w + (int64_t)row * row_bytes;
   for (int g = lane; g < k / 8; g += 64) {
     float v[8];
     decode8<C>(wrow, (int64_t)g * 8, v);
 #pragma unroll
-    for (int mm = 0; mm < 8; ++mm) {
+    for (int mm = 0; mm < QMV_MAX_M; ++mm) {
       if (mm < m) {
         const half8_t xv = *(const half8_t*)(x + (int64_t)mm * k + 8 * g);
 #pragma unroll
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(256) void qmv_generic_kernel(const uint8_t* __restr
     }
   }
 #pragma unroll
-  for (int mm = 0; mm < 8; ++mm) {
+  for (int mm = 0; mm < QMV_MAX_M; ++mm) {
     float s = acc[mm];
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
@@ -305,7 +307,7 @@ __global__ __launch_bounds__(256) void qmv_generic_kernel(const uint8_t* __restr
 }
 
 // ---------------------------------------------------------------------------
-// Matrix-core GEMV for 3 <= M <= 8 activation rows.  With more than two rows
+// Matrix-core GEMV for 3 <= M <= 16 activation rows.  With more than two rows
 // the dot2 path spends M v_dot2 per pair of weights; here each weight is
 // decoded once to float16 (its exact value rounded once) and the products go
 // to v_mfma_f32_16x16x32_f16.  B operand: 16 weight rows x 32 K values, lane
@@ -524,6 +526,15 @@ hipError_t launch_c(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
     case 6: return launch_m<C, 6>(w, n, k, rb, x, y, f16, s);
     case 7: return launch_m<C, 7>(w, n, k, rb, x, y, f16, s);
     case 8: return launch_m<C, 8>(w, n, k, rb, x, y, f16, s);
+    // 9..16 rows: the matrix-core GEMV (one 16-row MFMA A operand)
+    case 9: return launch_mma<C, 9>(w, n, k, rb, x, y, f16, s);
+    case 10: return launch_mma<C, 10>(w, n, k, rb, x, y, f16, s);
+    case 11: return launch_mma<C, 11>(w, n, k, rb, x, y, f16, s);
+    case 12: return launch_mma<C, 12>(w, n, k, rb, x, y, f16, s);
+    case 13: return launch_mma<C, 13>(w, n, k, rb, x, y, f16, s);
+    case 14: return launch_mma<C, 14>(w, n, k, rb, x, y, f16, s);
+    case 15: return launch_mma<C, 15>(w, n, k, rb, x, y, f16, s);
+    case 16: return launch_mma<C, 16>(w, n, k, rb, x, y, f16, s);
   }
   return hipErrorInvalidValue;
 }

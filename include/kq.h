@@ -104,9 +104,10 @@ int kq_dequantize(int codec, const void* w, int64_t rows, int64_t k,
  * y[m][n] = sum_k x[m][k] * dequant(w)[n][k], float32 accumulation.
  * w [N][row_bytes], x float16 [M][K], y [M][N] float32 or float16.
  *
- * kq_qmv: decode-shaped GEMV, 1 <= M <= 8 (one weight read serves all M rows).
+ * kq_qmv: decode-shaped GEMV, 1 <= M <= 16 (one weight read serves all M rows;
+ *         3 or more rows run on the matrix cores).
  * kq_qmm: prefill GEMM on f16 matrix cores, any M >= 1.
- * kq_quantized_matmul: kq_qmv for M <= 8, else kq_qmm.
+ * kq_quantized_matmul: kq_qmv for M <= 16, else kq_qmm.
  * The K-reduction order is fixed per (codec, N, K, M): results are
  * deterministic run to run, and a row's result does not depend on the other
  * rows of x. */

@@ -75,7 +75,7 @@ def _st(ret):
     "call, status, msg",
     [
         (lambda: L.kq_qmv(12, A16, 64, 4000, A16, 1, A16, 0, None), kq.KQ_ERR_SHAPE, "K=4000"),
-        (lambda: L.kq_qmv(12, A16, 64, 4096, A16, 9, A16, 0, None), kq.KQ_ERR_SHAPE, "M=9"),
+        (lambda: L.kq_qmv(12, A16, 64, 4096, A16, 17, A16, 0, None), kq.KQ_ERR_SHAPE, "M=17"),
         (lambda: L.kq_qmv(99, A16, 64, 4096, A16, 1, A16, 0, None), kq.KQ_ERR_CODEC, "codec"),
         (lambda: L.kq_qmv(12, A16 + 4, 64, 4096, A16, 1, A16, 0, None), kq.KQ_ERR_ALIGN, "w="),
         (lambda: L.kq_qmv(12, A16, 64, 4096, A16 + 2, 1, A16, 0, None), kq.KQ_ERR_ALIGN, "x="),

@@ -150,7 +150,7 @@ def _shapes_qmv(codec):
 
 
 @pytest.mark.parametrize("codec", CODECS)
-@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8, 12, 16])
 def test_qmv_parity(kq, codec, m):
     torch = _torch()
     for n, k in _shapes_qmv(codec):
@@ -304,7 +304,7 @@ def test_quantized_matmul_routes_by_m(kq):
     torch = _torch()
     n, k = 64, 512
     w = _weights("q4_k", n, k, 3)
-    for m in (1, 8, 9, 40):
+    for m in (1, 8, 9, 16, 17, 40):
         x = _x(m, k, m)
         y = torch.empty((m, n), dtype=torch.float32, device="cuda")
         kq.kq_quantized_matmul("q4_k", dev(w), n, k, dev(x), y)
