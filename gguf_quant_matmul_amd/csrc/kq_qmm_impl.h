@@ -665,10 +665,19 @@ hipError_t launch_dense(const uint8_t* w, int64_t n, int64_t k, int64_t rb, cons
   // prefill: 256 x 224 tiles (N = 14336 gives 64 tile columns) while they
   // give every CU at least one; fewer (N = 4096: 152) leave CUs idle for the
   // whole K walk, and 128 x 256 tiles fill them
+  // Below that, with one M tile (M <= 128), 64-column tiles (four times the
+  // tiles of 256 columns) keep the CUs busy when N / 256 tiles cannot: q4_K
+  // 14336 x 4096, M = 32 .. 128 measured 49 .. 53 us against 56 .. 82 us.
+  // With two M tiles they were slower (M = 192, 256: 87 us against 80).
   constexpr int64_t kCUs = 256;
   if (m > 128 && ((m + 255) / 256) * ((n + 223) / 224) >= kCUs)
     return launch_t<C, 256, 224, 4, 2, 1, 2, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
-  if (m > 64) return launch_t<C, 128, 256, 2, 4, 2, 3, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+  const bool narrow = ((m + 127) / 128) * ((n + 255) / 256) < kCUs;
+  if (m > 64) {
+    if (narrow && m <= 128) return launch_t<C, 128, 64, 4, 2, 2, 4, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+    return launch_t<C, 128, 256, 2, 4, 2, 3, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
+  }
+  if (narrow) return launch_t<C, 64, 64, 2, 4, 2, 4, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
   return launch_t<C, 64, 256, 2, 4, 2, 4, EP, ACT>(w, n, k, rb, x, m, y, f16, epi, s);
 }
 
