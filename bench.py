@@ -41,9 +41,9 @@ COPY_REF_BYTES = 256 << 20     # the elementwise copy that scales the HBM byte c
 # copy of COPY_REF_BYTES).  A figure is reported only while the digest of the
 # kernel's sources still matches the one the counters were taken on.
 TRAFFIC = {
-    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "f77811330ca8abb3",
-            "bytes": 9595110},
-    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "ae87c3af5033cfc2", "bytes": 357180690},
+    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "88602db09c5f400d",
+            "bytes": 9594282},
+    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "a29ab4592db268f4", "bytes": 357094654},
 }
 
 
@@ -260,7 +260,8 @@ def cold_gemv_row(torch, kq, cfg):
 
 def codec_rows(torch, kq):
     """q5_K on the decode GEMV, prefill GEMM and MoE segment shapes; the legacy
-    32-value codecs, q2_K and q3_K on the 14336x4096 GEMV."""
+    32-value codecs, q2_K and q3_K on the 14336x4096 GEMV; small prefill
+    batches (M = 16, 64, 128) on the q4_K GEMM weight."""
     from gguf_quant_matmul_amd import workloads as W
 
     rows = []
@@ -269,6 +270,25 @@ def codec_rows(torch, kq):
         rows.append(r)
     r, wq = cold_gemv_row(torch, kq, W.Q5K_GEMV)
     rows.append(r)
+    # small prefill batches on the q4_K 14336 x 4096 weight (kq_quantized_matmul
+    # routes M <= 16 to the GEMV, larger M to the GEMM), weight copies rotated
+    c4 = W.CFG4_Q4K_GEMM
+    w4 = gpu_weights(torch, kq, c4.codec, c4.seed, c4.n, c4.k, c4.dist)
+    nc = copies_for(w4.numel())
+    w4s = [w4] + [w4.clone() for _ in range(nc - 1)]
+    xa = torch.from_numpy(W.gemv_activations(c4)).cuda()
+    for m in (16, 64, 128):
+        ym = torch.empty((m, c4.n), dtype=torch.float16, device="cuda")
+        xm = xa[:m]
+        g = capture(torch, lambda: [kq.kq_quantized_matmul(c4.codec, w4s[i % nc], c4.n, c4.k, xm, ym) for i in range(nc)])
+        ms = time_graph(torch, g, nc, 5)
+        flop = 2 * m * c4.n * c4.k
+        alg = w4.numel() + xm.numel() * 2 + ym.numel() * 2
+        rows.append({"row": "kq_quantized_matmul", "workload": f"q4_K small prefill {m}x{c4.n}x{c4.k}, f16 out",
+                     "us": round(ms * 1e3, 2), "GB/s": round(alg / ms / 1e6, 1),
+                     "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3), "TFLOP/s": round(flop / ms / 1e9, 1),
+                     "alg_bytes": alg, "copies": nc})
+    del w4s, w4
     cfg = W.Q5K_GEMM
     xm = torch.from_numpy(W.gemv_activations(cfg)).cuda()
     ym = torch.empty((cfg.m, cfg.n), dtype=torch.float16, device="cuda")
