@@ -41,9 +41,9 @@ COPY_REF_BYTES = 256 << 20     # the elementwise copy that scales the HBM byte c
 # copy of COPY_REF_BYTES).  A figure is reported only while the digest of the
 # kernel's sources still matches the one the counters were taken on.
 TRAFFIC = {
-    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "88602db09c5f400d",
-            "bytes": 9594282},
-    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "a29ab4592db268f4", "bytes": 357094654},
+    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "d871621eeb18dab0",
+            "bytes": 9594246},
+    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "d025686bc26916b2", "bytes": 357188476},
 }
 
 
@@ -271,13 +271,14 @@ def codec_rows(torch, kq):
     r, wq = cold_gemv_row(torch, kq, W.Q5K_GEMV)
     rows.append(r)
     # small prefill batches on the q4_K 14336 x 4096 weight (kq_quantized_matmul
-    # routes M <= 16 to the GEMV, larger M to the GEMM), weight copies rotated
+    # routes M <= 16 to the GEMV, M <= 64 to the wide matrix-core GEMV, larger M
+    # to the GEMM), weight copies rotated
     c4 = W.CFG4_Q4K_GEMM
     w4 = gpu_weights(torch, kq, c4.codec, c4.seed, c4.n, c4.k, c4.dist)
     nc = copies_for(w4.numel())
     w4s = [w4] + [w4.clone() for _ in range(nc - 1)]
     xa = torch.from_numpy(W.gemv_activations(c4)).cuda()
-    for m in (16, 64, 128):
+    for m in (16, 32, 64, 128):
         ym = torch.empty((m, c4.n), dtype=torch.float16, device="cuda")
         xm = xa[:m]
         g = capture(torch, lambda: [kq.kq_quantized_matmul(c4.codec, w4s[i % nc], c4.n, c4.k, xm, ym) for i in range(nc)])

@@ -191,6 +191,15 @@ int kq_qmm(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_
 int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                         int y_dtype, void* stream) {
   if (m >= 0 && m <= kq::QMV_MAX_M) return kq_qmv(codec, w, n, k, x, m, y, y_dtype, stream);
+  if (m <= kq::QMV_WIDE_MAX_M && k % 64 == 0) {  // small prefill batch: the wide matrix-core GEMV
+    const char* op = "kq_quantized_matmul";
+    int64_t rb;
+    int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb);
+    if (st) return st;
+    if (n == 0) return KQ_OK;
+    return hip_status(op, kq::launch_qmv_wide(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, (int)m, y,
+                                              y_dtype == KQ_F16, (hipStream_t)stream));
+  }
   return kq_qmm(codec, w, n, k, x, m, y, y_dtype, stream);
 }
 

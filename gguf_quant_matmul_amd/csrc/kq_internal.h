@@ -183,6 +183,9 @@ __device__ __forceinline__ int q3k_scale(uint32_t A, uint32_t B, int up, int t) 
 constexpr int GLU_SILU = 0, GLU_GELU_TANH = 1, GLU_SILU_LIMIT = 2;
 // activation rows the GEMV takes (the matrix-core GEMV's A operand has 16)
 constexpr int QMV_MAX_M = 16;
+// activation rows up to which kq_quantized_matmul takes the matrix-core GEMV
+// with several A operands per decoded weight operand (kq_qmv_wide.hip)
+constexpr int QMV_WIDE_MAX_M = 64;
 // activation rows up to which the GLU product runs on the GEMV body (two
 // matrices' q3_K units fill the registers from two rows on)
 constexpr int QMV_GLU_MAX_M = 3;
@@ -308,6 +311,8 @@ hipError_t launch_dequantize(int codec, const uint8_t* w, int64_t rows, int64_t 
                              void* out, int f16out, hipStream_t s);
 hipError_t launch_qmv(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes,
                       const half_t* x, int m, void* y, int f16out, hipStream_t s);
+hipError_t launch_qmv_wide(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes,
+                           const half_t* x, int m, void* y, int f16out, hipStream_t s);
 hipError_t launch_qmm(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes,
                       const half_t* x, int64_t m, void* y, int f16out, hipStream_t s);
 hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,

@@ -311,6 +311,29 @@ def test_quantized_matmul_routes_by_m(kq):
         assert_close_rows(host(y), matmul.qmatmul("q4_k", w, k, x), what=f"quantized_matmul m={m}")
 
 
+@pytest.mark.parametrize("codec", CODECS)
+def test_quantized_matmul_small_prefill_wide_gemv(kq, codec):
+    # 17..64 rows with K a multiple of 64 take the wide matrix-core GEMV: two
+    # 16-row activation operands up to 32 rows, four up to 64.  N = 72 leaves a
+    # partial 32-row workgroup; K spans several activation chunks (1024 values
+    # for two operands, 512 for four) and ends in a short one.
+    torch = _torch()
+    n = 72
+    k = 1280 if codec in SUPER else 1344
+    w = _weights(codec, n, k, 31)
+    wd = dev(w)
+    for m in (17, 31, 32, 33, 50, 64):
+        x = _x(m, k, 40 + m)
+        want = matmul.qmatmul(codec, w, k, x)
+        for dt in (torch.float32, torch.float16):
+            y = torch.full((m, n), float("nan"), dtype=dt, device="cuda")
+            say(f"{codec} quantized_matmul m={m} n={n} k={k} {dt}")
+            kq.kq_quantized_matmul(codec, wd, n, k, dev(x), y)
+            got = host(y).astype(np.float64)
+            assert np.isfinite(got).all(), f"{codec} m={m}: unwritten outputs"
+            assert_close_rows(got, want, what=f"{codec} quantized_matmul m={m} {dt}")
+
+
 def test_qmm_row_independence_and_determinism(kq):
     torch = _torch()
     m, n, k = 200, 96, 1024
