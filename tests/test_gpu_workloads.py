@@ -212,3 +212,28 @@ def test_residual_prefill_workload(kq):
     assert_close_rows(host(y)[:, ns].astype(np.float64), ref, what="residual prefill")
     del wd, y
     torch.cuda.empty_cache()
+
+
+def test_small_prefill_workload(kq):
+    # the small-prefill bench rows: the GEMM workload's q4_K 14336 x 4096 weight
+    # with the first M of its activation rows through kq_quantized_matmul,
+    # float16 out (16 rows: the GEMV; 32 and 64: the wide matrix-core GEMV;
+    # 128: the GEMM)
+    import torch
+
+    c = W.CFG4_Q4K_GEMM
+    say("workload small prefill: weights")
+    wq = _gpu_encode(kq, c.codec, c.seed, c.n, c.k)
+    ns = _sample(c.n, 32, 13)
+    w_rows = encode.quantize(c.codec, W.weight_rows(c.seed, c.n, c.k, rows=ns))
+    assert np.array_equal(host(wq[torch.from_numpy(ns).cuda()]), w_rows)
+    xa = W.gemv_activations(c)
+    for m in (16, 32, 64, 128):
+        x = xa[:m]
+        y = torch.empty((m, c.n), dtype=torch.float16, device="cuda")
+        say(f"workload small prefill: M={m}")
+        kq.kq_quantized_matmul(c.codec, wq, c.n, c.k, dev(x), y)
+        ref = matmul.qmatmul(c.codec, w_rows, c.k, x)
+        assert_close_rows(host(y)[:, ns].astype(np.float64), ref, what=f"small prefill M={m}")
+    del wq, y
+    torch.cuda.empty_cache()
