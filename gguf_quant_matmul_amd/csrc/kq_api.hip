@@ -190,8 +190,11 @@ int kq_qmm(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_
 
 int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                         int y_dtype, void* stream) {
-  if (m >= 0 && m <= kq::QMV_MAX_M) return kq_qmv(codec, w, n, k, x, m, y, y_dtype, stream);
-  if (m <= kq::QMV_WIDE_MAX_M && k % 64 == 0) {  // small prefill batch: the wide matrix-core GEMV
+  // small prefill batches: the wide matrix-core GEMV (from 9 rows when the
+  // matrix has few rows, else from 17)
+  const bool wide = m <= kq::QMV_WIDE_MAX_M && k % 64 == 0 && (m > kq::QMV_MAX_M || (m >= 9 && kq::wide_narrow(n)));
+  if (m >= 0 && m <= kq::QMV_MAX_M && !wide) return kq_qmv(codec, w, n, k, x, m, y, y_dtype, stream);
+  if (wide) {
     const char* op = "kq_quantized_matmul";
     int64_t rb;
     int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb);
@@ -228,11 +231,15 @@ int kq_quantized_matmul_residual(int codec, const void* w, int64_t n, int64_t k,
     return fail(KQ_ERR_ARG, op, "residual overlaps y without being y");
   if (gate && overlaps(gate, gate_rows * n * es, y, ybytes)) return fail(KQ_ERR_ARG, op, "gate overlaps y");
   const kq::Epi epi{residual, gate, nullptr, gate ? (int)(m / gate_rows) : 1};
-  const hipError_t e =
-      m <= 8 ? kq::launch_qmv_epi(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, (int)m, epi, y,
-                                  y_dtype == KQ_F16, (hipStream_t)stream)
-             : kq::launch_qmm_epi(codec, (const uint8_t*)w, n, k, rb, (const kq::half_t*)x, m, epi, y,
-                                  y_dtype == KQ_F16, (hipStream_t)stream);
+  const bool f16 = y_dtype == KQ_F16;
+  const kq::half_t* xh = (const kq::half_t*)x;
+  hipError_t e;
+  if (m <= 8)  // the GEMV body
+    e = kq::launch_qmv_epi(codec, (const uint8_t*)w, n, k, rb, xh, (int)m, epi, y, f16, (hipStream_t)stream);
+  else if (m <= kq::QMV_WIDE_MAX_M && k % 64 == 0)  // small batches: the wide matrix-core GEMV
+    e = kq::launch_qmv_wide_epi(codec, (const uint8_t*)w, n, k, rb, xh, (int)m, epi, y, f16, (hipStream_t)stream);
+  else
+    e = kq::launch_qmm_epi(codec, (const uint8_t*)w, n, k, rb, xh, m, epi, y, f16, (hipStream_t)stream);
   return hip_status(op, e);
 }
 

@@ -186,6 +186,10 @@ constexpr int QMV_MAX_M = 16;
 // activation rows up to which kq_quantized_matmul takes the matrix-core GEMV
 // with several A operands per decoded weight operand (kq_qmv_wide.hip)
 constexpr int QMV_WIDE_MAX_M = 64;
+// A matrix with so few rows that the wide GEMV's 32-row workgroups leave CUs
+// idle (a 256-CU part): it splits K four ways per row group instead of two,
+// and takes the plain product's 9..16 rows as well.
+__host__ __device__ constexpr bool wide_narrow(int64_t n) { return (n + 31) / 32 < 256; }
 // activation rows up to which the GLU product runs on the GEMV body (two
 // matrices' q3_K units fill the registers from two rows on)
 constexpr int QMV_GLU_MAX_M = 3;
@@ -313,6 +317,8 @@ hipError_t launch_qmv(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t
                       const half_t* x, int m, void* y, int f16out, hipStream_t s);
 hipError_t launch_qmv_wide(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes,
                            const half_t* x, int m, void* y, int f16out, hipStream_t s);
+hipError_t launch_qmv_wide_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes,
+                               const half_t* x, int m, const Epi& epi, void* y, int f16out, hipStream_t s);
 hipError_t launch_qmm(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes,
                       const half_t* x, int64_t m, void* y, int f16out, hipStream_t s);
 hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,

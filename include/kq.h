@@ -109,7 +109,8 @@ int kq_dequantize(int codec, const void* w, int64_t rows, int64_t k,
  * kq_qmm: prefill GEMM on f16 matrix cores, any M >= 1.
  * kq_quantized_matmul: kq_qmv for M <= 16; for 17 <= M <= 64 with K a
  *         multiple of 64, a matrix-core GEMV that meets each decoded weight
- *         operand with two or four 16-row activation operands; else kq_qmm.
+ *         operand with two or four 16-row activation operands (from M = 9
+ *         when N < 8161); else kq_qmm.
  * The K-reduction order is fixed per (codec, N, K, M): results are
  * deterministic run to run, and a row's result does not depend on the other
  * rows of x. */
@@ -122,9 +123,10 @@ int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k,
 
 /* ---- fused epilogues (mlx-kquant bindings.cpp page: quantized_matmul_residual,
  *      quantized_matmul_qmv_bias and quantized_matmul_glu docstrings) ----
- * The product p[m][n] of kq_quantized_matmul (same w, x, M, N, K rules and
- * the same GEMV / GEMM split) finished in the store, in float32, rounded
- * once to y_dtype:
+ * The product p[m][n] of kq_quantized_matmul (same w, x, M, N, K rules)
+ * finished in the store, in float32, rounded once to y_dtype.  The residual
+ * and bias run on the GEMV body for M <= 8, on the wide matrix-core GEMV for
+ * 9 <= M <= 64 with K a multiple of 64, else on the GEMM:
  *
  * kq_quantized_matmul_residual:  y = residual + gate * p.
  *   residual [M][N] and gate [gate_rows][N] are in y_dtype; output row m takes

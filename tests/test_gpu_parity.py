@@ -191,6 +191,8 @@ def test_qmm_parity(kq, codec):
 def _epi_shapes(codec):
     kk = 256 * 9 if codec in SUPER else 64 * 9
     shapes = [(1, 37, kk), (3, 300, kk), (8, 45, kk), (130, 200, kk), (260, 131, kk)]
+    # 9..64 rows: the wide matrix-core GEMV (one, two, four A operands)
+    shapes += [(12, 70, kk), (24, 90, kk), (40, 45, kk), (64, 33, kk), (40, 8200, kk)]
     if codec not in SUPER:
         shapes += [(4, 45, 2048 + 32), (70, 40, 96)]  # odd block counts: generic kernels
     return shapes
@@ -198,7 +200,7 @@ def _epi_shapes(codec):
 
 @pytest.mark.parametrize("codec", CODECS)
 def test_quantized_matmul_residual_parity(kq, codec):
-    # y = residual + gate * p on the GEMV (M <= 8) and GEMM bodies; gate
+    # y = residual + gate * p on the GEMV (M <= 8), wide GEMV (M <= 64) and GEMM bodies; gate
     # absent, one row, or one row per batch of consecutive rows; in place
     # (residual is y) and out of place
     torch = _torch()
@@ -311,18 +313,20 @@ def test_quantized_matmul_routes_by_m(kq):
         assert_close_rows(host(y), matmul.qmatmul("q4_k", w, k, x), what=f"quantized_matmul m={m}")
 
 
+@pytest.mark.parametrize("n", (72, 8200))
 @pytest.mark.parametrize("codec", CODECS)
-def test_quantized_matmul_small_prefill_wide_gemv(kq, codec):
+def test_quantized_matmul_small_prefill_wide_gemv(kq, codec, n):
     # 17..64 rows with K a multiple of 64 take the wide matrix-core GEMV: two
-    # 16-row activation operands up to 32 rows, four up to 64.  N = 72 leaves a
-    # partial 32-row workgroup; K spans several activation chunks (1024 values
-    # for two operands, 512 for four) and ends in a short one.
+    # 16-row activation operands up to 32 rows, four up to 64; for a matrix
+    # with few rows (N = 72) also 9..16 rows, on one operand, with K split four
+    # ways per row group instead of two (N = 8200).  Both N leave a partial
+    # last workgroup; K spans several activation chunks (1024 values, or 512
+    # for four operands split two ways) and ends in a short one.
     torch = _torch()
-    n = 72
     k = 1280 if codec in SUPER else 1344
     w = _weights(codec, n, k, 31)
     wd = dev(w)
-    for m in (17, 31, 32, 33, 50, 64):
+    for m in ((9, 16) if n < 8000 else ()) + (17, 31, 32, 33, 50, 64):
         x = _x(m, k, 40 + m)
         want = matmul.qmatmul(codec, w, k, x)
         for dt in (torch.float32, torch.float16):
