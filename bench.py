@@ -41,9 +41,9 @@ COPY_REF_BYTES = 256 << 20     # the elementwise copy that scales the HBM byte c
 # copy of COPY_REF_BYTES).  A figure is reported only while the digest of the
 # kernel's sources still matches the one the counters were taken on.
 TRAFFIC = {
-    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "c29ffda5b4a91d50",
-            "bytes": 9594266},
-    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "7a84ee3027a29729", "bytes": 357108660},
+    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "24b31ed93c47d581",
+            "bytes": 9594941},
+    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "fc2cb12ef684b91e", "bytes": 357104697},
 }
 
 
@@ -367,6 +367,13 @@ def epilogue_rows(torch, kq):
         lambda i: kq.kq_quantized_matmul_glu(c4.codec, wgs[i % nc], wus[i % nc], n_ffn, k_ffn, x1, y1, "silu"),
         lambda i: kq.kq_quantized_matmul(c4.codec, wgs[i % nc], n_ffn, k_ffn, x1, y1), nl,
         0, 2 * nb + k_ffn * 2 + n_ffn * 4)
+    # a small decode batch: the two passes of the wide matrix-core GEMV
+    x16 = xp[:16].clone()
+    y16 = torch.empty((16, n_ffn), dtype=torch.float16, device="cuda")
+    row("kq_quantized_matmul_glu", f"q4_K GLU (silu) batch 16x{n_ffn}x{k_ffn}, gate+up, f16 out",
+        lambda i: kq.kq_quantized_matmul_glu(c4.codec, wgs[i % nc], wus[i % nc], n_ffn, k_ffn, x16, y16, "silu"),
+        lambda i: kq.kq_quantized_matmul(c4.codec, wgs[i % nc], n_ffn, k_ffn, x16, y16), nl,
+        2 * 2 * 16 * n_ffn * k_ffn, 2 * nb + x16.numel() * 2 + y16.numel() * 2)
     del wgs, wus, wg, wu, yp
     torch.cuda.empty_cache()
 

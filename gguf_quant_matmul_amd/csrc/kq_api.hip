@@ -271,12 +271,21 @@ int kq_quantized_matmul_glu(int codec, const void* w_gate, const void* w_up, int
   if (n == 0 || m == 0) return KQ_OK;
   if (!w_up) return fail(KQ_ERR_ARG, op, "null w_up");
   if (!aligned(w_up, 16)) return fail(KQ_ERR_ALIGN, op, "w_up=%p is not 16-byte aligned", w_up);
-  const hipError_t e =
-      m <= kq::qmv_glu_max_m(codec)
-          ? kq::launch_qmv_glu(codec, (const uint8_t*)w_gate, (const uint8_t*)w_up, n, k, rb, (const kq::half_t*)x,
-                               (int)m, act, y, y_dtype == KQ_F16, (hipStream_t)stream)
-          : kq::launch_qmm_glu(codec, (const uint8_t*)w_gate, (const uint8_t*)w_up, n, k, rb, (const kq::half_t*)x,
-                               m, act, y, y_dtype == KQ_F16, (hipStream_t)stream);
+  const bool f16 = y_dtype == KQ_F16;
+  const kq::half_t* xh = (const kq::half_t*)x;
+  hipError_t e;
+  if (m <= kq::qmv_glu_max_m(codec)) {  // one GEMV pass over both weights
+    e = kq::launch_qmv_glu(codec, (const uint8_t*)w_gate, (const uint8_t*)w_up, n, k, rb, xh, (int)m, act, y, f16,
+                           (hipStream_t)stream);
+  } else if (m <= kq::QMV_WIDE_MAX_M && k % 64 == 0) {  // two wide matrix-core GEMV passes
+    e = kq::launch_qmv_wide_glu_act(codec, (const uint8_t*)w_gate, n, k, rb, xh, (int)m, act, y, f16,
+                                    (hipStream_t)stream);
+    if (e == hipSuccess)
+      e = kq::launch_qmv_wide_glu_mul(codec, (const uint8_t*)w_up, n, k, rb, xh, (int)m, y, f16, (hipStream_t)stream);
+  } else {  // two GEMM passes
+    e = kq::launch_qmm_glu(codec, (const uint8_t*)w_gate, (const uint8_t*)w_up, n, k, rb, xh, m, act, y, f16,
+                           (hipStream_t)stream);
+  }
   return hip_status(op, e);
 }
 

@@ -319,6 +319,10 @@ hipError_t launch_qmv_wide(int codec, const uint8_t* w, int64_t n, int64_t k, in
                            const half_t* x, int m, void* y, int f16out, hipStream_t s);
 hipError_t launch_qmv_wide_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes,
                                const half_t* x, int m, const Epi& epi, void* y, int f16out, hipStream_t s);
+hipError_t launch_qmv_wide_glu_act(int codec, const uint8_t* w_gate, int64_t n, int64_t k, int64_t row_bytes,
+                                   const half_t* x, int m, int act, void* y, int f16out, hipStream_t s);
+hipError_t launch_qmv_wide_glu_mul(int codec, const uint8_t* w_up, int64_t n, int64_t k, int64_t row_bytes,
+                                   const half_t* x, int m, void* y, int f16out, hipStream_t s);
 hipError_t launch_qmm(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t row_bytes,
                       const half_t* x, int64_t m, void* y, int f16out, hipStream_t s);
 hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t n_experts, int64_t n, int64_t k,

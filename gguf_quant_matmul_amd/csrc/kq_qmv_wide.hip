@@ -8,7 +8,7 @@ namespace kq {
 hipError_t launch_qmv_wide(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m,
                            void* y, int f16, hipStream_t s) {
   if (m < 9 || m > QMV_WIDE_MAX_M || (m <= QMV_MAX_M && !wide_narrow(n)) || k % 64 != 0) return hipErrorInvalidValue;
-  return launch_wide<false>(codec, w, n, k, rb, x, m, Epi{nullptr, nullptr, nullptr, 1}, y, f16, s);
+  return launch_wide<EP_PLAIN>(codec, w, n, k, rb, x, m, Epi{nullptr, nullptr, nullptr, 1}, 0, y, f16, s);
 }
 
 }  // namespace kq

@@ -8,7 +8,7 @@ namespace kq {
 hipError_t launch_qmv_wide_epi(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m,
                                const Epi& epi, void* y, int f16, hipStream_t s) {
   if (m < 9 || m > QMV_WIDE_MAX_M || k % 64 != 0) return hipErrorInvalidValue;
-  return launch_wide<true>(codec, w, n, k, rb, x, m, epi, y, f16, s);
+  return launch_wide<EP_EPI>(codec, w, n, k, rb, x, m, epi, 0, y, f16, s);
 }
 
 }  // namespace kq

@@ -1,6 +1,7 @@
 // kq_qmv_wide_impl.h -- the matrix-core GEMV for small prefill batches (up to
 // 64 activation rows), shared by kq_qmv_wide.hip (the plain product of
-// kq_quantized_matmul) and kq_qmv_wide_epi.hip (its residual epilogue).
+// kq_quantized_matmul), kq_qmv_wide_epi.hip (its residual epilogue) and
+// kq_qmv_wide_glu.hip (the two passes of its GLU product).
 //
 // mlx-kquant bindings.cpp page, quantized_matmul docstring; the README's
 // remark that a matmul over few rows amortizes one weight read over all of
@@ -32,12 +33,13 @@ __host__ __device__ constexpr int wide_kchunk(int t, int ks) {
 // consumed.  M is a run-time argument: the kernel is sized for 16 T rows.
 // KS waves of the workgroup share a 16-row group, each a part of every chunk
 // (2, or 4 when the matrix has few rows, so that the grid still covers the
-// CUs).  EPI: the products go through epi_apply (residual, gate, bias)
-// before the store.
-template <int C, int T, int KS, bool F16, bool EPI>
+// CUs).  EP: the store mode (kq_internal.h: plain, epi_apply, or one pass of
+// the GLU product; the gate pass's activation is act, GLU_SILU or
+// GLU_GELU_TANH).
+template <int C, int T, int KS, bool F16, int EP>
 __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_wide_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                                    int64_t row_bytes, const half_t* __restrict__ x,
-                                                                   int m, Epi epi, void* __restrict__ y) {
+                                                                   int m, Epi epi, int act, void* __restrict__ y) {
   typedef typename UnitOf<C>::T Unit;
   static_assert(T >= 1 && T <= 4, "A operands per B operand");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -158,12 +160,14 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_wide_kernel(const uint8_t
         for (int i = 0; i < 4; ++i) {
           const int mr = 16 * t + 4 * (lane >> 4) + i;
           if (mr < m) {
-            float v = acc[t][i];
-            if constexpr (EPI) v = epi_apply<F16>(epi, mr, col, n, v);
-            if (F16)
-              ((half_t*)y)[(int64_t)mr * n + col] = (half_t)v;
-            else
-              ((float*)y)[(int64_t)mr * n + col] = v;
+            if constexpr (EP == EP_GLU_ACT) {
+              if (act == GLU_SILU)
+                store_out<F16, EP, GLU_SILU>(y, mr, col, n, epi, acc[t][i]);
+              else
+                store_out<F16, EP, GLU_GELU_TANH>(y, mr, col, n, epi, acc[t][i]);
+            } else {
+              store_out<F16, EP, 0>(y, mr, col, n, epi, acc[t][i]);
+            }
           }
         }
       }
@@ -172,9 +176,9 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_wide_kernel(const uint8_t
 }
 
 // m <= 16 T activation rows; K a whole number of 64-value units.
-template <int C, int T, int KS, bool EPI>
+template <int C, int T, int KS, int EP>
 hipError_t launch_mma_wide(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m, const Epi& epi,
-                           void* y, int f16, hipStream_t s) {
+                           int act, void* y, int f16, hipStream_t s) {
   const int kc = (int)(k < wide_kchunk(T, KS) ? k : wide_kchunk(T, KS));
   size_t lds = (size_t)(16 * T) * mma_xstride(kc) * 2;
   const size_t part_bytes = (size_t)(4 / KS) * (KS - 1) * 64 * T * sizeof(float4_t);
@@ -182,47 +186,47 @@ hipError_t launch_mma_wide(const uint8_t* w, int64_t n, int64_t k, int64_t rb, c
   constexpr int rows_per_block = 16 * (4 / KS);
   const dim3 grid((unsigned)((n + rows_per_block - 1) / rows_per_block));
   if (f16)
-    hipLaunchKernelGGL((qmv_mma_wide_kernel<C, T, KS, true, EPI>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k,
-                       rb, x, m, epi, y);
+    hipLaunchKernelGGL((qmv_mma_wide_kernel<C, T, KS, true, EP>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k,
+                       rb, x, m, epi, act, y);
   else
-    hipLaunchKernelGGL((qmv_mma_wide_kernel<C, T, KS, false, EPI>), grid, dim3(MMA_THREADS), lds, s, w, (int)n,
-                       (int)k, rb, x, m, epi, y);
+    hipLaunchKernelGGL((qmv_mma_wide_kernel<C, T, KS, false, EP>), grid, dim3(MMA_THREADS), lds, s, w, (int)n,
+                       (int)k, rb, x, m, epi, act, y);
   return hipGetLastError();
 }
 
 // Four waves per row group when two would leave CUs without a workgroup (a
 // 256-CU part); with enough rows, two (four measured 1.4 to 2.4 times slower
 // at N = 14336).
-template <int C, int T, bool EPI>
+template <int C, int T, int EP>
 hipError_t launch_mma_wide_ks(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m,
-                              const Epi& epi, void* y, int f16, hipStream_t s) {
-  if (wide_narrow(n)) return launch_mma_wide<C, T, 4, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-  return launch_mma_wide<C, T, 2, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
+                              const Epi& epi, int act, void* y, int f16, hipStream_t s) {
+  if (wide_narrow(n)) return launch_mma_wide<C, T, 4, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+  return launch_mma_wide<C, T, 2, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
 }
 
 // One A operand up to 16 rows, two up to 32, four up to 64.
-template <int C, bool EPI>
+template <int C, int EP>
 hipError_t launch_wide_c(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m, const Epi& epi,
-                         void* y, int f16, hipStream_t s) {
-  if (m <= 16) return launch_mma_wide_ks<C, 1, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-  if (m <= 32) return launch_mma_wide_ks<C, 2, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-  return launch_mma_wide_ks<C, 4, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
+                         int act, void* y, int f16, hipStream_t s) {
+  if (m <= 16) return launch_mma_wide_ks<C, 1, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+  if (m <= 32) return launch_mma_wide_ks<C, 2, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+  return launch_mma_wide_ks<C, 4, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
 }
 
-template <bool EPI>
+template <int EP>
 hipError_t launch_wide(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, int m,
-                       const Epi& epi, void* y, int f16, hipStream_t s) {
+                       const Epi& epi, int act, void* y, int f16, hipStream_t s) {
   switch (codec) {
-    case Q4_0: return launch_wide_c<Q4_0, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q8_0: return launch_wide_c<Q8_0, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q4_1: return launch_wide_c<Q4_1, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q5_0: return launch_wide_c<Q5_0, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q5_1: return launch_wide_c<Q5_1, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q2_K: return launch_wide_c<Q2_K, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q3_K: return launch_wide_c<Q3_K, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q4_K: return launch_wide_c<Q4_K, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q5_K: return launch_wide_c<Q5_K, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
-    case Q6_K: return launch_wide_c<Q6_K, EPI>(w, n, k, rb, x, m, epi, y, f16, s);
+    case Q4_0: return launch_wide_c<Q4_0, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q8_0: return launch_wide_c<Q8_0, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q4_1: return launch_wide_c<Q4_1, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q5_0: return launch_wide_c<Q5_0, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q5_1: return launch_wide_c<Q5_1, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q2_K: return launch_wide_c<Q2_K, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q3_K: return launch_wide_c<Q3_K, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q4_K: return launch_wide_c<Q4_K, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q5_K: return launch_wide_c<Q5_K, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
+    case Q6_K: return launch_wide_c<Q6_K, EP>(w, n, k, rb, x, m, epi, act, y, f16, s);
   }
   return hipErrorInvalidValue;
 }

@@ -145,8 +145,9 @@ int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k,
  *   float16 store turns a finite value beyond the float16 range into the
  *   largest finite half of its sign (infinities and NaN pass).  M <= 3
  *   (q3_K: M = 1) runs both weights through one GEMV pass; larger M runs two
- *   GEMM passes on the stream (gate, then up), with y as the only buffer
- *   between them.
+ *   passes on the stream (gate, then up), with y as the only buffer between
+ *   them: on the wide matrix-core GEMV for M <= 64 with K a multiple of 64,
+ *   else on the GEMM.
  *
  * Element alignment for residual, gate and bias; the rest as in
  * kq_quantized_matmul. */

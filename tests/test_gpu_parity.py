@@ -247,12 +247,15 @@ def test_quantized_matmul_qmv_bias_parity(kq, codec):
 
 @pytest.mark.parametrize("codec", CODECS)
 def test_quantized_matmul_glu_parity(kq, codec):
-    # act(x Wg^T) * (x Wu^T): one GEMV pass for M <= 3, two GEMM passes
-    # above; the activation rounded to y's type before the product.  Gate and
-    # up are row slices of one [2N, row_bytes] weight.
+    # act(x Wg^T) * (x Wu^T): one GEMV pass for M <= 3, two wide matrix-core
+    # GEMV passes up to 64 rows (K a multiple of 64; one, two or four A
+    # operands, K split four ways for narrow N and two ways for N = 8200),
+    # two GEMM passes above; the activation rounded to y's type before the
+    # product.  Gate and up are row slices of one [2N, row_bytes] weight.
     torch = _torch()
     kk = 256 * 5 if codec in SUPER else 64 * 5
-    shapes = [(1, 48, kk), (2, 304, kk), (3, 96, kk), (5, 48, kk), (8, 112, kk), (130, 208, kk), (257, 96, kk)]
+    shapes = [(1, 48, kk), (2, 304, kk), (3, 96, kk), (5, 48, kk), (8, 112, kk), (20, 80, kk), (48, 40, kk),
+              (16, 8200, kk), (130, 208, kk), (257, 96, kk)]
     if codec not in SUPER:
         shapes += [(2, 48, 96), (70, 48, 96)]
     for m, n, k in shapes:
@@ -272,10 +275,11 @@ def test_quantized_matmul_glu_parity(kq, codec):
                 assert_glu_close(host(y), ref, g, u, act, odt == "f16", what=f"glu {codec} m={m} {act} {odt}")
 
 
-@pytest.mark.parametrize("m", [2, 40])
+@pytest.mark.parametrize("m", [2, 40, 130])
 def test_quantized_matmul_glu_f16_saturates(kq, m):
     # products beyond the float16 range store the largest finite half of
-    # their sign, on both the GEMV and the GEMM path
+    # their sign, on the one-pass GEMV (M = 2) and the wide GEMV's two passes
+    # (M = 40), and on the GEMM's (M = 130)
     torch = _torch()
     n, k = 64, 256
     w = _weights("q8_0", 2 * n, k, 31, scale=25.0)

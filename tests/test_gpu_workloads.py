@@ -168,8 +168,8 @@ def _gpu_encode(kq, codec, seed, n, k, dist="normal"):
 
 
 def test_glu_prefill_workload(kq):
-    # the GLU bench row: q4_K gate (the GEMM workload's weights) and up (seed
-    # + 100), 2048 x 14336 x 4096, float16 out, silu
+    # the GLU bench rows: q4_K gate (the GEMM workload's weights) and up (seed
+    # + 100), 2048 x 14336 x 4096 and 16 x 14336 x 4096, float16 out, silu
     import torch
 
     c = W.CFG4_Q4K_GEMM
@@ -187,7 +187,14 @@ def test_glu_prefill_workload(kq):
     ref = matmul.quantized_matmul_glu(c.codec, g_rows, u_rows, c.k, x, "silu", "f16")
     g, u = matmul.qmatmul(c.codec, g_rows, c.k, x), matmul.qmatmul(c.codec, u_rows, c.k, x)
     assert_glu_close(host(y)[:, ns], ref, g, u, "silu", True, what="GLU prefill")
-    del wg, wu, y
+    # the small-batch GLU row: the first 16 activation rows (the wide
+    # matrix-core GEMV's two passes)
+    y16 = torch.empty((16, c.n), dtype=torch.float16, device="cuda")
+    say("workload GLU batch 16: kernel")
+    kq.kq_quantized_matmul_glu(c.codec, wg, wu, c.n, c.k, dev(x[:16]), y16, "silu")
+    ref16 = matmul.quantized_matmul_glu(c.codec, g_rows, u_rows, c.k, x[:16], "silu", "f16")
+    assert_glu_close(host(y16)[:, ns], ref16, g[:16], u[:16], "silu", True, what="GLU batch 16")
+    del wg, wu, y, y16
     torch.cuda.empty_cache()
 
 
