@@ -1,7 +1,8 @@
 // kq_qmv_wide_impl.h -- the matrix-core GEMV for small prefill batches (up to
 // 64 activation rows), shared by kq_qmv_wide.hip (the plain product of
-// kq_quantized_matmul), kq_qmv_wide_epi.hip (its residual epilogue) and
-// kq_qmv_wide_glu.hip (the two passes of its GLU product).
+// kq_quantized_matmul), kq_qmv_wide_epi.hip (its residual epilogue),
+// kq_qmv_wide_glu.hip and kq_qmv_wide_glum.hip (the two passes of its GLU
+// product).
 //
 // mlx-kquant bindings.cpp page, quantized_matmul docstring; the README's
 // remark that a matmul over few rows amortizes one weight read over all of
@@ -17,20 +18,20 @@ namespace {
 // K values per LDS chunk: 64 KiB of activations for 16 T rows, at most 1024
 // (a wave's two register rings then hold at most 2 x 2 unit groups), and at
 // least one unit group (256 values) for each of the KS waves that share a
-// row group (four rows of 1024 values: 148 KiB of LDS, one workgroup per CU).
+// row group (64 rows of 1024 values: 148 KiB of LDS, one workgroup per CU).
 __host__ __device__ constexpr int wide_kchunk(int t, int ks) {
-  return (mma_kchunk(16 * t) < 1024 ? mma_kchunk(16 * t) : 1024) > 256 * ks
-             ? (mma_kchunk(16 * t) < 1024 ? mma_kchunk(16 * t) : 1024)
-             : 256 * ks;
+  const int fit = mma_kchunk(16 * t) < 1024 ? mma_kchunk(16 * t) : 1024;
+  return fit > 256 * ks ? fit : 256 * ks;
 }
 
 // The matrix-core GEMV for M <= 16 T activation rows: each decoded B operand
 // meets T 16-row A operands (activation rows 16 t + (l & 15); rows past M
 // repeat row M - 1 and their outputs are dropped), so a weight is still
 // decoded once for every row.  The activation chunk is at most 1024 values
-// (512 for four operands), and a wave takes only G unit groups of each; the
-// next chunk's groups are loaded while the current one is staged and
-// consumed.  M is a run-time argument: the kernel is sized for 16 T rows.
+// (512 for four operands split two ways), and a wave takes only G unit
+// groups of each; the next chunk's groups are loaded while the current one
+// is staged and consumed.  M is a run-time argument: the kernel is sized for
+// 16 T rows.
 // KS waves of the workgroup share a 16-row group, each a part of every chunk
 // (2, or 4 when the matrix has few rows, so that the grid still covers the
 // CUs).  EP: the store mode (kq_internal.h: plain, epi_apply, or one pass of
