@@ -190,11 +190,9 @@ int kq_qmm(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_
 
 int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y,
                         int y_dtype, void* stream) {
-  // small prefill batches: the wide matrix-core GEMV (from 9 rows when the
-  // matrix has few rows, else from 17)
-  const bool wide = m <= kq::QMV_WIDE_MAX_M && k % 64 == 0 && (m > kq::QMV_MAX_M || (m >= 9 && kq::wide_narrow(n)));
-  if (m >= 0 && m <= kq::QMV_MAX_M && !wide) return kq_qmv(codec, w, n, k, x, m, y, y_dtype, stream);
-  if (wide) {
+  // 17..64 rows: the wide matrix-core GEMV (kq_qmv takes it from 9 rows)
+  if (m >= 0 && m <= kq::QMV_MAX_M) return kq_qmv(codec, w, n, k, x, m, y, y_dtype, stream);
+  if (m <= kq::QMV_WIDE_MAX_M && k % 64 == 0) {
     const char* op = "kq_quantized_matmul";
     int64_t rb;
     int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb);

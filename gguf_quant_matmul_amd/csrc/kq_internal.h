@@ -187,8 +187,7 @@ constexpr int QMV_MAX_M = 16;
 // with several A operands per decoded weight operand (kq_qmv_wide.hip)
 constexpr int QMV_WIDE_MAX_M = 64;
 // A matrix with so few rows that the wide GEMV's 32-row workgroups leave CUs
-// idle (a 256-CU part): it splits K four ways per row group instead of two,
-// and takes the plain product's 9..16 rows as well.
+// idle (a 256-CU part): it splits K four ways per row group instead of two.
 __host__ __device__ constexpr bool wide_narrow(int64_t n) { return (n + 31) / 32 < 256; }
 // activation rows up to which the GLU product runs on the GEMV body (two
 // matrices' q3_K units fill the registers from two rows on)

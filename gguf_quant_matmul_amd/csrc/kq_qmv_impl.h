@@ -526,16 +526,10 @@ hipError_t launch_c(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
     case 6: return launch_m<C, 6>(w, n, k, rb, x, y, f16, s);
     case 7: return launch_m<C, 7>(w, n, k, rb, x, y, f16, s);
     case 8: return launch_m<C, 8>(w, n, k, rb, x, y, f16, s);
-    // 9..16 rows: the matrix-core GEMV (one 16-row MFMA A operand)
-    case 9: return launch_mma<C, 9>(w, n, k, rb, x, y, f16, s);
-    case 10: return launch_mma<C, 10>(w, n, k, rb, x, y, f16, s);
-    case 11: return launch_mma<C, 11>(w, n, k, rb, x, y, f16, s);
-    case 12: return launch_mma<C, 12>(w, n, k, rb, x, y, f16, s);
-    case 13: return launch_mma<C, 13>(w, n, k, rb, x, y, f16, s);
-    case 14: return launch_mma<C, 14>(w, n, k, rb, x, y, f16, s);
-    case 15: return launch_mma<C, 15>(w, n, k, rb, x, y, f16, s);
-    case 16: return launch_mma<C, 16>(w, n, k, rb, x, y, f16, s);
   }
+  // 9..16 rows: the wide matrix-core GEMV on one 16-row A operand, whose
+  // next chunk's weights load while the current chunk is consumed
+  if (m >= 9 && m <= QMV_MAX_M) return launch_qmv_wide(C, w, n, k, rb, x, m, y, f16, s);
   return hipErrorInvalidValue;
 }
 

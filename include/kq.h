@@ -108,9 +108,9 @@ int kq_dequantize(int codec, const void* w, int64_t rows, int64_t k,
  *         3 or more rows run on the matrix cores).
  * kq_qmm: prefill GEMM on f16 matrix cores, any M >= 1.
  * kq_quantized_matmul: kq_qmv for M <= 16; for 17 <= M <= 64 with K a
- *         multiple of 64, a matrix-core GEMV that meets each decoded weight
- *         operand with two or four 16-row activation operands (from M = 9
- *         when N < 8161); else kq_qmm.
+ *         multiple of 64, the matrix-core GEMV that kq_qmv uses from 9 rows,
+ *         with each decoded weight operand meeting two or four 16-row
+ *         activation operands; else kq_qmm.
  * The K-reduction order is fixed per (codec, N, K, M): results are
  * deterministic run to run, and a row's result does not depend on the other
  * rows of x. */

@@ -320,17 +320,17 @@ def test_quantized_matmul_routes_by_m(kq):
 @pytest.mark.parametrize("n", (72, 8200))
 @pytest.mark.parametrize("codec", CODECS)
 def test_quantized_matmul_small_prefill_wide_gemv(kq, codec, n):
-    # 17..64 rows with K a multiple of 64 take the wide matrix-core GEMV: two
-    # 16-row activation operands up to 32 rows, four up to 64; for a matrix
-    # with few rows (N = 72) also 9..16 rows, on one operand, with K split four
-    # ways per row group instead of two (N = 8200).  Both N leave a partial
-    # last workgroup; K spans several activation chunks (1024 values, or 512
-    # for four operands split two ways) and ends in a short one.
+    # 9..64 rows with K a multiple of 64 take the wide matrix-core GEMV: one
+    # 16-row activation operand up to 16 rows, two up to 32, four up to 64;
+    # for a matrix with few rows (N = 72) K is split four ways per row group
+    # instead of two (N = 8200).  Both N leave a partial last workgroup; K
+    # spans several activation chunks (1024 values, or 512 for four operands
+    # split two ways) and ends in a short one.
     torch = _torch()
     k = 1280 if codec in SUPER else 1344
     w = _weights(codec, n, k, 31)
     wd = dev(w)
-    for m in ((9, 16) if n < 8000 else ()) + (17, 31, 32, 33, 50, 64):
+    for m in (9, 16, 17, 31, 32, 33, 50, 64):
         x = _x(m, k, 40 + m)
         want = matmul.qmatmul(codec, w, k, x)
         for dt in (torch.float32, torch.float16):

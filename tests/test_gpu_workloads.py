@@ -224,8 +224,8 @@ def test_residual_prefill_workload(kq):
 def test_small_prefill_workload(kq):
     # the small-prefill bench rows: the GEMM workload's q4_K 14336 x 4096 weight
     # with the first M of its activation rows through kq_quantized_matmul,
-    # float16 out (16 rows: the GEMV; 32 and 64: the wide matrix-core GEMV;
-    # 128: the GEMM)
+    # float16 out (16, 32 and 64 rows: the wide matrix-core GEMV on one, two
+    # and four activation operands; 128: the GEMM)
     import torch
 
     c = W.CFG4_Q4K_GEMM
