@@ -61,7 +61,8 @@ def test_graph_replays_match_eager():
 
 def test_graph_replays_fused_and_other_codecs():
     # the two-pass GLU GEMM (the up pass reads what the gate pass stored), the
-    # residual epilogue on the GEMV body and the GEMVs of other codecs
+    # residual epilogue on the GEMV body, the GEMVs of other codecs, and the
+    # wide matrix-core GEMV (plain, residual, and the GLU's two passes)
     import torch
 
     from gguf_quant_matmul_amd import kq
@@ -81,13 +82,21 @@ def test_graph_replays_fused_and_other_codecs():
     y_res = torch.zeros((5, n), dtype=torch.float32, device="cuda")
     y_l = torch.zeros((5, n), dtype=torch.float32, device="cuda")
     y_2 = torch.zeros((130, n), dtype=torch.float16, device="cuda")
-    outs = (y_glu, y_res, y_l, y_2)
+    xw = dev(rng.standard_normal((40, k)).astype(np.float16))
+    res_w = dev(rng.standard_normal((40, n)).astype(np.float16))
+    y_wglu = torch.zeros((24, n), dtype=torch.float16, device="cuda")
+    y_wres = torch.zeros((40, n), dtype=torch.float16, device="cuda")
+    y_w = torch.zeros((40, n), dtype=torch.float32, device="cuda")
+    outs = (y_glu, y_res, y_l, y_2, y_wglu, y_wres, y_w)
 
     def work():
         kq.kq_quantized_matmul_glu("q5_k", wg, wu, n, k, xm, y_glu, "gelu_tanh")
         kq.kq_quantized_matmul_residual("q3_k", wr, n, k, xr, res, y_res, gate)
         kq.kq_qmv("q4_1", wl, n, k, xr, y_l)
         kq.kq_qmm("q2_k", w2, n, k, xm, y_2)
+        kq.kq_quantized_matmul_glu("q5_k", wg, wu, n, k, xw[:24], y_wglu, "silu")
+        kq.kq_quantized_matmul_residual("q2_k", w2, n, k, xw, res_w, y_wres)
+        kq.kq_quantized_matmul("q4_1", wl, n, k, xw, y_w)
 
     work()
     torch.cuda.synchronize()
