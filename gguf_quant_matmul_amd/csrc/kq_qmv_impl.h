@@ -327,10 +327,10 @@ constexpr int MMA_PD = 4;      // units of a lane in flight ahead of the one dec
 __host__ __device__ constexpr int mma_kchunk(int m) { return (32768 / m) & ~255; }
 __host__ __device__ constexpr int mma_xstride(int kc) { return xpad(kc) + 8; }  // +16 B: rows start on different banks
 
-template <int C, int M, bool F16>
+template <int C, int M, bool F16, int EP = EP_PLAIN>
 __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                               int64_t row_bytes, const half_t* __restrict__ x,
-                                                              void* __restrict__ y) {
+                                                              void* __restrict__ y, Epi epi, int act) {
   typedef typename UnitOf<C>::T Unit;
   static_assert(M >= 1 && M <= 16, "activation rows");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -440,19 +440,25 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __r
       for (int i = 0; i < 4; ++i) {
         const int m = 4 * (lane >> 4) + i;
         if (m < M) {
-          if (F16)
-            ((half_t*)y)[(int64_t)m * n + col] = (half_t)acc[i];
-          else
-            ((float*)y)[(int64_t)m * n + col] = acc[i];
+          if constexpr (EP == EP_GLU_ACT) {
+            if (act == GLU_SILU)
+              store_out<F16, EP, GLU_SILU>(y, m, col, n, epi, acc[i]);
+            else
+              store_out<F16, EP, GLU_GELU_TANH>(y, m, col, n, epi, acc[i]);
+          } else {
+            store_out<F16, EP, 0>(y, m, col, n, epi, acc[i]);
+          }
         }
       }
     }
   }
 }
 
-template <int C, int M>
-hipError_t launch_mma(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
-                      hipStream_t s) {
+// The same kernel with a store mode (kq_internal.h; act: the GLU gate pass's
+// activation).
+template <int C, int M, int EP>
+hipError_t launch_mma_ep(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, const Epi& epi, int act,
+                         void* y, int f16, hipStream_t s) {
   const int kc = (int)(k < mma_kchunk(M) ? k : mma_kchunk(M));
   size_t lds = (size_t)M * mma_xstride(kc) * 2;
   const size_t part_bytes = (size_t)(4 / MMA_KSPLIT) * (MMA_KSPLIT - 1) * 64 * sizeof(float4_t);
@@ -460,10 +466,18 @@ hipError_t launch_mma(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const 
   constexpr int rows_per_block = 16 * (4 / MMA_KSPLIT);
   const dim3 grid((unsigned)((n + rows_per_block - 1) / rows_per_block));
   if (f16)
-    hipLaunchKernelGGL((qmv_mma_kernel<C, M, true>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x, y);
+    hipLaunchKernelGGL((qmv_mma_kernel<C, M, true, EP>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
+                       epi, act);
   else
-    hipLaunchKernelGGL((qmv_mma_kernel<C, M, false>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x, y);
+    hipLaunchKernelGGL((qmv_mma_kernel<C, M, false, EP>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x,
+                       y, epi, act);
   return hipGetLastError();
+}
+
+template <int C, int M>
+hipError_t launch_mma(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
+                      hipStream_t s) {
+  return launch_mma_ep<C, M, EP_PLAIN>(w, n, k, rb, x, Epi{nullptr, nullptr, nullptr, 1}, 0, y, f16, s);
 }
 
 template <int C, int M, int LPR>
