@@ -316,8 +316,9 @@ __global__ __launch_bounds__(256) void qmv_generic_kernel(const uint8_t* __restr
 // The contraction only needs A and B to agree on K, so the 32 K values of an
 // MFMA come from four different units.  A operand: the same K positions of
 // activation row (l & 15); rows past M repeat row M - 1 and their outputs are
-// dropped.  A wave owns 16 weight rows and a part of K (MMA_KSPLIT waves of a
-// workgroup share a row group); the parts meet in LDS at the end.
+// dropped.  A wave owns 16 weight rows and a part of K (KS waves of a
+// workgroup share a row group: MMA_KSPLIT, or four for a matrix with few
+// rows); the parts meet in LDS at the end.
 // ---------------------------------------------------------------------------
 
 constexpr int MMA_THREADS = 256;
@@ -327,7 +328,7 @@ constexpr int MMA_PD = 4;      // units of a lane in flight ahead of the one dec
 __host__ __device__ constexpr int mma_kchunk(int m) { return (32768 / m) & ~255; }
 __host__ __device__ constexpr int mma_xstride(int kc) { return xpad(kc) + 8; }  // +16 B: rows start on different banks
 
-template <int C, int M, bool F16, int EP = EP_PLAIN>
+template <int C, int M, bool F16, int EP = EP_PLAIN, int KS = MMA_KSPLIT>
 __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                               int64_t row_bytes, const half_t* __restrict__ x,
                                                               void* __restrict__ y, Epi epi, int act) {
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __r
   const int xstride = mma_xstride(kc_alloc);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int rgroup = blockIdx.x * (4 / MMA_KSPLIT) + wave / MMA_KSPLIT, kpart = wave % MMA_KSPLIT;
+  const int rgroup = blockIdx.x * (4 / KS) + wave / KS, kpart = wave % KS;
   const int r = lane & 15, cu = lane >> 4;
   const int row = rgroup * 16 + r;
   const uint8_t* wrow = w + (int64_t)min(row, n - 1) * row_bytes;
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __r
     const int kc = (k - c0) < KC ? (k - c0) : KC;
     const int ub = c0 / 64, ue = (c0 + kc) / 64;
     // this wave's groups (4 units each): [g0, g1) of the chunk's groups
-    const int ngroups = (ue - ub + 3) / 4, gper = (ngroups + MMA_KSPLIT - 1) / MMA_KSPLIT;
+    const int ngroups = (ue - ub + 3) / 4, gper = (ngroups + KS - 1) / KS;
     const int g0 = min(kpart * gper, ngroups), g1 = min(g0 + gper, ngroups);
     const int last = ue - 1;
     // Activation loads first (all of this thread's pieces at once, so their
@@ -428,12 +429,12 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __r
   acc += acc2;
   __syncthreads();
   float4_t* part = (float4_t*)smem;
-  const int pbase = (wave / MMA_KSPLIT) * (MMA_KSPLIT - 1) * 64;
+  const int pbase = (wave / KS) * (KS - 1) * 64;
   if (kpart) part[pbase + (kpart - 1) * 64 + lane] = acc;
   __syncthreads();
   if (kpart == 0) {
 #pragma unroll
-    for (int p = 0; p + 1 < MMA_KSPLIT; ++p) acc += part[pbase + p * 64 + lane];
+    for (int p = 0; p + 1 < KS; ++p) acc += part[pbase + p * 64 + lane];
     const int col = rgroup * 16 + (lane & 15);
     if (col < n) {
 #pragma unroll
@@ -456,22 +457,31 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __r
 
 // The same kernel with a store mode (kq_internal.h; act: the GLU gate pass's
 // activation).
-template <int C, int M, int EP>
-hipError_t launch_mma_ep(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, const Epi& epi, int act,
+template <int C, int M, int EP, int KS>
+hipError_t launch_mma_ks(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, const Epi& epi, int act,
                          void* y, int f16, hipStream_t s) {
   const int kc = (int)(k < mma_kchunk(M) ? k : mma_kchunk(M));
   size_t lds = (size_t)M * mma_xstride(kc) * 2;
-  const size_t part_bytes = (size_t)(4 / MMA_KSPLIT) * (MMA_KSPLIT - 1) * 64 * sizeof(float4_t);
+  const size_t part_bytes = (size_t)(4 / KS) * (KS - 1) * 64 * sizeof(float4_t);
   if (lds < part_bytes) lds = part_bytes;
-  constexpr int rows_per_block = 16 * (4 / MMA_KSPLIT);
+  constexpr int rows_per_block = 16 * (4 / KS);
   const dim3 grid((unsigned)((n + rows_per_block - 1) / rows_per_block));
   if (f16)
-    hipLaunchKernelGGL((qmv_mma_kernel<C, M, true, EP>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
+    hipLaunchKernelGGL((qmv_mma_kernel<C, M, true, EP, KS>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
                        epi, act);
   else
-    hipLaunchKernelGGL((qmv_mma_kernel<C, M, false, EP>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x,
+    hipLaunchKernelGGL((qmv_mma_kernel<C, M, false, EP, KS>), grid, dim3(MMA_THREADS), lds, s, w, (int)n, (int)k, rb, x,
                        y, epi, act);
   return hipGetLastError();
+}
+
+// Four waves per row group for a matrix so narrow that two leave CUs without
+// a workgroup (wide_narrow), else two.
+template <int C, int M, int EP>
+hipError_t launch_mma_ep(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, const Epi& epi, int act,
+                         void* y, int f16, hipStream_t s) {
+  if (wide_narrow(n)) return launch_mma_ks<C, M, EP, 4>(w, n, k, rb, x, epi, act, y, f16, s);
+  return launch_mma_ks<C, M, EP, 2>(w, n, k, rb, x, epi, act, y, f16, s);
 }
 
 template <int C, int M>
