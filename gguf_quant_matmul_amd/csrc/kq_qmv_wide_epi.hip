@@ -1,5 +1,5 @@
 // kq_qmv_wide_epi: the residual / gate epilogue of
-// kq_quantized_matmul_residual for 4..64 activation rows on the wide
+// kq_quantized_matmul_residual for 3..64 activation rows on the wide
 // matrix-core GEMV (the kernel and its launchers: kq_qmv_wide_impl.h).
 #include "kq_qmv_wide_impl.h"
 

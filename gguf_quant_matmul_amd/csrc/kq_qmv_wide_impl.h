@@ -206,7 +206,7 @@ hipError_t launch_mma_wide_ks(const uint8_t* w, int64_t n, int64_t k, int64_t rb
 }
 
 // One A operand up to 16 rows, two up to 32, four up to 64.  An epilogue or
-// GLU pass over 4..8 rows takes the 16-row kernel of kq_qmv_impl.h instead:
+// GLU pass over 3..8 rows takes the 16-row kernel of kq_qmv_impl.h instead:
 // its single 4096-value chunk at K = 4096 beats the one-operand wide kernel
 // there (as kq_qmv's own 3..8 rows do).
 template <int C, int EP>
@@ -214,6 +214,7 @@ hipError_t launch_wide_c(const uint8_t* w, int64_t n, int64_t k, int64_t rb, con
                          int act, void* y, int f16, hipStream_t s) {
   if constexpr (EP != EP_PLAIN) {
     switch (m) {
+      case 3: return launch_mma_ep<C, 3, EP>(w, n, k, rb, x, epi, act, y, f16, s);
       case 4: return launch_mma_ep<C, 4, EP>(w, n, k, rb, x, epi, act, y, f16, s);
       case 5: return launch_mma_ep<C, 5, EP>(w, n, k, rb, x, epi, act, y, f16, s);
       case 6: return launch_mma_ep<C, 6, EP>(w, n, k, rb, x, epi, act, y, f16, s);

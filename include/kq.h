@@ -125,7 +125,7 @@ int kq_quantized_matmul(int codec, const void* w, int64_t n, int64_t k,
  *      quantized_matmul_qmv_bias and quantized_matmul_glu docstrings) ----
  * The product p[m][n] of kq_quantized_matmul (same w, x, M, N, K rules)
  * finished in the store, in float32, rounded once to y_dtype.  The residual
- * and bias run on the dot2 GEMV body for M <= 3 (M <= 8 when K is not a
+ * and bias run on the dot2 GEMV body for M <= 2 (M <= 8 when K is not a
  * multiple of 64), on the matrix-core GEMVs up to M = 64 with K a multiple
  * of 64, else on the GEMM:
  *

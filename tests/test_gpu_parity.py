@@ -191,7 +191,7 @@ def test_qmm_parity(kq, codec):
 def _epi_shapes(codec):
     kk = 256 * 9 if codec in SUPER else 64 * 9
     shapes = [(1, 37, kk), (3, 300, kk), (4, 45, kk), (8, 45, kk), (130, 200, kk), (260, 131, kk)]
-    # 4..64 rows: the 16-row matrix-core GEMV up to 8 rows, then the wide one
+    # 3..64 rows: the 16-row matrix-core GEMV up to 8 rows, then the wide one
     # (one, two, four A operands)
     shapes += [(12, 70, kk), (24, 90, kk), (40, 45, kk), (64, 33, kk), (40, 8200, kk)]
     if codec not in SUPER:
@@ -201,7 +201,7 @@ def _epi_shapes(codec):
 
 @pytest.mark.parametrize("codec", CODECS)
 def test_quantized_matmul_residual_parity(kq, codec):
-    # y = residual + gate * p on the dot2 GEMV (M <= 3, or odd block counts),
+    # y = residual + gate * p on the dot2 GEMV (M <= 2, or odd block counts),
     # matrix-core GEMVs (M <= 64) and GEMM bodies; gate
     # absent, one row, or one row per batch of consecutive rows; in place
     # (residual is y) and out of place
