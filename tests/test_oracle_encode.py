@@ -137,3 +137,79 @@ def test_round_trip_error_small_relative_to_block(codec):
     rel = np.sqrt(np.mean((w - y) ** 2)) / np.sqrt(np.mean(w ** 2))
     # uniform-noise rms of a b-bit grid spanning roughly +-3 sigma: ~ 6 / 2^b / sqrt(12)
     assert rel < 2.5 * 6 / 2 ** bits / np.sqrt(12)
+
+
+# ---- hand-encoded blocks: the block-parameter rule (tests/golden/*_encode.txt) ----
+
+GOLDEN = __import__("os").path.join(__import__("os").path.dirname(__file__), "golden")
+
+
+def _load_encode_golden(name):
+    """Parse a hand-encoded golden: inputs (sub-block patterns or single values) and expectations."""
+    spec = {"subs": [], "w": [], "codes": []}
+    with open(__import__("os").path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, val = line.split(":", 1)
+            val = val.split()
+            if key == "codec":
+                spec["codec"] = val[0]
+            elif key == "sub":
+                spec["subs"].append((int(val[0]), float(val[1]), float(val[2]), float(val[3])))
+            elif key == "w":
+                spec["w"].append((int(val[0]), float(val[1])))
+            elif key == "code":
+                spec["codes"].append((int(val[0]), int(val[1])))
+            elif key in ("header", "bytes"):
+                spec[key] = bytes.fromhex("".join(val))
+            elif key in ("sc", "m"):
+                spec[key] = [int(v) for v in val]
+    return spec
+
+
+def _golden_input(spec):
+    codec = spec["codec"]
+    if spec["subs"]:
+        sub = {"q4_k": 32, "q6_k": 16}[codec]
+        w = np.zeros(256, np.float64)
+        for j, base, step, last in spec["subs"]:
+            w[sub * j: sub * j + sub - 1] = base + step * np.arange(sub - 1)
+            w[sub * j + sub - 1] = last
+    else:
+        n = len(spec["bytes"]) // codecs.block_bytes(codec) * codecs.block_values(codec)
+        w = np.zeros(n, np.float64)
+        for i, v in spec["w"]:
+            w[i] = v
+    w32 = w.astype(np.float32)
+    assert np.array_equal(w32.astype(np.float64), w), "golden inputs must be exact in float32"
+    return w32[None, :]
+
+
+@pytest.mark.parametrize("name", ["q4_k_encode.txt", "q6_k_encode.txt", "q8_0_encode.txt", "q4_0_encode.txt"])
+def test_golden_hand_encoded_blocks(name):
+    spec = _load_encode_golden(name)
+    codec = spec["codec"]
+    w = _golden_input(spec)
+    wq = encode.quantize(codec, w)[0]
+    if "bytes" in spec:
+        assert wq.tobytes().hex() == spec["bytes"].hex()
+    if "header" in spec:
+        if codec == "q4_k":  # d, dmin and the 12 packed scale bytes lead the block
+            assert wq[:16].tobytes().hex() == spec["header"].hex()
+        else:  # q6_K: d closes the block
+            assert wq[208:210].tobytes().hex() == spec["header"].hex()
+    blk = wq.reshape(1, 1, -1)
+    if codec == "q4_k":
+        _, _, sc, m, q = codecs.fields_q4_k(blk)
+        assert sc.reshape(-1).tolist() == spec["sc"] and m.reshape(-1).tolist() == spec["m"]
+        q = q.reshape(-1)
+    elif codec == "q6_k":
+        f = codecs.fields_q6_k(blk)
+        assert f[1].reshape(-1).tolist() == spec["sc"]
+        q = f[2].reshape(-1)
+    else:
+        q = _codes(codec, blk).reshape(-1)
+    for v, expect in spec["codes"]:
+        assert int(q[v]) == expect, (name, v, int(q[v]), expect)
