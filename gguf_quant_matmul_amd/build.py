@@ -45,12 +45,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
+def _stale(src: str) -> bool:
+    """True if src's object is missing or older than src or any header of csrc/."""
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if not os.path.exists(obj):
+        return True
+    newest = max([os.path.getmtime(src)] + [os.path.getmtime(h) for h in glob.glob(os.path.join(CSRC, "*.h"))])
+    return os.path.getmtime(obj) < newest
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every source and link libkq.so; with incremental=True only the
+    sources whose object is older than the source or a header are compiled."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    workers = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")), 16)
+    todo = [s for s in srcs if _stale(s)] if incremental else srcs
+    workers = max(1, min(len(todo), int(os.environ.get("MAX_JOBS", "8")), 16))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+        list(ex.map(lambda s: _compile(s, verbose), todo))
+    objs = [os.path.join(BUILD, os.path.basename(s) + ".o") for s in srcs]
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -63,5 +76,5 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)
     sys.exit(0)

@@ -232,7 +232,10 @@ int kq_quantized_matmul_residual(int codec, const void* w, int64_t n, int64_t k,
   const bool f16 = y_dtype == KQ_F16;
   const kq::half_t* xh = (const kq::half_t*)x;
   hipError_t e;
-  if (m <= 2 || (m <= 8 && k % 64 != 0))  // the dot2 GEMV body (its cost grows with M)
+  // the dot2 GEMV body (its cost grows with M); q8_0 keeps it to 4 rows, as
+  // kq_qmv does, because its decode costs the matrix-core GEMV more per byte
+  const int64_t dot2_max_m = codec == KQ_Q8_0 ? 4 : 2;
+  if (m <= dot2_max_m || (m <= 8 && k % 64 != 0))
     e = kq::launch_qmv_epi(codec, (const uint8_t*)w, n, k, rb, xh, (int)m, epi, y, f16, (hipStream_t)stream);
   else if (m <= kq::QMV_WIDE_MAX_M && k % 64 == 0)  // small batches: the wide matrix-core GEMV
     e = kq::launch_qmv_wide_epi(codec, (const uint8_t*)w, n, k, rb, xh, (int)m, epi, y, f16, (hipStream_t)stream);

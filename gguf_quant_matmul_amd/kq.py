@@ -160,7 +160,7 @@ def kq_dequantize(codec, w, k: int, out, stream=None) -> None:
 
 
 def kq_qmv(codec, w, n: int, k: int, x, y, stream=None) -> None:
-    """y[m, n] = x[m, :] . dequant(w)[n, :]; x float16 [m, k] with 1 <= m <= 8."""
+    """y[m, n] = x[m, :] . dequant(w)[n, :]; x float16 [m, k] with 1 <= m <= 16."""
     _check(_lib.kq_qmv(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(y), _dtype_id(y), _stream(stream)))
 
 

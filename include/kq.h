@@ -81,7 +81,8 @@ typedef enum {
 
 /* ---- codec registry (mlx-kquant bindings.cpp page: codecs(); README codec table) ---- */
 
-/* Name ("q4_k", "q6_k", "q8_0", "q4_0"; case-insensitive) -> codec id. */
+/* Name -> codec id: "q4_0", "q4_1", "q5_0", "q5_1", "q8_0", "q2_k", "q3_k",
+ * "q4_k", "q5_k", "q6_k" (case-insensitive); KQ_ERR_CODEC otherwise. */
 int kq_codec_from_name(const char* name, int* codec);
 /* Values and bytes per block of a codec. */
 int kq_codec_info(int codec, int* block_values, int* block_bytes);

@@ -11,6 +11,7 @@ import zlib
 import numpy as np
 import pytest
 
+import _full as F
 from _gpu import TOL, assert_close_rows, assert_glu_close, dev, host, say, u32
 from oracle import codecs, encode, matmul
 
@@ -34,9 +35,16 @@ def _torch():
 
 
 def _weights(codec, n, k, seed, scale=0.02):
-    rng = np.random.default_rng(seed)
-    w = (rng.standard_normal((n, k)) * scale).astype(np.float32)
-    return encode.quantize(codec, w)
+    # N(0, scale) float32 weights from one seeded draw, oracle-encoded in row
+    # chunks on a thread pool (cached: several tests share the large shapes)
+    return F.random_bytes(codec, n, k, seed, scale)
+
+
+# K for the 8200-row shapes: a multiple of 256 (and 64) above the 16-row
+# matrix-core GEMV's activation chunk for 5 and 8 rows (6400 and 4096 values),
+# so its chunk loop runs more than once with the two-way K split that N >= 8161
+# takes (the up/gate projections' and the lm-head's path)
+K_WIDE = 6656
 
 
 def _x(m, k, seed):
@@ -145,8 +153,8 @@ def test_dequantize_golden_blocks(kq, name):
 
 def _shapes_qmv(codec):
     if codec in SUPER:
-        return [(37, 512), (300, 256 * 17)]   # 17 superblocks: q6_K rows only 2-byte aligned
-    return [(37, 96), (300, 4160), (45, 2048 + 32)]  # 96 and 2080: odd block counts -> generic kernel
+        return [(37, 512), (300, 256 * 17), (8200, K_WIDE)]   # 17 superblocks: q6_K rows only 2-byte aligned
+    return [(37, 96), (300, 4160), (45, 2048 + 32), (8200, K_WIDE)]  # 96 and 2080: odd block counts -> generic kernel
 
 
 @pytest.mark.parametrize("codec", CODECS)
@@ -157,12 +165,12 @@ def test_qmv_parity(kq, codec, m):
         w = _weights(codec, n, k, 7 + n)
         x = _x(m, k, n)
         say(f"qmv {codec} m={m} n={n} k={k}")
-        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
         kq.kq_qmv(codec, dev(w), n, k, dev(x), y)
-        ref = matmul.qmatmul(codec, w, k, x)
+        ref = F.qmatmul(codec, w, k, x)
         assert_close_rows(host(y), ref, what=f"qmv {codec} m={m} n={n} k={k}")
         # float16 output
-        y16 = torch.empty((m, n), dtype=torch.float16, device="cuda")
+        y16 = torch.full((m, n), float("nan"), dtype=torch.float16, device="cuda")
         kq.kq_qmv(codec, dev(w), n, k, dev(x), y16)
         assert_close_rows(host(y16), ref, what=f"qmv f16 {codec} m={m}")
 
@@ -194,6 +202,9 @@ def _epi_shapes(codec):
     # 3..64 rows: the 16-row matrix-core GEMV up to 8 rows, then the wide one
     # (one, two, four A operands)
     shapes += [(12, 70, kk), (24, 90, kk), (40, 45, kk), (64, 33, kk), (40, 8200, kk)]
+    # 3 and 8 rows on N >= 8161: the 16-row kernel's two-way K split, with
+    # two activation chunks at 8 rows
+    shapes += [(3, 8200, K_WIDE), (8, 8200, K_WIDE)]
     if codec not in SUPER:
         shapes += [(4, 45, 2048 + 32), (70, 40, 96)]  # odd block counts: generic kernels
     return shapes
@@ -216,7 +227,7 @@ def test_quantized_matmul_residual_parity(kq, codec):
             res = rng.standard_normal((m, n)).astype(ndt)
             for gi, gate in enumerate(gates):
                 g = None if gate is None else gate.astype(ndt)
-                ref = matmul.quantized_matmul_residual(codec, w, k, x, res, g)
+                ref = F.residual(codec, w, k, x, res, g)
                 say(f"residual {codec} m={m} n={n} k={k} gate={gi} {tdt}")
                 y = torch.full((m, n), float("nan"), dtype=tdt, device="cuda")
                 kq.kq_quantized_matmul_residual(codec, dev(w), n, k, dev(x), dev(res), y,
@@ -226,7 +237,7 @@ def test_quantized_matmul_residual_parity(kq, codec):
             say(f"residual in place {codec} m={m} n={n} k={k} {tdt}")
             y = dev(res)
             kq.kq_quantized_matmul_residual(codec, dev(w), n, k, dev(x), y, y, dev(gates[1].astype(ndt)))
-            ref = matmul.quantized_matmul_residual(codec, w, k, x, res, gates[1].astype(ndt))
+            ref = F.residual(codec, w, k, x, res, gates[1].astype(ndt))
             assert_close_rows(host(y).astype(np.float64), ref, what=f"residual in place {codec} m={m}")
 
 
@@ -258,6 +269,9 @@ def test_quantized_matmul_glu_parity(kq, codec):
     kk = 256 * 5 if codec in SUPER else 64 * 5
     shapes = [(1, 48, kk), (2, 304, kk), (3, 96, kk), (5, 48, kk), (8, 112, kk), (20, 80, kk), (48, 40, kk),
               (16, 8200, kk), (130, 208, kk), (257, 96, kk)]
+    # the two passes of 4 and 8 rows on N >= 8161 (two-way K split, two
+    # activation chunks at 8 rows)
+    shapes += [(4, 8200, K_WIDE), (8, 8200, K_WIDE)]
     if codec not in SUPER:
         shapes += [(2, 48, 96), (70, 48, 96)]
     for m, n, k in shapes:
@@ -266,14 +280,14 @@ def test_quantized_matmul_glu_parity(kq, codec):
         x = _x(m, k, m + 5 * n)
         dcat = dev(wcat)
         rb = wcat.shape[1]
-        g, u = matmul.qmatmul(codec, wg, k, x), matmul.qmatmul(codec, wu, k, x)
+        g, u = F.qmatmul(codec, wg, k, x), F.qmatmul(codec, wu, k, x)
         assert (n * rb) % 16 == 0
         for act in ("silu", "gelu_tanh"):
             for tdt, odt in ((torch.float32, "f32"), (torch.float16, "f16")):
                 say(f"glu {codec} m={m} n={n} k={k} {act} {odt}")
                 y = torch.full((m, n), float("nan"), dtype=tdt, device="cuda")
                 kq.kq_quantized_matmul_glu(codec, dcat[:n], dcat[n:], n, k, dev(x), y, act)
-                ref = matmul.quantized_matmul_glu(codec, wg, wu, k, x, act, odt)
+                ref = F.glu(codec, wg, wu, k, x, act, odt)[0]
                 assert_glu_close(host(y), ref, g, u, act, odt == "f16", what=f"glu {codec} m={m} {act} {odt}")
 
 
