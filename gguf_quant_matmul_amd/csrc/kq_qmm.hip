@@ -29,6 +29,8 @@ hipError_t launch_gather_qmm_seg(int codec, const uint8_t* w, int64_t ne, int64_
     }
     return hipErrorInvalidValue;
   }
+  if (seg_exact_ok(codec, k))  // q4_K: exact integer weight operands
+    return launch_seg_exact(w, ne, n, k, rb, x, rows, map, counts, cap, y, f16, s);
   return launch_seg_mma(codec, w, ne, n, k, rb, x, rows, map, counts, cap, y, f16, s);
 }
 

@@ -446,7 +446,10 @@ def test_gather_qmm_seg_parity(kq, codec):
     torch = _torch()
     rng = np.random.default_rng(17)
     kq_ = codec in SUPER
-    for e, n, k in ((6, 96, 512 if kq_ else 320), (3, 200, 1280 if kq_ else 1344)):
+    shapes = [(6, 96, 512 if kq_ else 320), (3, 200, 1280 if kq_ else 1344)]
+    if kq_:  # several 512-value windows of the exact-operand q4_K kernel, a ragged 128-row block
+        shapes.append((4, 200, 2048))
+    for e, n, k in shapes:
         ids = np.sort(np.concatenate([rng.integers(0, e - 1, 190), [e - 1] * 3, [e + 2] * 4])).astype(np.uint32)
         rows = ids.size
         wf = (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32)
@@ -464,6 +467,27 @@ def test_gather_qmm_seg_parity(kq, codec):
             got = host(y).astype(np.float64)
             assert np.all(np.isnan(got[~covered])), "uncovered rows must stay unwritten"
             assert_close_rows(got[covered], ref[covered], what=f"seg {codec} n={n} k={k}")
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -14, 2.0 ** 9])
+def test_gather_seg_q4k_activation_range(kq, scale):
+    # the q4_K segment kernel forms sub-block sums of x for the min term:
+    # activations far below and far above 1 (sums near 2^-10 and near 2^16)
+    # keep the row bar
+    torch = _torch()
+    rng = np.random.default_rng(29)
+    e, n, k = 3, 136, 1024
+    ids = np.sort(rng.integers(0, e, 150)).astype(np.uint32)
+    rows = ids.size
+    w = encode.quantize("q4_k", (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32))
+    x = (np.random.default_rng(31).standard_normal((rows, k)) * scale).astype(np.float16)
+    map_, counts, count, status, cap = _tile_map_gpu(kq, ids, e)
+    tiles = host(map_)[:count].view(np.uint32)
+    ref = matmul.gather_qmm_seg("q4_k", w, k, x, tiles)
+    say(f"seg q4_k activation scale {scale}")
+    y = torch.full((rows, n), float("nan"), dtype=torch.float32, device="cuda")
+    kq.kq_gather_qmm_seg("q4_k", dev(w), e, n, k, dev(x), map_[:cap], counts, y)
+    assert_close_rows(host(y).astype(np.float64), ref, what=f"seg q4_k x scale {scale}")
 
 
 @pytest.mark.parametrize("codec", ["q4_k", "q4_0", "q8_0", "q5_k", "q4_1", "q5_0", "q5_1", "q2_k", "q3_k"])
