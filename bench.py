@@ -117,6 +117,24 @@ def gpu_weights(torch, kq, codec, seed, n, k, dist):
     return wq
 
 
+def plain_read(torch, kq, ws, nl, groups=(256, 512, 1024, 2048, 4096, 8192)):
+    """The plain-read reference: kq_stream_read over the same rotated weight
+    copies, in the same graph-replay protocol as the GEMV it stands beside;
+    the fastest of a few grid sizes."""
+    nc, nb = len(ws), ws[0].numel()
+    out = torch.empty((4 * max(groups),), dtype=torch.int32, device="cuda")
+    best = None
+    for gsz in groups:
+        g = capture(torch, lambda: [kq.kq_stream_read(ws[i % nc], out[:4 * gsz]) for i in range(nl)])
+        ms = time_graph(torch, g, nl, 5)
+        if best is None or ms < best[0]:
+            best = (ms, gsz)
+    ms, gsz = best
+    return {"row": "plain_read", "workload": f"plain read of {nb} B, {nc} rotating copies", "us": round(ms * 1e3, 2),
+            "GB/s": round(nb / ms / 1e6, 1), "hbm_frac": round(nb / ms / 1e6 / HBM_PEAK_GBS, 3), "groups": gsz,
+            "copies": nc}
+
+
 def copies_for(nbytes):
     return max(1, min(64, math.ceil(COLD_BYTES / nbytes)))
 
@@ -127,7 +145,7 @@ def measure_rows(torch, kq):
 
     rows = []
 
-    def gemv_row(cfg, reps=None):
+    def gemv_row(cfg, reps=None, read_ref=False):
         wq = gpu_weights(torch, kq, cfg.codec, cfg.seed, cfg.n, cfg.k, cfg.dist)
         nb = wq.numel()
         nc = copies_for(nb)
@@ -139,14 +157,20 @@ def measure_rows(torch, kq):
         ms = time_graph(torch, g, nl, 5)
         alg = nb + x.numel() * 2 + y.numel() * 4
         gbs = alg / ms / 1e6
-        rows.append({"row": "kq_qmv", "workload": cfg.name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 3), "alg_bytes": alg, "copies": nc})
+        row = {"row": "kq_qmv", "workload": cfg.name, "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+               "hbm_frac": round(gbs / HBM_PEAK_GBS, 3), "alg_bytes": alg, "copies": nc}
+        if read_ref:
+            rd = plain_read(torch, kq, ws, nl)
+            row["read_us"] = rd["us"]
+            row["of_read"] = round(rd["us"] / row["us"], 3)
+            rows.append(dict(rd, workload=f"{rd['workload']} ({cfg.name} weights)"))
+        rows.append(row)
         del ws, wq
         torch.cuda.empty_cache()
 
     for cfg in W.CFG2_GEMV:
-        gemv_row(cfg)
-    gemv_row(W.CFG3_Q6K_LMHEAD, reps=8)
+        gemv_row(cfg, read_ref=cfg.m == 1)
+    gemv_row(W.CFG3_Q6K_LMHEAD, reps=8, read_ref=True)
 
     # MoE: tile map + expert-segment GEMM
     cfg = W.CFG5_MOE_SEG
@@ -441,7 +465,9 @@ def counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4):
 
 
 def cpu_baseline():
-    """The oracle as it stands, on a bounded sample of the two workloads, on this host."""
+    """The oracle as it stands, timed on this host on a bounded sample of each of
+    the five workloads: NumPy decode (single-threaded) and the float64 matmul
+    (BLAS threads) timed separately, the lm-head in a 1024-row chunk of N."""
     from gguf_quant_matmul_amd import workloads as W
     from oracle import codecs, encode, matmul
 
@@ -451,32 +477,44 @@ def cpu_baseline():
         blas = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"), default=1)
     except Exception:  # pragma: no cover
         blas = 1
-    c1, c4 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM
-    # GEMV: 1024 of the 4096 weight rows, repeated for ~10 s
-    rows = 1024
-    wq = encode.quantize(c1.codec, W.weight_rows(c1.seed, c1.n, c1.k, c1.dist, rows=np.arange(rows)))
-    x = W.gemv_activations(c1)
-    reps, t0 = 0, time.perf_counter()
-    while reps < 2 or time.perf_counter() - t0 < 10.0:
-        matmul.qmatmul(c1.codec, wq, c1.k, x)
-        reps += 1
-    dt = (time.perf_counter() - t0) / reps
-    gbs = (wq.nbytes + x.nbytes + rows * 4) / dt / 1e9
-    # GEMM: 128 of the 14336 weight rows x all 2048 activation rows
-    nr = 128
-    wq4 = encode.quantize(c4.codec, W.weight_rows(c4.seed, c4.n, c4.k, c4.dist, rows=np.arange(nr)))
-    x4 = W.gemv_activations(c4)
-    t0 = time.perf_counter()
-    matmul.qmatmul(c4.codec, wq4, c4.k, x4)
-    dt4 = time.perf_counter() - t0
-    tflops = 2 * c4.m * nr * c4.k / dt4 / 1e12
+
+    def timed(fn, budget=1.5):
+        reps, t0 = 0, time.perf_counter()
+        while reps < 2 or time.perf_counter() - t0 < budget:
+            r = fn()
+            reps += 1
+        return (time.perf_counter() - t0) / reps, r
+
+    def one(name, codec, seed, n_full, k, dist, rows, x, flop_rate, unit):
+        wq = encode.quantize(codec, W.weight_rows(seed, n_full, k, dist, rows=np.arange(rows)))
+        t_dec, wd = timed(lambda: codecs.dequantize(codec, wq, k, np.float32))
+        t_mm, _ = timed(lambda: matmul.matmul_f64(x, wd))
+        tot = t_dec + t_mm
+        if flop_rate:
+            val = 2 * x.shape[0] * rows * k / tot / 1e12
+        else:
+            val = (wq.nbytes + x.size * 2 + x.shape[0] * rows * 4) / tot / 1e9
+        return {"workload": name, "sample": f"{rows} of {n_full} weight rows x {x.shape[0]} activation rows",
+                "decode_ms": round(t_dec * 1e3, 2), "matmul_ms": round(t_mm * 1e3, 2),
+                "value": round(val, 5 if flop_rate else 3), "unit": unit}
+
+    c1, c3, c4, c5 = W.CFG1_Q4K_GEMV, W.CFG3_Q6K_LMHEAD, W.CFG4_Q4K_GEMM, W.CFG5_MOE_SEG
+    cfgs = [one(c1.name, c1.codec, c1.seed, c1.n, c1.k, c1.dist, 1024, W.gemv_activations(c1), False, "GB/s")]
+    for c in W.CFG2_GEMV:
+        if c.m in (1, 8):
+            cfgs.append(one(c.name, c.codec, c.seed, c.n, c.k, c.dist, 1024, W.gemv_activations(c), False, "GB/s"))
+    cfgs.append(one(c3.name, c3.codec, c3.seed, c3.n, c3.k, c3.dist, 1024, W.gemv_activations(c3), False, "GB/s"))
+    cfgs.append(one(c4.name, c4.codec, c4.seed, c4.n, c4.k, c4.dist, 128, W.gemv_activations(c4), True, "TFLOP/s"))
+    # MoE segment GEMM: the first expert's first 256 weight rows times its routed rows
+    r = W.routing(c5.seed, c5.tokens, c5.top_k, c5.n_experts)
+    xs = W.activations(c5.seed, c5.tokens, c5.k)[r.token_of_row][r.sorted_ids == 0]
+    cfgs.append(one(c5.name, c5.codec, c5.seed, c5.n_experts * c5.n, c5.k, "normal", 256, xs, True, "TFLOP/s"))
+    head = cfgs[0]
     return {
-        "value": round(gbs, 3), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
-        "sample": f"q4_K GEMV on {rows} of 4096 weight rows (K=4096, M=1), NumPy decode + float64 matmul, "
-                  f"{reps} reps, {dt * 1e3:.0f} ms each; threads = BLAS threads (decode is single-threaded NumPy)",
-        "qmm": {"value": round(tflops, 5), "unit": "TFLOP/s",
-                "sample": f"q4_K GEMM on {nr} of 14336 weight rows x 2048 activation rows (NumPy decode + "
-                          f"float64 matmul), {dt4 * 1e3:.0f} ms"},
+        "value": head["value"], "unit": "GB/s", "cores": int(max(blas, 1)), "kind": "oracle",
+        "sample": f"q4_K GEMV on 1024 of 4096 weight rows (K=4096, M=1): NumPy decode {head['decode_ms']} ms "
+                  f"(single-threaded) + float64 matmul {head['matmul_ms']} ms (BLAS, {blas} threads)",
+        "configs": cfgs,
         "host_cpus": os.cpu_count(),
     }
 
@@ -584,11 +622,15 @@ def main():
                   "p90 over the timed steps",
         "device": dev_name,
     }
+    # the plain-read ceiling of the GEMV's weight stream, same protocol
+    rd = plain_read(torch, kq, w1s, n_cold)
+    out["roofline"]["read_ceiling"] = {"us": rd["us"], "GB/s": rd["GB/s"], "groups": rd["groups"],
+                                       "gemv_over_read": round(ms1 * 1e3 / rd["us"], 3)}
     del w1s, w1, w4, x4, y4
     torch.cuda.empty_cache()
     if not args.no_rows:
         log("measuring the other rows")
-        out["rows"] = measure_rows(torch, kq)
+        out["rows"] = [dict(rd, workload=f"{rd['workload']} (the q4_K decode GEMV's weights)")] + measure_rows(torch, kq)
     if not args.no_cpu:
         log("timing the oracle on the host")
         out["cpu_baseline"] = cpu_baseline()

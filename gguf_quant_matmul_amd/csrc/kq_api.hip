@@ -416,4 +416,15 @@ int kq_quantize(int codec, const float* w, int64_t rows, int64_t k, void* out, v
   return hip_status(op, kq::launch_quantize(codec, w, rows, k, rb, (uint8_t*)out, (hipStream_t)stream));
 }
 
+int kq_stream_read(const void* src, int64_t bytes, uint32_t* out, int64_t groups, void* stream) {
+  const char* op = "kq_stream_read";
+  if (bytes < 0 || bytes % 16 != 0 || bytes >= kMaxElems)
+    return fail(KQ_ERR_ARG, op, "bytes=%lld must be a non-negative multiple of 16", (long long)bytes);
+  if (groups < 1 || groups > (1 << 20)) return fail(KQ_ERR_ARG, op, "groups=%lld out of 1..2^20", (long long)groups);
+  // out holds 4 * groups words (one per wave)
+  if (!src || !out) return fail(KQ_ERR_ARG, op, "null pointer (src=%p out=%p)", src, (void*)out);
+  if (!aligned(src, 16) || !aligned(out, 4)) return fail(KQ_ERR_ALIGN, op, "src must be 16-byte, out 4-byte aligned");
+  return hip_status(op, kq::launch_stream_read(src, bytes, out, groups, (hipStream_t)stream));
+}
+
 }  // extern "C"

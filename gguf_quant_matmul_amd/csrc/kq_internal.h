@@ -356,5 +356,6 @@ hipError_t launch_tile_map(const uint32_t* ids, int64_t rows, int64_t n_experts,
                            uint32_t* counts, int64_t cap, uint32_t* status, hipStream_t s);
 hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, int64_t row_bytes,
                            uint8_t* out, hipStream_t s);
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int64_t groups, hipStream_t s);
 
 }  // namespace kq

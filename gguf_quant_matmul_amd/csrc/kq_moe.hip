@@ -3,20 +3,26 @@
 // expert_tile_map docstring: (expert, row_start, num_rows) tiles, only the
 // last tile of a segment partial, a valid-tile count, no host sync).
 //
-// One workgroup: each thread finds its expert's segment with two binary
-// searches over the sorted ids (lower bounds of e and e+1), a workgroup
-// prefix sum over ceil(count/64) gives each expert its first slot, and tiles
-// are written in expert-major order.  No atomics on the output: the map is
-// the same bits run to run.  A linear pass over the ids reports unsorted ids
-// and ids >= n_experts in the optional status word.
+// One workgroup: the ids are copied to LDS once (up to TM_LDS_IDS of them;
+// longer inputs are searched in place), each thread finds its expert's segment
+// with one binary search (the lower bound of e; the end of its segment is
+// the next expert's lower bound, taken from the next thread), a wave-level prefix
+// sum over ceil(count/64) plus one over the sixteen wave totals gives each
+// expert its first slot, and tiles are written in expert-major order.  No
+// atomics on the output: the map is the same bits run to run.  A linear pass
+// over the ids reports unsorted ids and ids >= n_experts in the optional
+// status word.
 #include "kq_internal.h"
 
 namespace kq {
 namespace {
 
 constexpr int TM_THREADS = 1024;
+constexpr int TM_WAVES = TM_THREADS / 64;
+constexpr uint32_t TM_LDS_IDS = 12288;  // 48 KB
 
-__device__ __forceinline__ uint32_t lower_bound(const uint32_t* __restrict__ ids, uint32_t rows, uint32_t key) {
+template <typename P>
+__device__ __forceinline__ uint32_t lower_bound(P ids, uint32_t rows, uint32_t key) {
   uint32_t lo = 0, hi = rows;
   while (lo < hi) {
     const uint32_t mid = lo + (hi - lo) / 2;
@@ -28,44 +34,57 @@ __device__ __forceinline__ uint32_t lower_bound(const uint32_t* __restrict__ ids
   return lo;
 }
 
-__global__ __launch_bounds__(TM_THREADS) void tile_map_kernel(const uint32_t* __restrict__ ids, uint32_t rows,
-                                                              uint32_t n_experts, uint32_t* __restrict__ map,
-                                                              uint32_t* __restrict__ counts, uint32_t cap,
-                                                              uint32_t* __restrict__ status) {
-  __shared__ uint64_t scan[TM_THREADS];
-  __shared__ uint32_t flags;
-  __shared__ uint64_t carry;
-  const uint32_t tid = threadIdx.x;
-  if (tid == 0) { flags = 0; carry = 0; }
-  __syncthreads();
+// inclusive prefix sum over the 64 lanes of a wave (64-bit: with unsorted
+// ids the segment counts are meaningless and their sum can pass 2^32)
+__device__ __forceinline__ uint64_t wave_scan(uint64_t v, int lane) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint64_t t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
 
+// The map from ids at src (LDS or global): status flags, per-expert segments,
+// the tile slots; returns through the shared carry / flags.
+template <typename P>
+__device__ __forceinline__ void tile_map_body(P src, uint32_t rows, uint32_t n_experts, uint32_t* __restrict__ map,
+                                              uint32_t cap, uint64_t* wsum, uint32_t* wlo, uint32_t& flags,
+                                              uint64_t& carry) {
+  const uint32_t tid = threadIdx.x;
+  const int lane = (int)(tid & 63), wave = (int)(tid >> 6);
   uint32_t f = 0;
   for (uint32_t i = tid; i < rows; i += TM_THREADS) {
-    const uint32_t v = ids[i];
+    const uint32_t v = src[i];
     if (v >= n_experts) f |= 2u;
-    if (i + 1 < rows && v > ids[i + 1]) f |= 1u;
+    if (i + 1 < rows && v > src[i + 1]) f |= 1u;
   }
   if (f) atomicOr(&flags, f);  // an OR: the result does not depend on the order
 
   for (uint32_t e0 = 0; e0 < n_experts; e0 += TM_THREADS) {
+    // expert e's segment is [lower_bound(e), lower_bound(e + 1)): each thread
+    // searches once and takes the end of its segment from the next lane (the
+    // last lane of a wave from LDS, the last thread of the round searches it)
     const uint32_t e = e0 + tid;
-    uint32_t lo = 0, cnt = 0, nt = 0;
+    const uint32_t lo = e <= n_experts ? lower_bound(src, rows, e) : rows;  // e = n_experts: the first id >= E
+    uint32_t hi = __shfl_down(lo, 1, 64);
+    if (lane == 0) wlo[wave] = lo;  // the end of the previous wave's last segment
+    const uint32_t last_hi = tid == TM_THREADS - 1 && e < n_experts ? lower_bound(src, rows, e + 1) : rows;
+    __syncthreads();
+    if (lane == 63) hi = wave + 1 < TM_WAVES ? wlo[wave + 1] : last_hi;
+    uint32_t cnt = 0, nt = 0;
     if (e < n_experts) {
-      lo = lower_bound(ids, rows, e);
-      const uint32_t hi = lower_bound(ids, rows, e + 1);
       cnt = hi > lo ? hi - lo : 0;
       nt = (cnt + 63) / 64;
     }
-    // inclusive Hillis-Steele scan of nt over the workgroup
-    scan[tid] = nt;
+    // tiles before this expert: the wave's inclusive scan, plus the totals of
+    // the waves before it, plus the experts of earlier rounds (carry)
+    const uint64_t incl = wave_scan(nt, lane);
+    if (lane == 63) wsum[wave] = incl;
     __syncthreads();
-    for (uint32_t o = 1; o < TM_THREADS; o <<= 1) {
-      const uint64_t add = tid >= o ? scan[tid - o] : 0;
-      __syncthreads();
-      scan[tid] += add;
-      __syncthreads();
-    }
-    const uint64_t first = carry + scan[tid] - nt;
+    uint64_t before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    const uint64_t first = before + incl - nt;
     for (uint32_t t = 0; t < nt; ++t) {
       const uint64_t slot = first + t;
       if (slot < cap) {
@@ -77,8 +96,29 @@ __global__ __launch_bounds__(TM_THREADS) void tile_map_kernel(const uint32_t* __
       }
     }
     __syncthreads();
-    if (tid == TM_THREADS - 1) carry += scan[tid];
+    if (tid == TM_THREADS - 1) carry = first + nt;
     __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(TM_THREADS) void tile_map_kernel(const uint32_t* __restrict__ ids, uint32_t rows,
+                                                              uint32_t n_experts, uint32_t* __restrict__ map,
+                                                              uint32_t* __restrict__ counts, uint32_t cap,
+                                                              uint32_t* __restrict__ status) {
+  __shared__ uint32_t sid[TM_LDS_IDS];
+  __shared__ uint64_t wsum[TM_WAVES];
+  __shared__ uint32_t wlo[TM_WAVES];
+  __shared__ uint32_t flags;
+  __shared__ uint64_t carry;
+  const uint32_t tid = threadIdx.x;
+  if (tid == 0) { flags = 0; carry = 0; }
+  if (rows <= TM_LDS_IDS) {
+    for (uint32_t i = tid; i < rows; i += TM_THREADS) sid[i] = ids[i];
+    __syncthreads();
+    tile_map_body((const uint32_t*)sid, rows, n_experts, map, cap, wsum, wlo, flags, carry);
+  } else {
+    __syncthreads();
+    tile_map_body(ids, rows, n_experts, map, cap, wsum, wlo, flags, carry);
   }
   if (tid == 0) {
     uint64_t total = carry;

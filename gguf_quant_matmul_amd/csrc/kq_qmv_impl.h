@@ -28,6 +28,7 @@
 //    lane swaps across 16-lane rows).
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "kq_units.h"
@@ -214,6 +215,102 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_kernel(const uint8_t* __restr
                                                           int64_t row_bytes, const half_t* __restrict__ x,
                                                           void* __restrict__ y) {
   qmv_rows<C, M, LPR, F16>(w, n, k, row_bytes, x, y, blockIdx.x);
+}
+
+// Streaming GEMV for one or two activation rows with K <= 4096 (a row's
+// units fit one load group) over many weight rows: each workgroup stages x
+// once and walks the row blocks b, b + G, b + 2G, ... (G workgroups),
+// loading block b + G's units into registers while block b's are consumed,
+// so the activation staging and its barrier are paid once per workgroup
+// rather than once per block.
+template <int C, int M, int LPR, bool F16, int PD = 1>
+__global__ __launch_bounds__(QMV_THREADS) void qmv_stream_kernel(const uint8_t* __restrict__ w, int n, int k,
+                                                                 int64_t row_bytes, const half_t* __restrict__ x,
+                                                                 void* __restrict__ y, int nblocks) {
+  typedef typename UnitOf<C>::T Unit;
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  half_t* xs = (half_t*)smem;
+  const int xstride = xpad(k);
+  float* xsum = (float*)(smem + (size_t)M * xstride * 2);
+  const int sstride = k / 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int ROWS_PER_WAVE = 64 / LPR, UNROLL = UNITS_PER_GROUP / LPR;
+  const int rslot = lane / LPR, uslot = lane % LPR;
+  const int ue = k / 64;
+  auto row_of = [&](int b) { return (b * (QMV_THREADS / 64) + wave) * ROWS_PER_WAVE + rslot; };
+  auto load_block = [&](Unit* dst, int b) __attribute__((always_inline)) {
+    const int row = row_of(b);
+    const uint8_t* wrow = w + (int64_t)(row < n ? row : n - 1) * row_bytes;
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      const int u = uslot + LPR * j;
+      dst[j].load(wrow, u < ue ? u : ue - 1);
+    }
+  };
+
+  // x first (its loads retire before the weights'), then the first block's units
+  constexpr int XPT = (M * 4096 / 8 + QMV_THREADS - 1) / QMV_THREADS;
+  const int xpieces = M * (k / 8);
+  u32x4 xr[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    int c = tid + i * QMV_THREADS;
+    c = c < xpieces ? c : xpieces - 1;
+    const int m = c / (k / 8), v = (c % (k / 8)) * 8;
+    xr[i] = *(const u32x4*)(x + (int64_t)m * k + v);
+  }
+  int b = blockIdx.x;
+  Unit ring[PD][UNROLL];
+#pragma unroll
+  for (int p = 0; p < PD; ++p) load_block(ring[p], min(b + p * (int)gridDim.x, nblocks - 1));
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = tid + i * QMV_THREADS;
+    const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0)
+    float s = 0.f;
+    s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
+    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+    if (c < xpieces) {
+      const int m = c / (k / 8), v = (c % (k / 8)) * 8;
+      *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
+      if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
+    }
+  }
+  __syncthreads();
+  const Xv xv{xs, xsum, xstride, sstride, 0};
+
+  for (; b < nblocks; b += gridDim.x) {
+    Unit nxt[UNROLL];
+    if (b + PD * (int)gridDim.x < nblocks) load_block(nxt, b + PD * gridDim.x);  // uniform
+    Unit* cur = ring[0];
+    const int row = row_of(b);
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.f;
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) {
+      const int u = uslot + LPR * j;
+      if (row < n && u < ue) cur[j].template dot<M>(u, xv, acc);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = lanes_sum<LPR>(acc[m]);
+    if (row < n && uslot < M) {
+      float v = acc[0];
+#pragma unroll
+      for (int m = 1; m < M; ++m)
+        if (uslot == m) v = acc[m];
+      if (F16)
+        ((half_t*)y)[(int64_t)uslot * n + row] = (half_t)v;
+      else
+        ((float*)y)[(int64_t)uslot * n + row] = v;
+    }
+#pragma unroll
+    for (int p = 0; p + 1 < PD; ++p)
+#pragma unroll
+      for (int j = 0; j < UNROLL; ++j) ring[p][j] = ring[p + 1][j];
+#pragma unroll
+    for (int j = 0; j < UNROLL; ++j) ring[PD - 1][j] = nxt[j];
+  }
 }
 
 // GEMV with the matmul epilogue (residual, gate, bias), and the GLU product
@@ -503,6 +600,38 @@ hipError_t launch_ml(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const h
   return hipGetLastError();
 }
 
+// The streaming GEMV: one or two activation rows, K <= 4096 and at least
+// 8192 weight rows (the q6_K 128256 x 4096 lm-head: 119 -> 89 us; q4_0
+// 14336 x 4096, one row: 9.4 -> 8.5 us; at 4096 rows the one-pass kernel
+// stays ahead).  One row: a wave per row and about four row blocks per
+// workgroup (1024 to 8192 workgroups); two rows: 16 lanes per row and one
+// block per workgroup (5% ahead of the one-pass kernel at 14336 rows).
+__host__ inline bool qmv_stream_ok(int m, int64_t n, int64_t k) { return m <= 2 && k <= 4096 && n >= 8192; }
+__host__ inline int64_t qmv_stream_grid(int m, int64_t nblocks) {
+  if (m > 1) return nblocks;
+  return std::max<int64_t>(1, std::min<int64_t>(nblocks, std::max<int64_t>(1024, std::min<int64_t>(8192, nblocks / 4))));
+}
+
+template <int C, int M, int LPR, int PD>
+hipError_t launch_stream_pd(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
+                            hipStream_t s) {
+  const size_t lds = (size_t)M * xpad((int)k) * 2 + (size_t)M * (k / 16) * 4;
+  const int64_t nblocks = (n + rows_per_block(LPR) - 1) / rows_per_block(LPR);
+  const dim3 grid((unsigned)qmv_stream_grid(M, nblocks));
+  if (f16)
+    hipLaunchKernelGGL((qmv_stream_kernel<C, M, LPR, true, PD>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb,
+                       x, y, (int)nblocks);
+  else
+    hipLaunchKernelGGL((qmv_stream_kernel<C, M, LPR, false, PD>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k,
+                       rb, x, y, (int)nblocks);
+  return hipGetLastError();
+}
+template <int C, int M, int LPR>
+hipError_t launch_stream(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
+                         hipStream_t s) {
+  return launch_stream_pd<C, M, LPR, 1>(w, n, k, rb, x, y, f16, s);
+}
+
 // Three or more activation rows (five or more for q8_0) go to the matrix
 // cores.  Fewer take the dot2 kernel: one wave per row (64 lanes, one 64-value unit each at
 // K = 4096) for one activation row and a matrix with few rows (four times
@@ -518,6 +647,7 @@ hipError_t launch_m(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
   if constexpr (M >= mma_from) {
     return launch_mma<C, M>(w, n, k, rb, x, y, f16, s);
   } else {
+    if (qmv_stream_ok(M, n, k)) return launch_stream<C, M, (M == 1 ? 64 : 16)>(w, n, k, rb, x, y, f16, s);
     if (M == 1 && n <= 32768) return launch_ml<C, M, 64>(w, n, k, rb, x, y, f16, s);
     return launch_ml<C, M, 16>(w, n, k, rb, x, y, f16, s);
   }

@@ -51,6 +51,7 @@ _SIGS = {
                                   ctypes.c_float, c_vp, c_int, c_vp]),
     "kq_gather_mix": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_i64, c_vp, c_int, c_vp]),
     "kq_quantize": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_vp]),
+    "kq_stream_read": (c_int, [c_vp, c_i64, c_vp, c_i64, c_vp]),
 }
 
 #: every symbol the header declares
@@ -236,6 +237,13 @@ def kq_quantize(codec, w, out, stream=None) -> None:
     """w float32 [rows, k] -> out uint8 [rows, row_bytes]."""
     rows, k = (w.shape[0], w.shape[1]) if w.dim() > 1 else (1, w.shape[0])
     _check(_lib.kq_quantize(_codec(codec), _ptr(w), rows, k, _ptr(out), _stream(stream)))
+
+
+def kq_stream_read(src, out, nbytes: int | None = None, stream=None) -> None:
+    """Plain read of src's bytes (a multiple of 16) by out.numel() // 4 workgroups; out int32/uint32 [4 * groups]
+    (one word per wave)."""
+    nb = src.numel() * src.element_size() if nbytes is None else nbytes
+    _check(_lib.kq_stream_read(_ptr(src), nb, _ptr(out), out.numel() // 4, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -254,6 +254,16 @@ int kq_moe_glu_gather(int codec, const void* gate_w, const void* up_w, int64_t n
 int kq_quantize(int codec, const float* w, int64_t rows, int64_t k,
                 void* out, void* stream);
 
+/* ---- measurement helper: plain read of device memory ----
+ * Reads `bytes` (a multiple of 16) at src with nontemporal 16-byte loads,
+ * split over `groups` workgroups (1..2^20) of four waves that each read one
+ * contiguous share; wave v of group g writes the XOR of the words it read to
+ * out[4 g + v], so out (device, 4-byte aligned, caller-owned) holds
+ * 4 * groups words.  It moves a GEMV's weight bytes with no decode,
+ * which gives the measured read ceiling the GEMV rates are set against (the
+ * mlx-kquant README calls decode weight-read bound). */
+int kq_stream_read(const void* src, int64_t bytes, uint32_t* out, int64_t groups, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

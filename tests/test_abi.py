@@ -123,6 +123,10 @@ def _st(ret):
         (lambda: L.kq_gather_mix(A16, 8, 8, A16, A16, 2, 4, None, 1, None), kq.KQ_ERR_ARG, "out"),
         (lambda: L.kq_gather_mix(A16 + 4, 8, 8, A16, A16, 2, 4, A16, 1, None), kq.KQ_ERR_ALIGN, "y="),
         (lambda: L.kq_gather_mix(A16, 8, 8, A16 + 2, A16, 2, 4, A16, 1, None), kq.KQ_ERR_ALIGN, "inv_order"),
+        (lambda: L.kq_stream_read(A16, 24, A16, 4, None), kq.KQ_ERR_ARG, "bytes=24"),
+        (lambda: L.kq_stream_read(A16, 64, A16, 0, None), kq.KQ_ERR_ARG, "groups=0"),
+        (lambda: L.kq_stream_read(None, 64, A16, 4, None), kq.KQ_ERR_ARG, "null"),
+        (lambda: L.kq_stream_read(A16 + 4, 64, A16, 4, None), kq.KQ_ERR_ALIGN, "16-byte"),
         (lambda: L.kq_gather_mix(A16, 8, 8, A16, A16, -1, 4, A16, 1, None), kq.KQ_ERR_ARG, "tokens"),
         (lambda: L.kq_quantized_matmul_residual(12, A16, 64, 256, A16, 4, A16 * 4, A16 * 8, 3, A16, 0, None),
          kq.KQ_ERR_SHAPE, "gate_rows=3"),

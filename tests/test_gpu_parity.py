@@ -152,9 +152,10 @@ def test_dequantize_golden_blocks(kq, name):
 # ---------------------------------------------------------------------------
 
 def _shapes_qmv(codec):
+    # (8300, 1024): one or two rows take the streaming GEMV (N >= 8192, K <= 4096), 8300 rows a ragged last block
     if codec in SUPER:
-        return [(37, 512), (300, 256 * 17), (8200, K_WIDE)]   # 17 superblocks: q6_K rows only 2-byte aligned
-    return [(37, 96), (300, 4160), (45, 2048 + 32), (8200, K_WIDE)]  # 96 and 2080: odd block counts -> generic kernel
+        return [(37, 512), (300, 256 * 17), (8200, K_WIDE), (8300, 1024)]   # 17 superblocks: q6_K rows only 2-byte aligned
+    return [(37, 96), (300, 4160), (45, 2048 + 32), (8200, K_WIDE), (8300, 1024)]  # 96 and 2080: odd block counts -> generic kernel
 
 
 @pytest.mark.parametrize("codec", CODECS)
@@ -682,3 +683,21 @@ def test_quantize_bytes_match_oracle(kq, codec, dist):
     got = host(out)
     ref = encode.quantize(codec, w)
     assert np.array_equal(got, ref), f"{np.sum(got != ref)} bytes differ"
+
+
+@pytest.mark.parametrize("groups", [1, 7, 300])
+def test_stream_read_xor(kq, groups):
+    # the plain-read reference: group g XORs the 32-bit words of the g-th
+    # contiguous share of ceil(n16 / groups) 16-byte pieces
+    torch = _torch()
+    rng = np.random.default_rng(groups)
+    n16 = 10007
+    src = rng.integers(0, 2 ** 32, size=n16 * 4, dtype=np.uint64).astype(np.uint32)
+    out = torch.full((4 * groups,), -1, dtype=torch.int32, device="cuda")
+    kq.kq_stream_read(dev(src.view(np.int32)), out)
+    per = -(-n16 // groups)
+    got = host(out).view(np.uint32).reshape(groups, 4)
+    want = np.array([np.bitwise_xor.reduce(src[4 * g * per: 4 * min(n16, (g + 1) * per)]) if g * per < n16 else 0
+                     for g in range(groups)], dtype=np.uint32)
+    # each wave's word covers its lanes' pieces; the four of a group XOR to the share's XOR
+    assert np.array_equal(np.bitwise_xor.reduce(got, axis=1), want)
