@@ -260,7 +260,63 @@ def measure_rows(torch, kq):
     torch.cuda.empty_cache()
     rows += epilogue_rows(torch, kq)
     rows += codec_rows(torch, kq)
+    rows += bf16_rows(torch, kq)
     return rows
+
+
+def bf16_rows(torch, kq):
+    """bfloat16 activations on the q4_K decode GEMV (float32 out), the prefill
+    GEMM and the MoE segment GEMM (bfloat16 out), same protocol as the float16
+    rows."""
+    from gguf_quant_matmul_amd import workloads as W
+
+    out = []
+    c1, c4, c5 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM, W.CFG5_MOE_SEG
+    w1 = gpu_weights(torch, kq, c1.codec, c1.seed, c1.n, c1.k, c1.dist)
+    nc = copies_for(w1.numel())
+    ws = [w1] + [w1.clone() for _ in range(nc - 1)]
+    x = torch.from_numpy(W.activations_bf16(c1.seed, c1.m, c1.k)).cuda().to(torch.bfloat16)
+    y = torch.empty((c1.m, c1.n), dtype=torch.float32, device="cuda")
+    g = capture(torch, lambda: [kq.kq_qmv(c1.codec, ws[i], c1.n, c1.k, x, y) for i in range(nc)])
+    ms = time_graph(torch, g, nc, 5)
+    alg = w1.numel() + x.numel() * 2 + y.numel() * 4
+    out.append({"row": "kq_qmv_bf16", "workload": f"{c1.name} M=1, bf16 x, f32 out", "us": round(ms * 1e3, 2),
+                "GB/s": round(alg / ms / 1e6, 1), "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3),
+                "alg_bytes": alg, "copies": nc})
+    del ws, w1
+    w4 = gpu_weights(torch, kq, c4.codec, c4.seed, c4.n, c4.k, c4.dist)
+    x4 = torch.from_numpy(W.activations_bf16(c4.seed, c4.m, c4.k)).cuda().to(torch.bfloat16)
+    y4 = torch.empty((c4.m, c4.n), dtype=torch.bfloat16, device="cuda")
+    g = capture(torch, lambda: kq.kq_qmm(c4.codec, w4, c4.n, c4.k, x4, y4))
+    ms = time_graph(torch, g, 1, 5)
+    flop = 2 * c4.m * c4.n * c4.k
+    out.append({"row": "kq_qmm_bf16", "workload": f"{c4.name}, bf16 x, bf16 out", "us": round(ms * 1e3, 2),
+                "TFLOP/s": round(flop / ms / 1e9, 1), "mfma_frac": round(flop / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 3)})
+    del w4, x4, y4
+    w5 = gpu_weights(torch, kq, c5.codec, c5.seed, c5.n_experts * c5.n, c5.k, "normal")
+    nc = copies_for(w5.numel())
+    ws = [w5] + [w5.clone() for _ in range(nc - 1)]
+    r = W.routing(c5.seed, c5.tokens, c5.top_k, c5.n_experts)
+    x5 = torch.from_numpy(W.activations_bf16(c5.seed, c5.tokens, c5.k)[r.token_of_row]).cuda().to(torch.bfloat16)
+    ids = torch.from_numpy(r.sorted_ids.view(np.int32)).cuda()
+    cap = kq.kq_expert_tile_map_capacity(ids.numel(), c5.n_experts)
+    map_ = torch.empty((cap, 3), dtype=torch.int32, device="cuda")
+    counts = torch.empty((1,), dtype=torch.int32, device="cuda")
+    kq.kq_expert_tile_map(ids, c5.n_experts, map_, counts)
+    y5 = torch.empty((x5.shape[0], c5.n), dtype=torch.bfloat16, device="cuda")
+    nl = max(nc, 6)
+    g = capture(torch, lambda: [kq.kq_gather_qmm_seg(c5.codec, ws[i % nc], c5.n_experts, c5.n, c5.k, x5, map_,
+                                                     counts, y5) for i in range(nl)])
+    ms = time_graph(torch, g, nl, 5)
+    alg = w5.numel() + x5.numel() * 2 + y5.numel() * 2
+    flop = 2 * x5.shape[0] * c5.n * c5.k
+    out.append({"row": "kq_gather_qmm_seg_bf16", "workload": f"{c5.name}, bf16 x, bf16 out",
+                "us": round(ms * 1e3, 2), "GB/s": round(alg / ms / 1e6, 1),
+                "hbm_frac": round(alg / ms / 1e6 / HBM_PEAK_GBS, 3), "TFLOP/s": round(flop / ms / 1e9, 1),
+                "mfma_frac": round(flop / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 3), "alg_bytes": alg, "copies": nc})
+    del ws, w5
+    torch.cuda.empty_cache()
+    return out
 
 
 def cold_gemv_row(torch, kq, cfg):

@@ -78,8 +78,10 @@ int check_codec_k(const char* op, int codec, int64_t k, int64_t* row_bytes) {
   return KQ_OK;
 }
 
-int check_dtype(const char* op, int dt) {
-  if (dt != KQ_F32 && dt != KQ_F16) return fail(KQ_ERR_ARG, op, "output dtype %d is not KQ_F32 or KQ_F16", dt);
+int check_dtype(const char* op, int dt, bool bf16 = false) {
+  if (bf16 && dt == KQ_BF16) return KQ_OK;
+  if (dt != KQ_F32 && dt != KQ_F16)
+    return fail(KQ_ERR_ARG, op, "output dtype %d is not KQ_F32 or KQ_F16%s", dt, bf16 ? " or KQ_BF16" : "");
   return KQ_OK;
 }
 
@@ -90,10 +92,10 @@ int hip_status(const char* op, hipError_t e) {
 }
 
 int check_matmul(const char* op, int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m,
-                 const void* y, int y_dtype, int64_t* rb) {
+                 const void* y, int y_dtype, int64_t* rb, bool bf16 = false) {
   int st = check_codec_k(op, codec, k, rb);
   if (st) return st;
-  if ((st = check_dtype(op, y_dtype))) return st;
+  if ((st = check_dtype(op, y_dtype, bf16))) return st;
   if (n < 0 || n >= kMaxDim) return fail(KQ_ERR_ARG, op, "N=%lld out of range", (long long)n);
   if (m < 0 || m >= kMaxDim) return fail(KQ_ERR_ARG, op, "M=%lld out of range", (long long)m);
   if (n * k >= kMaxElems || m * k >= kMaxElems || m * n >= kMaxElems)
@@ -425,6 +427,51 @@ int kq_stream_read(const void* src, int64_t bytes, uint32_t* out, int64_t groups
   if (!src || !out) return fail(KQ_ERR_ARG, op, "null pointer (src=%p out=%p)", src, (void*)out);
   if (!aligned(src, 16) || !aligned(out, 4)) return fail(KQ_ERR_ALIGN, op, "src must be 16-byte, out 4-byte aligned");
   return hip_status(op, kq::launch_stream_read(src, bytes, out, groups, (hipStream_t)stream));
+}
+
+// ---- bfloat16 activations ----
+// y dtype: KQ_F32, KQ_F16 or KQ_BF16 (2)
+static int bf16_out(int y_dtype) { return y_dtype == KQ_BF16 ? 2 : y_dtype == KQ_F16 ? 1 : 0; }
+
+int kq_qmv_bf16(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y, int y_dtype,
+                void* stream) {
+  const char* op = "kq_qmv_bf16";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb, true);
+  if (st) return st;
+  if (m > kq::QMV_MAX_M)
+    return fail(KQ_ERR_SHAPE, op, "M=%lld rows; the GEMV takes 1..%d (use kq_qmm_bf16)", (long long)m, kq::QMV_MAX_M);
+  if (n == 0 || m == 0) return KQ_OK;
+  return hip_status(op, kq::launch_mm_bf16(codec, (const uint8_t*)w, n, k, rb, x, m, y, bf16_out(y_dtype),
+                                           (hipStream_t)stream));
+}
+
+int kq_qmm_bf16(int codec, const void* w, int64_t n, int64_t k, const void* x, int64_t m, void* y, int y_dtype,
+                void* stream) {
+  const char* op = "kq_qmm_bf16";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, m, y, y_dtype, &rb, true);
+  if (st) return st;
+  if (n == 0 || m == 0) return KQ_OK;
+  return hip_status(op, kq::launch_mm_bf16(codec, (const uint8_t*)w, n, k, rb, x, m, y, bf16_out(y_dtype),
+                                           (hipStream_t)stream));
+}
+
+int kq_gather_qmm_seg_bf16(int codec, const void* w, int64_t n_experts, int64_t n, int64_t k, const void* x,
+                           int64_t rows, const uint32_t* map, const uint32_t* counts, int64_t cap, void* y,
+                           int y_dtype, void* stream) {
+  const char* op = "kq_gather_qmm_seg_bf16";
+  int64_t rb;
+  int st = check_matmul(op, codec, w, n, k, x, rows, y, y_dtype, &rb, true);
+  if (st) return st;
+  if (n_experts <= 0 || n_experts >= kMaxDim || n_experts * n >= kMaxDim * 64)
+    return fail(KQ_ERR_ARG, op, "n_experts=%lld out of range", (long long)n_experts);
+  if (cap < 0 || cap >= kMaxDim) return fail(KQ_ERR_ARG, op, "cap=%lld out of range", (long long)cap);
+  if (n == 0 || rows == 0 || cap == 0) return KQ_OK;
+  if (!map || !counts) return fail(KQ_ERR_ARG, op, "null map or counts");
+  if (!aligned(map, 4) || !aligned(counts, 4)) return fail(KQ_ERR_ALIGN, op, "map/counts must be 4-byte aligned");
+  return hip_status(op, kq::launch_seg_bf16(codec, (const uint8_t*)w, n_experts, n, k, rb, x, rows, map, counts, cap,
+                                            y, bf16_out(y_dtype), (hipStream_t)stream));
 }
 
 }  // extern "C"

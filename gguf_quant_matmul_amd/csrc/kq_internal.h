@@ -357,5 +357,11 @@ hipError_t launch_tile_map(const uint32_t* ids, int64_t rows, int64_t n_experts,
 hipError_t launch_quantize(int codec, const float* w, int64_t rows, int64_t k, int64_t row_bytes,
                            uint8_t* out, hipStream_t s);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* out, int64_t groups, hipStream_t s);
+// bfloat16 activations; out: 0 float32, 1 float16, 2 bfloat16
+hipError_t launch_mm_bf16(int codec, const uint8_t* w, int64_t n, int64_t k, int64_t rb, const void* x, int64_t m,
+                          void* y, int out, hipStream_t s);
+hipError_t launch_seg_bf16(int codec, const uint8_t* w, int64_t ne, int64_t n, int64_t k, int64_t rb, const void* x,
+                           int64_t rows, const uint32_t* map, const uint32_t* counts, int64_t cap, void* y, int out,
+                           hipStream_t s);
 
 }  // namespace kq

@@ -52,6 +52,10 @@ _SIGS = {
     "kq_gather_mix": (c_int, [c_vp, c_i64, c_i64, c_vp, c_vp, c_i64, c_i64, c_vp, c_int, c_vp]),
     "kq_quantize": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_vp]),
     "kq_stream_read": (c_int, [c_vp, c_i64, c_vp, c_i64, c_vp]),
+    "kq_qmv_bf16": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_int, c_vp]),
+    "kq_qmm_bf16": (c_int, [c_int, c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_int, c_vp]),
+    "kq_gather_qmm_seg_bf16": (c_int, [c_int, c_vp, c_i64, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_i64, c_vp, c_int,
+                                       c_vp]),
 }
 
 #: every symbol the header declares
@@ -65,7 +69,7 @@ for _name, (_res, _args) in _SIGS.items():
 # ids and enums of include/kq.h
 KQ_Q4_0, KQ_Q4_1, KQ_Q5_0, KQ_Q5_1, KQ_Q8_0 = 2, 3, 6, 7, 8
 KQ_Q2_K, KQ_Q3_K, KQ_Q4_K, KQ_Q5_K, KQ_Q6_K = 10, 11, 12, 13, 14
-KQ_F32, KQ_F16 = 0, 1
+KQ_F32, KQ_F16, KQ_BF16 = 0, 1, 2
 KQ_GLU_SILU, KQ_GLU_GELU_TANH, KQ_GLU_SILU_LIMIT = 0, 1, 2
 _GLU_ACTS = {"silu": KQ_GLU_SILU, "gelu": KQ_GLU_GELU_TANH, "gelu_tanh": KQ_GLU_GELU_TANH,
              "silu_limit": KQ_GLU_SILU_LIMIT}
@@ -113,7 +117,20 @@ def _dtype_id(t) -> int:
         return KQ_F32
     if t.dtype == torch.float16:
         return KQ_F16
-    raise TypeError(f"output dtype must be float32 or float16, got {t.dtype}")
+    if t.dtype == torch.bfloat16:
+        return KQ_BF16
+    raise TypeError(f"output dtype must be float32, float16 or bfloat16, got {t.dtype}")
+
+
+def _bf16(x) -> bool:
+    """True for bfloat16 activations (the *_bf16 entry points), False for float16."""
+    import torch
+
+    if x.dtype == torch.bfloat16:
+        return True
+    if x.dtype == torch.float16:
+        return False
+    raise TypeError(f"activations must be float16 or bfloat16, got {x.dtype}")
 
 
 # ---------------------------------------------------------------------------
@@ -161,15 +178,21 @@ def kq_dequantize(codec, w, k: int, out, stream=None) -> None:
 
 
 def kq_qmv(codec, w, n: int, k: int, x, y, stream=None) -> None:
-    """y[m, n] = x[m, :] . dequant(w)[n, :]; x float16 [m, k] with 1 <= m <= 16."""
-    _check(_lib.kq_qmv(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(y), _dtype_id(y), _stream(stream)))
+    """y[m, n] = x[m, :] . dequant(w)[n, :]; x float16 or bfloat16 [m, k] with 1 <= m <= 16."""
+    fn = _lib.kq_qmv_bf16 if _bf16(x) else _lib.kq_qmv
+    _check(fn(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(y), _dtype_id(y), _stream(stream)))
 
 
 def kq_qmm(codec, w, n: int, k: int, x, y, stream=None) -> None:
-    _check(_lib.kq_qmm(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(y), _dtype_id(y), _stream(stream)))
+    fn = _lib.kq_qmm_bf16 if _bf16(x) else _lib.kq_qmm
+    _check(fn(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(y), _dtype_id(y), _stream(stream)))
 
 
 def kq_quantized_matmul(codec, w, n: int, k: int, x, y, stream=None) -> None:
+    if _bf16(x):  # bfloat16: the GEMV to 16 rows, the GEMM above
+        fn = _lib.kq_qmv_bf16 if x.shape[0] <= 16 else _lib.kq_qmm_bf16
+        _check(fn(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(y), _dtype_id(y), _stream(stream)))
+        return
     _check(_lib.kq_quantized_matmul(_codec(codec), _ptr(w), n, k, _ptr(x), x.shape[0], _ptr(y), _dtype_id(y),
                                     _stream(stream)))
 
@@ -202,9 +225,10 @@ def kq_expert_tile_map(sorted_ids, n_experts: int, map_, counts, status=None, st
 
 
 def kq_gather_qmm_seg(codec, w, n_experts: int, n: int, k: int, x, map_, counts, y, stream=None) -> None:
-    """w uint8 [E, n, row_bytes]; x float16 [rows, k] expert-sorted; y [rows, n]."""
-    _check(_lib.kq_gather_qmm_seg(_codec(codec), _ptr(w), n_experts, n, k, _ptr(x), x.shape[0], _ptr(map_),
-                                  _ptr(counts), map_.shape[0], _ptr(y), _dtype_id(y), _stream(stream)))
+    """w uint8 [E, n, row_bytes]; x float16 or bfloat16 [rows, k] expert-sorted; y [rows, n]."""
+    fn = _lib.kq_gather_qmm_seg_bf16 if _bf16(x) else _lib.kq_gather_qmm_seg
+    _check(fn(_codec(codec), _ptr(w), n_experts, n, k, _ptr(x), x.shape[0], _ptr(map_), _ptr(counts), map_.shape[0],
+              _ptr(y), _dtype_id(y), _stream(stream)))
 
 
 def kq_gather_qmv(codec, w, n_experts: int, n: int, k: int, x, ids, y, stream=None) -> None:

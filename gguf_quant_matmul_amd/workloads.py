@@ -72,6 +72,21 @@ def activations(seed: int, m: int, k: int) -> np.ndarray:
     return rng.standard_normal((m, k), dtype=np.float32).astype(np.float16)
 
 
+def to_bf16(a: np.ndarray) -> np.ndarray:
+    """Finite float32 values rounded to the nearest bfloat16 (ties to even),
+    returned as float32 holding bfloat16 values (NumPy has no bfloat16)."""
+    bits = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bits = (bits + 0x7FFF + ((bits >> 16) & 1)) & 0xFFFF0000
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def activations_bf16(seed: int, m: int, k: int) -> np.ndarray:
+    """Bfloat16 activations [m, k] (as float32 values): the same N(0,1) draw
+    as ``activations``, rounded to bfloat16."""
+    rng = np.random.default_rng([seed, 1])
+    return to_bf16(rng.standard_normal((m, k), dtype=np.float32))
+
+
 @dataclass
 class Routing:
     tokens: int

@@ -58,8 +58,8 @@ typedef enum {
   KQ_Q2_K = 10, KQ_Q3_K = 11, KQ_Q4_K = 12, KQ_Q5_K = 13, KQ_Q6_K = 14
 } kq_codec;
 
-/* Output element types. */
-typedef enum { KQ_F32 = 0, KQ_F16 = 1 } kq_dtype;
+/* Output element types (KQ_BF16: the bfloat16-activation entry points only). */
+typedef enum { KQ_F32 = 0, KQ_F16 = 1, KQ_BF16 = 2 } kq_dtype;
 
 /* GLU epilogues of kq_moe_glu_gather and kq_quantized_matmul_glu (the pages'
  * act names in comments; kq_quantized_matmul_glu takes the first two). */
@@ -192,6 +192,25 @@ int kq_gather_qmm_seg(int codec, const void* w, int64_t n_experts, int64_t n, in
                       const void* x, int64_t rows,
                       const uint32_t* map, const uint32_t* counts, int64_t cap,
                       void* y, int y_dtype, void* stream);
+
+/* ---- bfloat16 activations (mlx-kquant bindings.cpp page: quantized_matmul
+ *      and gather_qmm_seg return x's dtype, float32 promoted to bfloat16) ----
+ * kq_qmv_bf16, kq_qmm_bf16 and kq_gather_qmm_seg_bf16 are kq_qmv, kq_qmm and
+ * kq_gather_qmm_seg with x bfloat16 [M][K] (16-byte aligned); y_dtype is
+ * KQ_F32, KQ_F16 or KQ_BF16 (the store rounds once, to nearest even).  Same
+ * shapes, map semantics and errors as the float16 calls (kq_qmv_bf16:
+ * 1 <= M <= 16).  On the matrix cores the activations are exact and each
+ * weight enters as the sum of two bfloat16 terms holding 16 significant
+ * bits of its exact value (relative error below 2^-16); accumulation is
+ * float32. */
+int kq_qmv_bf16(int codec, const void* w, int64_t n, int64_t k,
+                const void* x, int64_t m, void* y, int y_dtype, void* stream);
+int kq_qmm_bf16(int codec, const void* w, int64_t n, int64_t k,
+                const void* x, int64_t m, void* y, int y_dtype, void* stream);
+int kq_gather_qmm_seg_bf16(int codec, const void* w, int64_t n_experts, int64_t n, int64_t k,
+                           const void* x, int64_t rows,
+                           const uint32_t* map, const uint32_t* counts, int64_t cap,
+                           void* y, int y_dtype, void* stream);
 
 /* ---- unsort and score mix (mlx-kquant bindings.cpp page, gather_mix
  * docstring) ----

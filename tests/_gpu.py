@@ -97,3 +97,23 @@ def assert_glu_close(y, ref, g, u, act, f16, what=""):
     assert frac.max() <= 1.0, f"{what}: error {abs(y[i] - ref[i]):.3e} at {i} exceeds its bound {bound[i]:.3e}"
     say(f"  {what}: bound use {frac.max():.2f}, row-normalized error {row_rel_err(y, ref).max():.2e}")
     return float(frac.max())
+
+
+def bf16_bound(ref, out, tol=TOL):
+    """Per-element bound for bfloat16-activation products: the row bar (tol of
+    the row's largest |ref|) plus, for a bfloat16 store, the one rounding the
+    store defines (at most 2^-8 of the element: bfloat16 keeps 8 significant
+    bits); float16 and float32 stores need nothing beyond the row bar."""
+    ref = np.asarray(ref, np.float64)
+    row = tol * np.max(np.abs(ref), axis=1, keepdims=True)
+    return row + (2.0 ** -8 * np.abs(ref) if out == "bf16" else 0.0)
+
+
+def assert_close_bf16(y, ref, out, what=""):
+    y = np.asarray(y, np.float64)
+    assert np.all(np.isfinite(y)), f"{what}: non-finite output"
+    err = np.abs(y - ref)
+    b = bf16_bound(ref, out)
+    i = np.unravel_index(int((err / b).argmax()), err.shape)
+    assert np.all(err <= b), f"{what}: error {err[i]:.3e} at {i} exceeds its bound {b[i]:.3e}"
+    say(f"  {what}: row-normalized error {row_rel_err(y, ref).max():.2e}, bound use {(err / b).max():.2f}")

@@ -368,3 +368,33 @@ def test_glu_product_f32_equals_activation_times_up(act):
     np.testing.assert_allclose(y16, a * u, rtol=2 * 2.0 ** -11 + 1e-6, atol=2.0 ** -24)
     with pytest.raises(ValueError):
         matmul.quantized_matmul_glu("q4_k", wg, wu, k, x, "silu_limit")
+
+
+def test_bf16_activation_generator_matches_torch_rounding():
+    # the input generator's bfloat16 rounding is the library routine's (RNE)
+    import torch
+
+    rng = np.random.default_rng(41)
+    a = (rng.standard_normal(4096) * np.exp2(rng.integers(-60, 60, 4096))).astype(np.float32)
+    a[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 3.3895313892515355e38]  # ties and the max
+    want = torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(workloads.to_bf16(a), want)
+    assert workloads.to_bf16(np.float32([1.0 + 2.0 ** -8]))[0] == 1.0            # tie to even: down
+    assert workloads.to_bf16(np.float32([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6  # tie to even: up
+
+
+@pytest.mark.parametrize("codec", ["q4_k", "q6_k", "q8_0", "q3_k"])
+def test_qmatmul_bf16_activations_exact_over_wide_range(codec):
+    # bfloat16 activations far outside float16's range (2^-100 .. 2^100) are
+    # exact in the oracle's float64 product
+    rng = np.random.default_rng(43)
+    m, n, k = 3, 3, 256
+    wq = encode.quantize(codec, (rng.standard_normal((n, k)) * 0.02).astype(np.float32))
+    x = workloads.to_bf16((rng.standard_normal((m, k)) * np.exp2(rng.integers(-100, 100, (m, 1)))).astype(np.float32))
+    y = matmul.qmatmul(codec, wq, k, x)
+    wd = codecs.dequantize(codec, wq, k)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(float(x[i, t])) * Fraction(float(wd[j, t])) for t in range(k))
+            scale = sum(abs(Fraction(float(x[i, t])) * Fraction(float(wd[j, t]))) for t in range(k))
+            assert abs(Fraction(y[i, j]) - exact) <= Fraction(1, 2 ** 50) * scale
