@@ -41,9 +41,9 @@ COPY_REF_BYTES = 256 << 20     # the elementwise copy that scales the HBM byte c
 # copy of COPY_REF_BYTES).  A figure is reported only while the digest of the
 # kernel's sources still matches the one the counters were taken on.
 TRAFFIC = {
-    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "7e62792a7f993b50",
-            "bytes": 9594236},
-    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "8eac7a6ed1a3e2ee", "bytes": 357096103},
+    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "7b3cb9dc2da4e8dc",
+            "bytes": 9594180},
+    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "0c120a5652fbacb2", "bytes": 357102245},
 }
 
 
@@ -501,8 +501,10 @@ def counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4):
     """Eager launches for hardware-counter passes.  First a plain elementwise
     copy (torch.neg) of COPY_REF_BYTES four times: it reads and writes exactly
     that many bytes, which calibrates FETCH_SIZE and WRITE_SIZE.  Then the
-    timed workloads as the timed region runs them: one GEMV per cold weight
-    copy and two GEMMs."""
+    timed workloads as the timed region runs them (one GEMV per cold weight
+    copy, two GEMMs), and after them two launches each of the q8_0 and q4_0
+    GEMVs at M = 8, one q6_K lm-head GEMV and two MoE tile maps and segment
+    GEMMs, so one pass covers every HBM- and MFMA-bound row."""
     from gguf_quant_matmul_amd import workloads as W
 
     c1, c4 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM
@@ -511,13 +513,53 @@ def counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4):
     for _ in range(4):
         torch.neg(src, out=dst)
     torch.cuda.synchronize()
+    del src, dst
     for w in w1s:
         kq.kq_qmv(c1.codec, w, c1.n, c1.k, x1, y1)
     for _ in range(2):
         kq.kq_qmm(c4.codec, w4, c4.n, c4.k, x4, y4)
     torch.cuda.synchronize()
-    return {"mode": "counters", "copy_ref_bytes": COPY_REF_BYTES, "copy_launches": 4,
-            "qmv_launches": len(w1s), "qmm_launches": 2}
+    launched = {"copy": 4, "qmv q4_K 4096x4096 M=1": len(w1s), "qmm q4_K 2048x14336x4096": 2}
+
+    for cfg in W.CFG2_GEMV:
+        if cfg.m != 8:
+            continue
+        w = gpu_weights(torch, kq, cfg.codec, cfg.seed, cfg.n, cfg.k, cfg.dist)
+        x = torch.from_numpy(W.gemv_activations(cfg)).cuda()
+        y = torch.empty((cfg.m, cfg.n), dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        for _ in range(2):
+            kq.kq_qmv(cfg.codec, w, cfg.n, cfg.k, x, y)
+        torch.cuda.synchronize()
+        launched[f"qmv {cfg.codec} {cfg.n}x{cfg.k} M=8"] = 2
+        del w
+    c3 = W.CFG3_Q6K_LMHEAD
+    w = gpu_weights(torch, kq, c3.codec, c3.seed, c3.n, c3.k, c3.dist)
+    x = torch.from_numpy(W.gemv_activations(c3)).cuda()
+    y = torch.empty((c3.m, c3.n), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    kq.kq_qmv(c3.codec, w, c3.n, c3.k, x, y)
+    torch.cuda.synchronize()
+    launched["qmv q6_K 128256x4096 M=1"] = 1
+    del w
+    torch.cuda.empty_cache()
+
+    c5 = W.CFG5_MOE_SEG
+    w = gpu_weights(torch, kq, c5.codec, c5.seed, c5.n_experts * c5.n, c5.k, "normal")
+    r = W.routing(c5.seed, c5.tokens, c5.top_k, c5.n_experts)
+    x = torch.from_numpy(W.activations(c5.seed, c5.tokens, c5.k)[r.token_of_row]).cuda()
+    ids = torch.from_numpy(r.sorted_ids.view(np.int32)).cuda()
+    cap = kq.kq_expert_tile_map_capacity(ids.numel(), c5.n_experts)
+    map_ = torch.empty((cap, 3), dtype=torch.int32, device="cuda")
+    counts = torch.empty((1,), dtype=torch.int32, device="cuda")
+    y = torch.empty((x.shape[0], c5.n), dtype=torch.float16, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(2):
+        kq.kq_expert_tile_map(ids, c5.n_experts, map_, counts)
+        kq.kq_gather_qmm_seg(c5.codec, w, c5.n_experts, c5.n, c5.k, x, map_, counts, y)
+    torch.cuda.synchronize()
+    launched["tile map + seg q4_K MoE 512 tok top-8"] = 2
+    return {"mode": "counters", "copy_ref_bytes": COPY_REF_BYTES, "launches": launched}
 
 
 def cpu_baseline():

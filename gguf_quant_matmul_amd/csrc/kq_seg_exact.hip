@@ -56,6 +56,13 @@ __device__ __forceinline__ void sx_for(F&& f) {
   }
 }
 
+// A window buffer row is eight 8-byte slots: the hi sums of sub-block pairs
+// 0..3, then the lo sums.  Slot c of row r sits at c ^ ((r >> 1) & 7), so the
+// 8-byte reads of rows 0..15 at one slot (16 lanes), or at two neighbouring
+// slots (32 lanes), fall on distinct banks; unswizzled, rows r and r + 4
+// share banks.  Returns the index of the slot's first bfloat16.
+__device__ __forceinline__ int sx_wslot(int row, int c) { return 4 * (8 * row + (c ^ ((row >> 1) & 7))); }
+
 // float32 v -> (hi, lo) bfloat16 bit patterns with v = hi + lo + O(2^-16 |v|):
 // hi is v truncated to 8 significant bits, lo the (exact) remainder truncated.
 __device__ __forceinline__ void bf16_split(float v, uint32_t& hi, uint32_t& lo) {
@@ -156,8 +163,8 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
   };
   // Store the staged pieces of superblock sb into buffer sb & 1 and their
   // sub-block sums (float32 over 32 values: four lanes' 8 each) into window
-  // buffer (sb >> 1) & 1 at [row][cu * 4 + (sb & 1) * 2 + e] for sub-block
-  // j = 2 cu + e, as bfloat16 hi and lo.
+  // buffer (sb >> 1) & 1 at position cu * 4 + (sb & 1) * 2 + e of the row's
+  // hi and lo halves for sub-block j = 2 cu + e.
   auto store_x = [&](int sb) __attribute__((always_inline)) {
     half_t* xb = xs + (sb & 1) * SX_XBUF;
     uint16_t* wb = xw + ((sb >> 1) & 1) * SX_WBUF;
@@ -176,8 +183,8 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
       if ((pc & 3) == 0) {
         uint32_t hi, lo;
         bf16_split(s, hi, lo);
-        wb[row * 2 * SX_WROW + pos] = (uint16_t)(hi >> 16);
-        wb[row * 2 * SX_WROW + SX_WROW + pos] = (uint16_t)(lo >> 16);
+        wb[sx_wslot(row, pos >> 2) + (pos & 3)] = (uint16_t)(hi >> 16);
+        wb[sx_wslot(row, 4 + (pos >> 2)) + (pos & 3)] = (uint16_t)(lo >> 16);
       }
     }
   };
@@ -237,8 +244,8 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
       const uint16_t* wb = xw + ((sb >> 1) & 1) * SX_WBUF;
 #pragma unroll
       for (int i = 0; i < XG; ++i) {
-        const uint16_t* wr = wb + (16 * i + r) * 2 * SX_WROW + 4 * cu;
-        const bf16x4_t ah = *(const bf16x4_t*)wr, al = *(const bf16x4_t*)(wr + SX_WROW);
+        const bf16x4_t ah = *(const bf16x4_t*)(wb + sx_wslot(16 * i + r, cu));
+        const bf16x4_t al = *(const bf16x4_t*)(wb + sx_wslot(16 * i + r, 4 + cu));
 #pragma unroll
         for (int j = 0; j < SX_RG; ++j) {
           const bf16x4_t h = __builtin_bit_cast(bf16x4_t, bh[j]), l = __builtin_bit_cast(bf16x4_t, bl[j]);
