@@ -27,9 +27,26 @@
 // values of unit (superblock, sub-block pair l >> 4) per MFMA, so one MFMA's 32
 // K values are the four sub-block pairs of one superblock at one offset, and
 // all of them share the superblock's d.  Activations are staged in LDS one
-// superblock (256 values) per chunk, double-buffered, rows swizzled by 16-byte
-// chunk (chunk c of row r at c ^ (r & 15)); the sub-block sums are formed
-// while staging.
+// superblock (256 values) per chunk, double-buffered; the sub-block sums are
+// formed while staging.
+//
+// LDS placement of the activation rows.  Measured on gfx950 with a probe of
+// lane address patterns against SQ_LDS_BANK_CONFLICT: a 16-byte read of a
+// wave is served in 32-lane halves over sixteen 16-byte bank slots
+// (address / 16 mod 16); two lanes of a half that hit one slot at different
+// addresses conflict unless they are exactly 16 lanes apart.  A fragment read
+// has lane (r, cu) take 16-byte chunk 8 cu + S of row 16 i + r, so chunk c of
+// row r is stored at swap34(c) ^ (r & 15) (bits 3 and 4 of c exchanged): lanes
+// 16 apart then share a slot and each 16-lane group covers all sixteen.  The
+// staging lane that writes physical chunk pc loads logical chunk
+// swap34(pc ^ (r & 15)), so the writes are contiguous.
+//
+// A tile of 64 rows followed in the map by a tail of at most 16 rows of the
+// same expert (contiguous rows) is worked as one 80-row tile: otherwise the
+// tail's workgroups decode every weight of the expert again for a handful of
+// rows.  The two tiles' workgroups then take 64-row weight blocks (one 16-row
+// group per wave) against five activation groups, the activation chunk
+// single-buffered so the kernel's LDS stays within two workgroups per CU.
 #include <type_traits>
 
 #include "kq_units.h"
@@ -46,6 +63,8 @@ constexpr int SX_KC = 256;                 // K values per chunk: one superblock
 constexpr int SX_XBUF = 64 * SX_KC;        // halves per activation chunk buffer (64 rows)
 constexpr int SX_WROW = 16;                // sub-block sums per row per window: 8 sub-blocks x 2 superblocks
 constexpr int SX_WBUF = 64 * 2 * SX_WROW;  // bfloat16 per window buffer: [row][hi, lo][16]
+constexpr int SX_LDS = 2 * SX_XBUF * 2 + 2 * SX_WBUF * 2;  // bytes: both paths' buffers fit
+constexpr int SX_MERGE_MAX = 16;           // largest tail merged into the full tile before it
 constexpr int SX_NXCD = 8;
 
 template <int N, typename F>
@@ -56,11 +75,17 @@ __device__ __forceinline__ void sx_for(F&& f) {
   }
 }
 
+// Bits 3 and 4 of a 16-byte chunk index exchanged.
+__device__ __forceinline__ int sx_swap34(int c) { return (c & ~24) | ((c & 8) << 1) | ((c & 16) >> 1); }
+
 // A window buffer row is eight 8-byte slots: the hi sums of sub-block pairs
 // 0..3, then the lo sums.  Slot c of row r sits at c ^ ((r >> 1) & 7), so the
 // 8-byte reads of rows 0..15 at one slot (16 lanes), or at two neighbouring
 // slots (32 lanes), fall on distinct banks; unswizzled, rows r and r + 4
-// share banks.  Returns the index of the slot's first bfloat16.
+// share banks.  Returns the index of the slot's first bfloat16.  A lo slot
+// (c + 4) is its hi slot's index with bit 4 flipped, and rows 8 apart differ
+// by 256 and by that same flip, so the kernel forms every address from one
+// base register and immediate offsets.
 __device__ __forceinline__ int sx_wslot(int row, int c) { return 4 * (8 * row + (c ^ ((row >> 1) & 7))); }
 
 // float32 v -> (hi, lo) bfloat16 bit patterns with v = hi + lo + O(2^-16 |v|):
@@ -82,6 +107,7 @@ struct SxConst {
   half2_t k1, k2;  // (sc0, sc1 / 16), (-1024 sc0, -64 sc1): exact float16
   float d;
   uint32_t bh, bl;  // bfloat16 pairs (sub-block 2cu, 2cu + 1) of -dmin m
+  SxConst() = default;
   __device__ __forceinline__ SxConst(const UnitQ4K& un, int cu) {
     uint32_t sc0, m0, sc1, m1;
     q4k_scale_min_pair(un.h.y, un.h.z, un.h.w, cu, sc0, m0, sc1, m1);
@@ -119,60 +145,73 @@ __device__ __forceinline__ half8_t sx_slice(const UnitQ4K& un, const SxConst& c)
   return __builtin_bit_cast(half8_t, f);
 }
 
-// One tile of XG live 16-row activation groups against SX_BN weight rows.
-template <bool F16, int XG>
+// One tile of XG live 16-row activation groups against 4 * 16 * RG weight rows
+// (RG 16-row groups per wave).  DB: activation chunks double-buffered (one
+// barrier per superblock) or single-buffered (two).
+template <bool F16, int XG, int RG, bool DB>
 __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n, int k, int64_t row_bytes,
                                         const half_t* __restrict__ xtile, int64_t x_bytes, int nr, int64_t yrow0,
-                                        int n0, half_t* xs, uint16_t* xw, void* __restrict__ y) {
+                                        int n0, uint8_t* lds, void* __restrict__ y) {
   constexpr int NS = 2;                        // ring slots, one superblock each
   constexpr int XPT = XG * 16 * 32 / SX_THREADS;  // 16-byte activation pieces per thread per chunk
+  constexpr int ROWS = DB ? 64 : 16 * XG;      // activation rows a buffer holds
+  constexpr int XBUF = ROWS * SX_KC, WBUF = ROWS * 2 * SX_WROW;
+  static_assert((DB ? 2 : 1) * XBUF * 2 + 2 * WBUF * 2 <= SX_LDS, "LDS");
+  half_t* xs = (half_t*)lds;
+  uint16_t* xw = (uint16_t*)(lds + (DB ? 2 : 1) * XBUF * 2);
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, cu = lane >> 4;
   const int nsb = k / 256;
 
-  // the wave's 32 weight rows from their (16-byte aligned) base; rows past N read as zeros
-  const int64_t wrow0 = (int64_t)(n0 + wave * 16 * SX_RG);
+  // the wave's 16 RG weight rows from their (16-byte aligned) base; rows past N read as zeros
+  const int64_t wrow0 = (int64_t)(n0 + wave * 16 * RG);
   const rsrc_t wrs = make_rsrc(wbase + wrow0 * row_bytes, (int64_t)(n - wrow0) * row_bytes);
-  int rowoff[SX_RG];
+  int rowoff[RG];
 #pragma unroll
-  for (int j = 0; j < SX_RG; ++j) rowoff[j] = (16 * j + r) * (int)row_bytes;
+  for (int j = 0; j < RG; ++j) rowoff[j] = (16 * j + r) * (int)row_bytes;
   auto refill = [&](UnitQ4K* slot, int sb) __attribute__((always_inline)) {
     const int g = 4 * min(sb, nsb - 1);
 #pragma unroll
-    for (int j = 0; j < SX_RG; ++j) slot[j].bload(wrs, rowoff[j], cu, g);
+    for (int j = 0; j < RG; ++j) slot[j].bload(wrs, rowoff[j], cu, g);
   };
 
-  float4_t acc[SX_RG][XG], part[SX_RG][XG];
+  float4_t acc[RG][XG], part[RG][XG];
 #pragma unroll
-  for (int j = 0; j < SX_RG; ++j)
+  for (int j = 0; j < RG; ++j)
 #pragma unroll
     for (int i = 0; i < XG; ++i) acc[j][i] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Staging: piece i of a thread is row (tid >> 5) + 8 i, values 8 (tid & 31)
-  // .. of the chunk.  Rows past the tile hold whatever follows in x (offsets
-  // past its end read as zeros); no stored output reads them.
+  // Staging: piece i of a thread is row prow + 8 i (prow = tid >> 5), stored
+  // at physical chunk pc = tid & 31 of the row: logical chunk lc = swap34(pc ^
+  // prow) for even i, lc ^ 16 for odd i (row & 15 = prow + 8 (i & 1)).  A
+  // quad of lanes holds the four chunks of one 32-value sub-block.  Rows past
+  // the tile hold whatever follows in x (offsets past its end read as zeros);
+  // no stored output reads them.
   const rsrc_t xrs = make_rsrc(xtile, x_bytes);
   const int pc = tid & 31, prow = tid >> 5;
-  const int xvoff = prow * k * 2 + pc * 16;
+  const int lc = sx_swap34(pc ^ prow);
+  const int xvoff0 = prow * k * 2 + lc * 16, xvoff1 = prow * k * 2 + (lc ^ 16) * 16;
   u32x4 xr[XPT];
   auto load_x = [&](int sb) __attribute__((always_inline)) {
     const int so = min(sb, nsb - 1) * 512;
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) xr[i] = bld16(xrs, xvoff + i * 8 * 2 * k, so);
+    for (int i = 0; i < XPT; ++i) xr[i] = bld16(xrs, (i & 1 ? xvoff1 : xvoff0) + i * 8 * 2 * k, so);
   };
   // Store the staged pieces of superblock sb into buffer sb & 1 and their
   // sub-block sums (float32 over 32 values: four lanes' 8 each) into window
   // buffer (sb >> 1) & 1 at position cu * 4 + (sb & 1) * 2 + e of the row's
-  // hi and lo halves for sub-block j = 2 cu + e.
+  // hi and lo halves for sub-block j = 2 cu + e.  An odd piece's sub-block is
+  // j ^ 4, which moves its slots by 24 (hi) and 8 (lo) from the even pieces'.
   auto store_x = [&](int sb) __attribute__((always_inline)) {
-    half_t* xb = xs + (sb & 1) * SX_XBUF;
-    uint16_t* wb = xw + ((sb >> 1) & 1) * SX_WBUF;
-    const int j = pc >> 2, pos = (j >> 1) * 4 + (sb & 1) * 2 + (j & 1);
+    half_t* xb = xs + (DB ? (sb & 1) * XBUF : 0);
+    uint16_t* wb = xw + ((sb >> 1) & 1) * WBUF;
+    const int j = lc >> 2, pos = (j >> 1) * 4 + (sb & 1) * 2 + (j & 1);
+    const int w0 = sx_wslot(prow, pos >> 2) + (pos & 3);  // even pieces' hi; lo is w0 ^ 16
 #pragma unroll
     for (int i = 0; i < XPT; ++i) {
       const int row = prow + 8 * i;
-      *(u32x4*)(xb + row * SX_KC + 8 * (pc ^ (row & 15))) = xr[i];
+      *(u32x4*)(xb + row * SX_KC + 8 * pc) = xr[i];
       float s = 0.f;
       s = dot2(xr[i].x, 0x3C003C00u, s);
       s = dot2(xr[i].y, 0x3C003C00u, s);
@@ -183,14 +222,14 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
       if ((pc & 3) == 0) {
         uint32_t hi, lo;
         bf16_split(s, hi, lo);
-        wb[sx_wslot(row, pos >> 2) + (pos & 3)] = (uint16_t)(hi >> 16);
-        wb[sx_wslot(row, 4 + (pos >> 2)) + (pos & 3)] = (uint16_t)(lo >> 16);
+        wb[(i & 1 ? w0 ^ 24 : w0) + 256 * i] = (uint16_t)(hi >> 16);
+        wb[(i & 1 ? w0 ^ 8 : w0 ^ 16) + 256 * i] = (uint16_t)(lo >> 16);
       }
     }
   };
 
   load_x(0);
-  UnitQ4K ring[NS][SX_RG];
+  UnitQ4K ring[NS][RG];
 #pragma unroll
   for (int p = 0; p < NS; ++p) {
     __builtin_amdgcn_sched_barrier(0);
@@ -200,23 +239,31 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
   store_x(0);
   __syncthreads();
 
+  // physical chunk of this lane's fragment reads: swap34(8 cu + S) ^ r
+  const int ca = sx_swap34(8 * cu) ^ r;
+
   // bfloat16 -dmin m of the window's two superblocks, per weight group:
   // dword L holds sub-blocks (2 cu, 2 cu + 1) of superblock L of the window
-  u32x2 bh[SX_RG], bl[SX_RG];
+  u32x2 bh[RG], bl[RG];
 
   // Superblock sb (L = sb & 1 its place in the window and its ring slot).
   auto chunk = [&](auto lc, int sb) __attribute__((always_inline)) {
     constexpr int L = decltype(lc)::value;
-    const half_t* cur = xs + L * SX_XBUF;
+    const half_t* cur = xs + (DB ? L * XBUF : 0);
     load_x(sb + 1);  // stored after this chunk's products
     UnitQ4K* slot = ring[L];
-    const SxConst c0(slot[0], cu), c1(slot[1], cu);
-    bh[0][L] = c0.bh; bl[0][L] = c0.bl;
-    bh[1][L] = c1.bh; bl[1][L] = c1.bl;
+    SxConst c[RG];
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+      c[j] = SxConst(slot[j], cu);
+      bh[j][L] = c[j].bh;
+      bl[j][L] = c[j].bl;
+    }
     auto step = [&](auto sc) __attribute__((always_inline)) {
       constexpr int S = decltype(sc)::value;
-      const half8_t b0 = sx_slice<S>(slot[0], c0);
-      const half8_t b1 = sx_slice<S>(slot[1], c1);
+      half8_t b[RG];
+#pragma unroll
+      for (int j = 0; j < RG; ++j) b[j] = sx_slice<S>(slot[j], c[j]);
       if constexpr (S == 7) {
         // every step of the superblock is decoded: refill its registers
         __builtin_amdgcn_sched_barrier(0);
@@ -225,9 +272,10 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
 #pragma unroll
       for (int i = 0; i < XG; ++i) {
         const int row = 16 * i + r;
-        const half8_t a = *(const half8_t*)(cur + row * SX_KC + 8 * ((8 * cu + S) ^ r));
-        part[0][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b0, S == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : part[0][i], 0, 0, 0);
-        part[1][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b1, S == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : part[1][i], 0, 0, 0);
+        const half8_t a = *(const half8_t*)(cur + row * SX_KC + 8 * (ca ^ S));
+#pragma unroll
+        for (int j = 0; j < RG; ++j)
+          part[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], S == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : part[j][i], 0, 0, 0);
       }
     };
     sx_for<8>(step);
@@ -235,19 +283,20 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
     for (int i = 0; i < XG; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        acc[0][i][q] = fmaf(c0.d, part[0][i][q], acc[0][i][q]);
-        acc[1][i][q] = fmaf(c1.d, part[1][i][q], acc[1][i][q]);
+#pragma unroll
+        for (int j = 0; j < RG; ++j) acc[j][i][q] = fmaf(c[j].d, part[j][i][q], acc[j][i][q]);
       }
     }
     if constexpr (L == 1) {
       // the window's min term: (X hi + X lo) . (b hi + b lo) without lo . lo
-      const uint16_t* wb = xw + ((sb >> 1) & 1) * SX_WBUF;
+      const uint16_t* wb = xw + ((sb >> 1) & 1) * WBUF;
+      const int r0 = sx_wslot(r, cu);  // rows 16 i + r: + 512 i; lo: ^ 16
 #pragma unroll
       for (int i = 0; i < XG; ++i) {
-        const bf16x4_t ah = *(const bf16x4_t*)(wb + sx_wslot(16 * i + r, cu));
-        const bf16x4_t al = *(const bf16x4_t*)(wb + sx_wslot(16 * i + r, 4 + cu));
+        const bf16x4_t ah = *(const bf16x4_t*)(wb + r0 + 512 * i);
+        const bf16x4_t al = *(const bf16x4_t*)(wb + (r0 ^ 16) + 512 * i);
 #pragma unroll
-        for (int j = 0; j < SX_RG; ++j) {
+        for (int j = 0; j < RG; ++j) {
           const bf16x4_t h = __builtin_bit_cast(bf16x4_t, bh[j]), l = __builtin_bit_cast(bf16x4_t, bl[j]);
           acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, h, acc[j][i], 0, 0, 0);
           acc[j][i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ah, l, acc[j][i], 0, 0, 0);
@@ -255,7 +304,10 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
         }
       }
     }
-    store_x(sb + 1);  // the other buffers were last read before the previous barrier
+    // double-buffered: the other buffers were last read before the previous
+    // barrier; single-buffered: wait until every wave has read this chunk
+    if constexpr (!DB) __syncthreads();
+    store_x(sb + 1);
     __syncthreads();
   };
   for (int sb = 0; sb < nsb; sb += 2) {
@@ -264,10 +316,10 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
   }
 
   // lane l holds activation rows 16 i + 4 (l >> 4) + q of weight row
-  // n0 + 32 wave + 16 j + (l & 15)
+  // n0 + 16 RG wave + 16 j + (l & 15)
 #pragma unroll
-  for (int j = 0; j < SX_RG; ++j) {
-    const int col = n0 + wave * 16 * SX_RG + 16 * j + (lane & 15);
+  for (int j = 0; j < RG; ++j) {
+    const int col = n0 + wave * 16 * RG + 16 * j + (lane & 15);
     if (col >= n) continue;
 #pragma unroll
     for (int i = 0; i < XG; ++i) {
@@ -286,6 +338,19 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
   }
 }
 
+// Map entry t is a full tile whose successor is a tail of the same expert on
+// the rows right after it, of at most SX_MERGE_MAX rows: the two are worked as
+// one tile.  Both tiles' workgroups evaluate this on the same entries, so a
+// tail is covered either by itself or by its merged head, never both.
+__device__ __forceinline__ bool sx_merges(const uint32_t* __restrict__ map, int t, int live_tiles, int m_total,
+                                          int n_experts) {
+  if (t < 0 || t + 1 >= live_tiles) return false;
+  const uint32_t* a = map + 3 * (size_t)t;
+  const uint32_t e0 = a[0], r0 = a[1], n0 = a[2], e1 = a[3], r1 = a[4], n1 = a[5];
+  return e0 < (uint32_t)n_experts && e1 == e0 && n0 == 64 && r0 < (uint32_t)m_total && r1 == r0 + 64 && n1 >= 1 &&
+         n1 <= SX_MERGE_MAX && r1 <= (uint32_t)m_total && n1 <= (uint32_t)m_total - r1;
+}
+
 template <bool F16>
 __global__ __launch_bounds__(SX_THREADS, 2) void seg_exact_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                                   int64_t row_bytes, int64_t expert_stride,
@@ -293,8 +358,7 @@ __global__ __launch_bounds__(SX_THREADS, 2) void seg_exact_kernel(const uint8_t*
                                                                   int m_total, const uint32_t* __restrict__ map,
                                                                   const uint32_t* __restrict__ counts, int cap,
                                                                   void* __restrict__ y) {
-  __shared__ __attribute__((aligned(16))) half_t xs[2 * SX_XBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t xw[2 * SX_WBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[SX_LDS];
 
   // Workgroup b runs on XCD b % 8; the map's live (tile, column block) pairs
   // are split into eight contiguous ranges, one per XCD, so the blocks of a
@@ -307,7 +371,20 @@ __global__ __launch_bounds__(SX_THREADS, 2) void seg_exact_kernel(const uint8_t*
   if (idx >= per_xcd) return;
   const int64_t t = (int64_t)(blockIdx.x % SX_NXCD) * per_xcd + idx;
   if (t >= live) return;
-  const int by = (int)(t / nb), n0 = (int)(t - (int64_t)by * nb) * SX_BN;
+  const int by = (int)(t / nb), blk = (int)(t - (int64_t)by * nb);
+  const int live_tiles = (int)min(counts[0], (uint32_t)cap);
+  // a full tile and its merged tail share both tiles' workgroups: 2 nb blocks of 64 weight rows
+  const bool tail = sx_merges(map, by - 1, live_tiles, m_total, n_experts);
+  if (tail || sx_merges(map, by, live_tiles, m_total, n_experts)) {
+    const uint32_t* mt = map + 3 * (size_t)(tail ? by - 1 : by);
+    const int n0 = (tail ? nb + blk : blk) * 64;
+    if (n0 >= n) return;
+    const uint32_t e = mt[0], rs = mt[1], nr = 64 + mt[5];
+    sx_tile<F16, 5, 1, false>(w + (int64_t)e * expert_stride, n, k, row_bytes, x + (int64_t)rs * k,
+                              (int64_t)(m_total - rs) * k * 2, (int)nr, rs, n0, lds, y);
+    return;
+  }
+  const int n0 = blk * SX_BN;
   const uint32_t* mt = map + 3 * (size_t)by;
   const uint32_t e = mt[0], rs = mt[1], nr = mt[2];
   if (e >= (uint32_t)n_experts || nr == 0 || nr > 64 || rs >= (uint32_t)m_total || nr > (uint32_t)m_total - rs)
@@ -316,10 +393,10 @@ __global__ __launch_bounds__(SX_THREADS, 2) void seg_exact_kernel(const uint8_t*
   const half_t* xtile = x + (int64_t)rs * k;
   const int64_t x_bytes = (int64_t)(m_total - rs) * k * 2;
   switch ((nr + 15) >> 4) {  // 16-row activation groups holding live rows
-    case 1: sx_tile<F16, 1>(wbase, n, k, row_bytes, xtile, x_bytes, (int)nr, rs, n0, xs, xw, y); break;
-    case 2: sx_tile<F16, 2>(wbase, n, k, row_bytes, xtile, x_bytes, (int)nr, rs, n0, xs, xw, y); break;
-    case 3: sx_tile<F16, 3>(wbase, n, k, row_bytes, xtile, x_bytes, (int)nr, rs, n0, xs, xw, y); break;
-    default: sx_tile<F16, 4>(wbase, n, k, row_bytes, xtile, x_bytes, (int)nr, rs, n0, xs, xw, y); break;
+    case 1: sx_tile<F16, 1, SX_RG, true>(wbase, n, k, row_bytes, xtile, x_bytes, (int)nr, rs, n0, lds, y); break;
+    case 2: sx_tile<F16, 2, SX_RG, true>(wbase, n, k, row_bytes, xtile, x_bytes, (int)nr, rs, n0, lds, y); break;
+    case 3: sx_tile<F16, 3, SX_RG, true>(wbase, n, k, row_bytes, xtile, x_bytes, (int)nr, rs, n0, lds, y); break;
+    default: sx_tile<F16, 4, SX_RG, true>(wbase, n, k, row_bytes, xtile, x_bytes, (int)nr, rs, n0, lds, y); break;
   }
 }
 

@@ -519,6 +519,43 @@ def test_gather_seg_tile_boundaries(kq, codec):
         assert_close_rows(got[covered], ref[covered], what=f"seg tile boundaries {codec}")
 
 
+@pytest.mark.parametrize("n", [200, 50])
+def test_gather_seg_q4k_merged_tails(kq, n):
+    # the q4_K segment kernel works a full tile and a following tail of at most
+    # 16 rows of the same expert as one 80-row tile.  Expert rows 80 (64 + 16,
+    # merged), 65 (64 + 1, merged), 81 (64 + 17, not merged), 144 (64 + 64 +
+    # 16: the second full tile takes the tail), 16 and 64; N = 200 leaves the
+    # last 64-row weight block ragged, N = 50 leaves the tails' blocks empty.
+    # The same map with its entries reversed merges nothing (a tail then
+    # precedes its full tile) and must give the same bits.
+    torch = _torch()
+    rng = np.random.default_rng(37)
+    e, k = 6, 1024
+    sizes = [80, 65, 81, 144, 16, 64]
+    ids = np.concatenate([np.full(c, i, np.uint32) for i, c in enumerate(sizes)] + [np.full(2, e + 3, np.uint32)])
+    rows = ids.size
+    w = encode.quantize("q4_k", (rng.standard_normal((e, n, k)) * 0.02).astype(np.float32))
+    x = _x(rows, k, 9)
+    map_, counts, count, status, cap = _tile_map_gpu(kq, ids, e)
+    tiles = host(map_)[:count].view(np.uint32)
+    assert [int(t[2]) for t in tiles] == [64, 16, 64, 1, 64, 17, 64, 64, 16, 16, 64]
+    ref = matmul.gather_qmm_seg("q4_k", w, k, x, tiles)
+    covered = ids < e
+    rev = torch.from_numpy(np.ascontiguousarray(host(map_)[:count][::-1])).cuda()
+    for tdt in (torch.float16, torch.float32):
+        say(f"seg q4_k merged tails n={n} {tdt}")
+        y = torch.full((rows, n), float("nan"), dtype=tdt, device="cuda")
+        kq.kq_gather_qmm_seg("q4_k", dev(w), e, n, k, dev(x), map_[:cap], counts, y)
+        got = host(y).astype(np.float64)
+        assert np.all(np.isnan(got[~covered])), "uncovered rows must stay unwritten"
+        assert_close_rows(got[covered], ref[covered], what=f"seg q4_k merged tails n={n}")
+        y2 = torch.full((rows, n), float("nan"), dtype=tdt, device="cuda")
+        kq.kq_gather_qmm_seg("q4_k", dev(w), e, n, k, dev(x), rev, counts, y2)
+        b1 = host(y).view(np.uint16 if tdt == torch.float16 else np.uint32)
+        b2 = host(y2).view(np.uint16 if tdt == torch.float16 else np.uint32)
+        assert np.array_equal(b1, b2), "merged and unmerged tiles must give the same bits"
+
+
 @pytest.mark.parametrize("codec", CODECS)
 def test_gather_qmv_parity(kq, codec):
     # one activation row per routed slot, ids in any order; an id past the
