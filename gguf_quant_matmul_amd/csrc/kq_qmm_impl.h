@@ -38,11 +38,29 @@ namespace kq {
 namespace {
 
 constexpr int BK = 64;
-constexpr int LDS_STRIDE = BK;  // halves: 128-byte rows of eight 16-byte chunks
-// Chunk c of row r lives at chunk c ^ (r & 7): the MFMA operand reads (16 rows
-// x 16 bytes at one column) then touch every bank once (a plain or 16-byte
-// padded row stride makes them conflict, measured with SQ_LDS_BANK_CONFLICT).
-__device__ __forceinline__ void st_chunk(half_t* row, int sw, int c, u32x4 v) { *(u32x4*)(row + 8 * (c ^ sw)) = v; }
+// An LDS tile of R rows x BK values is two planes of R 64-byte rows: 16-byte
+// chunk c (of eight per row) of row r sits in plane c & 1 at slot
+// (c >> 1) ^ ((r >> 2) & 3) ^ (2 ((r >> 1) & 1)) of its plane row.  Measured
+// on gfx950 (probes of lane address patterns, and variants of this kernel,
+// against SQ_LDS_BANK_CONFLICT): 16-byte reads are served per 32-lane half
+// over sixteen 16-byte bank slots (address / 16 mod 16), lanes 16 apart
+// sharing a slot without conflict; 16-byte writes are served 8 lanes at a
+// time over 128 bytes.  A fragment read has lane (r, g) take chunk 4 ks + g
+// of row r (r < 16): lanes 16 apart read the two planes of one chunk pair, at
+// one slot, and each 16-lane group covers all sixteen slots.  A weight store
+// has lanes 2q, 2q + 1 write one chunk each of row q: any 8 lanes (4 rows)
+// hit 8 distinct slots of 128 bytes.  Planes are 64 R bytes apart, a
+// multiple of 256 for R a multiple of 4.
+__device__ __forceinline__ int lds_off(int plane, int row, int c) {  // halves
+  return (c & 1) * plane + row * 32 + 8 * ((c >> 1) ^ ((row >> 2) & 3) ^ (2 * ((row >> 1) & 1)));
+}
+struct LdsRow {  // one row of an LDS tile: base, halves per plane, row index
+  half_t* tile;
+  int plane, row;
+};
+__device__ __forceinline__ void st_chunk(const LdsRow& d, int c, u32x4 v) {
+  *(u32x4*)(d.tile + lds_off(d.plane, d.row, c)) = v;
+}
 constexpr int NXCD = 8;
 
 // Row offset of segment t (16 values) of unit u.
@@ -87,7 +105,7 @@ template <> struct HalfUnit<Q4_K> {
     h = ld_16B(blk);
     q = ld_16B(blk + 16 + 32 * (u & 3) + 16 * hh);
   }
-  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+  __device__ __forceinline__ void store(int u, int hh, const LdsRow& dst) const {
     const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
     uint32_t sc0, m0, sc1, m1;
     q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3), sc0, m0);
@@ -110,10 +128,10 @@ template <> struct HalfUnit<Q4_K> {
       hi[2 * i] = pack_h2(fmaf((float)t01.x, s1, c1), fmaf((float)t01.y, s1, c1));
       hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, s1, c1), fmaf((float)t23.y, s1, c1));
     }
-    st_chunk(dst, sw, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    st_chunk(dst, sw, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
-    st_chunk(dst, sw, 4 + 2 * hh, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    st_chunk(dst, sw, 5 + 2 * hh, u32x4{hi[4], hi[5], hi[6], hi[7]});
+    st_chunk(dst, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    st_chunk(dst, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
+    st_chunk(dst, 4 + 2 * hh, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    st_chunk(dst, 5 + 2 * hh, u32x4{hi[4], hi[5], hi[6], hi[7]});
   }
 };
 
@@ -131,7 +149,7 @@ template <> struct HalfUnit<Q2_K> {
     sc = ld_u32(blk + 4 * up);
     dd = ld_u32(blk + 80);
   }
-  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+  __device__ __forceinline__ void store(int u, int hh, const LdsRow& dst) const {
     const float d = f16_to_f32(dd), dmin = f16_to_f32(dd >> 16);
     const int shift = 2 * (2 * (u & 1) + hh);
     const uint32_t qw[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
@@ -147,8 +165,8 @@ template <> struct HalfUnit<Q2_K> {
         o[2 * i] = pack_h2(fmaf((float)c01.x, s, c), fmaf((float)c01.y, s, c));
         o[2 * i + 1] = pack_h2(fmaf((float)c23.x, s, c), fmaf((float)c23.y, s, c));
       }
-      st_chunk(dst, sw, 4 * hh + 2 * g, u32x4{o[0], o[1], o[2], o[3]});
-      st_chunk(dst, sw, 4 * hh + 2 * g + 1, u32x4{o[4], o[5], o[6], o[7]});
+      st_chunk(dst, 4 * hh + 2 * g, u32x4{o[0], o[1], o[2], o[3]});
+      st_chunk(dst, 4 * hh + 2 * g + 1, u32x4{o[4], o[5], o[6], o[7]});
     }
   }
 };
@@ -169,7 +187,7 @@ template <> struct HalfUnit<Q3_K> {
     rs.load(blk + 92, sh);
     dbits = ld_u16(blk + 108);
   }
-  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+  __device__ __forceinline__ void store(int u, int hh, const LdsRow& dst) const {
     const int up = u & 3, h = up >> 1, c0 = 2 * (up & 1);
     uint32_t Q[4], H[4], S[4];
     rq.get(sh, Q); rh.get(sh, H); rs.get(sh, S);
@@ -187,8 +205,8 @@ template <> struct HalfUnit<Q3_K> {
         o[2 * i] = pack_h2(fmaf((float)c01.x, s, c), fmaf((float)c01.y, s, c));
         o[2 * i + 1] = pack_h2(fmaf((float)c23.x, s, c), fmaf((float)c23.y, s, c));
       }
-      st_chunk(dst, sw, 4 * g + 2 * hh, u32x4{o[0], o[1], o[2], o[3]});
-      st_chunk(dst, sw, 4 * g + 2 * hh + 1, u32x4{o[4], o[5], o[6], o[7]});
+      st_chunk(dst, 4 * g + 2 * hh, u32x4{o[0], o[1], o[2], o[3]});
+      st_chunk(dst, 4 * g + 2 * hh + 1, u32x4{o[4], o[5], o[6], o[7]});
     }
   }
 };
@@ -203,7 +221,7 @@ template <> struct HalfUnit<Q5_K> {
     e = ld_16B(blk + 16 + 16 * hh);
     q = ld_16B(blk + 48 + 32 * (u & 3) + 16 * hh);
   }
-  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+  __device__ __forceinline__ void store(int u, int hh, const LdsRow& dst) const {
     const float d = f16_to_f32(h.x), dmin = f16_to_f32(h.x >> 16);
     uint32_t sc0, m0, sc1, m1;
     q4k_scale_min(h.y, h.z, h.w, 2 * (u & 3), sc0, m0);
@@ -226,10 +244,10 @@ template <> struct HalfUnit<Q5_K> {
       hi[2 * i] = pack_h2(fmaf((float)t01.x, s1, c1), fmaf((float)t01.y, s1, c1));
       hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, s1, c1), fmaf((float)t23.y, s1, c1));
     }
-    st_chunk(dst, sw, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    st_chunk(dst, sw, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
-    st_chunk(dst, sw, 4 + 2 * hh, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    st_chunk(dst, sw, 5 + 2 * hh, u32x4{hi[4], hi[5], hi[6], hi[7]});
+    st_chunk(dst, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    st_chunk(dst, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
+    st_chunk(dst, 4 + 2 * hh, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    st_chunk(dst, 5 + 2 * hh, u32x4{hi[4], hi[5], hi[6], hi[7]});
   }
 };
 
@@ -247,7 +265,7 @@ template <> struct HalfUnit<Q6_K> {
     rs.load(blk + 192, sh);
     dbits = ld_u16(blk + 208);
   }
-  __device__ __forceinline__ void store(int u, int hh, half_t* dst, int sw) const {
+  __device__ __forceinline__ void store(int u, int hh, const LdsRow& dst) const {
     const int h = (u >> 1) & 1, half = u & 1;
     uint32_t Q[4], H[4], S[4];
     rq.get(sh, Q);
@@ -273,10 +291,10 @@ template <> struct HalfUnit<Q6_K> {
       b[2 * i] = as_u32(((as_h2(pair01(cb)) - k1056) * sb) * dd);
       b[2 * i + 1] = as_u32(((as_h2(pair23(cb)) - k1056) * sb) * dd);
     }
-    st_chunk(dst, sw, 2 * hh, u32x4{a[0], a[1], a[2], a[3]});
-    st_chunk(dst, sw, 2 * hh + 1, u32x4{a[4], a[5], a[6], a[7]});
-    st_chunk(dst, sw, 2 * hh + 4, u32x4{b[0], b[1], b[2], b[3]});
-    st_chunk(dst, sw, 2 * hh + 5, u32x4{b[4], b[5], b[6], b[7]});
+    st_chunk(dst, 2 * hh, u32x4{a[0], a[1], a[2], a[3]});
+    st_chunk(dst, 2 * hh + 1, u32x4{a[4], a[5], a[6], a[7]});
+    st_chunk(dst, 2 * hh + 4, u32x4{b[0], b[1], b[2], b[3]});
+    st_chunk(dst, 2 * hh + 5, u32x4{b[4], b[5], b[6], b[7]});
   }
 };
 
@@ -293,7 +311,7 @@ template <> struct HalfUnit<Q8_0> {
     r1 = ld_16B_a4(a + 16);
     r8 = ld_u32(a + 32);
   }
-  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
+  __device__ __forceinline__ void store(int, int hh, const LdsRow& dst) const {
     const uint32_t R[9] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w, r8};
     const half2_t d = h2(__builtin_bit_cast(half_t, (uint16_t)(sh ? (R[0] >> 16) : (R[0] & 0xFFFFu))));
     const half2_t k1152 = h2((half_t)1152.f);
@@ -305,7 +323,7 @@ template <> struct HalfUnit<Q8_0> {
       o[2 * i + 1] = as_u32((as_h2(pair23(c)) - k1152) * d);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) st_chunk(dst, sw, 4 * hh + i, u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]});
+    for (int i = 0; i < 4; ++i) st_chunk(dst, 4 * hh + i, u32x4{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]});
   }
 };
 
@@ -321,7 +339,7 @@ template <> struct HalfUnit<Q4_0> {
     r0 = ld_16B_a4(a);
     r4 = ld_u32(a + 16);
   }
-  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
+  __device__ __forceinline__ void store(int, int hh, const LdsRow& dst) const {
     const uint32_t R[5] = {r0.x, r0.y, r0.z, r0.w, r4};
     const half2_t d = h2(__builtin_bit_cast(half_t, (uint16_t)(sh ? (R[0] >> 16) : (R[0] & 0xFFFFu))));
     const half2_t k1032 = h2((half_t)1032.f);
@@ -335,10 +353,10 @@ template <> struct HalfUnit<Q4_0> {
       hi[2 * i] = as_u32((as_h2(pair01(t)) - k1032) * d);
       hi[2 * i + 1] = as_u32((as_h2(pair23(t)) - k1032) * d);
     }
-    st_chunk(dst, sw, 4 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    st_chunk(dst, sw, 4 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
-    st_chunk(dst, sw, 4 * hh + 2, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    st_chunk(dst, sw, 4 * hh + 3, u32x4{hi[4], hi[5], hi[6], hi[7]});
+    st_chunk(dst, 4 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    st_chunk(dst, 4 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
+    st_chunk(dst, 4 * hh + 2, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    st_chunk(dst, 4 * hh + 3, u32x4{hi[4], hi[5], hi[6], hi[7]});
   }
 };
 
@@ -371,7 +389,7 @@ struct HalfUnitLeg {
       return sh ? R[(O + 2) / 4] : alignbyte(R[O / 4 + 1], R[O / 4], 2);
     }
   }
-  __device__ __forceinline__ void store(int, int hh, half_t* dst, int sw) const {
+  __device__ __forceinline__ void store(int, int hh, const LdsRow& dst) const {
     constexpr int qso = L::QS, qho = L::QH >= 0 ? L::QH : 0;
     const uint32_t w0 = at<0>();
     const uint32_t qh = L::QH >= 0 ? at<qho>() : 0u;
@@ -402,10 +420,10 @@ struct HalfUnitLeg {
         hi[2 * i + 1] = as_u32((as_h2(pair23(t)) - k) * d);
       }
     }
-    st_chunk(dst, sw, 4 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
-    st_chunk(dst, sw, 4 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
-    st_chunk(dst, sw, 4 * hh + 2, u32x4{hi[0], hi[1], hi[2], hi[3]});
-    st_chunk(dst, sw, 4 * hh + 3, u32x4{hi[4], hi[5], hi[6], hi[7]});
+    st_chunk(dst, 4 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
+    st_chunk(dst, 4 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
+    st_chunk(dst, 4 * hh + 2, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    st_chunk(dst, 4 * hh + 3, u32x4{hi[4], hi[5], hi[6], hi[7]});
   }
 };
 template <> struct HalfUnit<Q4_1> : HalfUnitLeg<Q4_1> {};
@@ -445,8 +463,9 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
   constexpr int A_CHUNKS = BM * 8, A_PER_T = (A_CHUNKS + QMM_THREADS - 1) / QMM_THREADS;
   constexpr int B_HALVES = BN * 2, B_PER_T = (B_HALVES + QMM_THREADS - 1) / QMM_THREADS;
   constexpr int UNR = lcm_c(lcm_c(PDA, PDB), 2);
-  __shared__ __attribute__((aligned(16))) half_t As[2][BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) half_t Bs[2][BN * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) half_t As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) half_t Bs[2][BN * BK];
+  static_assert(BM % 4 == 0 && BN % 4 == 0, "planes 256-byte aligned");
 
   const int t = xcd_tile(per_xcd);
   if (t >= tiles_total) return;
@@ -473,19 +492,24 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
   HalfUnit<C> braw[PDB][B_PER_T];
 
   // Activation chunks: 8 per tile row (4 segments x 2 halves of 8 values).
+  // Chunk index c (thread + i x threads) takes row 8 (c >> 6) + 4 ((c >> 5) & 1)
+  // + ((c & 15) >> 2) and chunk 2 (c & 3) + ((c >> 4) & 1): the 64 lanes of a
+  // wave write 8 rows, and lanes 16 apart the two planes of one chunk pair.
   // Rows past the tile read a clamped valid row; their outputs are never
   // stored, so no predicate sits in the K loop.
+  auto a_row = [](int c) { return 8 * (c >> 6) + 4 * ((c >> 5) & 1) + ((c & 15) >> 2); };
+  auto a_part = [](int c) { return 2 * (c & 3) + ((c >> 4) & 1); };
   const half_t* xrow[A_PER_T];
 #pragma unroll
   for (int i = 0; i < A_PER_T; ++i) {
-    const int c = min(tid + i * QMM_THREADS, A_CHUNKS - 1), r = c >> 3;
-    xrow[i] = x + (int64_t)min(m0 + r, m_total - 1) * k + 8 * (c & 1);
+    const int c = min(tid + i * QMM_THREADS, A_CHUNKS - 1);
+    xrow[i] = x + (int64_t)min(m0 + a_row(c), m_total - 1) * k + 8 * (a_part(c) & 1);
   }
   // Weight half-units: wave w decodes rows [w * RPW, (w+1) * RPW), two lanes
   // (halves) per row, so every wave has the same decode work.  Spare lanes
-  // redo the wave's last row (same values to the same LDS bytes), so no lane
-  // is masked off.  Rows past N read a clamped valid row (finite values,
-  // outputs never stored).
+  // decode the wave's last row again but do not store it: several lanes
+  // writing one LDS address serialize (SQ_LDS_BANK_CONFLICT).  Rows past N
+  // read a clamped valid row (finite values, outputs never stored).
   constexpr int RPW = BN / 8;  // rows per wave
   static_assert(BN % 8 == 0 && 2 * RPW <= 64 && B_PER_T == 1, "one half-unit per lane");
   const int brow0 = wave * RPW + min(lane >> 1, RPW - 1);
@@ -494,7 +518,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
   auto issue_a = [&](int slot, int u) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
-      const int part = (tid + i * QMM_THREADS) & 7;
+      const int part = a_part(tid + i * QMM_THREADS);
       areg[slot][i] = *(const u32x4*)(xrow[i] + seg_off<C>(u, part >> 1));
     }
   };
@@ -504,11 +528,10 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
     for (int i = 0; i < A_PER_T; ++i) {
       const int c = tid + i * QMM_THREADS;
       if (A_CHUNKS % QMM_THREADS == 0 || c < A_CHUNKS) {
-        const int r = c >> 3, part = c & 7;
-        st_chunk(&As[buf][r * LDS_STRIDE], r & 7, part, areg[sa][i]);
+        st_chunk(LdsRow{As[buf], BM * 32, a_row(c)}, a_part(c), areg[sa][i]);
       }
     }
-    braw[sb][0].store(u, lane & 1, &Bs[buf][brow0 * LDS_STRIDE], brow0 & 7);
+    if (lane < 2 * RPW) braw[sb][0].store(u, lane & 1, LdsRow{Bs[buf], BN * 32, brow0});
   };
   // All fragment reads of a 32-wide K slice are issued before its MFMAs, in
   // the order the MFMAs consume them, so one LDS round trip per slice is
@@ -516,13 +539,13 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
   // the dead-fragment test.
   auto mfma_slice = [&](int buf, int ks, auto full) {
     constexpr bool FULL = decltype(full)::value;
-    const int kk = 8 * ((4 * ks + (lane >> 4)) ^ (lane & 7));
+    const int c = 4 * ks + (lane >> 4), r = lane & 15;
     half8_t a[TM], b[TN];
-    a[0] = *(const half8_t*)(&As[buf][(wr0 + (lane & 15)) * LDS_STRIDE + kk]);
+    a[0] = *(const half8_t*)(As[buf] + lds_off(BM * 32, wr0 + r, c));
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = *(const half8_t*)(&Bs[buf][(wc0 + 16 * j + (lane & 15)) * LDS_STRIDE + kk]);
+    for (int j = 0; j < TN; ++j) b[j] = *(const half8_t*)(Bs[buf] + lds_off(BN * 32, wc0 + 16 * j + r, c));
 #pragma unroll
-    for (int i = 1; i < TM; ++i) a[i] = *(const half8_t*)(&As[buf][(wr0 + 16 * i + (lane & 15)) * LDS_STRIDE + kk]);
+    for (int i = 1; i < TM; ++i) a[i] = *(const half8_t*)(As[buf] + lds_off(BM * 32, wr0 + 16 * i + r, c));
     asm volatile("" ::: "memory");  // keep every read above the MFMAs (the scheduler would sink them)
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
