@@ -141,7 +141,7 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
       s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
       s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
       if (c < xpieces) {
-        const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
+        const int m = c / (kc / 8), v = xperm<C>((c % (kc / 8)) * 8);
         *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
         if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
       }
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stream_kernel(const uint8_t* 
     s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
     s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
     if (c < xpieces) {
-      const int m = c / (k / 8), v = (c % (k / 8)) * 8;
+      const int m = c / (k / 8), v = xperm<C>((c % (k / 8)) * 8);
       *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
       if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
     }

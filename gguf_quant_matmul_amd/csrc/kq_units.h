@@ -14,6 +14,20 @@ namespace {
 
 __host__ __device__ constexpr int xpad(int v) { return v + (v >> 6) * 8; }  // padded LDS offset (halves)
 
+// Where the GEMV kernels stage activation value v of a chunk (before the
+// padding): in order, except for q6_K, whose 64-value units each take four
+// 16-value segments 32 values apart.  For q6_K the segments are put in unit
+// order (segment (cc, f) of a 128-value half, value 32 cc + 16 f of it, at
+// 64 f + 16 cc), so a unit's 64 values are contiguous: 16 lanes reading one
+// segment of 16 consecutive units then hit 16 different LDS bank slots (in
+// place order they hit only the even ones), and its four 16-value sums are one
+// aligned 16-byte read.
+template <int C>
+__host__ __device__ constexpr int xperm(int v) {
+  if (C == Q6_K) return (v & ~127) | (((v >> 4) & 1) << 6) | (((v >> 5) & 3) << 4) | (v & 15);
+  return v;
+}
+
 // ---------------------------------------------------------------------------
 // Buffer loads: a wave-uniform base and byte count in a resource descriptor,
 // a per-lane offset that stays fixed across the K loop, and a wave-uniform
@@ -47,6 +61,10 @@ struct Xv {  // activation views for one chunk
     return (const uint32_t*)(xs + m * xstride + xpad(off - c0));
   }
   __device__ __forceinline__ float sum16(int m, int off) const { return xsum[m * sstride + ((off - c0) >> 4)]; }
+  // the four 16-value sums from staged position off (a multiple of 64)
+  __device__ __forceinline__ float4_t sum64(int m, int off) const {
+    return *(const float4_t*)(xsum + m * sstride + ((off - c0) >> 4));
+  }
 };
 
 // sum over 16 values: (float16 pairs of codes) . (x pairs), 4 code dwords (p01, p23 per dword)
@@ -307,16 +325,15 @@ struct UnitQ6K {
     uint32_t p[4][8];
 #pragma unroll
     for (int cc = 0; cc < 4; ++cc) pairs16(c[cc], p[cc]);
-    const int base = 256 * (u >> 2) + 128 * h + 16 * half;
+    // staged in unit order (xperm): segment cc of the unit at 64 u + 16 cc
 #pragma unroll
     for (int m = 0; m < M; ++m) {
+      const float4_t xs = xv.sum64(m, 64 * u);
       float t = 0.f;
 #pragma unroll
       for (int cc = 0; cc < 4; ++cc) {
-        const int off = base + 32 * cc;
-        const float s = dot16(p[cc], xv.pairs(m, off), 0.f);
-        const float xs = xv.sum16(m, off);
-        t += dsc[cc] * (s - 1056.f * xs);
+        const float s = dot16(p[cc], xv.pairs(m, 64 * u + 16 * cc), 0.f);
+        t += dsc[cc] * (s - 1056.f * xs[cc]);
       }
       acc[m] += t;
     }
