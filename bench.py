@@ -168,12 +168,12 @@ def measure_rows(torch, kq):
         del ws, wq
         torch.cuda.empty_cache()
 
-    for cfg in W.CFG2_GEMV:
+    for cfg in W.Q8_0_Q4_0_GEMVS:
         gemv_row(cfg, read_ref=cfg.m == 1)
-    gemv_row(W.CFG3_Q6K_LMHEAD, reps=8, read_ref=True)
+    gemv_row(W.Q6K_LMHEAD_GEMV, reps=8, read_ref=True)
 
     # MoE: tile map + expert-segment GEMM
-    cfg = W.CFG5_MOE_SEG
+    cfg = W.MOE_SEG_Q4K
     wq = gpu_weights(torch, kq, cfg.codec, cfg.seed, cfg.n_experts * cfg.n, cfg.k, "normal")
     nc = copies_for(wq.numel())
     ws = [wq] + [wq.clone() for _ in range(nc - 1)]
@@ -245,7 +245,7 @@ def measure_rows(torch, kq):
     torch.cuda.empty_cache()
 
     # dequantize (q4_K 4096 x 4096 -> float16)
-    c1 = W.CFG1_Q4K_GEMV
+    c1 = W.Q4K_DECODE_GEMV
     wq = gpu_weights(torch, kq, c1.codec, c1.seed, c1.n, c1.k, c1.dist)
     out = torch.empty((c1.n, c1.k), dtype=torch.float16, device="cuda")
     nc = copies_for(wq.numel() + out.numel() * 2)
@@ -271,7 +271,7 @@ def bf16_rows(torch, kq):
     from gguf_quant_matmul_amd import workloads as W
 
     out = []
-    c1, c4, c5 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM, W.CFG5_MOE_SEG
+    c1, c4, c5 = W.Q4K_DECODE_GEMV, W.Q4K_PREFILL_GEMM, W.MOE_SEG_Q4K
     w1 = gpu_weights(torch, kq, c1.codec, c1.seed, c1.n, c1.k, c1.dist)
     nc = copies_for(w1.numel())
     ws = [w1] + [w1.clone() for _ in range(nc - 1)]
@@ -353,7 +353,7 @@ def codec_rows(torch, kq):
     # small prefill batches on the q4_K 14336 x 4096 weight (kq_quantized_matmul
     # routes M <= 16 to the GEMV, M <= 64 to the wide matrix-core GEMV, larger M
     # to the GEMM), weight copies rotated
-    c4 = W.CFG4_Q4K_GEMM
+    c4 = W.Q4K_PREFILL_GEMM
     w4 = gpu_weights(torch, kq, c4.codec, c4.seed, c4.n, c4.k, c4.dist)
     nc = copies_for(w4.numel())
     w4s = [w4] + [w4.clone() for _ in range(nc - 1)]
@@ -380,7 +380,7 @@ def codec_rows(torch, kq):
                  "TFLOP/s": round(flop / ms / 1e9, 1), "mfma_frac": round(flop / ms / 1e9 / MFMA_F16_PEAK_TFLOPS, 3)})
     del wq, xm, ym
     # the MoE segment workload with q5_K experts
-    c5 = W.CFG5_MOE_SEG
+    c5 = W.MOE_SEG_Q4K
     we = gpu_weights(torch, kq, "q5_k", c5.seed, c5.n_experts * c5.n, c5.k, "normal")
     nc = copies_for(we.numel())
     wes = [we] + [we.clone() for _ in range(nc - 1)]
@@ -414,7 +414,7 @@ def epilogue_rows(torch, kq):
     from gguf_quant_matmul_amd import workloads as W
 
     rows = []
-    c4 = W.CFG4_Q4K_GEMM
+    c4 = W.Q4K_PREFILL_GEMM
     m_pf, k_ffn, n_ffn = c4.m, c4.k, c4.n
 
     def row(name, workload, fused, plain, nl, flop, alg, extra=None):
@@ -479,7 +479,7 @@ def epilogue_rows(torch, kq):
     torch.cuda.empty_cache()
 
     # bias: q8_0 14336x4096, one row
-    c2 = W.CFG2_GEMV[0]
+    c2 = W.Q8_0_Q4_0_GEMVS[0]
     wq = gpu_weights(torch, kq, c2.codec, c2.seed, c2.n, c2.k, c2.dist)
     nb = wq.numel()
     nc = copies_for(nb)
@@ -507,7 +507,7 @@ def counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4):
     GEMMs, so one pass covers every HBM- and MFMA-bound row."""
     from gguf_quant_matmul_amd import workloads as W
 
-    c1, c4 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM
+    c1, c4 = W.Q4K_DECODE_GEMV, W.Q4K_PREFILL_GEMM
     src = torch.ones(COPY_REF_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
     for _ in range(4):
@@ -521,7 +521,7 @@ def counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4):
     torch.cuda.synchronize()
     launched = {"copy": 4, "qmv q4_K 4096x4096 M=1": len(w1s), "qmm q4_K 2048x14336x4096": 2}
 
-    for cfg in W.CFG2_GEMV:
+    for cfg in W.Q8_0_Q4_0_GEMVS:
         if cfg.m != 8:
             continue
         w = gpu_weights(torch, kq, cfg.codec, cfg.seed, cfg.n, cfg.k, cfg.dist)
@@ -533,7 +533,7 @@ def counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4):
         torch.cuda.synchronize()
         launched[f"qmv {cfg.codec} {cfg.n}x{cfg.k} M=8"] = 2
         del w
-    c3 = W.CFG3_Q6K_LMHEAD
+    c3 = W.Q6K_LMHEAD_GEMV
     w = gpu_weights(torch, kq, c3.codec, c3.seed, c3.n, c3.k, c3.dist)
     x = torch.from_numpy(W.gemv_activations(c3)).cuda()
     y = torch.empty((c3.m, c3.n), dtype=torch.float32, device="cuda")
@@ -544,7 +544,7 @@ def counters_pass(torch, kq, w1s, x1, y1, w4, x4, y4):
     del w
     torch.cuda.empty_cache()
 
-    c5 = W.CFG5_MOE_SEG
+    c5 = W.MOE_SEG_Q4K
     w = gpu_weights(torch, kq, c5.codec, c5.seed, c5.n_experts * c5.n, c5.k, "normal")
     r = W.routing(c5.seed, c5.tokens, c5.top_k, c5.n_experts)
     x = torch.from_numpy(W.activations(c5.seed, c5.tokens, c5.k)[r.token_of_row]).cuda()
@@ -596,9 +596,9 @@ def cpu_baseline():
                 "decode_ms": round(t_dec * 1e3, 2), "matmul_ms": round(t_mm * 1e3, 2),
                 "value": round(val, 5 if flop_rate else 3), "unit": unit}
 
-    c1, c3, c4, c5 = W.CFG1_Q4K_GEMV, W.CFG3_Q6K_LMHEAD, W.CFG4_Q4K_GEMM, W.CFG5_MOE_SEG
+    c1, c3, c4, c5 = W.Q4K_DECODE_GEMV, W.Q6K_LMHEAD_GEMV, W.Q4K_PREFILL_GEMM, W.MOE_SEG_Q4K
     cfgs = [one(c1.name, c1.codec, c1.seed, c1.n, c1.k, c1.dist, 1024, W.gemv_activations(c1), False, "GB/s")]
-    for c in W.CFG2_GEMV:
+    for c in W.Q8_0_Q4_0_GEMVS:
         if c.m in (1, 8):
             cfgs.append(one(c.name, c.codec, c.seed, c.n, c.k, c.dist, 1024, W.gemv_activations(c), False, "GB/s"))
     cfgs.append(one(c3.name, c3.codec, c3.seed, c3.n, c3.k, c3.dist, 1024, W.gemv_activations(c3), False, "GB/s"))
@@ -636,7 +636,7 @@ def main():
     dev_name = torch.cuda.get_device_properties(0).name
     log(f"device: {dev_name}")
 
-    c1, c4 = W.CFG1_Q4K_GEMV, W.CFG4_Q4K_GEMM
+    c1, c4 = W.Q4K_DECODE_GEMV, W.Q4K_PREFILL_GEMM
     log("preparing inputs (weights drawn on the host, encoded on the GPU by kq_quantize)")
     w1 = gpu_weights(torch, kq, c1.codec, c1.seed, c1.n, c1.k, c1.dist)
     n_cold = 64

@@ -139,13 +139,13 @@ class GemvConfig:
     out_dtype: str  # "f32" or "f16"
 
 
-CFG1_Q4K_GEMV = GemvConfig("q4_K decode GEMV 4096x4096", "q4_k", 4096, 4096, 1, 0, "normal", "f32")
-CFG2_GEMV = tuple(
+Q4K_DECODE_GEMV = GemvConfig("q4_K decode GEMV 4096x4096", "q4_k", 4096, 4096, 1, 0, "normal", "f32")
+Q8_0_Q4_0_GEMVS = tuple(
     GemvConfig(f"{c} GEMV 14336x4096 M={m}", c, 14336, 4096, m, 1, "normal", "f32")
     for c in ("q8_0", "q4_0") for m in (1, 2, 4, 8)
 )
-CFG3_Q6K_LMHEAD = GemvConfig("q6_K lm-head GEMV 128256x4096", "q6_k", 128256, 4096, 1, 2, "t5", "f32")
-CFG4_Q4K_GEMM = GemvConfig("q4_K prefill GEMM 2048x14336x4096", "q4_k", 14336, 4096, 2048, 3, "normal", "f16")
+Q6K_LMHEAD_GEMV = GemvConfig("q6_K lm-head GEMV 128256x4096", "q6_k", 128256, 4096, 1, 2, "t5", "f32")
+Q4K_PREFILL_GEMM = GemvConfig("q4_K prefill GEMM 2048x14336x4096", "q4_k", 14336, 4096, 2048, 3, "normal", "f16")
 
 
 # q5_K on the q4_K decode and prefill shapes (a widening of the codec set; seed 5)
@@ -172,7 +172,7 @@ class MoeConfig:
     out_dtype: str
 
 
-CFG5_MOE_SEG = MoeConfig("MoE gather_qmm_seg 512 tok top-8 of 64 experts, 1536x4096", "q4_k", 64, 1536, 4096, 512, 8, 4, "f16")
+MOE_SEG_Q4K = MoeConfig("MoE gather_qmm_seg 512 tok top-8 of 64 experts, 1536x4096", "q4_k", 64, 1536, 4096, 512, 8, 4, "f16")
 
 
 def gemv_activations(cfg: GemvConfig) -> np.ndarray:

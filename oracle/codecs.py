@@ -21,7 +21,7 @@ What the pages fix
     sub-block, fp16 d and dmin) and the q6_K one (16 sub-blocks of 16, int8
     scales, fp16 d) are stated with the workloads.
 
-Readings taken where the pages are silent (each is also listed in the design doc)
+Readings taken where the pages are silent
   R1  Byte layout inside a block: GGUF's (the README acknowledges ggml for the
       formats, the ``load_gguf`` docstring maps GGUF tensors zero-copy, and the
       CPU decoder is described as bit-exact against the ``gguf`` reference

@@ -1,6 +1,6 @@
 """Oracle: a plain round-to-nearest encoder for the codecs (CPU, NumPy).
 
-Test infrastructure only (see ``oracle/__init__``).  It makes the configs'
+Test infrastructure only (see ``oracle/__init__``).  It makes the workloads'
 weights; it is not part of the decode contract.
 
 What the pages fix: only the interface (mlx-kquant ``bindings.cpp`` page,
@@ -8,7 +8,7 @@ What the pages fix: only the interface (mlx-kquant ``bindings.cpp`` page,
 block size go to uint8 wire bytes; an optional importance vector steers the
 encoder; it is not used here).  The algorithm is not on the pages.
 
-Reading taken (listed in the design doc as reading R5): plain deterministic
+Reading R5, taken where the pages are silent: plain deterministic
 round-to-nearest against the STORED (fp16-rounded) block parameters.  Every
 arithmetic step is IEEE fp32 with round-to-nearest-even, in the order written,
 so that any other implementation that performs the same fp32 operations gets

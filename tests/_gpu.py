@@ -5,7 +5,8 @@ import sys
 import numpy as np
 
 # The fp64-oracle tolerance for matmul outputs: per output row,
-# max_n |y - ref| / max_n |ref| <= 2e-3 (tolerance reading).
+# max_n |y - ref| / max_n |ref| <= 2e-3 (the pages' maximum relative error read per
+# row: an element-wise relative error is unbounded near zero outputs).
 TOL = 2e-3
 
 

@@ -137,7 +137,7 @@ def test_bf16_workloads_full(kq, which):
     import torch
 
     if which in ("gemv", "gemm"):
-        c = W.CFG1_Q4K_GEMV if which == "gemv" else W.CFG4_Q4K_GEMM
+        c = W.Q4K_DECODE_GEMV if which == "gemv" else W.Q4K_PREFILL_GEMM
         wq, ob = _encoded(kq, c.codec, c.seed, c.n, c.k)
         x = W.activations_bf16(c.seed, c.m, c.k)
         out = "f32" if which == "gemv" else "bf16"
@@ -146,7 +146,7 @@ def test_bf16_workloads_full(kq, which):
         (kq.kq_qmv if which == "gemv" else kq.kq_qmm)(c.codec, wq, c.n, c.k, _devb(x), y)
         assert_close_bf16(_got(y), F.qmatmul(c.codec, ob, c.k, x), out, what=f"bf16 {c.name}")
     else:
-        c = W.CFG5_MOE_SEG
+        c = W.MOE_SEG_Q4K
         wq, ob = _encoded(kq, c.codec, c.seed, c.n_experts * c.n, c.k)
         r = W.routing(c.seed, c.tokens, c.top_k, c.n_experts)
         x = W.activations_bf16(c.seed, c.tokens, c.k)[r.token_of_row]

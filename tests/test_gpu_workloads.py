@@ -51,7 +51,7 @@ def _encoded(kq, codec, seed, n, k, dist="normal"):
     return wq, ob
 
 
-GEMV_CFGS = [W.CFG1_Q4K_GEMV, *W.CFG2_GEMV, W.CFG3_Q6K_LMHEAD, W.CFG4_Q4K_GEMM,
+GEMV_CFGS = [W.Q4K_DECODE_GEMV, *W.Q8_0_Q4_0_GEMVS, W.Q6K_LMHEAD_GEMV, W.Q4K_PREFILL_GEMM,
              W.Q5K_GEMV, W.Q5K_GEMM, *W.LEGACY_GEMV, W.Q2K_GEMV, W.Q3K_GEMV]
 
 
@@ -91,7 +91,7 @@ def test_gemv_gemm_workload(kq, cfg):
 def test_moe_seg_workload(kq):
     import torch
 
-    cfg = W.CFG5_MOE_SEG
+    cfg = W.MOE_SEG_Q4K
     rows_w = cfg.n_experts * cfg.n
     say(f"workload {cfg.name}: encoding (GPU and oracle)")
     wq, ob = _encoded(kq, cfg.codec, cfg.seed, rows_w, cfg.k)
@@ -161,7 +161,7 @@ def test_glu_prefill_workload(kq):
     # + 100), 2048 x 14336 x 4096 and 16 x 14336 x 4096, float16 out, silu
     import torch
 
-    c = W.CFG4_Q4K_GEMM
+    c = W.Q4K_PREFILL_GEMM
     say("workload GLU prefill: encoding (GPU and oracle)")
     wg, og = _encoded(kq, c.codec, c.seed, c.n, c.k)
     wu, ou = _encoded(kq, c.codec, c.seed + 100, c.n, c.k)
@@ -189,7 +189,7 @@ def test_residual_prefill_workload(kq):
     # (seed + 201) updated in place, float16
     import torch
 
-    c = W.CFG4_Q4K_GEMM
+    c = W.Q4K_PREFILL_GEMM
     n, k = c.k, c.n
     say("workload residual prefill: encoding (GPU and oracle)")
     wd, od = _encoded(kq, c.codec, c.seed + 200, n, k)
@@ -212,7 +212,7 @@ def test_small_prefill_workload(kq):
     # and four activation operands; 128: the GEMM)
     import torch
 
-    c = W.CFG4_Q4K_GEMM
+    c = W.Q4K_PREFILL_GEMM
     say("workload small prefill: encoding (GPU and oracle)")
     wq, ob = _encoded(kq, c.codec, c.seed, c.n, c.k)
     xa = W.gemv_activations(c)

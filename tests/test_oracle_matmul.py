@@ -93,7 +93,7 @@ def test_tile_map_capacity_is_tight_bound():
 
 
 def test_moe_workload_routing_and_tiles():
-    cfg = workloads.CFG5_MOE_SEG
+    cfg = workloads.MOE_SEG_Q4K
     r = workloads.routing(cfg.seed, cfg.tokens, cfg.top_k, cfg.n_experts)
     assert r.sorted_ids.size == 4096
     assert np.all(np.diff(r.sorted_ids.astype(np.int64)) >= 0)
