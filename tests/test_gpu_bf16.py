@@ -74,6 +74,23 @@ def test_bf16_qmv_qmm_parity(kq, codec):
         assert_close_bf16(_got(yq), ref, "f32", what=f"bf16 quantized_matmul {codec} m={m}")
 
 
+@pytest.mark.parametrize("codec", ["q4_k", "q6_k", "q8_0", "q4_0"])
+def test_bf16_long_k(kq, codec):
+    # K = 14336 (a down projection): the GEMV's sixteen waves each walk seven
+    # groups of four K steps, the matmul tile 112 staged chunks
+    import torch
+
+    k, n = 14336, 72
+    w = F.random_bytes(codec, n, k, 81)
+    for m in (2, 40):
+        x = _xb(m, k, 82 + m)
+        ref = F.qmatmul(codec, w, k, x)
+        say(f"bf16 long K {codec} m={m}")
+        y = torch.full((m, n), float("nan"), dtype=torch.float32, device="cuda")
+        (kq.kq_qmv if m <= 16 else kq.kq_qmm)(codec, dev(w), n, k, _devb(x), y)
+        assert_close_bf16(_got(y), ref, "f32", what=f"bf16 long K {codec} m={m}")
+
+
 @pytest.mark.parametrize("scale", [2.0 ** -60, 2.0 ** 60])
 def test_bf16_activations_outside_f16_range(kq, scale):
     import torch
