@@ -153,8 +153,9 @@ def test_dequantize_golden_blocks(kq, name):
 
 def _shapes_qmv(codec):
     # (8300, 1024): one or two rows take the streaming GEMV (N >= 8192, K <= 4096), 8300 rows a ragged last block
+    # (8200, 768): three superblocks, so q3_K and q6_K rows start 2 bytes off a dword on every other row
     if codec in SUPER:
-        return [(37, 512), (300, 256 * 17), (8200, K_WIDE), (8300, 1024)]   # 17 superblocks: q6_K rows only 2-byte aligned
+        return [(37, 512), (300, 256 * 17), (8200, K_WIDE), (8300, 1024), (8200, 768)]   # 17 superblocks: q6_K rows only 2-byte aligned
     return [(37, 96), (300, 4160), (45, 2048 + 32), (8200, K_WIDE), (8300, 1024)]  # 96 and 2080: odd block counts -> generic kernel
 
 
