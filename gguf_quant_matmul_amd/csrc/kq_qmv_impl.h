@@ -313,6 +313,127 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stream_kernel(const uint8_t* 
   }
 }
 
+// One activation row on a tall matrix with 16-byte aligned rows: a wave per
+// row, as in qmv_stream_kernel, but the row reaches the lanes through LDS.
+// The units' own loads (16-byte fields scattered over a block, several per
+// 128-byte line) run the lm-head's weight stream at 78 us where a plain read
+// of the same bytes takes 64 us; read as consecutive 16-byte pieces per lane
+// with the nontemporal hint, the same bytes stream at the plain-read rate.
+// So each wave copies its row into its own LDS buffer with such loads (the
+// next row's pieces in flight in registers while the current row is
+// dotted) and the units load their fields from the LDS copy.
+__host__ __device__ constexpr int64_t qmv_stage_xbytes(int64_t k) {
+  return ((int64_t)xpad((int)k) * 2 + (k / 16) * 4 + 15) / 16 * 16;
+}
+// 16-byte pieces per lane that cover a row of K <= 4096 values
+template <int C>
+__host__ __device__ constexpr int qmv_stage_pieces() {
+  return (Geo<C>::BB * (4096 / Geo<C>::BV) + 1023) / 1024;
+}
+// One activation row, K <= 4096 (the whole row of x in LDS), and at least
+// 4096 weight rows: q4_K 4096 x 4096 4.54 -> 4.46 us, the q6_K lm-head 80 ->
+// 70 us, q8_0 14336 x 4096 13.2 -> 12.1 us against the one-pass and
+// streaming kernels.
+__host__ inline bool qmv_stage_use(int64_t n, int64_t k) { return k <= 4096 && n >= 4096; }
+template <int C>
+__host__ inline bool qmv_stage_ok(const void* w, int64_t rb) {
+  return ((uintptr_t)w & 15) == 0 && rb % 16 == 0 && rb <= qmv_stage_pieces<C>() * 64 * 16;
+}
+
+template <int C, bool F16>
+__global__ __launch_bounds__(QMV_THREADS) void qmv_stage_kernel(const uint8_t* __restrict__ w, int n, int k,
+                                                                int64_t row_bytes, const half_t* __restrict__ x,
+                                                                void* __restrict__ y, int nblocks) {
+  typedef typename UnitOf<C>::T Unit;
+  constexpr int NPL = qmv_stage_pieces<C>();
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  half_t* xs = (half_t*)smem;
+  const int xstride = xpad(k);
+  float* xsum = (float*)(smem + (size_t)xstride * 2);
+  const int sstride = k / 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ue = k / 64;
+  const int np = (int)(row_bytes / 16);  // 16-byte pieces per row
+  uint8_t* wl = smem + qmv_stage_xbytes(k) + (int64_t)wave * row_bytes;  // this wave's row copy
+  auto row_of = [&](int b) { return b * (QMV_THREADS / 64) + wave; };
+
+  // the pieces of one row, lane l taking pieces l + 64 i (indices past the
+  // row re-read its last piece and are not stored)
+  auto issue = [&](u32x4* pr, int row) __attribute__((always_inline)) {
+    const u32x4* src = (const u32x4*)(w + (int64_t)(row < n ? row : n - 1) * row_bytes);
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int p = lane + 64 * i;
+      pr[i] = __builtin_nontemporal_load(src + (p < np ? p : np - 1));
+    }
+  };
+  // the row's pieces into the wave's buffer: the previous row's unit fields
+  // were read from it before that row's dot, earlier in the wave's program
+  // order (a wave's LDS accesses are performed in order)
+  auto stage = [&](const u32x4* pr) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const int p = lane + 64 * i;
+      if (p < np) *(u32x4*)(wl + 16 * p) = pr[i];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  auto xv_of = [&]() { return Xv{xs, xsum, xstride, sstride, 0}; };
+  auto row_dot = [&](int b) __attribute__((always_inline)) {
+    const int row = row_of(b);
+    const int u = lane < ue ? lane : ue - 1;
+    Unit un;
+    un.load(wl, u);
+    float acc[1] = {0.f};
+    if (lane < ue) un.template dot<1>(u, xv_of(), acc);
+    acc[0] = lanes_sum<64>(acc[0]);
+    if (row < n && lane == 0) {
+      if (F16)
+        ((half_t*)y)[row] = (half_t)acc[0];
+      else
+        ((float*)y)[row] = acc[0];
+    }
+  };
+
+  // x first (its loads retire before the weights'), then the first rows' pieces
+  constexpr int XPT = 4096 / 8 / QMV_THREADS;
+  const int xpieces = k / 8;
+  u32x4 xr[XPT];
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    int c = tid + i * QMV_THREADS;
+    c = c < xpieces ? c : xpieces - 1;
+    xr[i] = *(const u32x4*)(x + (int64_t)c * 8);
+  }
+  const int g = gridDim.x;
+  int b = blockIdx.x;
+  u32x4 pa[NPL];
+  issue(pa, row_of(b));
+#pragma unroll
+  for (int i = 0; i < XPT; ++i) {
+    const int c = tid + i * QMV_THREADS;
+    const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0)
+    float s = 0.f;
+    s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
+    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+    if (c < xpieces) {
+      const int v = xperm<C>(c * 8);
+      *(u32x4*)(xs + xpad(v)) = xr[i];
+      if ((c & 1) == 0) xsum[v >> 4] = s;
+    }
+  }
+  __syncthreads();
+
+  for (; b < nblocks; b += g) {
+    stage(pa);
+    if (b + g < nblocks) issue(pa, row_of(b + g));  // uniform
+    row_dot(b);
+  }
+}
+
 // GEMV with the matmul epilogue (residual, gate, bias), and the GLU product
 // of two matrices sharing x (mlx-kquant bindings.cpp page,
 // quantized_matmul_residual / _qmv_bias / _glu docstrings), on the dot2 body:
@@ -632,6 +753,21 @@ hipError_t launch_stream(const uint8_t* w, int64_t n, int64_t k, int64_t rb, con
   return launch_stream_pd<C, M, LPR, 1>(w, n, k, rb, x, y, f16, s);
 }
 
+template <int C>
+hipError_t launch_stage(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
+                        hipStream_t s) {
+  const int64_t nblocks = (n + QMV_THREADS / 64 - 1) / (QMV_THREADS / 64);
+  const size_t lds = (size_t)qmv_stage_xbytes(k) + (size_t)(QMV_THREADS / 64) * rb;
+  const dim3 grid((unsigned)qmv_stream_grid(1, nblocks));
+  if (f16)
+    hipLaunchKernelGGL((qmv_stage_kernel<C, true>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
+                       (int)nblocks);
+  else
+    hipLaunchKernelGGL((qmv_stage_kernel<C, false>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
+                       (int)nblocks);
+  return hipGetLastError();
+}
+
 // Three or more activation rows (five or more for q8_0) go to the matrix
 // cores.  Fewer take the dot2 kernel: one wave per row (64 lanes, one 64-value unit each at
 // K = 4096) for one activation row and a matrix with few rows (four times
@@ -647,6 +783,7 @@ hipError_t launch_m(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
   if constexpr (M >= mma_from) {
     return launch_mma<C, M>(w, n, k, rb, x, y, f16, s);
   } else {
+    if (M == 1 && qmv_stage_use(n, k) && qmv_stage_ok<C>(w, rb)) return launch_stage<C>(w, n, k, rb, x, y, f16, s);
     if (qmv_stream_ok(M, n, k)) return launch_stream<C, M, (M == 1 ? 64 : 16)>(w, n, k, rb, x, y, f16, s);
     if (M == 1 && n <= 32768) return launch_ml<C, M, 64>(w, n, k, rb, x, y, f16, s);
     return launch_ml<C, M, 16>(w, n, k, rb, x, y, f16, s);

@@ -154,9 +154,13 @@ def test_dequantize_golden_blocks(kq, name):
 def _shapes_qmv(codec):
     # (8300, 1024): one or two rows take the streaming GEMV (N >= 8192, K <= 4096), 8300 rows a ragged last block
     # (8200, 768): three superblocks, so q3_K and q6_K rows start 2 bytes off a dword on every other row
+    # (4102, 2048): rows a multiple of 16 bytes for every codec, so one row takes the LDS-staged GEMV, 4102
+    # rows a ragged last block of four
     if codec in SUPER:
-        return [(37, 512), (300, 256 * 17), (8200, K_WIDE), (8300, 1024), (8200, 768)]   # 17 superblocks: q6_K rows only 2-byte aligned
-    return [(37, 96), (300, 4160), (45, 2048 + 32), (8200, K_WIDE), (8300, 1024)]  # 96 and 2080: odd block counts -> generic kernel
+        return [(37, 512), (300, 256 * 17), (8200, K_WIDE), (8300, 1024), (8200, 768),   # 17 superblocks: q6_K rows only 2-byte aligned
+                (4102, 2048)]
+    return [(37, 96), (300, 4160), (45, 2048 + 32), (8200, K_WIDE), (8300, 1024),  # 96 and 2080: odd block counts -> generic kernel
+            (4102, 2048)]
 
 
 @pytest.mark.parametrize("codec", CODECS)
