@@ -313,8 +313,9 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stream_kernel(const uint8_t* 
   }
 }
 
-// One activation row on a tall matrix with 16-byte aligned rows: a wave per
-// row, as in qmv_stream_kernel, but the row reaches the lanes through LDS.
+// One to four activation rows on a matrix of at least 4096 rows whose rows
+// are a multiple of 16 bytes: a wave per weight row, as in qmv_stream_kernel
+// for one activation row, but the row reaches the lanes through LDS.
 // The units' own loads (16-byte fields scattered over a block, several per
 // 128-byte line) run the lm-head's weight stream at 78 us where a plain read
 // of the same bytes takes 64 us; read as consecutive 16-byte pieces per lane
@@ -322,25 +323,34 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stream_kernel(const uint8_t* 
 // So each wave copies its row into its own LDS buffer with such loads (the
 // next row's pieces in flight in registers while the current row is
 // dotted) and the units load their fields from the LDS copy.
-__host__ __device__ constexpr int64_t qmv_stage_xbytes(int64_t k) {
-  return ((int64_t)xpad((int)k) * 2 + (k / 16) * 4 + 15) / 16 * 16;
+__host__ __device__ constexpr int64_t qmv_stage_xbytes(int m, int64_t k) {
+  return (m * ((int64_t)xpad((int)k) * 2 + (k / 16) * 4) + 15) / 16 * 16;
 }
 // 16-byte pieces per lane that cover a row of K <= 4096 values
 template <int C>
 __host__ __device__ constexpr int qmv_stage_pieces() {
   return (Geo<C>::BB * (4096 / Geo<C>::BV) + 1023) / 1024;
 }
-// One activation row, K <= 4096 (the whole row of x in LDS), and at least
-// 4096 weight rows: q4_K 4096 x 4096 4.54 -> 4.46 us, the q6_K lm-head 80 ->
-// 70 us, q8_0 14336 x 4096 13.2 -> 12.1 us against the one-pass and
-// streaming kernels.
+// K <= 4096 (the activation rows whole in LDS) and at least 4096 weight
+// rows.  One or two rows: against the one-pass and streaming kernels, q4_K
+// 4096 x 4096 4.50 -> 4.40 us, the q6_K lm-head 81 -> 70 us, q8_0 14336 x
+// 4096 13.2 -> 12.1 us (M = 1) and 16.7 -> 13.4 us (M = 2).  Three rows, and
+// four for the codecs whose matrix-core decode is dearest, against the
+// matrix-core GEMV (14336 x 4096 unless noted): q3_K 26.2 -> 14.1 us (M = 3)
+// and 26.3 -> 17.9 us (M = 4), q6_K 25.8 -> 15.9 / 26.0 -> 20.2, q8_0 22.5 ->
+// 17.8 / 24.0 -> 19.1, q5_K 18.9 -> 14.8 / 19.0 -> 17.3, q4_K 4096 x 4096
+// 7.20 -> 6.23 at M = 3 but 7.32 -> 7.71 at M = 4.
+template <int C>
+__host__ __device__ constexpr int qmv_stage_max_m() {
+  return C == Q8_0 || C == Q5_K || C == Q3_K || C == Q6_K || C == Q5_0 ? 4 : 3;
+}
 __host__ inline bool qmv_stage_use(int64_t n, int64_t k) { return k <= 4096 && n >= 4096; }
 template <int C>
 __host__ inline bool qmv_stage_ok(const void* w, int64_t rb) {
   return ((uintptr_t)w & 15) == 0 && rb % 16 == 0 && rb <= qmv_stage_pieces<C>() * 64 * 16;
 }
 
-template <int C, bool F16>
+template <int C, int M, bool F16>
 __global__ __launch_bounds__(QMV_THREADS) void qmv_stage_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                                 int64_t row_bytes, const half_t* __restrict__ x,
                                                                 void* __restrict__ y, int nblocks) {
@@ -349,13 +359,13 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stage_kernel(const uint8_t* _
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   half_t* xs = (half_t*)smem;
   const int xstride = xpad(k);
-  float* xsum = (float*)(smem + (size_t)xstride * 2);
+  float* xsum = (float*)(smem + (size_t)M * xstride * 2);
   const int sstride = k / 16;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ue = k / 64;
   const int np = (int)(row_bytes / 16);  // 16-byte pieces per row
-  uint8_t* wl = smem + qmv_stage_xbytes(k) + (int64_t)wave * row_bytes;  // this wave's row copy
+  uint8_t* wl = smem + qmv_stage_xbytes(M, k) + (int64_t)wave * row_bytes;  // this wave's row copy
   auto row_of = [&](int b) { return b * (QMV_THREADS / 64) + wave; };
 
   // the pieces of one row, lane l taking pieces l + 64 i (indices past the
@@ -387,26 +397,34 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stage_kernel(const uint8_t* _
     const int u = lane < ue ? lane : ue - 1;
     Unit un;
     un.load(wl, u);
-    float acc[1] = {0.f};
-    if (lane < ue) un.template dot<1>(u, xv_of(), acc);
-    acc[0] = lanes_sum<64>(acc[0]);
-    if (row < n && lane == 0) {
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.f;
+    if (lane < ue) un.template dot<M>(u, xv_of(), acc);
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = lanes_sum<64>(acc[m]);
+    if (row < n && lane < M) {
+      float v = acc[0];
+#pragma unroll
+      for (int m = 1; m < M; ++m)
+        if (lane == m) v = acc[m];
       if (F16)
-        ((half_t*)y)[row] = (half_t)acc[0];
+        ((half_t*)y)[(int64_t)lane * n + row] = (half_t)v;
       else
-        ((float*)y)[row] = acc[0];
+        ((float*)y)[(int64_t)lane * n + row] = v;
     }
   };
 
   // x first (its loads retire before the weights'), then the first rows' pieces
-  constexpr int XPT = 4096 / 8 / QMV_THREADS;
-  const int xpieces = k / 8;
+  // piece c of x: row m = c / kp, K offset 8 (c - m kp)
+  constexpr int XPT = M * 4096 / 8 / QMV_THREADS;
+  const int kp = k / 8, xpieces = M * kp;
   u32x4 xr[XPT];
 #pragma unroll
   for (int i = 0; i < XPT; ++i) {
     int c = tid + i * QMV_THREADS;
     c = c < xpieces ? c : xpieces - 1;
-    xr[i] = *(const u32x4*)(x + (int64_t)c * 8);
+    xr[i] = *(const u32x4*)(x + (int64_t)c * 8);  // rows are contiguous: row m, K offset v at m k + v = 8 c
   }
   const int g = gridDim.x;
   int b = blockIdx.x;
@@ -420,9 +438,12 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stage_kernel(const uint8_t* _
     s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
     s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
     if (c < xpieces) {
-      const int v = xperm<C>(c * 8);
-      *(u32x4*)(xs + xpad(v)) = xr[i];
-      if ((c & 1) == 0) xsum[v >> 4] = s;
+      int m = 0;
+#pragma unroll
+      for (int j = 1; j < M; ++j) m += c >= j * kp ? 1 : 0;
+      const int v = xperm<C>((c - m * kp) * 8);
+      *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
+      if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
     }
   }
   __syncthreads();
@@ -753,17 +774,17 @@ hipError_t launch_stream(const uint8_t* w, int64_t n, int64_t k, int64_t rb, con
   return launch_stream_pd<C, M, LPR, 1>(w, n, k, rb, x, y, f16, s);
 }
 
-template <int C>
+template <int C, int M>
 hipError_t launch_stage(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const half_t* x, void* y, int f16,
                         hipStream_t s) {
   const int64_t nblocks = (n + QMV_THREADS / 64 - 1) / (QMV_THREADS / 64);
-  const size_t lds = (size_t)qmv_stage_xbytes(k) + (size_t)(QMV_THREADS / 64) * rb;
+  const size_t lds = (size_t)qmv_stage_xbytes(M, k) + (size_t)(QMV_THREADS / 64) * rb;
   const dim3 grid((unsigned)qmv_stream_grid(1, nblocks));
   if (f16)
-    hipLaunchKernelGGL((qmv_stage_kernel<C, true>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
+    hipLaunchKernelGGL((qmv_stage_kernel<C, M, true>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
                        (int)nblocks);
   else
-    hipLaunchKernelGGL((qmv_stage_kernel<C, false>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
+    hipLaunchKernelGGL((qmv_stage_kernel<C, M, false>), grid, dim3(QMV_THREADS), lds, s, w, (int)n, (int)k, rb, x, y,
                        (int)nblocks);
   return hipGetLastError();
 }
@@ -780,10 +801,11 @@ hipError_t launch_m(const uint8_t* w, int64_t n, int64_t k, int64_t rb, const ha
   // q8_0's decode costs the matrix path more per byte: its dot2 kernel is
   // still the faster one at four rows.
   constexpr int mma_from = C == Q8_0 ? 5 : 3;
+  if constexpr (M <= qmv_stage_max_m<C>())
+    if (qmv_stage_use(n, k) && qmv_stage_ok<C>(w, rb)) return launch_stage<C, M>(w, n, k, rb, x, y, f16, s);
   if constexpr (M >= mma_from) {
     return launch_mma<C, M>(w, n, k, rb, x, y, f16, s);
   } else {
-    if (M == 1 && qmv_stage_use(n, k) && qmv_stage_ok<C>(w, rb)) return launch_stage<C>(w, n, k, rb, x, y, f16, s);
     if (qmv_stream_ok(M, n, k)) return launch_stream<C, M, (M == 1 ? 64 : 16)>(w, n, k, rb, x, y, f16, s);
     if (M == 1 && n <= 32768) return launch_ml<C, M, 64>(w, n, k, rb, x, y, f16, s);
     return launch_ml<C, M, 16>(w, n, k, rb, x, y, f16, s);
