@@ -58,6 +58,16 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// Sum over the 64 lanes of a wave, complete in lane 63 only: DPP row sums,
+// then row_bcast:15 (row r - 1's last lane into rows 1 and 3) and
+// row_bcast:31 (lane 31 into rows 2 and 3), without an LDS round trip.
+__device__ __forceinline__ float wave_sum_last(float v) {
+  v = row16_sum(v);
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xA, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x143, 0xC, 0xF, false));
+  return v;
+}
+
 // Sum over the LPR lanes of a row: DPP within 16-lane rows, then swaps
 // across them.
 template <int LPR>
@@ -402,16 +412,15 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stage_kernel(const uint8_t* _
     for (int m = 0; m < M; ++m) acc[m] = 0.f;
     if (lane < ue) un.template dot<M>(u, xv_of(), acc);
 #pragma unroll
-    for (int m = 0; m < M; ++m) acc[m] = lanes_sum<64>(acc[m]);
-    if (row < n && lane < M) {
-      float v = acc[0];
+    for (int m = 0; m < M; ++m) acc[m] = wave_sum_last(acc[m]);
+    if (row < n && lane == 63) {
 #pragma unroll
-      for (int m = 1; m < M; ++m)
-        if (lane == m) v = acc[m];
-      if (F16)
-        ((half_t*)y)[(int64_t)lane * n + row] = (half_t)v;
-      else
-        ((float*)y)[(int64_t)lane * n + row] = v;
+      for (int m = 0; m < M; ++m) {
+        if (F16)
+          ((half_t*)y)[(int64_t)m * n + row] = (half_t)acc[m];
+        else
+          ((float*)y)[(int64_t)m * n + row] = acc[m];
+      }
     }
   };
 
