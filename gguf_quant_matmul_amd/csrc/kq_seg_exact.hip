@@ -75,6 +75,13 @@ __device__ __forceinline__ void sx_for(F&& f) {
   }
 }
 
+// LDS (address space 3) views: a 32-bit LDS byte address and the 16-byte
+// fragment it points at.
+typedef __attribute__((address_space(3))) const half8_t lds_half8_t;
+__device__ __forceinline__ uint32_t lds_addr(const half_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const half_t*)p;
+}
+
 // Bits 3 and 4 of a 16-byte chunk index exchanged.
 __device__ __forceinline__ int sx_swap34(int c) { return (c & ~24) | ((c & 8) << 1) | ((c & 16) >> 1); }
 
@@ -192,31 +199,47 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
   const int pc = tid & 31, prow = tid >> 5;
   const int lc = sx_swap34(pc ^ prow);
   const int xvoff0 = prow * k * 2 + lc * 16, xvoff1 = prow * k * 2 + (lc ^ 16) * 16;
-  u32x4 xr[XPT];
-  auto load_x = [&](int sb) __attribute__((always_inline)) {
+  // Double-buffered chunks stage the next superblock in two halves of the
+  // pieces (loaded at the chunk start and mid-chunk, each stored a half chunk
+  // later), so only half of them occupy registers at a time; single-buffered
+  // chunks hold all of them until every wave has read the chunk.
+  constexpr int XH = DB ? XPT / 2 : XPT;  // pieces per staging half
+  static_assert(XPT % 2 == 0, "staging halves");
+  u32x4 xr[XH];
+  auto load_x = [&](int sb, auto hc) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
     const int so = min(sb, nsb - 1) * 512;
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) xr[i] = bld16(xrs, (i & 1 ? xvoff1 : xvoff0) + i * 8 * 2 * k, so);
+    for (int h = 0; h < XH; ++h) {
+      const int i = H * XH + h;
+      // each piece's offset is formed here from an opaque base, so the
+      // compiler does not keep all of them in registers across the chunk
+      int vo = i & 1 ? xvoff1 : xvoff0;
+      asm volatile("" : "+v"(vo));
+      xr[h] = bld16(xrs, vo + i * 8 * 2 * k, so);
+    }
   };
   // Store the staged pieces of superblock sb into buffer sb & 1 and their
   // sub-block sums (float32 over 32 values: four lanes' 8 each) into window
   // buffer (sb >> 1) & 1 at position cu * 4 + (sb & 1) * 2 + e of the row's
   // hi and lo halves for sub-block j = 2 cu + e.  An odd piece's sub-block is
   // j ^ 4, which moves its slots by 24 (hi) and 8 (lo) from the even pieces'.
-  auto store_x = [&](int sb) __attribute__((always_inline)) {
+  auto store_x = [&](int sb, auto hc) __attribute__((always_inline)) {
+    constexpr int H = decltype(hc)::value;
     half_t* xb = xs + (DB ? (sb & 1) * XBUF : 0);
     uint16_t* wb = xw + ((sb >> 1) & 1) * WBUF;
     const int j = lc >> 2, pos = (j >> 1) * 4 + (sb & 1) * 2 + (j & 1);
     const int w0 = sx_wslot(prow, pos >> 2) + (pos & 3);  // even pieces' hi; lo is w0 ^ 16
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
+    for (int h = 0; h < XH; ++h) {
+      const int i = H * XH + h;
       const int row = prow + 8 * i;
-      *(u32x4*)(xb + row * SX_KC + 8 * pc) = xr[i];
+      *(u32x4*)(xb + row * SX_KC + 8 * pc) = xr[h];
       float s = 0.f;
-      s = dot2(xr[i].x, 0x3C003C00u, s);
-      s = dot2(xr[i].y, 0x3C003C00u, s);
-      s = dot2(xr[i].z, 0x3C003C00u, s);
-      s = dot2(xr[i].w, 0x3C003C00u, s);
+      s = dot2(xr[h].x, 0x3C003C00u, s);
+      s = dot2(xr[h].y, 0x3C003C00u, s);
+      s = dot2(xr[h].z, 0x3C003C00u, s);
+      s = dot2(xr[h].w, 0x3C003C00u, s);
       s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
       s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, true));
       if ((pc & 3) == 0) {
@@ -227,16 +250,25 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
       }
     }
   };
+  const auto h0 = std::integral_constant<int, 0>{};
+  const auto h1 = std::integral_constant<int, 1>{};
 
-  load_x(0);
+  // prologue: superblock 0's activations and the first NS superblocks' weights
   UnitQ4K ring[NS][RG];
-#pragma unroll
-  for (int p = 0; p < NS; ++p) {
-    __builtin_amdgcn_sched_barrier(0);
-    refill(ring[p], p);
-  }
+  load_x(0, h0);
   __builtin_amdgcn_sched_barrier(0);
-  store_x(0);
+  refill(ring[0], 0);
+  __builtin_amdgcn_sched_barrier(0);
+  store_x(0, h0);
+  if constexpr (DB) {
+    load_x(0, h1);
+    __builtin_amdgcn_sched_barrier(0);
+    refill(ring[1], 1);
+    __builtin_amdgcn_sched_barrier(0);
+    store_x(0, h1);
+  } else {
+    refill(ring[1], 1);
+  }
   __syncthreads();
 
   // physical chunk of this lane's fragment reads: swap34(8 cu + S) ^ r
@@ -247,10 +279,19 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
   u32x2 bh[RG], bl[RG];
 
   // Superblock sb (L = sb & 1 its place in the window and its ring slot).
+  // The activation fragments of step S + 1 are read from LDS while step S is
+  // decoded and multiplied, so each step waits on reads issued a step earlier.
   auto chunk = [&](auto lc, int sb) __attribute__((always_inline)) {
     constexpr int L = decltype(lc)::value;
     const half_t* cur = xs + (DB ? L * XBUF : 0);
-    load_x(sb + 1);  // stored after this chunk's products
+    // x loads first, then the refill of the slot the previous chunk decoded
+    // (superblock sb + 1; at sb = 0 the same bytes the prologue loaded), so a
+    // wait for the x pieces does not wait for these weights
+    load_x(sb + 1, h0);
+    if constexpr (DB) {
+      __builtin_amdgcn_sched_barrier(0);
+      refill(ring[L ^ 1], sb + 1);
+    }
     UnitQ4K* slot = ring[L];
     SxConst c[RG];
 #pragma unroll
@@ -259,23 +300,48 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
       bh[j][L] = c[j].bh;
       bl[j][L] = c[j].bl;
     }
+    // Activation fragments of step S + 1 are read into the other register set
+    // before step S's products, so their LDS latency runs under step S.
+    half8_t a[2][XG];
+    // The byte address of chunk ca ^ S of row r is a0 ^ 16 S (the chunk bits
+    // lie below the row and buffer bits); a0 is made opaque at every step so
+    // the eight addresses are not all held in registers.
+    const uint32_t a0 = lds_addr(cur + r * SX_KC + 8 * ca);
+    auto read_a = [&](half8_t* dst, auto sc) __attribute__((always_inline)) {
+      constexpr int S = decltype(sc)::value;
+      uint32_t ab = a0;
+      asm volatile("" : "+v"(ab));
+      const lds_half8_t* p = (const lds_half8_t*)(uintptr_t)(ab ^ (16u * S));
+#pragma unroll
+      for (int i = 0; i < XG; ++i) dst[i] = p[i * SX_KC * 2];  // rows 16 i + r: 16 i * 512 bytes
+    };
+    read_a(a[0], std::integral_constant<int, 0>{});
     auto step = [&](auto sc) __attribute__((always_inline)) {
       constexpr int S = decltype(sc)::value;
+      if constexpr (S < 7) {
+        read_a(a[(S + 1) & 1], std::integral_constant<int, S + 1>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
       half8_t b[RG];
 #pragma unroll
       for (int j = 0; j < RG; ++j) b[j] = sx_slice<S>(slot[j], c[j]);
-      if constexpr (S == 7) {
+      if constexpr (!DB && S == 7) {
         // every step of the superblock is decoded: refill its registers
         __builtin_amdgcn_sched_barrier(0);
         refill(slot, sb + NS);
       }
 #pragma unroll
       for (int i = 0; i < XG; ++i) {
-        const int row = 16 * i + r;
-        const half8_t a = *(const half8_t*)(cur + row * SX_KC + 8 * (ca ^ S));
 #pragma unroll
         for (int j = 0; j < RG; ++j)
-          part[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b[j], S == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : part[j][i], 0, 0, 0);
+          part[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[S & 1][i], b[j],
+                                                              S == 0 ? float4_t{0.f, 0.f, 0.f, 0.f} : part[j][i], 0, 0, 0);
+      }
+      if constexpr (DB && S == 3) {
+        // the first half of the next superblock's pieces into the free buffer
+        __builtin_amdgcn_sched_barrier(0);
+        store_x(sb + 1, h0);
+        load_x(sb + 1, h1);
       }
     };
     sx_for<8>(step);
@@ -306,8 +372,12 @@ __device__ __forceinline__ void sx_tile(const uint8_t* __restrict__ wbase, int n
     }
     // double-buffered: the other buffers were last read before the previous
     // barrier; single-buffered: wait until every wave has read this chunk
-    if constexpr (!DB) __syncthreads();
-    store_x(sb + 1);
+    if constexpr (DB) {
+      store_x(sb + 1, h1);
+    } else {
+      __syncthreads();
+      store_x(sb + 1, h0);
+    }
     __syncthreads();
   };
   for (int sb = 0; sb < nsb; sb += 2) {
