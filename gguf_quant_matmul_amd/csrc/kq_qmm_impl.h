@@ -72,6 +72,15 @@ __device__ __forceinline__ int seg_off(int u, int t) {
 
 __device__ __forceinline__ half2_t h2(half_t a) { return half2_t{a, a}; }
 
+// f(integral_constant<int, 0>) ... f(integral_constant<int, N - 1>), in order
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
 // 16 bytes at a 2-byte-aligned address: dwords from the dword-aligned address
 // below it (never past the 16 bytes), shifted by sh = addr & 3 bytes.
 struct Raw16 {
@@ -515,15 +524,15 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
   const int brow0 = wave * RPW + min(lane >> 1, RPW - 1);
   const uint8_t* const wrow0 = wbase + (int64_t)min(n0 + brow0, n - 1) * row_bytes;
 
-  auto issue_a = [&](int slot, int u) {
+  auto issue_a = [&](int slot, int u) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       const int part = a_part(tid + i * QMM_THREADS);
       areg[slot][i] = *(const u32x4*)(xrow[i] + seg_off<C>(u, part >> 1));
     }
   };
-  auto issue_b = [&](int slot, int u) { braw[slot][0].load(wrow0, u, lane & 1); };
-  auto stage = [&](int sa, int sb, int buf, int u) {
+  auto issue_b = [&](int slot, int u) __attribute__((always_inline)) { braw[slot][0].load(wrow0, u, lane & 1); };
+  auto stage = [&](int sa, int sb, int buf, int u) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < A_PER_T; ++i) {
       const int c = tid + i * QMM_THREADS;
@@ -533,37 +542,60 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
     }
     if (lane < 2 * RPW) braw[sb][0].store(u, lane & 1, LdsRow{Bs[buf], BN * 32, brow0});
   };
-  // All fragment reads of a 32-wide K slice are issued before its MFMAs, in
-  // the order the MFMAs consume them, so one LDS round trip per slice is
-  // exposed instead of one per A fragment.  Full tiles take a copy without
-  // the dead-fragment test.
-  auto mfma_slice = [&](int buf, int ks, auto full) {
+  // Fragment reads.  A step's first 32-wide K slice reads all its fragments
+  // before its MFMAs, in the order the MFMAs consume them.  Every later slice's
+  // fragments are read into the registers of the slice before, right after
+  // their last use there: A fragment i once row group i's products have
+  // issued, B fragment j once the last row group's product with it has.  So
+  // that slice's LDS latency runs under the rest of the slice before, with
+  // no extra registers.  Full tiles take a copy without the dead-fragment
+  // test.
+  const int fr = lane & 15, fc = lane >> 4;
+  auto rd_a = [&](half8_t& d, int buf, int ks, int i) __attribute__((always_inline)) {
+    d = *(const half8_t*)(As[buf] + lds_off(BM * 32, wr0 + 16 * i + fr, 4 * ks + fc));
+  };
+  auto rd_b = [&](half8_t& d, int buf, int ks, int j) __attribute__((always_inline)) {
+    d = *(const half8_t*)(Bs[buf] + lds_off(BN * 32, wc0 + 16 * j + fr, 4 * ks + fc));
+  };
+  auto mfma_steps = [&](int buf, auto full) __attribute__((always_inline)) {
     constexpr bool FULL = decltype(full)::value;
-    const int c = 4 * ks + (lane >> 4), r = lane & 15;
+    constexpr int NKS = BK / 32;
     half8_t a[TM], b[TN];
-    a[0] = *(const half8_t*)(As[buf] + lds_off(BM * 32, wr0 + r, c));
+    rd_a(a[0], buf, 0, 0);
 #pragma unroll
-    for (int j = 0; j < TN; ++j) b[j] = *(const half8_t*)(Bs[buf] + lds_off(BN * 32, wc0 + 16 * j + r, c));
+    for (int j = 0; j < TN; ++j) rd_b(b[j], buf, 0, j);
 #pragma unroll
-    for (int i = 1; i < TM; ++i) a[i] = *(const half8_t*)(As[buf] + lds_off(BM * 32, wr0 + 16 * i + r, c));
+    for (int i = 1; i < TM; ++i) rd_a(a[i], buf, 0, i);
     asm volatile("" ::: "memory");  // keep every read above the MFMAs (the scheduler would sink them)
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      if (FULL || i < live_tm) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    }
+    static_for<NKS>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int ks = decltype(kc)::value;
+      constexpr bool more = ks + 1 < NKS;
+      static_for<TM>([&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        const bool live = FULL || i < live_tm;
+        static_for<TN>([&](auto jc) __attribute__((always_inline)) {
+          constexpr int j = decltype(jc)::value;
+          if (live) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[i], b[j], acc[i][j], 0, 0, 0);
+          if constexpr (more && i == TM - 1) {
+            __builtin_amdgcn_sched_barrier(0);
+            rd_b(b[j], buf, ks + 1, j);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
+        if constexpr (more) {
+          __builtin_amdgcn_sched_barrier(0);
+          rd_a(a[i], buf, ks + 1, i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    });
   };
   const bool full_rows = live_tm == TM;
-  auto mfma_step = [&](int buf) {
-    if (full_rows) {
-#pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) mfma_slice(buf, ks, std::true_type{});
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < BK / 32; ++ks) mfma_slice(buf, ks, std::false_type{});
-    }
+  auto mfma_step = [&](int buf) __attribute__((always_inline)) {
+    if (full_rows)
+      mfma_steps(buf, std::true_type{});
+    else
+      mfma_steps(buf, std::false_type{});
   };
 
   // Waves w and w+4 share a SIMD: the first four stage the next step before
@@ -580,7 +612,7 @@ __global__ __launch_bounds__(QMM_THREADS) void qmm_kernel(const uint8_t* __restr
   stage(0, 0, 0, 0);
   __syncthreads();
   const int units_main = units - units % UNR;
-  auto kloop = [&](auto sf) {
+  auto kloop = [&](auto sf) __attribute__((always_inline)) {
     constexpr bool SF = decltype(sf)::value;
     for (int u0 = 0; u0 < units_main; u0 += UNR) {
 #pragma unroll
