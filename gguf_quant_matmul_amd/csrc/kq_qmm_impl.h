@@ -128,14 +128,9 @@ template <> struct HalfUnit<Q4_K> {
     const uint32_t qw[4] = {q.x, q.y, q.z, q.w};
     uint32_t lo[8], hi[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t l = qw[i] & 0x0F0F0F0Fu, t = (qw[i] >> 4) & 0x0F0F0F0Fu;
-      const half2_t l01 = as_h2(pair01(l)), l23 = as_h2(pair23(l));
-      const half2_t t01 = as_h2(pair01(t)), t23 = as_h2(pair23(t));
-      lo[2 * i] = pack_h2(fmaf((float)l01.x, s0, c0), fmaf((float)l01.y, s0, c0));
-      lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, s0, c0), fmaf((float)l23.y, s0, c0));
-      hi[2 * i] = pack_h2(fmaf((float)t01.x, s1, c1), fmaf((float)t01.y, s1, c1));
-      hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, s1, c1), fmaf((float)t23.y, s1, c1));
+    for (int i = 0; i < 2; ++i) {
+      slice8(qw[2 * i] & 0x0F0F0F0Fu, qw[2 * i + 1] & 0x0F0F0F0Fu, s0, c0, lo + 4 * i);
+      slice8((qw[2 * i] >> 4) & 0x0F0F0F0Fu, (qw[2 * i + 1] >> 4) & 0x0F0F0F0Fu, s1, c1, hi + 4 * i);
     }
     st_chunk(dst, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
     st_chunk(dst, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
@@ -168,12 +163,9 @@ template <> struct HalfUnit<Q2_K> {
       const float s = d * (float)(b & 15u), c = -(1024.f * s + dmin * (float)(b >> 4));
       uint32_t o[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t code = (qw[4 * g + i] >> shift) & 0x03030303u;
-        const half2_t c01 = as_h2(pair01(code)), c23 = as_h2(pair23(code));
-        o[2 * i] = pack_h2(fmaf((float)c01.x, s, c), fmaf((float)c01.y, s, c));
-        o[2 * i + 1] = pack_h2(fmaf((float)c23.x, s, c), fmaf((float)c23.y, s, c));
-      }
+      for (int i = 0; i < 2; ++i)
+        slice8((qw[4 * g + 2 * i] >> shift) & 0x03030303u, (qw[4 * g + 2 * i + 1] >> shift) & 0x03030303u, s, c,
+               o + 4 * i);
       st_chunk(dst, 4 * hh + 2 * g, u32x4{o[0], o[1], o[2], o[3]});
       st_chunk(dst, 4 * hh + 2 * g + 1, u32x4{o[4], o[5], o[6], o[7]});
     }
@@ -206,14 +198,12 @@ template <> struct HalfUnit<Q3_K> {
     for (int g = 0; g < 2; ++g) {  // shift c0 + g: sub-block 2g + hh, segment 2g + hh
       const float s = d * (float)q3k_scale(A, B, up, 2 * g + hh), c = -1028.f * s;
       const int c2 = c0 + g;
-      uint32_t o[8];
+      uint32_t code[4], o[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t code = ((Q[i] >> (2 * c2)) & 0x03030303u) | (((H[i] >> (4 * h + c2)) & 0x01010101u) << 2);
-        const half2_t c01 = as_h2(pair01(code)), c23 = as_h2(pair23(code));
-        o[2 * i] = pack_h2(fmaf((float)c01.x, s, c), fmaf((float)c01.y, s, c));
-        o[2 * i + 1] = pack_h2(fmaf((float)c23.x, s, c), fmaf((float)c23.y, s, c));
-      }
+      for (int i = 0; i < 4; ++i)
+        code[i] = ((Q[i] >> (2 * c2)) & 0x03030303u) | (((H[i] >> (4 * h + c2)) & 0x01010101u) << 2);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) slice8(code[2 * i], code[2 * i + 1], s, c, o + 4 * i);
       st_chunk(dst, 4 * g + 2 * hh, u32x4{o[0], o[1], o[2], o[3]});
       st_chunk(dst, 4 * g + 2 * hh + 1, u32x4{o[4], o[5], o[6], o[7]});
     }
@@ -240,18 +230,17 @@ template <> struct HalfUnit<Q5_K> {
     const float s1 = d * (float)sc1, c1 = -(1024.f * s1 + dmin * (float)m1);
     const uint32_t qw[4] = {q.x, q.y, q.z, q.w}, qe[4] = {e.x, e.y, e.z, e.w};
     const int j0 = 2 * (u & 3);
-    uint32_t lo[8], hi[8];
+    uint32_t l[4], t[4], lo[8], hi[8];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t qhs = qe[i] >> j0;
-      const uint32_t l = (qw[i] & 0x0F0F0F0Fu) | ((qhs << 4) & 0x10101010u);
-      const uint32_t t = ((qw[i] >> 4) & 0x0F0F0F0Fu) | ((qhs << 3) & 0x10101010u);
-      const half2_t l01 = as_h2(pair01(l)), l23 = as_h2(pair23(l));
-      const half2_t t01 = as_h2(pair01(t)), t23 = as_h2(pair23(t));
-      lo[2 * i] = pack_h2(fmaf((float)l01.x, s0, c0), fmaf((float)l01.y, s0, c0));
-      lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, s0, c0), fmaf((float)l23.y, s0, c0));
-      hi[2 * i] = pack_h2(fmaf((float)t01.x, s1, c1), fmaf((float)t01.y, s1, c1));
-      hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, s1, c1), fmaf((float)t23.y, s1, c1));
+      l[i] = (qw[i] & 0x0F0F0F0Fu) | ((qhs << 4) & 0x10101010u);
+      t[i] = ((qw[i] >> 4) & 0x0F0F0F0Fu) | ((qhs << 3) & 0x10101010u);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      slice8(l[2 * i], l[2 * i + 1], s0, c0, lo + 4 * i);
+      slice8(t[2 * i], t[2 * i + 1], s1, c1, hi + 4 * i);
     }
     st_chunk(dst, 2 * hh, u32x4{lo[0], lo[1], lo[2], lo[3]});
     st_chunk(dst, 2 * hh + 1, u32x4{lo[4], lo[5], lo[6], lo[7]});
@@ -408,13 +397,9 @@ struct HalfUnitLeg {
       // fma((1024 + q), d, m - 1024 d) in float32, rounded once to float16
       const float d = f16_to_f32(w0), c = fmaf(-1024.f, d, f16_to_f32(w0 >> 16));
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const half2_t l01 = as_h2(pair01(leg_lo<C>(q[i], qh, i))), l23 = as_h2(pair23(leg_lo<C>(q[i], qh, i)));
-        const half2_t t01 = as_h2(pair01(leg_hi<C>(q[i], qh, i))), t23 = as_h2(pair23(leg_hi<C>(q[i], qh, i)));
-        lo[2 * i] = pack_h2(fmaf((float)l01.x, d, c), fmaf((float)l01.y, d, c));
-        lo[2 * i + 1] = pack_h2(fmaf((float)l23.x, d, c), fmaf((float)l23.y, d, c));
-        hi[2 * i] = pack_h2(fmaf((float)t01.x, d, c), fmaf((float)t01.y, d, c));
-        hi[2 * i + 1] = pack_h2(fmaf((float)t23.x, d, c), fmaf((float)t23.y, d, c));
+      for (int i = 0; i < 2; ++i) {
+        slice8(leg_lo<C>(q[2 * i], qh, 2 * i), leg_lo<C>(q[2 * i + 1], qh, 2 * i + 1), d, c, lo + 4 * i);
+        slice8(leg_hi<C>(q[2 * i], qh, 2 * i), leg_hi<C>(q[2 * i + 1], qh, 2 * i + 1), d, c, hi + 4 * i);
       }
     } else {
       // (1024 + q - 1024 - ZP) is the exact code; times d, one rounding

@@ -578,28 +578,6 @@ template <> struct UnitOf<Q5_1> { typedef UnitLeg<Q5_1> T; };
 // Matrix-core operand slices of a unit.
 // ---------------------------------------------------------------------------
 
-// Eight codes (two dwords of code bytes) -> eight float16 weights
-// fma(1024 + code, s, c), each rounded to float32 and then to float16 (both to
-// nearest even): per byte pair one v_perm_b32 builds the float16 pair
-// (1024 + code), two v_fma_mix_f32 take its halves through the affine map,
-// one v_cvt_pk_f16_f32 packs the results.  The float32 results pass through
-// an empty register-only asm statement so the compiler does not fold each map
-// and conversion into v_fma_mixlo/hi_f16, which write half a register and
-// issue at about half the rate of this sequence on gfx950.
-__device__ __forceinline__ void slice8(uint32_t c0, uint32_t c1, float s, float c, uint32_t f[4]) {
-  const uint32_t p[4] = {pair01(c0), pair23(c0), pair01(c1), pair23(c1)};
-  float v[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const half2_t h = as_h2(p[i]);
-    v[2 * i] = fmaf((float)h.x, s, c);
-    v[2 * i + 1] = fmaf((float)h.y, s, c);
-  }
-  asm("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f[i] = pack_h2(v[2 * i], v[2 * i + 1]);
-}
-
 // Slice S (8 consecutive K values) of a unit: get<S> gives its float16
 // weights f[4] (all zero for a lane that keeps nothing); koff(u) is the row
 // offset of the unit's first value and xstep<S> the slice's offset from it in
