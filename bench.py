@@ -41,9 +41,9 @@ COPY_REF_BYTES = 256 << 20     # the elementwise copy that scales the HBM byte c
 # copy of COPY_REF_BYTES).  A figure is reported only while the digest of the
 # kernel's sources still matches the one the counters were taken on.
 TRAFFIC = {
-    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "39a29c630b848e4d",
-            "bytes": 9594209},
-    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "9ff5d4f674e5acb5", "bytes": 357273946},
+    "qmv": {"sources": ("kq_qmv.hip", "kq_qmv_impl.h", "kq_units.h", "kq_decode.h", "kq_internal.h"), "digest": "8455c3aae673d5e0",
+            "bytes": 9587926},
+    "qmm": {"sources": ("kq_qmm.hip", "kq_qmm_impl.h", "kq_internal.h", "kq_decode.h"), "digest": "487a56eec2c3c32a", "bytes": 357300037},
 }
 
 
@@ -720,7 +720,7 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic("qmv"),
-            "kernel": "kq_qmv q4_K (qmv_kernel<12,1,false>)", "alg_bytes_per_launch": alg1,
+            "kernel": "kq_qmv q4_K (qmv_stage_kernel<q4_K, M=1>)", "alg_bytes_per_launch": alg1,
             "mean_launch_us": round(ms1 * 1e3, 3),
             "median_launch_us": round(float(np.median(per1)) * 1e3, 3),
             "p90_launch_us": round(float(np.percentile(per1, 90)) * 1e3, 3),
@@ -731,7 +731,7 @@ def main():
             "p90_launch_us": round(float(np.percentile(per4, 90)) * 1e3, 2),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": MFMA_F16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tflops / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic("qmm"),
-                         "kernel": "kq_qmm q4_K (qmm_kernel)", "alg_flop_per_launch": flop4,
+                         "kernel": "kq_qmm q4_K (qmm_kernel<q4_K, 256, 224>)", "alg_flop_per_launch": flop4,
                          "alg_bytes_per_launch": alg4},
         },
         "timing": "HIP graphs: one replay = 64 GEMVs over distinct cold weight copies (back to back on one "

@@ -466,9 +466,12 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stage_kernel(const uint8_t* _
 
 // GEMV with the matmul epilogue (residual, gate, bias), and the GLU product
 // of two matrices sharing x (mlx-kquant bindings.cpp page,
-// quantized_matmul_residual / _qmv_bias / _glu docstrings), on the dot2 body:
-// the epilogue for every M <= 8, the GLU product for M <= QMV_GLU_MAX_M (two
-// matrices' units for more rows overflow the registers; those take the GEMM).
+// quantized_matmul_residual / _qmv_bias / _glu docstrings), on the dot2 body.
+// The callers route the residual epilogue here for M <= 2 (q8_0: M <= 4), and
+// for M <= 8 when K is not a multiple of 64; 3 .. 8 rows otherwise take the
+// 16-row matrix-core GEMV and 9 .. 64 the wide one, each with the same store.
+// The GLU product takes this body for M <= QMV_GLU_MAX_M (two matrices' units
+// for more rows overflow the registers).
 template <int C, int M, int LPR, bool F16>
 __global__ __launch_bounds__(QMV_THREADS) void qmv_epi_kernel(const uint8_t* __restrict__ w, int n, int k,
                                                               int64_t row_bytes, const half_t* __restrict__ x,
