@@ -745,6 +745,13 @@ def main():
     rd = plain_read(torch, kq, w1s, n_cold)
     out["roofline"]["read_ceiling"] = {"us": rd["us"], "GB/s": rd["GB/s"], "groups": rd["groups"],
                                        "gemv_over_read": round(ms1 * 1e3 / rd["us"], 3)}
+    # the launch floor of that protocol: the same graph of back-to-back launches
+    # of a near-empty kernel (one workgroup reading 16 bytes)
+    tiny = torch.zeros((16,), dtype=torch.uint8, device="cuda")
+    tout = torch.empty((4,), dtype=torch.int32, device="cuda")
+    gl = capture(torch, lambda: [kq.kq_stream_read(tiny, tout) for _ in range(n_cold)])
+    out["roofline"]["launch_floor_us"] = round(time_graph(torch, gl, n_cold, 5) * 1e3, 2)
+    del gl, tiny, tout
     del w1s, w1, w4, x4, y4
     torch.cuda.empty_cache()
     if not args.no_rows:
