@@ -728,15 +728,28 @@ template <> struct MmaSlices<Q6_K> {
   }
 };
 
+// Eight codes -> eight float16 weights d (code - k), for codecs whose weight
+// is the scale times an exact integer: the byte permute builds 1024 + code,
+// the packed subtract of k is exact, and the packed multiply by d rounds the
+// exact product once to nearest even -- the same bits as slice8's float32
+// FMA and conversion (d (code - k) is exact in float32), in two packed
+// operations per pair instead of three.  d2 holds d in both halves, k2 holds
+// k (an integer below 2048) in both halves.
+__device__ __forceinline__ void slice8_dq(uint32_t c0, uint32_t c1, uint32_t k2, uint32_t d2, uint32_t f[4]) {
+  const uint32_t p[4] = {pair01(c0), pair23(c0), pair01(c1), pair23(c1)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[i] = as_u32((as_h2(p[i]) - as_h2(k2)) * as_h2(d2));
+}
+
 template <> struct MmaSlices<Q8_0> {
   // block b = S >> 2 (values 32 b ..); code + 128 from a sign-bit flip; weight = d q
   uint32_t c[2][8];
-  float d[2];
+  uint32_t d[2];  // the block's float16 d in both halves (zero for a lane that keeps nothing)
   __device__ __forceinline__ MmaSlices(const UnitQ8_0& un, int, bool keep) {
     const uint32_t R[17] = {un.r0.x, un.r0.y, un.r0.z, un.r0.w, un.r1.x, un.r1.y, un.r1.z, un.r1.w,
                             un.r2.x, un.r2.y, un.r2.z, un.r2.w, un.r3.x, un.r3.y, un.r3.z, un.r3.w, un.r4};
-    d[0] = keep ? f16_to_f32(R[0]) : 0.f;
-    d[1] = keep ? f16_to_f32(R[8] >> 16) : 0.f;
+    d[0] = keep ? perm(R[0], R[0], 0x01000100u) : 0u;
+    d[1] = keep ? perm(R[8], R[8], 0x03020302u) : 0u;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       c[0][i] = alignbyte(R[i + 1], R[i], 2) ^ 0x80808080u;
@@ -749,7 +762,7 @@ template <> struct MmaSlices<Q8_0> {
   template <int S>
   __device__ __forceinline__ void get(uint32_t f[4]) const {
     constexpr int b = S >> 2, t = S & 3;
-    slice8(c[b][2 * t], c[b][2 * t + 1], d[b], -1152.f * d[b], f);
+    slice8_dq(c[b][2 * t], c[b][2 * t + 1], 0x64806480u, d[b], f);  // (1024 + 128 + q) - 1152 = q
   }
 };
 
@@ -757,11 +770,11 @@ template <> struct MmaSlices<Q4_0> {
   // block b = S >> 2: values 0..15 low nibbles of its 16 bytes, 16..31 high;
   // weight = d (q - 8).  High nibbles are used in place (16 q) with step d / 16.
   uint32_t q[2][4];
-  float d[2];
+  uint32_t d[2];  // the block's float16 d in both halves (zero for a lane that keeps nothing)
   __device__ __forceinline__ MmaSlices(const UnitQ4_0& un, int, bool keep) {
     const uint32_t R[9] = {un.r0.x, un.r0.y, un.r0.z, un.r0.w, un.r1.x, un.r1.y, un.r1.z, un.r1.w, un.r2};
-    d[0] = keep ? f16_to_f32(R[0]) : 0.f;
-    d[1] = keep ? f16_to_f32(R[4] >> 16) : 0.f;
+    d[0] = keep ? perm(R[0], R[0], 0x01000100u) : 0u;
+    d[1] = keep ? perm(R[4], R[4], 0x03020302u) : 0u;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       q[0][i] = alignbyte(R[i + 1], R[i], 2);
@@ -774,10 +787,10 @@ template <> struct MmaSlices<Q4_0> {
   template <int S>
   __device__ __forceinline__ void get(uint32_t f[4]) const {
     constexpr int b = S >> 2, t = S & 3, dw = 2 * (t & 1);
-    if (t < 2)  // fma(1024 + q, d, -1032 d) = d (q - 8)
-      slice8(q[b][dw] & 0x0F0F0F0Fu, q[b][dw + 1] & 0x0F0F0F0Fu, d[b], -1032.f * d[b], f);
-    else  // fma(1024 + 16 q, d / 16, -72 d) = d (q - 8)
-      slice8(q[b][dw] & 0xF0F0F0F0u, q[b][dw + 1] & 0xF0F0F0F0u, 0.0625f * d[b], -72.f * d[b], f);
+    if (t < 2)  // ((1024 + q) - 1032) d = d (q - 8)
+      slice8_dq(q[b][dw] & 0x0F0F0F0Fu, q[b][dw + 1] & 0x0F0F0F0Fu, 0x64086408u, d[b], f);
+    else  // the high nibbles shifted down, same map
+      slice8_dq((q[b][dw] >> 4) & 0x0F0F0F0Fu, (q[b][dw + 1] >> 4) & 0x0F0F0F0Fu, 0x64086408u, d[b], f);
   }
 };
 
