@@ -364,4 +364,28 @@ hipError_t launch_seg_bf16(int codec, const uint8_t* w, int64_t ne, int64_t n, i
                            int64_t rows, const uint32_t* map, const uint32_t* counts, int64_t cap, void* y, int out,
                            hipStream_t s);
 
+
+// Row m and piece r of the 16-byte activation pieces c, c + step, c + 2 step,
+// ... of a block whose rows hold kp pieces each: one division for the first
+// piece, then an exact carry per step (c + step = (m + step / kp) kp + r +
+// step % kp, and r + step % kp < 2 kp), instead of a division by the run-time
+// kp for every piece.
+struct PieceWalk {
+  int m, r, kp, qs, rs;
+  __device__ __forceinline__ PieceWalk(int c, int kp_, int step) : kp(kp_) {
+    m = c / kp;
+    r = c - m * kp;
+    qs = step / kp;
+    rs = step - qs * kp;
+  }
+  __device__ __forceinline__ void next() {
+    m += qs;
+    r += rs;
+    if (r >= kp) {
+      r -= kp;
+      ++m;
+    }
+  }
+};
+
 }  // namespace kq

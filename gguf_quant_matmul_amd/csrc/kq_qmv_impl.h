@@ -611,23 +611,24 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_kernel(const uint8_t* __r
     constexpr int XPT = (M * KC / 8 + MMA_THREADS - 1) / MMA_THREADS;
     const int xpieces = M * (kc / 8);
     u32x4 xr[XPT];
+    {
+      PieceWalk pw(tid, kc / 8, MMA_THREADS);  // pieces past the block re-read its last one
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      int c = tid + i * MMA_THREADS;
-      c = c < xpieces ? c : xpieces - 1;
-      const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
-      xr[i] = *(const u32x4*)(x + (int64_t)m * k + c0 + v);
+      for (int i = 0; i < XPT; ++i, pw.next()) {
+        const bool in = tid + i * MMA_THREADS < xpieces;
+        const int m = in ? pw.m : M - 1, v = (in ? pw.r : kc / 8 - 1) * 8;
+        xr[i] = *(const u32x4*)(x + (int64_t)m * k + c0 + v);
+      }
     }
     Unit ring[MMA_PD];
 #pragma unroll
     for (int p = 0; p < MMA_PD; ++p) ring[p].load(wrow, min(ub + 4 * (g0 + p) + cu, last));
     if (c0) __syncthreads();  // previous chunk done with LDS
+    {
+      PieceWalk pw(tid, kc / 8, MMA_THREADS);
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int c = tid + i * MMA_THREADS;
-      if (c < xpieces) {
-        const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
-        *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
+      for (int i = 0; i < XPT; ++i, pw.next()) {
+        if (tid + i * MMA_THREADS < xpieces) *(u32x4*)(xs + pw.m * xstride + xpad(pw.r * 8)) = xr[i];
       }
     }
     __syncthreads();

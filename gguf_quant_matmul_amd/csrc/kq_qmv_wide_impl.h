@@ -86,21 +86,22 @@ __global__ __launch_bounds__(MMA_THREADS) void qmv_mma_wide_kernel(const uint8_t
     constexpr int XPT = (MT * KC / 8 + MMA_THREADS - 1) / MMA_THREADS;
     const int xpieces = m * (kc / 8);
     u32x4 xr[XPT];
+    {
+      PieceWalk pw(tid, kc / 8, MMA_THREADS);  // pieces past the block re-read its last one
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      int c = tid + i * MMA_THREADS;
-      c = c < xpieces ? c : xpieces - 1;
-      const int mr = c / (kc / 8), v = (c % (kc / 8)) * 8;
-      xr[i] = *(const u32x4*)(x + (int64_t)mr * k + c0 + v);
+      for (int i = 0; i < XPT; ++i, pw.next()) {
+        const bool in = tid + i * MMA_THREADS < xpieces;
+        const int mr = in ? pw.m : m - 1, v = (in ? pw.r : kc / 8 - 1) * 8;
+        xr[i] = *(const u32x4*)(x + (int64_t)mr * k + c0 + v);
+      }
     }
     if (c0 + KC < k) load_chunk(c0 + KC, nxt);  // uniform across the block
     if (c0) __syncthreads();  // previous chunk done with LDS
+    {
+      PieceWalk pw(tid, kc / 8, MMA_THREADS);
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int c = tid + i * MMA_THREADS;
-      if (c < xpieces) {
-        const int mr = c / (kc / 8), v = (c % (kc / 8)) * 8;
-        *(u32x4*)(xs + mr * xstride + xpad(v)) = xr[i];
+      for (int i = 0; i < XPT; ++i, pw.next()) {
+        if (tid + i * MMA_THREADS < xpieces) *(u32x4*)(xs + pw.m * xstride + xpad(pw.r * 8)) = xr[i];
       }
     }
     __syncthreads();
