@@ -125,12 +125,14 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
     constexpr int XPT = (M * KC / 8 + QMV_THREADS - 1) / QMV_THREADS;
     const int xpieces = M * (kc / 8);
     u32x4 xr[XPT];
+    {
+      PieceWalk pw(tid, kc / 8, QMV_THREADS);  // pieces past the block re-read its last one
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      int c = tid + i * QMV_THREADS;
-      c = c < xpieces ? c : xpieces - 1;
-      const int m = c / (kc / 8), v = (c % (kc / 8)) * 8;
-      xr[i] = *(const u32x4*)(x + (int64_t)m * k + c0 + v);
+      for (int i = 0; i < XPT; ++i, pw.next()) {
+        const bool in = tid + i * QMV_THREADS < xpieces;
+        const int m = in ? pw.m : M - 1, v = (in ? pw.r : kc / 8 - 1) * 8;
+        xr[i] = *(const u32x4*)(x + (int64_t)m * k + c0 + v);
+      }
     }
     Unit cur[UNROLL], cur2[NW == 2 ? UNROLL : 1];
 #pragma unroll
@@ -143,17 +145,20 @@ __device__ __forceinline__ void qmv_rows(const uint8_t* __restrict__ w, int n, i
     // Stage x and its 16-value sums in one pass: pieces 2g and 2g + 1 (8
     // values each) sit in adjacent lanes, so each lane sums its own 8 values
     // and adds its neighbour's with a DPP quad permutation [1, 0, 3, 2].
+    {
+      PieceWalk pw(tid, kc / 8, QMV_THREADS);
 #pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-      const int c = tid + i * QMV_THREADS;
-      const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0)
-      float s = 0.f;
-      s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
-      s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
-      if (c < xpieces) {
-        const int m = c / (kc / 8), v = xperm<C>((c % (kc / 8)) * 8);
-        *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
-        if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
+      for (int i = 0; i < XPT; ++i, pw.next()) {
+        const int c = tid + i * QMV_THREADS;
+        const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0)
+        float s = 0.f;
+        s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
+        s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+        if (c < xpieces) {
+          const int m = pw.m, v = xperm<C>(pw.r * 8);
+          *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
+          if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
+        }
       }
     }
     __syncthreads();
@@ -262,28 +267,33 @@ __global__ __launch_bounds__(QMV_THREADS) void qmv_stream_kernel(const uint8_t* 
   constexpr int XPT = (M * 4096 / 8 + QMV_THREADS - 1) / QMV_THREADS;
   const int xpieces = M * (k / 8);
   u32x4 xr[XPT];
+  {
+    PieceWalk pw(tid, k / 8, QMV_THREADS);  // pieces past x re-read its last one
 #pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    int c = tid + i * QMV_THREADS;
-    c = c < xpieces ? c : xpieces - 1;
-    const int m = c / (k / 8), v = (c % (k / 8)) * 8;
-    xr[i] = *(const u32x4*)(x + (int64_t)m * k + v);
+    for (int i = 0; i < XPT; ++i, pw.next()) {
+      const bool in = tid + i * QMV_THREADS < xpieces;
+      const int m = in ? pw.m : M - 1, v = (in ? pw.r : k / 8 - 1) * 8;
+      xr[i] = *(const u32x4*)(x + (int64_t)m * k + v);
+    }
   }
   int b = blockIdx.x;
   Unit ring[PD][UNROLL];
 #pragma unroll
   for (int p = 0; p < PD; ++p) load_block(ring[p], min(b + p * (int)gridDim.x, nblocks - 1));
+  {
+    PieceWalk pw(tid, k / 8, QMV_THREADS);
 #pragma unroll
-  for (int i = 0; i < XPT; ++i) {
-    const int c = tid + i * QMV_THREADS;
-    const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0)
-    float s = 0.f;
-    s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
-    s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
-    if (c < xpieces) {
-      const int m = c / (k / 8), v = xperm<C>((c % (k / 8)) * 8);
-      *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
-      if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
+    for (int i = 0; i < XPT; ++i, pw.next()) {
+      const int c = tid + i * QMV_THREADS;
+      const uint32_t one2 = 0x3C003C00u;  // (1.0, 1.0)
+      float s = 0.f;
+      s = dot2(xr[i].x, one2, s); s = dot2(xr[i].y, one2, s); s = dot2(xr[i].z, one2, s); s = dot2(xr[i].w, one2, s);
+      s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, false));
+      if (c < xpieces) {
+        const int m = pw.m, v = xperm<C>(pw.r * 8);
+        *(u32x4*)(xs + m * xstride + xpad(v)) = xr[i];
+        if ((c & 1) == 0) xsum[m * sstride + (v >> 4)] = s;
+      }
     }
   }
   __syncthreads();
